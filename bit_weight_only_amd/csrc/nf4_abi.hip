@@ -1,0 +1,196 @@
+// nf4_abi.hip -- the exported C entry points declared in include/nf4.h:
+// host-side validation, codebook preparation, launch on the caller's stream.
+//
+// Conventions follow the vibevoice.c README: a kernel call is launches on the
+// caller's stream and nothing else (no allocation, free or sync; "The speech
+// front end"), never the legacy default stream by the library's own choice
+// ("The decode step is one submission"), split-K partials live in the
+// caller's scratch ("Quantization" > "Weights", M > 1 bullet), and failures
+// are named status codes.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/nf4.h"
+#include "nf4_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr int64_t kMaxGemvM = 8;
+constexpr int64_t kMaxGemmM = int64_t(1) << 23;
+
+bool shape_ok(int64_t N, int64_t K) {
+  if (N < nf4::kTileRows || N % nf4::kTileRows != 0) return false;
+  if (K < nf4::kBlock || K % nf4::kBlock != 0) return false;
+  if (N > kMaxDim || K > kMaxDim) return false;
+  return N * K <= kMaxElems;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+uint32_t f32_bits(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return u;
+}
+
+float bits_f32(uint32_t u) {
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+// fp32 -> bf16 with ties to even (inputs are finite).
+uint16_t bf16_rne(float f) {
+  uint32_t u = f32_bits(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+float bf16_value(uint16_t h) { return bits_f32((uint32_t)h << 16); }
+
+// Split every code into up to three bf16 terms whose sum is the fp32 value
+// exactly.  Returns the number of terms needed (1 or 3), or 0 when a code is
+// not finite or cannot be split exactly.
+int split_codebook(const float *cb, nf4::CodeTerms &ct) {
+  int nterm = 1;
+  for (int i = 0; i < 16; ++i) {
+    const float c = cb[i];
+    if (!isfinite(c)) return 0;
+    const uint16_t t0 = bf16_rne(c);
+    const float r0 = c - bf16_value(t0);
+    const uint16_t t1 = bf16_rne(r0);
+    const float r1 = r0 - bf16_value(t1);
+    const uint16_t t2 = bf16_rne(r1);
+    const double sum = (double)bf16_value(t0) + (double)bf16_value(t1) + (double)bf16_value(t2);
+    if (!isfinite(bf16_value(t0)) || sum != (double)c) return 0;
+    ct.t[0][i] = t0;
+    ct.t[1][i] = t1;
+    ct.t[2][i] = t2;
+    if (bf16_value(t1) != 0.0f || bf16_value(t2) != 0.0f) nterm = 3;
+  }
+  return nterm;
+}
+
+nf4_status from_hip(hipError_t e) { return e == hipSuccess ? NF4_OK : NF4_ERR_HIP; }
+
+nf4_status check_linear_args(const uint16_t *x, int64_t M, const uint8_t *qw, const float *am,
+                             const float *cb, int64_t N, int64_t K, const float *y,
+                             int64_t max_m) {
+  if (!x || !qw || !am || !cb || !y) return NF4_ERR_NULL;
+  if (M < 1 || M > max_m || !shape_ok(N, K)) return NF4_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(qw) || !aligned16(am) || !aligned16(y)) return NF4_ERR_ALIGN;
+  return NF4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *nf4_status_string(nf4_status status) {
+  switch (status) {
+    case NF4_OK: return "NF4_OK";
+    case NF4_ERR_NULL: return "NF4_ERR_NULL: a required pointer is NULL";
+    case NF4_ERR_SHAPE: return "NF4_ERR_SHAPE: M, N or K outside the supported limits";
+    case NF4_ERR_ALIGN: return "NF4_ERR_ALIGN: a device pointer is not 16-byte aligned";
+    case NF4_ERR_CODEBOOK: return "NF4_ERR_CODEBOOK: codebook not usable by this entry point";
+    case NF4_ERR_WORKSPACE: return "NF4_ERR_WORKSPACE: workspace smaller than nf4_workspace_bytes()";
+    case NF4_ERR_HIP: return "NF4_ERR_HIP: the HIP runtime rejected a launch";
+  }
+  return "NF4 unknown status";
+}
+
+size_t nf4_qweight_bytes(int64_t N, int64_t K) {
+  if (!shape_ok(N, K)) return 0;
+  return (size_t)(N / nf4::kTileRows) * (size_t)nf4::tiles_k(K) * nf4::kTileBytes;
+}
+
+size_t nf4_absmax_bytes(int64_t N, int64_t K) {
+  if (!shape_ok(N, K)) return 0;
+  return (size_t)(N / nf4::kTileRows) * (size_t)nf4::tiles_k(K) * nf4::kTileScales * sizeof(float);
+}
+
+size_t nf4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || M > kMaxGemmM || !shape_ok(N, K)) return 0;
+  return nf4::gemm_workspace_bytes(M, N, K);
+}
+
+nf4_status nf4_pack(const float *W, int64_t N, int64_t K, const float codebook[16],
+                    uint8_t *qweight, float *absmax, hipStream_t stream) {
+  if (!W || !codebook || !qweight || !absmax) return NF4_ERR_NULL;
+  if (!shape_ok(N, K)) return NF4_ERR_SHAPE;
+  if (!aligned16(W) || !aligned16(qweight) || !aligned16(absmax)) return NF4_ERR_ALIGN;
+  nf4::PackConsts pc;
+  pc.zero_index = -1;
+  for (int i = 0; i < 16; ++i) {
+    if (!isfinite(codebook[i])) return NF4_ERR_CODEBOOK;
+    if (i > 0 && !(codebook[i] > codebook[i - 1])) return NF4_ERR_CODEBOOK;
+    if (codebook[i] == 0.0f && !signbit(codebook[i])) pc.zero_index = i;
+  }
+  if (pc.zero_index < 0) return NF4_ERR_CODEBOOK;
+  for (int i = 0; i < 15; ++i) pc.mid[i] = ((double)codebook[i] + (double)codebook[i + 1]) / 2.0;
+  return from_hip(nf4::launch_pack(W, N, K, pc, qweight, absmax, stream));
+}
+
+nf4_status nf4_dequant(const uint8_t *qweight, const float *absmax, const float codebook[16],
+                       int64_t N, int64_t K, float *W_out, hipStream_t stream) {
+  if (!qweight || !absmax || !codebook || !W_out) return NF4_ERR_NULL;
+  if (!shape_ok(N, K)) return NF4_ERR_SHAPE;
+  if (!aligned16(qweight) || !aligned16(absmax) || !aligned16(W_out)) return NF4_ERR_ALIGN;
+  nf4::Codebook cb;
+  for (int i = 0; i < 16; ++i) {
+    if (!isfinite(codebook[i])) return NF4_ERR_CODEBOOK;
+    cb.c[i] = codebook[i];
+  }
+  return from_hip(nf4::launch_dequant(qweight, absmax, cb, N, K, W_out, stream));
+}
+
+nf4_status nf4_repack(const uint8_t *codes, const float *scales, int64_t N, int64_t K,
+                      uint8_t *qweight, float *absmax, hipStream_t stream) {
+  if (!codes || !scales || !qweight || !absmax) return NF4_ERR_NULL;
+  if (!shape_ok(N, K)) return NF4_ERR_SHAPE;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(qweight) || !aligned16(absmax))
+    return NF4_ERR_ALIGN;
+  return from_hip(nf4::launch_repack(codes, scales, N, K, qweight, absmax, stream));
+}
+
+nf4_status nf4_unpack(const uint8_t *qweight, const float *absmax, int64_t N, int64_t K,
+                      uint8_t *codes, float *scales, hipStream_t stream) {
+  if (!codes || !scales || !qweight || !absmax) return NF4_ERR_NULL;
+  if (!shape_ok(N, K)) return NF4_ERR_SHAPE;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(qweight) || !aligned16(absmax))
+    return NF4_ERR_ALIGN;
+  return from_hip(nf4::launch_unpack(qweight, absmax, N, K, codes, scales, stream));
+}
+
+nf4_status nf4_gemv(const uint16_t *x, int64_t M, const uint8_t *qweight, const float *absmax,
+                    const float codebook[16], int64_t N, int64_t K, float *y, void *workspace,
+                    size_t ws_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  nf4_status st = check_linear_args(x, M, qweight, absmax, codebook, N, K, y, kMaxGemvM);
+  if (st != NF4_OK) return st;
+  nf4::CodeTerms ct;
+  const int nterm = split_codebook(codebook, ct);
+  if (nterm == 0) return NF4_ERR_CODEBOOK;
+  return from_hip(nf4::launch_gemv(x, (int)M, qweight, absmax, ct, nterm, N, K, y, stream));
+}
+
+nf4_status nf4_gemm(const uint16_t *x, int64_t M, const uint8_t *qweight, const float *absmax,
+                    const float codebook[16], int64_t N, int64_t K, float *y, void *workspace,
+                    size_t ws_bytes, hipStream_t stream) {
+  nf4_status st = check_linear_args(x, M, qweight, absmax, codebook, N, K, y, kMaxGemmM);
+  if (st != NF4_OK) return st;
+  const size_t need = nf4::gemm_workspace_bytes(M, N, K);
+  if (need > 0 && !workspace) return NF4_ERR_NULL;
+  if (need > ws_bytes) return NF4_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return NF4_ERR_ALIGN;
+  nf4::CodeTerms ct;
+  const int nterm = split_codebook(codebook, ct);
+  if (nterm == 0) return NF4_ERR_CODEBOOK;
+  return from_hip(nf4::launch_gemm(x, M, qweight, absmax, ct, nterm, N, K, y, workspace,
+                                   ws_bytes, stream));
+}
+
+}  // extern "C"

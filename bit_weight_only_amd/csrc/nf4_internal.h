@@ -1,0 +1,65 @@
+// nf4_internal.h -- device layout geometry, kernel argument blocks and the
+// launchers shared by the entry points in nf4_abi.hip.  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nf4 {
+
+// Quantization block along K (vibevoice.c README, "Quantization" >
+// "Weights": blocks of 64 with one absmax scale each).
+constexpr int kBlock = 64;
+// Device tile: 16 rows x 128 k = 1024 bytes of codes, one 16-byte run per
+// lane of a 64-wide wavefront.  Lane l owns row l % 16 and, in dword j,
+// k = 32j + 8(l / 16) + 0..7: the bf16 B operand of
+// v_mfma_f32_16x16x32_bf16 for k-step j.
+constexpr int kTileRows = 16;
+constexpr int kTileK = 128;
+constexpr int kTileBytes = 1024;
+constexpr int kTileScales = 32;  // 16 rows x 2 blocks
+
+// Replicated lookup table of code pairs: entry e (a packed byte holding the
+// codes of k and k+1) maps to (bf16 c[e & 15]) | (bf16 c[e >> 4]) << 16.
+// kPairCopies copies interleave so that lane l reads copy l % 32 and the
+// dword address is e * 32 + copy: 32 lanes of a half-wave hit 32 banks.
+constexpr int kPairCopies = 32;
+constexpr int kPairWords = 256 * kPairCopies;
+
+// Codebook split into bf16 terms c = t0 + t1 + t2 (exact for binary32 when
+// the host check passes); the GEMV/GEMM products with each term are exact in
+// fp32.
+struct CodeTerms {
+  uint16_t t[3][16];
+};
+
+// Quantizer constants: midpoints of neighbouring codes in double, and the
+// index of the +0.0 code.
+struct PackConsts {
+  double mid[15];
+  int zero_index;
+};
+
+struct Codebook {
+  float c[16];
+};
+
+inline int64_t tiles_k(int64_t K) { return (K + kTileK - 1) / kTileK; }
+
+hipError_t launch_pack(const float *W, int64_t N, int64_t K, const PackConsts &pc, uint8_t *qw,
+                       float *am, hipStream_t s);
+hipError_t launch_dequant(const uint8_t *qw, const float *am, const Codebook &cb, int64_t N,
+                          int64_t K, float *out, hipStream_t s);
+hipError_t launch_repack(const uint8_t *codes, const float *scales, int64_t N, int64_t K,
+                         uint8_t *qw, float *am, hipStream_t s);
+hipError_t launch_unpack(const uint8_t *qw, const float *am, int64_t N, int64_t K, uint8_t *codes,
+                         float *scales, hipStream_t s);
+hipError_t launch_gemv(const uint16_t *x, int M, const uint8_t *qw, const float *am,
+                       const CodeTerms &ct, int nterm, int64_t N, int64_t K, float *y,
+                       hipStream_t s);
+hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, const float *am,
+                       const CodeTerms &ct, int nterm, int64_t N, int64_t K, float *y,
+                       void *ws, size_t ws_bytes, hipStream_t s);
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+}  // namespace nf4

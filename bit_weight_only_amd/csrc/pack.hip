@@ -1,0 +1,220 @@
+// pack.hip -- load-time kernels: quantize fp32 weights into the device
+// layout, the debug dequant, and the canonical <-> device layout copies.
+//
+// Method (vibevoice.c README, "Quantization" > "Weights"): every projection
+// is quantized once as it is loaded, before placement, deterministically;
+// blocks of 64 weights along K share one absmax scale.  The nearest-code rule
+// with ties to the lower code is the reading taken where the page is silent.
+//
+// Each wavefront owns one 16-row x 128-k device tile; lane l handles row
+// l % 16 and the four 8-element runs k = 128t + 32j + 8(l/16) + 0..7.
+#include "nf4_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace nf4 {
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+
+struct TileCoord {
+  int64_t tile, g;
+  int t, lane, r, h;
+};
+
+__device__ inline bool tile_coord(int64_t ntiles, int64_t KT, TileCoord &c) {
+  c.tile = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (c.tile >= ntiles) return false;
+  c.lane = threadIdx.x & 63;
+  c.g = c.tile / KT;
+  c.t = (int)(c.tile - c.g * KT);
+  c.r = c.lane & 15;
+  c.h = c.lane >> 4;
+  return true;
+}
+
+// Quantizer: s = max |w| over the block (exact); s == 0 -> zero code;
+// else code = #{ i : (double)w > mid_i * (double)s }.  The max over a block
+// combines the four lanes that share a row (lanes r, r+16, r+32, r+48).
+__global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ W, int64_t K,
+                                                   int64_t KT, int64_t ntiles, PackConsts pc,
+                                                   uint4 *__restrict__ qw,
+                                                   float *__restrict__ am) {
+  TileCoord c;
+  if (!tile_coord(ntiles, KT, c)) return;
+  const float *row = W + (c.g * kTileRows + c.r) * K;
+  float w[4][8];
+  bool valid[4];
+  float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t k0 = (int64_t)c.t * kTileK + 32 * j + 8 * c.h;
+    valid[j] = k0 < K;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+    if (valid[j]) {
+      a = *reinterpret_cast<const float4 *>(row + k0);
+      b = *reinterpret_cast<const float4 *>(row + k0 + 4);
+    }
+    w[j][0] = a.x; w[j][1] = a.y; w[j][2] = a.z; w[j][3] = a.w;
+    w[j][4] = b.x; w[j][5] = b.y; w[j][6] = b.z; w[j][7] = b.w;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float m = fabsf(w[j][i]);
+      if (j < 2)
+        s0 = fmaxf(s0, m);
+      else
+        s1 = fmaxf(s1, m);
+    }
+  }
+  s0 = fmaxf(s0, __shfl_xor(s0, 16));
+  s0 = fmaxf(s0, __shfl_xor(s0, 32));
+  s1 = fmaxf(s1, __shfl_xor(s1, 16));
+  s1 = fmaxf(s1, __shfl_xor(s1, 32));
+
+  uint32_t out[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float s = j < 2 ? s0 : s1;
+    const double sd = (double)s;
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t code;
+      if (!valid[j]) {
+        code = 0;
+      } else if (s == 0.0f) {
+        code = (uint32_t)pc.zero_index;
+      } else {
+        const double wd = (double)w[j][i];
+        code = 0;
+#pragma unroll
+        for (int q = 0; q < 15; ++q) code += (wd > pc.mid[q] * sd) ? 1u : 0u;
+      }
+      word |= code << (4 * i);
+    }
+    out[j] = word;
+  }
+  qw[c.tile * 64 + c.lane] = make_uint4(out[0], out[1], out[2], out[3]);
+  if (c.h == 0) {
+    am[c.tile * kTileScales + 2 * c.r] = s0;
+    am[c.tile * kTileScales + 2 * c.r + 1] = s1;
+  }
+}
+
+// Debug dequant: W'[n][k] = fl32(c[code] * s), one binary32 multiply.
+__global__ __launch_bounds__(256) void dequant_kernel(const uint4 *__restrict__ qw,
+                                                      const float *__restrict__ am, Codebook cb,
+                                                      int64_t K, int64_t KT, int64_t ntiles,
+                                                      float *__restrict__ out) {
+  __shared__ float cbs[16];
+  if (threadIdx.x < 16) cbs[threadIdx.x] = cb.c[threadIdx.x];
+  __syncthreads();
+  TileCoord c;
+  if (!tile_coord(ntiles, KT, c)) return;
+  const uint4 q = qw[c.tile * 64 + c.lane];
+  const float s0 = am[c.tile * kTileScales + 2 * c.r];
+  const float s1 = am[c.tile * kTileScales + 2 * c.r + 1];
+  const uint32_t words[4] = {q.x, q.y, q.z, q.w};
+  float *row = out + (c.g * kTileRows + c.r) * K;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t k0 = (int64_t)c.t * kTileK + 32 * j + 8 * c.h;
+    if (k0 >= K) continue;
+    const float s = j < 2 ? s0 : s1;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = cbs[(words[j] >> (4 * i)) & 15u] * s;
+    *reinterpret_cast<float4 *>(row + k0) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4 *>(row + k0 + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+// Canonical -> device layout.  A device dword holds exactly the four
+// canonical bytes of its 8-k run, so this is a permutation of dwords.
+__global__ __launch_bounds__(256) void repack_kernel(const uint32_t *__restrict__ codes,
+                                                     const float *__restrict__ scales, int64_t K,
+                                                     int64_t KT, int64_t ntiles,
+                                                     uint4 *__restrict__ qw,
+                                                     float *__restrict__ am) {
+  TileCoord c;
+  if (!tile_coord(ntiles, KT, c)) return;
+  const int64_t n = c.g * kTileRows + c.r;
+  const uint32_t *row = codes + n * (K / 8);  // K/2 bytes = K/8 dwords
+  uint32_t wd[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t k0 = (int64_t)c.t * kTileK + 32 * j + 8 * c.h;
+    wd[j] = k0 < K ? row[k0 / 8] : 0u;
+  }
+  qw[c.tile * 64 + c.lane] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  if (c.h == 0) {
+    const int64_t nb = K / kBlock, b0 = 2 * (int64_t)c.t;
+    am[c.tile * kTileScales + 2 * c.r] = scales[n * nb + b0];
+    am[c.tile * kTileScales + 2 * c.r + 1] = b0 + 1 < nb ? scales[n * nb + b0 + 1] : 0.0f;
+  }
+}
+
+__global__ __launch_bounds__(256) void unpack_kernel(const uint4 *__restrict__ qw,
+                                                     const float *__restrict__ am, int64_t K,
+                                                     int64_t KT, int64_t ntiles,
+                                                     uint32_t *__restrict__ codes,
+                                                     float *__restrict__ scales) {
+  TileCoord c;
+  if (!tile_coord(ntiles, KT, c)) return;
+  const int64_t n = c.g * kTileRows + c.r;
+  uint32_t *row = codes + n * (K / 8);
+  const uint4 q = qw[c.tile * 64 + c.lane];
+  const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t k0 = (int64_t)c.t * kTileK + 32 * j + 8 * c.h;
+    if (k0 < K) row[k0 / 8] = wd[j];
+  }
+  if (c.h == 0) {
+    const int64_t nb = K / kBlock, b0 = 2 * (int64_t)c.t;
+    scales[n * nb + b0] = am[c.tile * kTileScales + 2 * c.r];
+    if (b0 + 1 < nb) scales[n * nb + b0 + 1] = am[c.tile * kTileScales + 2 * c.r + 1];
+  }
+}
+
+inline dim3 tile_grid(int64_t ntiles) {
+  return dim3((unsigned)((ntiles + kWavesPerBlock - 1) / kWavesPerBlock));
+}
+
+}  // namespace
+
+hipError_t launch_pack(const float *W, int64_t N, int64_t K, const PackConsts &pc, uint8_t *qw,
+                       float *am, hipStream_t s) {
+  const int64_t KT = tiles_k(K), ntiles = (N / kTileRows) * KT;
+  hipLaunchKernelGGL(pack_kernel, tile_grid(ntiles), dim3(256), 0, s, W, K, KT, ntiles, pc,
+                     reinterpret_cast<uint4 *>(qw), am);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t *qw, const float *am, const Codebook &cb, int64_t N,
+                          int64_t K, float *out, hipStream_t s) {
+  const int64_t KT = tiles_k(K), ntiles = (N / kTileRows) * KT;
+  hipLaunchKernelGGL(dequant_kernel, tile_grid(ntiles), dim3(256), 0, s,
+                     reinterpret_cast<const uint4 *>(qw), am, cb, K, KT, ntiles, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_repack(const uint8_t *codes, const float *scales, int64_t N, int64_t K,
+                         uint8_t *qw, float *am, hipStream_t s) {
+  const int64_t KT = tiles_k(K), ntiles = (N / kTileRows) * KT;
+  hipLaunchKernelGGL(repack_kernel, tile_grid(ntiles), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t *>(codes), scales, K, KT, ntiles,
+                     reinterpret_cast<uint4 *>(qw), am);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack(const uint8_t *qw, const float *am, int64_t N, int64_t K, uint8_t *codes,
+                         float *scales, hipStream_t s) {
+  const int64_t KT = tiles_k(K), ntiles = (N / kTileRows) * KT;
+  hipLaunchKernelGGL(unpack_kernel, tile_grid(ntiles), dim3(256), 0, s,
+                     reinterpret_cast<const uint4 *>(qw), am, K, KT, ntiles,
+                     reinterpret_cast<uint32_t *>(codes), scales);
+  return hipGetLastError();
+}
+
+}  // namespace nf4

@@ -1,0 +1,162 @@
+"""ctypes binding of libnf4.so with the same entry-point names as include/nf4.h.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels.
+Tensors supply device pointers; the stream defaults to torch's current
+stream.  A missing library is an error, never a fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnf4.so")
+
+NF4_OK, NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_CODEBOOK, NF4_ERR_WORKSPACE, \
+    NF4_ERR_HIP = range(7)
+
+EXPORTS = ("nf4_status_string", "nf4_qweight_bytes", "nf4_absmax_bytes", "nf4_workspace_bytes",
+           "nf4_pack", "nf4_dequant", "nf4_repack", "nf4_unpack", "nf4_gemv", "nf4_gemm")
+
+_lib = None
+
+
+class NF4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {nf4_status_string(status)}")
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m bit_weight_only_amd.build` (no fallback path exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, sz, st = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        fp = ctypes.POINTER(ctypes.c_float)
+        L.nf4_status_string.restype = ctypes.c_char_p
+        L.nf4_status_string.argtypes = [st]
+        for f in (L.nf4_qweight_bytes, L.nf4_absmax_bytes):
+            f.restype = sz
+            f.argtypes = [i64, i64]
+        L.nf4_workspace_bytes.restype = sz
+        L.nf4_workspace_bytes.argtypes = [i64, i64, i64]
+        L.nf4_pack.restype = st
+        L.nf4_pack.argtypes = [vp, i64, i64, fp, vp, vp, vp]
+        L.nf4_dequant.restype = st
+        L.nf4_dequant.argtypes = [vp, vp, fp, i64, i64, vp, vp]
+        L.nf4_repack.restype = st
+        L.nf4_repack.argtypes = [vp, vp, i64, i64, vp, vp, vp]
+        L.nf4_unpack.restype = st
+        L.nf4_unpack.argtypes = [vp, vp, i64, i64, vp, vp, vp]
+        for f in (L.nf4_gemv, L.nf4_gemm):
+            f.restype = st
+            f.argtypes = [vp, i64, vp, vp, fp, i64, i64, vp, vp, sz, vp]
+        _lib = L
+    return _lib
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _codebook(cb) -> ctypes.Array:
+    a = np.ascontiguousarray(np.asarray(cb, dtype=np.float32).reshape(16))
+    return (ctypes.c_float * 16)(*a.tolist())
+
+
+def _check(status: int, where: str) -> None:
+    if status != NF4_OK:
+        raise NF4Error(status, where)
+
+
+def nf4_status_string(status: int) -> str:
+    return lib().nf4_status_string(int(status)).decode()
+
+
+def nf4_qweight_bytes(N: int, K: int) -> int:
+    return lib().nf4_qweight_bytes(N, K)
+
+
+def nf4_absmax_bytes(N: int, K: int) -> int:
+    return lib().nf4_absmax_bytes(N, K)
+
+
+def nf4_workspace_bytes(M: int, N: int, K: int) -> int:
+    return lib().nf4_workspace_bytes(M, N, K)
+
+
+def nf4_pack(W, N: int, K: int, codebook, qweight, absmax, stream=None) -> None:
+    _check(lib().nf4_pack(_ptr(W), N, K, _codebook(codebook), _ptr(qweight), _ptr(absmax),
+                          _stream(stream)), "nf4_pack")
+
+
+def nf4_dequant(qweight, absmax, codebook, N: int, K: int, W_out, stream=None) -> None:
+    _check(lib().nf4_dequant(_ptr(qweight), _ptr(absmax), _codebook(codebook), N, K,
+                             _ptr(W_out), _stream(stream)), "nf4_dequant")
+
+
+def nf4_repack(codes, scales, N: int, K: int, qweight, absmax, stream=None) -> None:
+    _check(lib().nf4_repack(_ptr(codes), _ptr(scales), N, K, _ptr(qweight), _ptr(absmax),
+                            _stream(stream)), "nf4_repack")
+
+
+def nf4_unpack(qweight, absmax, N: int, K: int, codes, scales, stream=None) -> None:
+    _check(lib().nf4_unpack(_ptr(qweight), _ptr(absmax), N, K, _ptr(codes), _ptr(scales),
+                            _stream(stream)), "nf4_unpack")
+
+
+def nf4_gemv(x, M: int, qweight, absmax, codebook, N: int, K: int, y, workspace=None,
+             ws_bytes: int = 0, stream=None) -> None:
+    _check(lib().nf4_gemv(_ptr(x), M, _ptr(qweight), _ptr(absmax), _codebook(codebook), N, K,
+                          _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)), "nf4_gemv")
+
+
+def nf4_gemm(x, M: int, qweight, absmax, codebook, N: int, K: int, y, workspace=None,
+             ws_bytes: int = 0, stream=None) -> None:
+    _check(lib().nf4_gemm(_ptr(x), M, _ptr(qweight), _ptr(absmax), _codebook(codebook), N, K,
+                          _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)), "nf4_gemm")
+
+
+# ------------------------------------------------------------ conveniences
+class PackedWeight:
+    """Device-layout codes and scales of one N x K weight (torch uint8/fp32)."""
+
+    def __init__(self, N: int, K: int, device="cuda"):
+        import torch
+        qb, ab = nf4_qweight_bytes(N, K), nf4_absmax_bytes(N, K)
+        if qb == 0:
+            raise NF4Error(NF4_ERR_SHAPE, "PackedWeight")
+        self.N, self.K = N, K
+        self.qweight = torch.empty(qb, dtype=torch.uint8, device=device)
+        self.absmax = torch.empty(ab // 4, dtype=torch.float32, device=device)
+
+    @property
+    def nbytes(self) -> int:
+        """Algorithmic bytes a full read moves: 4-bit codes plus fp32 scales."""
+        return self.N * self.K // 2 + 4 * self.N * (self.K // 64)
+
+
+def pack_weight(W, codebook, stream=None) -> PackedWeight:
+    """Quantize a device fp32 [N, K] tensor into a new PackedWeight."""
+    N, K = W.shape
+    pw = PackedWeight(N, K, device=W.device)
+    nf4_pack(W, N, K, codebook, pw.qweight, pw.absmax, stream)
+    return pw

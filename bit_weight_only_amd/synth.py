@@ -7,13 +7,24 @@ distributions.  Draws come from SplitMix64 (Steele, Lea and Flood, 2014: add
 the golden-ratio increment to a 64-bit state and pass it through the
 published two-multiply finaliser), which is counter based, so any row of any
 matrix can be regenerated on its own.  Normals use the Box-Muller transform
-in double.
+in double.  The bulk generation runs in ``synth.c`` (threaded, gcc-built
+``libsynth.so``); ``splitmix64`` and ``normal_numpy`` here restate the same
+definitions in numpy for the generator's own tests.
 
 Every stream's seed is  MASTER ^ cfg << 32 ^ layer << 16 ^ matrix_id.
 """
 from __future__ import annotations
 
+import ctypes
+import os
+import subprocess
+
 import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "synth.c")
+_LIB = os.path.join(_HERE, "libsynth.so")
+_clib = None
 
 MASTER = 0x4E4634  # "NF4"
 _GAMMA = np.uint64(0x9E3779B97F4A7C15)
@@ -40,9 +51,48 @@ def splitmix64(seed: int, n: int, offset: int = 0) -> np.ndarray:
     return z ^ (z >> np.uint64(31))
 
 
+def build() -> str:
+    cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared", "-std=c11",
+           "-Wall", "-o", _LIB + ".tmp", _SRC, "-lm", "-lpthread"]
+    subprocess.check_call(cmd)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _c():
+    global _clib
+    if _clib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        L.synth_fill.restype = None
+        L.synth_fill.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64,
+                                 ctypes.c_double, ctypes.c_void_p, ctypes.c_int]
+        _clib = L
+    return _clib
+
+
+def _threads() -> int:
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    return min(n, int(env)) if env and env.isdigit() and int(env) > 0 else n
+
+
+def _fill(kind: int, seed: int, n: int, offset: int, dtype, scale: float = 1.0) -> np.ndarray:
+    out = np.empty(n, dtype)
+    _c().synth_fill(kind, seed & 0xFFFFFFFFFFFFFFFF, offset, n, scale, out.ctypes.data,
+                    _threads())
+    return out
+
+
 def normal(seed: int, n: int, offset: int = 0) -> np.ndarray:
-    """Standard normals offset .. offset+n-1 (float64).  Normal 2i and 2i+1 come
-    from draws 2i and 2i+1 of the stream by Box-Muller."""
+    """Standard normals offset .. offset+n-1 (float64)."""
+    return _fill(0, seed, n, offset, np.float64)
+
+
+def normal_numpy(seed: int, n: int, offset: int = 0) -> np.ndarray:
+    """The same normals restated in numpy (slow; for the generator's tests).
+    Normal 2i and 2i+1 come from draws 2i and 2i+1 by Box-Muller."""
     out = np.empty(n, np.float64)
     done = 0
     while done < n:
@@ -80,12 +130,11 @@ def weights(cfg: int, layer: int, matrix_id: int, N: int, K: int, rows=None,
     `rows` selects a subset of rows (returned in that order)."""
     seed = stream_seed(cfg, layer, matrix_id)
     if rows is None:
-        z = normal(seed, N * K)
-        return (std * z).astype(np.float32).reshape(N, K)
+        return _fill(1, seed, N * K, 0, np.float32, std).reshape(N, K)
     rows = np.asarray(rows, np.int64)
     out = np.empty((rows.size, K), np.float32)
     for i, n in enumerate(rows):
-        out[i] = (std * normal(seed, K, int(n) * K)).astype(np.float32)
+        out[i] = _fill(1, seed, K, int(n) * K, np.float32, std)
     return out
 
 
@@ -93,10 +142,9 @@ def activations(cfg: int, M: int, K: int, stream: int = 0, rows=None) -> np.ndar
     """bf16 bit patterns x[M][K] ~ N(0, 1), one stream per (cfg, K, stream)."""
     seed = stream_seed(cfg, X_LAYER, (K << 4 | stream) & 0xFFFF_FFFF)
     if rows is None:
-        z = normal(seed, M * K).astype(np.float32)
-        return fp32_to_bf16_bits(z).reshape(M, K)
+        return _fill(2, seed, M * K, 0, np.uint16).reshape(M, K)
     rows = np.asarray(rows, np.int64)
     out = np.empty((rows.size, K), np.uint16)
     for i, m in enumerate(rows):
-        out[i] = fp32_to_bf16_bits(normal(seed, K, int(m) * K).astype(np.float32))
+        out[i] = _fill(2, seed, K, int(m) * K, np.uint16)
     return out

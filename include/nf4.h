@@ -1,0 +1,134 @@
+/*
+ * nf4.h -- C ABI of libnf4.so: an NF4-style 4-bit weight-only linear layer
+ * y = x . dequant(W)^T for AMD Instinct MI355X (gfx950).
+ *
+ * The method (vibevoice.c README, section "Quantization" > "Weights"): each
+ * projection weight W[N][K] (PyTorch Linear orientation, out x in) is cut
+ * into blocks of 64 consecutive weights along K; every block keeps one
+ * absmax scale s and every weight a 4-bit code into a 16-entry non-uniform
+ * table c[] ("Int8 activations" section).  A weight reads back as c[idx]*s.
+ * The decode GEMV and the prefill GEMM ("The kernels that matter": the
+ * dequantization is fused into the multiply so the weights stay 4-bit into
+ * the product) both read one shared repacked weight layout (same README,
+ * "Quantization" > "Weights": one row-major layout permuted inside each
+ * 16-byte run so one load feeds both the GEMV and the matrix-core operand).
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer except `codebook` is DEVICE memory owned by the caller.
+ *    `codebook` is a HOST array of 16 floats, read during the call and baked
+ *    into the kernel arguments (so a captured graph keeps its values).
+ *  - Work is enqueued on `stream` only; nothing is allocated, freed or
+ *    synchronised.  Passing 0 selects the null stream, which the library
+ *    never picks by itself.
+ *  - Arguments are validated on the host before any HIP call; a rejected call
+ *    enqueues nothing.  A launch failure reported by hipGetLastError maps to
+ *    NF4_ERR_HIP.  Device faults surface at the caller's next synchronisation.
+ *  - The library holds no state: calls are reentrant and thread safe.
+ *  - Shapes: N % 16 == 0, N >= 16; K % 64 == 0, K >= 64; M >= 1.
+ *    N, K <= 2^30 and N*K <= 2^40.
+ *  - Device pointers must be 16-byte aligned (else NF4_ERR_ALIGN).
+ *  - x is bfloat16 bit patterns, [M][K] row-major.  y is fp32 [M][N]
+ *    row-major, overwritten (never accumulated), no bias.
+ *
+ * Device weight layout (what nf4_pack writes and the GEMV/GEMM read)
+ *  - Rows are taken 16 at a time (row group g = n / 16) and K 128 at a time
+ *    (tile t = k / 128; the last tile is zero-padded when K % 128 == 64).
+ *    Tile (g, t) is 1024 bytes at byte offset (g * KT + t) * 1024 with
+ *    KT = ceil(K / 128).
+ *  - Inside a tile, 64 lanes own 16 bytes each at lane * 16.  Lane l holds
+ *    row 16g + (l % 16); its dword j (0..3) holds the codes of
+ *    k = 128t + 32j + 8(l / 16) + i, i = 0..7, code i in bits 4i..4i+3.
+ *    Each dword is therefore four canonical bytes (low nibble = even k).
+ *  - absmax: for tile (g, t), 32 floats at float offset (g * KT + t) * 32;
+ *    entry 2r + h is the scale of row 16g + r, block 2t + h.
+ *  - Padding codes are 0 and padding scales are +0.0.
+ */
+#ifndef NF4_H
+#define NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nf4_status {
+  NF4_OK = 0,
+  NF4_ERR_NULL = 1,      /* a required pointer is NULL */
+  NF4_ERR_SHAPE = 2,     /* M, N or K outside the limits above */
+  NF4_ERR_ALIGN = 3,     /* a device pointer is not 16-byte aligned */
+  NF4_ERR_CODEBOOK = 4,  /* codebook not usable by this entry point */
+  NF4_ERR_WORKSPACE = 5, /* workspace smaller than nf4_workspace_bytes() */
+  NF4_ERR_HIP = 6        /* the HIP runtime rejected a launch */
+} nf4_status;
+
+/* Static string naming a status; never NULL. */
+const char *nf4_status_string(nf4_status status);
+
+/* Bytes of the device-layout code buffer: ceil(K/128) * (N/16) * 1024.
+ * Returns 0 for shapes the library rejects. */
+size_t nf4_qweight_bytes(int64_t N, int64_t K);
+
+/* Bytes of the device-layout scale buffer: ceil(K/128) * (N/16) * 128.
+ * Returns 0 for shapes the library rejects. */
+size_t nf4_absmax_bytes(int64_t N, int64_t K);
+
+/* Bytes of scratch that nf4_gemm needs for an M x N x K call (split-K
+ * partial sums and arrival counters); 0 when it needs none.  nf4_gemv needs
+ * none.  A workspace must be zero-filled once when it is allocated; every
+ * call leaves its counters at zero again.  Calls sharing one workspace must
+ * be ordered (the same stream, or synchronised). */
+size_t nf4_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* Quantize fp32 W[N][K] (row-major) into the device layout.  Per block of
+ * 64: s = max |w| (exact); s == 0 gives every weight the index of the +0.0
+ * code; otherwise idx = #{ i < 15 : (double)w > m_i * (double)s } with
+ * m_i = ((double)c_i + (double)c_{i+1}) / 2, i.e. the nearest code with an
+ * exact midpoint going to the lower index.  The codebook must be finite,
+ * strictly increasing and contain +0.0 (else NF4_ERR_CODEBOOK).  W must be
+ * finite (not checked).  qweight: nf4_qweight_bytes(N, K) bytes; absmax:
+ * nf4_absmax_bytes(N, K) bytes. */
+nf4_status nf4_pack(const float *W, int64_t N, int64_t K, const float codebook[16],
+                    uint8_t *qweight, float *absmax, hipStream_t stream);
+
+/* Debug path: W_out[n][k] = fl32(c[idx] * s), one binary32 multiply per
+ * weight, fp32 [N][K] row-major.  Any finite codebook. */
+nf4_status nf4_dequant(const uint8_t *qweight, const float *absmax, const float codebook[16],
+                       int64_t N, int64_t K, float *W_out, hipStream_t stream);
+
+/* Layout conversion from the canonical format (codes[N][K/2] bytes, byte j
+ * = idx[2j] | idx[2j+1] << 4; scales[N][K/64] fp32 row-major) into the
+ * device layout; for weights quantized elsewhere. */
+nf4_status nf4_repack(const uint8_t *codes, const float *scales, int64_t N, int64_t K,
+                      uint8_t *qweight, float *absmax, hipStream_t stream);
+
+/* Inverse of nf4_repack: device layout back to the canonical format. */
+nf4_status nf4_unpack(const uint8_t *qweight, const float *absmax, int64_t N, int64_t K,
+                      uint8_t *codes, float *scales, hipStream_t stream);
+
+/* Decode GEMV, 1 <= M <= 8: y[m][n] = sum_b s[n][b] * sum_{k in b} x[m][k] *
+ * c[idx[n][k]], fp32 accumulation.  Codebook: any finite values whose fp32
+ * entries are sums of at most three bfloat16 values (every normal fp32 is);
+ * else NF4_ERR_CODEBOOK.  workspace may be NULL (ws_bytes 0).  Results are
+ * bitwise reproducible run to run. */
+nf4_status nf4_gemv(const uint16_t *x, int64_t M, const uint8_t *qweight, const float *absmax,
+                    const float codebook[16], int64_t N, int64_t K, float *y, void *workspace,
+                    size_t ws_bytes, hipStream_t stream);
+
+/* Prefill GEMM, any M >= 1: same result definition as nf4_gemv, computed on
+ * bf16 matrix cores with the codes as exact bf16 operands and the fp32
+ * scales applied outside the matrix product once per 64-block.  workspace:
+ * at least nf4_workspace_bytes(M, N, K) bytes (may be NULL when that is 0).
+ * Results are bitwise reproducible run to run. */
+nf4_status nf4_gemm(const uint16_t *x, int64_t M, const uint8_t *qweight, const float *absmax,
+                    const float codebook[16], int64_t N, int64_t K, float *y, void *workspace,
+                    size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NF4_H */

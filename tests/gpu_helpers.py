@@ -1,0 +1,113 @@
+"""Helpers for the GPU parity tests: oracle-side reference data and HIP-side
+calls through the C ABI on the same seeded inputs."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from bit_weight_only_amd import synth
+
+# decoder shapes (N = out features, K = in features)
+QWEN = {"q": (3584, 3584), "k": (512, 3584), "v": (512, 3584), "o": (3584, 3584),
+        "gate": (18944, 3584), "up": (18944, 3584), "down": (3584, 18944),
+        "lm_head": (152064, 3584)}
+QWEN_FUSED = {"qkv": (4608, 3584), "o": (3584, 3584), "gate_up": (37888, 3584),
+              "down": (3584, 18944)}
+VOXTRAL_FUSED = {"qkv": (6144, 3072), "wo": (3072, 4096), "w13": (18432, 3072),
+                 "w2": (3072, 9216)}
+
+
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Side:
+    """Torch device memory and a non-default stream for one test module."""
+
+    def __init__(self):
+        self.torch = torch_cuda()
+        from bit_weight_only_amd import nf4
+        self.nf4 = nf4
+        nf4.lib()
+        self.stream = self.torch.cuda.Stream()
+
+    def to_dev(self, a: np.ndarray):
+        t = self.torch.from_numpy(np.ascontiguousarray(a))
+        return t.to("cuda", non_blocking=False)
+
+    def sync(self):
+        self.stream.synchronize()
+
+    def pack(self, W: np.ndarray, cb):
+        N, K = W.shape
+        Wd = self.to_dev(W.astype(np.float32))
+        pw = self.nf4.PackedWeight(N, K)
+        self.nf4.nf4_pack(Wd, N, K, cb, pw.qweight, pw.absmax, stream=self.stream)
+        self.sync()
+        del Wd
+        return pw
+
+    def repack(self, packed: np.ndarray, absmax: np.ndarray):
+        N, K2 = packed.shape
+        K = 2 * K2
+        pw = self.nf4.PackedWeight(N, K)
+        c, s = self.to_dev(packed), self.to_dev(absmax.astype(np.float32))
+        self.nf4.nf4_repack(c, s, N, K, pw.qweight, pw.absmax, stream=self.stream)
+        self.sync()
+        return pw
+
+    def unpack(self, pw):
+        t = self.torch
+        codes = t.empty((pw.N, pw.K // 2), dtype=t.uint8, device="cuda")
+        scales = t.empty((pw.N, pw.K // 64), dtype=t.float32, device="cuda")
+        self.nf4.nf4_unpack(pw.qweight, pw.absmax, pw.N, pw.K, codes, scales, stream=self.stream)
+        self.sync()
+        return codes.cpu().numpy(), scales.cpu().numpy()
+
+    def dequant(self, pw, cb):
+        t = self.torch
+        out = t.empty((pw.N, pw.K), dtype=t.float32, device="cuda")
+        self.nf4.nf4_dequant(pw.qweight, pw.absmax, cb, pw.N, pw.K, out, stream=self.stream)
+        self.sync()
+        return out.cpu().numpy()
+
+    def x_dev(self, x_bits: np.ndarray):
+        return self.to_dev(x_bits.astype(np.uint16).view(np.int16))
+
+    def linear(self, kind: str, xd, M: int, pw, cb, y=None):
+        t = self.torch
+        if y is None:
+            y = t.empty((M, pw.N), dtype=t.float32, device="cuda")
+        fn = self.nf4.nf4_gemv if kind == "gemv" else self.nf4.nf4_gemm
+        ws_bytes = 0 if kind == "gemv" else self.nf4.nf4_workspace_bytes(M, pw.N, pw.K)
+        ws = t.zeros(max(ws_bytes, 16), dtype=t.uint8, device="cuda") if ws_bytes else None
+        fn(xd, M, pw.qweight, pw.absmax, cb, pw.N, pw.K, y, ws, ws_bytes, stream=self.stream)
+        self.sync()
+        return y
+
+    def run(self, kind: str, x_bits: np.ndarray, pw, cb) -> np.ndarray:
+        M = x_bits.shape[0]
+        return self.linear(kind, self.x_dev(x_bits), M, pw, cb).cpu().numpy()
+
+
+def oracle_layer(cfg, layer, mid, N, K, cb, rows=None):
+    """Oracle quantization of the seeded weight (all rows or selected rows)."""
+    W = synth.weights(cfg, layer, mid, N, K, rows=rows)
+    codes, absmax = oracle.quantize(W, cb)
+    return W, oracle.pack(codes), absmax
+
+
+def assert_linear_ok(y_test, y_ref, bound, what=""):
+    ok, rel, worst = oracle.check_linear(y_test, y_ref, bound)
+    assert ok, f"{what}: rel-L2 {rel:.3e} (bar 1e-5), worst element {worst:.3f} x bar"
+    return rel, worst

@@ -1,0 +1,137 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, answers size queries, and rejects bad arguments on the host
+before any HIP call (no compute call is made here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from bit_weight_only_amd import nf4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nf4.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nf4_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    declared = header_functions()
+    assert set(declared) == set(nf4.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", nf4.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (nf4_\w+)", out))
+    assert set(declared) <= exported, set(declared) - exported
+    L = nf4.lib()
+    for name in declared:
+        assert hasattr(L, name)
+
+
+def test_status_strings():
+    for s in range(7):
+        assert nf4.nf4_status_string(s).startswith("NF4_")
+    assert "unknown" in nf4.nf4_status_string(99)
+
+
+@pytest.mark.parametrize("N,K", [(16, 64), (48, 192), (4608, 3584), (152064, 3584), (3072, 9216)])
+def test_size_queries(N, K):
+    KT = -(-K // 128)
+    assert nf4.nf4_qweight_bytes(N, K) == (N // 16) * KT * 1024
+    assert nf4.nf4_absmax_bytes(N, K) == (N // 16) * KT * 128
+    assert nf4.nf4_qweight_bytes(N, K) >= N * K // 2
+    assert nf4.nf4_absmax_bytes(N, K) >= 4 * N * K // 64
+
+
+@pytest.mark.parametrize("N,K", [(0, 64), (8, 64), (24, 64), (16, 0), (16, 32), (16, 100),
+                                 (-16, 64), (1 << 31, 64)])
+def test_size_queries_reject_bad_shapes(N, K):
+    assert nf4.nf4_qweight_bytes(N, K) == 0
+    assert nf4.nf4_absmax_bytes(N, K) == 0
+    assert nf4.nf4_workspace_bytes(1, N, K) == 0
+
+
+A = 1 << 20  # a 16-byte aligned stand-in address; never dereferenced
+CB = np.linspace(-1, 1, 16, dtype=np.float32)
+CB[7] = 0.0
+
+
+def call(name, *args):
+    return getattr(nf4.lib(), name)(*args)
+
+
+def cbarr(v=CB):
+    return (ctypes.c_float * 16)(*np.asarray(v, np.float32).tolist())
+
+
+def test_linear_validation():
+    g = lambda *a: call("nf4_gemv", *a)
+    m = lambda *a: call("nf4_gemm", *a)
+    ok = (A, 1, A, A, cbarr(), 16, 64, A, None, 0, None)
+    for f in (g, m):
+        for i in (0, 2, 3, 7):
+            bad = list(ok)
+            bad[i] = None
+            assert f(*bad) == nf4.NF4_ERR_NULL
+        assert f(A, 0, A, A, cbarr(), 16, 64, A, None, 0, None) == nf4.NF4_ERR_SHAPE
+        assert f(A, 1, A, A, cbarr(), 24, 64, A, None, 0, None) == nf4.NF4_ERR_SHAPE
+        assert f(A, 1, A, A, cbarr(), 16, 96, A, None, 0, None) == nf4.NF4_ERR_SHAPE
+        assert f(A + 8, 1, A, A, cbarr(), 16, 64, A, None, 0, None) == nf4.NF4_ERR_ALIGN
+        assert f(A, 1, A + 4, A, cbarr(), 16, 64, A, None, 0, None) == nf4.NF4_ERR_ALIGN
+        assert f(A, 1, A, A + 8, cbarr(), 16, 64, A, None, 0, None) == nf4.NF4_ERR_ALIGN
+        assert f(A, 1, A, A, cbarr(), 16, 64, A + 4, None, 0, None) == nf4.NF4_ERR_ALIGN
+        bad = CB.copy()
+        bad[3] = np.inf
+        assert f(A, 1, A, A, cbarr(bad), 16, 64, A, None, 0, None) == nf4.NF4_ERR_CODEBOOK
+        bad[3] = np.nan
+        assert f(A, 1, A, A, cbarr(bad), 16, 64, A, None, 0, None) == nf4.NF4_ERR_CODEBOOK
+        bad[3] = 3.4e38  # rounds past the bf16 range: no exact term split
+        assert f(A, 1, A, A, cbarr(bad), 16, 64, A, None, 0, None) == nf4.NF4_ERR_CODEBOOK
+    assert g(A, 9, A, A, cbarr(), 16, 64, A, None, 0, None) == nf4.NF4_ERR_SHAPE
+
+
+def test_pack_validation():
+    p = lambda *a: call("nf4_pack", *a)
+    assert p(None, 16, 64, cbarr(), A, A, None) == nf4.NF4_ERR_NULL
+    assert p(A, 16, 64, None, A, A, None) == nf4.NF4_ERR_NULL
+    assert p(A, 16, 64, cbarr(), None, A, None) == nf4.NF4_ERR_NULL
+    assert p(A, 17, 64, cbarr(), A, A, None) == nf4.NF4_ERR_SHAPE
+    assert p(A + 4, 16, 64, cbarr(), A, A, None) == nf4.NF4_ERR_ALIGN
+    for mutate in ("unsorted", "no_zero", "neg_zero", "dup", "nan"):
+        bad = CB.copy()
+        if mutate == "unsorted":
+            bad[[2, 3]] = bad[[3, 2]]
+        elif mutate == "no_zero":
+            bad[7] = 0.01
+        elif mutate == "neg_zero":
+            bad[7] = -0.0
+        elif mutate == "dup":
+            bad[9] = bad[8]
+        else:
+            bad[0] = np.nan
+        assert p(A, 16, 64, cbarr(bad), A, A, None) == nf4.NF4_ERR_CODEBOOK, mutate
+
+
+def test_layout_entry_validation():
+    for name in ("nf4_repack", "nf4_unpack"):
+        f = lambda *a: call(name, *a)
+        assert f(None, A, 16, 64, A, A, None) == nf4.NF4_ERR_NULL
+        assert f(A, A, 16, 32, A, A, None) == nf4.NF4_ERR_SHAPE
+        assert f(A, A + 4, 16, 64, A, A, None) == nf4.NF4_ERR_ALIGN
+    d = lambda *a: call("nf4_dequant", *a)
+    assert d(A, A, None, 16, 64, A, None) == nf4.NF4_ERR_NULL
+    assert d(A, A, cbarr(), 16, 65, A, None) == nf4.NF4_ERR_SHAPE
+    bad = CB.copy()
+    bad[0] = np.inf
+    assert d(A, A, cbarr(bad), 16, 64, A, None) == nf4.NF4_ERR_CODEBOOK
+
+
+def test_binding_raises_named_errors():
+    with pytest.raises(nf4.NF4Error) as e:
+        nf4.nf4_gemv(A, 9, A, A, CB, 16, 64, A, stream=0)
+    assert e.value.status == nf4.NF4_ERR_SHAPE and "NF4_ERR_SHAPE" in str(e.value)

@@ -10,6 +10,17 @@ def test_splitmix64_published_vectors():
         0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
 
 
+def test_c_generator_matches_numpy_restatement():
+    """The threaded C generator equals the numpy restatement of the same
+    definitions (draws bit for bit, normals to the last few ulps of libm)."""
+    import ctypes
+    raw = np.empty(1000, np.uint64)
+    synth._c().synth_fill(3, 12345, 77, 1000, 1.0, raw.ctypes.data, 4)
+    np.testing.assert_array_equal(raw, synth.splitmix64(12345, 1000, 77))
+    np.testing.assert_allclose(synth.normal(99, 100_001, 5), synth.normal_numpy(99, 100_001, 5),
+                               rtol=1e-13, atol=1e-13)
+
+
 def test_normal_is_counter_based_and_standard():
     z = synth.normal(7, 300_001)
     assert abs(z.mean()) < 0.01 and abs(z.std() - 1) < 0.01
