@@ -143,8 +143,10 @@ def main():
     y1["lm_head"] = torch.empty((1, VOCAB), dtype=torch.float32, device=dev)
     yp = {name: torch.empty((PREFILL_M, N), dtype=torch.float32, device=dev)
           for name, N, _ in LINEARS}
-    ws_bytes = max(nf4.nf4_workspace_bytes(PREFILL_M, N, K) for _, N, K in LINEARS)
+    ws_bytes = max([nf4.nf4_workspace_bytes(M, N, K) for M in (1, PREFILL_M)
+                    for _, N, K in LINEARS] + [nf4.nf4_workspace_bytes(1, VOCAB, HIDDEN)])
     ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()  # inputs and the zeroed workspace are ready before stream s runs
 
     decode_bytes = sum(packed_bytes(N, K) for _, N, K in LINEARS) * LAYERS \
         + packed_bytes(VOCAB, HIDDEN)
@@ -154,9 +156,9 @@ def main():
         for lw in weights:
             for name, N, K in LINEARS:
                 pw = lw[name]
-                nf4.nf4_gemv(x1[K], 1, pw.qweight, pw.absmax, cb, N, K, y1[name])
+                nf4.nf4_gemv(x1[K], 1, pw.qweight, pw.absmax, cb, N, K, y1[name], ws, ws_bytes)
         nf4.nf4_gemv(x1[HIDDEN], 1, lm_head.qweight, lm_head.absmax, cb, VOCAB, HIDDEN,
-                     y1["lm_head"])
+                     y1["lm_head"], ws, ws_bytes)
 
     def prefill_step():
         for lw in weights:

@@ -14,6 +14,8 @@
 // product is exact).  The fp32 block scale multiplies each 64-block's sum.
 // Lanes sharing a row combine with cross-lane shuffles, waves through LDS in
 // a fixed order, so the result is reproducible bit for bit.
+#include <atomic>
+
 #include "nf4_internal.h"
 
 namespace nf4 {
@@ -29,7 +31,7 @@ __device__ inline float dot2(uint32_t a, uint32_t b, float c) {
 constexpr int kMaxWaves = 16;
 
 template <int M, int NTERM, int TT>
-__global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
+__global__ __launch_bounds__(kMaxWaves * 64) void gemv_generic_kernel(
     const uint16_t *__restrict__ x, const uint4 *__restrict__ qw,
     const float2 *__restrict__ am, CodeTerms ct, int64_t N, int64_t K, int64_t KT, int T,
     float *__restrict__ y) {
@@ -121,6 +123,264 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Fast path (codebook of bf16 values, x small enough for LDS).
+//
+// Work split: workgroup b owns the whole row groups [G*b/P, G*(b+1)/P), a
+// contiguous run of device tiles in memory order.  Its 8 waves take the run's
+// tiles round robin (wave w: local tiles w, w+8, w+16, ...), so each round
+// the workgroup reads 8 KB of consecutive codes, and every wave gets the same
+// number of tiles to within one.  A wave keeps kFastDepth tiles in flight.
+// Each wave accumulates one partial per row group it touches and leaves it in
+// LDS; after one barrier the partials of every row group are summed in wave
+// order.  No workspace, no atomics, and a fixed summation order.
+//
+// LDS (dynamic, sized per launch): the pair table in 64 copies with a
+// 256-byte entry stride, so the address (code byte << 8) | (lane << 2) is one
+// v_perm_b32 and the 64 lanes of a wave hit 64 different banks; x for all M
+// rows, each padded with zeros to a whole number of 128-k tiles; and the
+// partial sums [row group][wave][16 rows][M].
+// ---------------------------------------------------------------------------
+constexpr int kFastWaves = 8;
+constexpr int kFastCopies = 64;
+constexpr int kFastTableWords = 256 * kFastCopies;  // 64 KB
+constexpr int kFastDepth = 4;                        // tiles in flight per wave
+constexpr int kLdsBytes = 160 * 1024;                // LDS per workgroup on gfx950
+// sched_barrier mask: ALU, VALU, SALU, MFMA, all LDS and transcendental
+// instructions may cross; vector memory instructions may not.
+constexpr int kSchedAllButGlobalLoads = 0x1 | 0x2 | 0x4 | 0x8 | 0x80 | 0x100 | 0x200 | 0x400;
+
+template <int M>
+__global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
+    const uint16_t *__restrict__ x, const uint4 *__restrict__ qw,
+    const float2 *__restrict__ am, CodeTerms ct, int N, int K, int KT, int G, int P,
+    float *__restrict__ y) {
+  constexpr int D = kFastDepth;
+  // The table is the kernel's only static LDS array, so it sits at address
+  // 0 and a lookup address needs no base added; x and the partials follow in
+  // dynamic LDS.
+  __shared__ __attribute__((aligned(16))) uint32_t table[kFastTableWords];
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds_dyn[];
+  const int KP = KT * kTileK;                 // padded x row length
+  uint16_t *xs = reinterpret_cast<uint16_t *>(lds_dyn);
+  float *red = reinterpret_cast<float *>(lds_dyn + M * KP / 2);
+  uint16_t *codes_lds = reinterpret_cast<uint16_t *>(red);  // until the table is built
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, h = lane >> 4;
+  const int g0 = (int)((int64_t)G * blockIdx.x / P), g1 = (int)((int64_t)G * (blockIdx.x + 1) / P);
+  const int Gw = g1 - g0, T0 = g0 * KT, Twg = Gw * KT;
+  const int n = Twg > wave ? (Twg - wave + kFastWaves - 1) / kFastWaves : 0;
+  const char *qbase = reinterpret_cast<const char *>(qw);
+  const char *sbase = reinterpret_cast<const char *>(am);
+  const uint32_t tile_end = (uint32_t)(T0 + Twg);
+
+  // Prefetch cursor; steps past the wave's share re-read the workgroup's
+  // first tile so that every step issues the same loads.
+  uint32_t ptau = (uint32_t)(T0 + wave);
+  uint4 wb[D];
+  float2 sb[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    const uint32_t lt = ptau < tile_end ? ptau : (uint32_t)T0;
+    wb[d] = *reinterpret_cast<const uint4 *>(qbase + (lt * 1024u + lane * 16u));
+    sb[d] = *reinterpret_cast<const float2 *>(sbase + (lt * 128u + r * 8u));
+    ptau += kFastWaves;
+  }
+
+  // Setup.  The 16 codes go through LDS (indexing the kernel-argument block
+  // with a per-thread index would be one memory round trip per use); the x
+  // loads are issued before the first barrier and stored after the table is
+  // built, so their latency hides behind it.
+  if (threadIdx.x < 16) codes_lds[threadIdx.x] = ct.t[0][threadIdx.x];
+  const int chunks = M * KP / 8, cpr = KP / 8;
+  constexpr int kStage = 4;
+  uint4 xv0[kStage];
+#pragma unroll
+  for (int u = 0; u < kStage; ++u) {
+    const int c = (int)threadIdx.x + u * (int)blockDim.x;
+    const int m = c / cpr, k = (c - m * cpr) * 8;
+    xv0[u] = make_uint4(0u, 0u, 0u, 0u);
+    if (c < chunks && k < K) xv0[u] = *reinterpret_cast<const uint4 *>(x + (int64_t)m * K + k);
+  }
+  __syncthreads();
+  // Pair table: consecutive lanes fill consecutive 16-byte chunks (four
+  // copies of one entry each), so the stores are free of bank conflicts.
+  for (int c = threadIdx.x; c < kFastTableWords / 4; c += blockDim.x) {
+    const int e = c / (kFastCopies / 4);
+    const uint32_t v = (uint32_t)codes_lds[e & 15] | ((uint32_t)codes_lds[e >> 4] << 16);
+    reinterpret_cast<uint4 *>(table)[c] = make_uint4(v, v, v, v);
+  }
+#pragma unroll
+  for (int u = 0; u < kStage; ++u) {
+    const int c = (int)threadIdx.x + u * (int)blockDim.x;
+    const int m = c / cpr, k = (c - m * cpr) * 8;
+    if (c < chunks) *reinterpret_cast<uint4 *>(&xs[m * KP + k]) = xv0[u];
+  }
+  for (int c0 = (int)threadIdx.x + kStage * (int)blockDim.x; c0 < chunks;
+       c0 += kStage * (int)blockDim.x) {
+    uint4 v[kStage];
+#pragma unroll
+    for (int u = 0; u < kStage; ++u) {
+      const int c = c0 + u * (int)blockDim.x;
+      const int m = c / cpr, k = (c - m * cpr) * 8;
+      v[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (c < chunks && k < K) v[u] = *reinterpret_cast<const uint4 *>(x + (int64_t)m * K + k);
+    }
+#pragma unroll
+    for (int u = 0; u < kStage; ++u) {
+      const int c = c0 + u * (int)blockDim.x;
+      const int m = c / cpr, k = (c - m * cpr) * 8;
+      if (c < chunks) *reinterpret_cast<uint4 *>(&xs[m * KP + k]) = v[u];
+    }
+  }
+  __syncthreads();
+  // Partial slots start at zero (a wave may touch no tile of a row group
+  // when a row group has fewer than 8 tiles).  The codes' words are reused
+  // here, after the barrier above.
+  for (int c = threadIdx.x; c < Gw * kFastWaves * 16 * M; c += blockDim.x) red[c] = 0.0f;
+  __syncthreads();
+
+  const uint32_t lane4 = (uint32_t)lane << 2;
+  const char *tabc = reinterpret_cast<const char *>(table);
+  float acc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+
+  // consumed-tile position: local row group j, tile t within it
+  const int q8 = kFastWaves / KT, r8 = kFastWaves % KT;
+  int j = wave / KT, t = wave % KT;
+  const int nsteps = (n + D - 1) / D * D;
+  for (int base = 0; base < nsteps; base += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int i = base + d;
+      const bool live = i < n;
+      // ---- one 16-row x 128-k tile: lane owns row r, k = 128t + 32j + 8h + 0..7
+      float p[2][M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) p[0][m] = p[1][m] = 0.0f;
+      const uint16_t *xt = xs + t * kTileK + 8 * h;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const uint32_t wd = jj == 0 ? wb[d].x : jj == 1 ? wb[d].y : jj == 2 ? wb[d].z : wb[d].w;
+        uint4 xv[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) xv[m] = *reinterpret_cast<const uint4 *>(xt + m * KP + 32 * jj);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t addr = __builtin_amdgcn_perm(wd, lane4, 0x0c0c0400u + (q << 8));
+          const uint32_t pr = *reinterpret_cast<const uint32_t *>(tabc + addr);
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+            const uint32_t xp = q == 0 ? xv[m].x : q == 1 ? xv[m].y : q == 2 ? xv[m].z : xv[m].w;
+            p[jj >> 1][m] = dot2(pr, xp, p[jj >> 1][m]);
+          }
+        }
+      }
+      const float s0 = live ? sb[d].x : 0.0f, s1 = live ? sb[d].y : 0.0f;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        acc[m] = fmaf(s0, p[0][m], acc[m]);
+        acc[m] = fmaf(s1, p[1][m], acc[m]);
+      }
+      // ---- refill this slot (D tiles ahead).  The empty asm pins the
+      // accumulation before this point and the barrier keeps the scheduler
+      // from hoisting the global loads above the slot's last use (either
+      // would rotate the slot registers and force a full wait per step);
+      // ALU and LDS instructions may still move across it, so the next
+      // tile's table lookups overlap this tile's arithmetic.
+#pragma unroll
+      for (int m = 0; m < M; ++m) asm volatile("" ::"v"(acc[m]));
+      __builtin_amdgcn_sched_barrier(kSchedAllButGlobalLoads);
+      {
+        const uint32_t lt = ptau < tile_end ? ptau : (uint32_t)T0;
+        wb[d] = *reinterpret_cast<const uint4 *>(qbase + (lt * 1024u + lane * 16u));
+        sb[d] = *reinterpret_cast<const float2 *>(sbase + (lt * 128u + r * 8u));
+        ptau += kFastWaves;
+      }
+      // ---- advance; when the row group changes (or the share ends), leave
+      // this wave's partial for it in LDS
+      int tn = t + r8, jn = j + q8;
+      if (tn >= KT) {
+        tn -= KT;
+        ++jn;
+      }
+      if (live && (jn != j || i == n - 1)) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          acc[m] += __shfl_xor(acc[m], 16);
+          acc[m] += __shfl_xor(acc[m], 32);
+        }
+        if (h == 0) {
+#pragma unroll
+          for (int m = 0; m < M; ++m) red[((j * kFastWaves + wave) * 16 + r) * M + m] = acc[m];
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+      }
+      j = jn;
+      t = tn;
+    }
+  }
+
+  // ---- every row group of the workgroup: sum the waves' partials in order
+  __syncthreads();
+  for (int c = threadIdx.x; c < Gw * 16 * M; c += blockDim.x) {
+    const int jj = c / (16 * M), rem = c - jj * 16 * M, rr = rem / M, m = rem - rr * M;
+    float sum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kFastWaves; ++w) sum += red[((jj * kFastWaves + w) * 16 + rr) * M + m];
+    y[(int64_t)m * N + (int64_t)(g0 + jj) * 16 + rr] = sum;
+  }
+}
+
+struct FastPlan {
+  int P;
+  size_t lds;
+};
+
+// dynamic LDS bytes (x and partials); the 64 KB table is static
+size_t fast_dyn_bytes(int M, int64_t K, int64_t Gw) {
+  return (size_t)M * tiles_k(K) * kTileK * 2 + (size_t)Gw * kFastWaves * 16 * M * 4;
+}
+constexpr size_t kDynMax = (size_t)kLdsBytes - (size_t)kFastTableWords * 4;
+
+FastPlan fast_plan(int M, int64_t N, int64_t K) {
+  const int64_t G = N / kTileRows;
+  int64_t P = device_cu_count();
+  if (P > G) P = G;
+  // more workgroups when the partial slots of ceil(G/P) row groups do not fit
+  while (fast_dyn_bytes(M, K, (G + P - 1) / P) > kDynMax && P < G) P += P / 4 + 1;
+  if (P > G) P = G;
+  return FastPlan{(int)P, fast_dyn_bytes(M, K, (G + P - 1) / P)};
+}
+
+bool fast_eligible(int M, int64_t N, int64_t K, int nterm) {
+  // 32-bit tile indices and byte offsets into the code buffer, and LDS room
+  // for x plus one row group's partials
+  const int64_t qbytes = (N / kTileRows) * tiles_k(K) * kTileBytes;
+  return nterm == 1 && qbytes < (int64_t(1) << 32) && fast_dyn_bytes(M, K, 1) <= kDynMax;
+}
+
+template <int M>
+hipError_t launch_fast(const uint16_t *x, const uint4 *qw, const float2 *am, const CodeTerms &ct,
+                       int64_t N, int64_t K, float *y, hipStream_t s) {
+  static std::atomic<bool> attr_set{false};
+  if (!attr_set.load(std::memory_order_acquire)) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&gemv_fast_kernel<M>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDynMax);
+    if (e != hipSuccess) return e;
+    attr_set.store(true, std::memory_order_release);
+  }
+  const FastPlan p = fast_plan(M, N, K);
+  hipLaunchKernelGGL((gemv_fast_kernel<M>), dim3(p.P), dim3(kFastWaves * 64), p.lds, s, x, qw,
+                     am, ct, (int)N, (int)K, (int)tiles_k(K), (int)(N / kTileRows), p.P, y);
+  return hipGetLastError();
+}
+
 template <int M, int NTERM>
 hipError_t launch_m(const uint16_t *x, const uint4 *qw, const float2 *am, const CodeTerms &ct,
                     int64_t N, int64_t K, float *y, hipStream_t s) {
@@ -130,13 +390,13 @@ hipError_t launch_m(const uint16_t *x, const uint4 *qw, const float2 *am, const 
   nw = (int)((KT + T - 1) / T);
   const dim3 grid((unsigned)(N / kTileRows)), block(nw * 64);
   if (T >= 8)
-    hipLaunchKernelGGL((gemv_kernel<M, NTERM, 8>), grid, block, 0, s, x, qw, am, ct, N, K, KT, T, y);
+    hipLaunchKernelGGL((gemv_generic_kernel<M, NTERM, 8>), grid, block, 0, s, x, qw, am, ct, N, K, KT, T, y);
   else if (T >= 4)
-    hipLaunchKernelGGL((gemv_kernel<M, NTERM, 4>), grid, block, 0, s, x, qw, am, ct, N, K, KT, T, y);
+    hipLaunchKernelGGL((gemv_generic_kernel<M, NTERM, 4>), grid, block, 0, s, x, qw, am, ct, N, K, KT, T, y);
   else if (T >= 2)
-    hipLaunchKernelGGL((gemv_kernel<M, NTERM, 2>), grid, block, 0, s, x, qw, am, ct, N, K, KT, T, y);
+    hipLaunchKernelGGL((gemv_generic_kernel<M, NTERM, 2>), grid, block, 0, s, x, qw, am, ct, N, K, KT, T, y);
   else
-    hipLaunchKernelGGL((gemv_kernel<M, NTERM, 1>), grid, block, 0, s, x, qw, am, ct, N, K, KT, T, y);
+    hipLaunchKernelGGL((gemv_generic_kernel<M, NTERM, 1>), grid, block, 0, s, x, qw, am, ct, N, K, KT, T, y);
   return hipGetLastError();
 }
 
@@ -158,11 +418,26 @@ hipError_t launch_t(const uint16_t *x, int M, const uint4 *qw, const float2 *am,
 
 }  // namespace
 
+size_t gemv_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+
 hipError_t launch_gemv(const uint16_t *x, int M, const uint8_t *qw, const float *am,
-                       const CodeTerms &ct, int nterm, int64_t N, int64_t K, float *y,
+                       const CodeTerms &ct, int nterm, int64_t N, int64_t K, float *y, void *ws,
                        hipStream_t s) {
   const uint4 *q = reinterpret_cast<const uint4 *>(qw);
   const float2 *a = reinterpret_cast<const float2 *>(am);
+  if (fast_eligible(M, N, K, nterm)) {
+    switch (M) {
+      case 1: return launch_fast<1>(x, q, a, ct, N, K, y, s);
+      case 2: return launch_fast<2>(x, q, a, ct, N, K, y, s);
+      case 3: return launch_fast<3>(x, q, a, ct, N, K, y, s);
+      case 4: return launch_fast<4>(x, q, a, ct, N, K, y, s);
+      case 5: return launch_fast<5>(x, q, a, ct, N, K, y, s);
+      case 6: return launch_fast<6>(x, q, a, ct, N, K, y, s);
+      case 7: return launch_fast<7>(x, q, a, ct, N, K, y, s);
+      case 8: return launch_fast<8>(x, q, a, ct, N, K, y, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   if (nterm == 1) return launch_t<1>(x, M, q, a, ct, N, K, y, s);
   return launch_t<3>(x, M, q, a, ct, N, K, y, s);
 }

@@ -10,6 +10,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/nf4.h"
 #include "nf4_internal.h"
 
@@ -86,6 +88,24 @@ nf4_status check_linear_args(const uint16_t *x, int64_t M, const uint8_t *qw, co
 
 }  // namespace
 
+namespace nf4 {
+
+// A device property, cached per device id after the first query.
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+}  // namespace nf4
+
 extern "C" {
 
 const char *nf4_status_string(nf4_status status) {
@@ -113,7 +133,12 @@ size_t nf4_absmax_bytes(int64_t N, int64_t K) {
 
 size_t nf4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || M > kMaxGemmM || !shape_ok(N, K)) return 0;
-  return nf4::gemm_workspace_bytes(M, N, K);
+  size_t need = nf4::gemm_workspace_bytes(M, N, K);
+  if (M <= kMaxGemvM) {
+    const size_t v = nf4::gemv_workspace_bytes(M, N, K);
+    need = v > need ? v : need;
+  }
+  return need;
 }
 
 nf4_status nf4_pack(const float *W, int64_t N, int64_t K, const float codebook[16],
@@ -167,14 +192,17 @@ nf4_status nf4_unpack(const uint8_t *qweight, const float *absmax, int64_t N, in
 nf4_status nf4_gemv(const uint16_t *x, int64_t M, const uint8_t *qweight, const float *absmax,
                     const float codebook[16], int64_t N, int64_t K, float *y, void *workspace,
                     size_t ws_bytes, hipStream_t stream) {
-  (void)workspace;
-  (void)ws_bytes;
   nf4_status st = check_linear_args(x, M, qweight, absmax, codebook, N, K, y, kMaxGemvM);
   if (st != NF4_OK) return st;
+  const size_t need = nf4::gemv_workspace_bytes(M, N, K);
+  if (need > 0 && !workspace) return NF4_ERR_NULL;
+  if (need > ws_bytes) return NF4_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return NF4_ERR_ALIGN;
   nf4::CodeTerms ct;
   const int nterm = split_codebook(codebook, ct);
   if (nterm == 0) return NF4_ERR_CODEBOOK;
-  return from_hip(nf4::launch_gemv(x, (int)M, qweight, absmax, ct, nterm, N, K, y, stream));
+  return from_hip(
+      nf4::launch_gemv(x, (int)M, qweight, absmax, ct, nterm, N, K, y, workspace, stream));
 }
 
 nf4_status nf4_gemm(const uint16_t *x, int64_t M, const uint8_t *qweight, const float *absmax,

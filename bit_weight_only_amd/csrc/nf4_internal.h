@@ -55,8 +55,11 @@ hipError_t launch_repack(const uint8_t *codes, const float *scales, int64_t N, i
 hipError_t launch_unpack(const uint8_t *qw, const float *am, int64_t N, int64_t K, uint8_t *codes,
                          float *scales, hipStream_t s);
 hipError_t launch_gemv(const uint16_t *x, int M, const uint8_t *qw, const float *am,
-                       const CodeTerms &ct, int nterm, int64_t N, int64_t K, float *y,
+                       const CodeTerms &ct, int nterm, int64_t N, int64_t K, float *y, void *ws,
                        hipStream_t s);
+size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// Compute units of the current device (queried once per device).
+int device_cu_count();
 hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, const float *am,
                        const CodeTerms &ct, int nterm, int64_t N, int64_t K, float *y,
                        void *ws, size_t ws_bytes, hipStream_t s);

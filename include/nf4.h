@@ -24,7 +24,7 @@
  *    enqueues nothing.  A launch failure reported by hipGetLastError maps to
  *    NF4_ERR_HIP.  Device faults surface at the caller's next synchronisation.
  *  - The library holds no state: calls are reentrant and thread safe.
- *  - Shapes: N % 16 == 0, N >= 16; K % 64 == 0, K >= 64; M >= 1.
+ *  - Shapes: N % 16 == 0, N >= 16; K % 64 == 0, K >= 64; 1 <= M <= 2^23.
  *    N, K <= 2^30 and N*K <= 2^40.
  *  - Device pointers must be 16-byte aligned (else NF4_ERR_ALIGN).
  *  - x is bfloat16 bit patterns, [M][K] row-major.  y is fp32 [M][N]
@@ -76,11 +76,12 @@ size_t nf4_qweight_bytes(int64_t N, int64_t K);
  * Returns 0 for shapes the library rejects. */
 size_t nf4_absmax_bytes(int64_t N, int64_t K);
 
-/* Bytes of scratch that nf4_gemm needs for an M x N x K call (split-K
- * partial sums and arrival counters); 0 when it needs none.  nf4_gemv needs
- * none.  A workspace must be zero-filled once when it is allocated; every
- * call leaves its counters at zero again.  Calls sharing one workspace must
- * be ordered (the same stream, or synchronised). */
+/* Bytes of scratch that nf4_gemv / nf4_gemm need for an M x N x K call on
+ * the current device (partial sums of row groups split across waves and
+ * their arrival counters); the larger of the two needs.  A workspace must be
+ * zero-filled once when it is allocated; every call leaves its counters at
+ * zero again.  Calls sharing one workspace must be ordered (the same
+ * stream, or synchronised). */
 size_t nf4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Quantize fp32 W[N][K] (row-major) into the device layout.  Per block of
@@ -112,8 +113,9 @@ nf4_status nf4_unpack(const uint8_t *qweight, const float *absmax, int64_t N, in
 /* Decode GEMV, 1 <= M <= 8: y[m][n] = sum_b s[n][b] * sum_{k in b} x[m][k] *
  * c[idx[n][k]], fp32 accumulation.  Codebook: any finite values whose fp32
  * entries are sums of at most three bfloat16 values (every normal fp32 is);
- * else NF4_ERR_CODEBOOK.  workspace may be NULL (ws_bytes 0).  Results are
- * bitwise reproducible run to run. */
+ * else NF4_ERR_CODEBOOK.  workspace: at least nf4_workspace_bytes(M, N, K)
+ * bytes, zero-filled once at allocation.  Results are bitwise reproducible
+ * run to run for a given shape and device. */
 nf4_status nf4_gemv(const uint16_t *x, int64_t M, const uint8_t *qweight, const float *absmax,
                     const float codebook[16], int64_t N, int64_t K, float *y, void *workspace,
                     size_t ws_bytes, hipStream_t stream);

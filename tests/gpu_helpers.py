@@ -89,8 +89,9 @@ class Side:
         if y is None:
             y = t.empty((M, pw.N), dtype=t.float32, device="cuda")
         fn = self.nf4.nf4_gemv if kind == "gemv" else self.nf4.nf4_gemm
-        ws_bytes = 0 if kind == "gemv" else self.nf4.nf4_workspace_bytes(M, pw.N, pw.K)
+        ws_bytes = self.nf4.nf4_workspace_bytes(M, pw.N, pw.K)
         ws = t.zeros(max(ws_bytes, 16), dtype=t.uint8, device="cuda") if ws_bytes else None
+        self.stream.wait_stream(t.cuda.current_stream())  # the zero fill ran on torch's stream
         fn(xd, M, pw.qweight, pw.absmax, cb, pw.N, pw.K, y, ws, ws_bytes, stream=self.stream)
         self.sync()
         return y
