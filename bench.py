@@ -9,13 +9,29 @@ Qwen2-7B-shaped decoder (hidden 3584, MLP 18944, k/v 512, head 152064):
 Weights are seeded N(0, 0.02^2) fp32 drawn on the GPU and quantized there by
 nf4_pack (load time, untimed); activations are seeded N(0, 1) in bf16.  Each
 sequence is captured once in a HIP graph and replayed.  The JSON line's
-`value` is decode packed-weight GB/s; prefill TFLOP/s sits beside it.
+`value` is decode packed-weight GB/s over the whole step (launch gaps
+included); prefill TFLOP/s sits beside it.
+
+`roofline` covers the dominant decode kernel (the gate|up GEMV, 28 launches
+per step): its 28 launches on distinct weights are replayed back to back in
+one graph, each replay timed with events on the launch stream; the median
+replay / 28 is the launch duration.  `roofline_prefill`
+does the same for the gate|up GEMM.  `traffic` is the HBM bytes per launch
+from rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, each scaled by what the
+counter reads for a plain 1 GiB copy), recorded below together with a hash of
+the kernel source they were taken on; it is null when the source differs.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu]
+    python bench.py --pmc-pass          # workload for rocprofv3 --pmc runs
+    python bench.py --summarize DIR --launch-log FILE --title T --command C
 """
 from __future__ import annotations
 
 import argparse
+import collections
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -24,6 +40,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
+CSRC = os.path.join(ROOT, "bit_weight_only_amd", "csrc")
 
 METRIC = "decode GEMV packed-weight GB/s (M=1) + prefill GEMM TFLOP/s (M=1024), Qwen2-7B"
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
@@ -34,6 +51,18 @@ HIDDEN, MLP, KV, VOCAB = 3584, 18944, 512, 152064
 LINEARS = [("qkv", HIDDEN + 2 * KV, HIDDEN), ("o", HIDDEN, HIDDEN),
            ("gate_up", 2 * MLP, HIDDEN), ("down", HIDDEN, MLP)]
 PREFILL_M = 1024
+DOMINANT = ("gate_up", 2 * MLP, HIDDEN)
+
+# HBM traffic per launch of the dominant kernels, from rocprofv3 --pmc runs of
+# `python bench.py --pmc-pass` (profiles/hbm_traffic_gate_up.md): counter KiB
+# per dispatch and the calibration of each counter on a plain 1 GiB copy.
+TRAFFIC = {
+    "gemv": {"source": "gemv.hip", "fetch_kib": 37534, "write_kib": 148,
+             "sha256": "3fcc9b8377df3b2668ad17d1558b277e9bc4ab282ef7ada7d73dd481f88a7ea3"},
+    "gemm": {"source": "gemm.hip", "fetch_kib": 206644, "write_kib": 151552,
+             "sha256": "c0f983011d51f4d5192906691df56c0c652e641d0ac15a155ddd3300d4209d06"},
+}
+COPY_CALIBRATION = {"fetch_kib_per_gib": 524308, "write_kib_per_gib": 1048576}
 
 
 def log(*a):
@@ -50,6 +79,25 @@ def cpu_threads():
     if env and env.isdigit() and int(env) > 0:
         n = min(n, int(env))
     return n
+
+
+def source_sha256(name):
+    with open(os.path.join(CSRC, name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_bytes(kind):
+    """HBM bytes per launch from the recorded counters, or None when they
+    were not taken or the kernel source changed since."""
+    t, cal = TRAFFIC[kind], COPY_CALIBRATION
+    if None in (t["sha256"], t["fetch_kib"], t["write_kib"], cal["fetch_kib_per_gib"],
+                cal["write_kib_per_gib"]):
+        return None
+    if source_sha256(t["source"]) != t["sha256"]:
+        return None
+    gib = float(1 << 30)
+    return int(t["fetch_kib"] / cal["fetch_kib_per_gib"] * gib +
+               t["write_kib"] / cal["write_kib_per_gib"] * gib)
 
 
 def cpu_baseline(target_s: float):
@@ -85,6 +133,99 @@ def cpu_baseline(target_s: float):
                       f"{done} passes of {per_pass / 1e6:.1f} MB packed weight in {el:.1f} s"}
 
 
+class Model:
+    """Packed weights of the 28 layers + lm_head and the activation buffers."""
+
+    def __init__(self, torch, nf4, cb, seed, stream, layers=LAYERS, with_head=True,
+                 only=None):
+        dev = "cuda"
+        self.torch, self.nf4, self.cb, self.s = torch, nf4, cb, stream
+        gen = torch.Generator(device=dev)
+        self.weights = []
+        with torch.cuda.stream(stream):
+            for layer in range(layers):
+                lw = {}
+                for i, (name, N, K) in enumerate(LINEARS):
+                    if only is not None and name not in only:
+                        continue
+                    gen.manual_seed(seed + 16 * layer + i)
+                    W = torch.randn((N, K), generator=gen, device=dev, dtype=torch.float32) * 0.02
+                    lw[name] = nf4.pack_weight(W, cb, stream=stream)
+                    del W
+                self.weights.append(lw)
+            self.lm_head = None
+            if with_head:
+                gen.manual_seed(seed + 16 * LAYERS)
+                W = torch.randn((VOCAB, HIDDEN), generator=gen, device=dev,
+                                dtype=torch.float32) * 0.02
+                self.lm_head = nf4.pack_weight(W, cb, stream=stream)
+                del W
+        stream.synchronize()
+        torch.cuda.empty_cache()
+
+        def bf16_randn(M, K, s):
+            gen.manual_seed(s)
+            return torch.randn((M, K), generator=gen, device=dev).to(torch.bfloat16).view(
+                torch.int16)
+
+        self.x1 = {K: bf16_randn(1, K, seed + 1000 + K) for K in (HIDDEN, MLP)}
+        self.xp = {K: bf16_randn(PREFILL_M, K, seed + 2000 + K) for K in (HIDDEN, MLP)}
+        self.y1 = {name: torch.empty((1, N), dtype=torch.float32, device=dev)
+                   for name, N, _ in LINEARS}
+        self.y1["lm_head"] = torch.empty((1, VOCAB), dtype=torch.float32, device=dev)
+        self.yp = {name: torch.empty((PREFILL_M, N), dtype=torch.float32, device=dev)
+                   for name, N, _ in LINEARS}
+        self.ws_bytes = max([nf4.nf4_workspace_bytes(M, N, K) for M in (1, PREFILL_M)
+                             for _, N, K in LINEARS] + [nf4.nf4_workspace_bytes(1, VOCAB, HIDDEN)])
+        self.ws = torch.zeros(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()  # inputs and the zeroed workspace are ready before stream s runs
+
+    def gemv(self, name, layer):
+        if name == "lm_head":
+            pw, K = self.lm_head, HIDDEN
+        else:
+            pw, K = self.weights[layer][name], dict((n, k) for n, _, k in LINEARS)[name]
+        self.nf4.nf4_gemv(self.x1[K], 1, pw.qweight, pw.absmax, self.cb, pw.N, K, self.y1[name],
+                          self.ws, self.ws_bytes)
+
+    def gemm(self, name, layer):
+        pw = self.weights[layer][name]
+        K = pw.K
+        self.nf4.nf4_gemm(self.xp[K], PREFILL_M, pw.qweight, pw.absmax, self.cb, pw.N, K,
+                          self.yp[name], self.ws, self.ws_bytes)
+
+
+def decode_labels():
+    return [name for _ in range(LAYERS) for name, _, _ in LINEARS] + ["lm_head"]
+
+
+def prefill_labels():
+    return [name for _ in range(LAYERS) for name, _, _ in LINEARS]
+
+
+def graph_ms(torch, stream, fn, replays, warm=1):
+    """Capture fn once on `stream`, replay it, return the median ms per
+    replay (a pair of events on the launch stream around each replay)."""
+    import statistics
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    stream.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(warm):
+            g.replay()
+    stream.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(replays)]
+    with torch.cuda.stream(stream):
+        for e0, e1 in ev:
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+    stream.synchronize()
+    return statistics.median(e0.elapsed_time(e1) for e0, e1 in ev)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,7 +234,19 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--seed", type=int, default=0x4E4634)
+    ap.add_argument("--dominant-replays", type=int, default=9)
+    ap.add_argument("--launch-log", default=None,
+                    help="write the label of every nf4_gemv/nf4_gemm launch, in order, to FILE")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="run only the counter workload: a 1 GiB copy, 3 gate|up GEMVs, 1 GEMM")
+    ap.add_argument("--summarize", default=None, metavar="DIR",
+                    help="print a markdown summary of rocprofv3 CSV output under DIR")
+    ap.add_argument("--title", default="")
+    ap.add_argument("--command", default="")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -109,69 +262,37 @@ def main():
     torch.cuda.set_device(0)
     nf4.lib()
     cb, _ = oracle.codebook()
-    dev = "cuda"
     s = torch.cuda.Stream()
+    if args.pmc_pass:
+        pmc_pass(torch, nf4, cb, args.seed, s)
+        return
 
-    # ---- weights: seeded fp32 on the GPU, quantized by nf4_pack (untimed)
-    gen = torch.Generator(device=dev)
-    weights = []
     t0 = time.perf_counter()
-    with torch.cuda.stream(s):
-        for layer in range(LAYERS):
-            lw = {}
-            for i, (name, N, K) in enumerate(LINEARS):
-                gen.manual_seed(args.seed + 16 * layer + i)
-                W = torch.randn((N, K), generator=gen, device=dev, dtype=torch.float32) * 0.02
-                lw[name] = nf4.pack_weight(W, cb, stream=s)
-                del W
-            weights.append(lw)
-        gen.manual_seed(args.seed + 16 * LAYERS)
-        W = torch.randn((VOCAB, HIDDEN), generator=gen, device=dev, dtype=torch.float32) * 0.02
-        lm_head = nf4.pack_weight(W, cb, stream=s)
-        del W
-    s.synchronize()
-    torch.cuda.empty_cache()
+    mdl = Model(torch, nf4, cb, args.seed, s)
     log(f"[bench] packed {LAYERS} layers + lm_head in {time.perf_counter() - t0:.1f} s")
-
-    def bf16_randn(M, K, seed):
-        gen.manual_seed(seed)
-        return torch.randn((M, K), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
-
-    x1 = {K: bf16_randn(1, K, args.seed + 1000 + K) for K in (HIDDEN, MLP)}
-    xp = {K: bf16_randn(PREFILL_M, K, args.seed + 2000 + K) for K in (HIDDEN, MLP)}
-    y1 = {name: torch.empty((1, N), dtype=torch.float32, device=dev) for name, N, _ in LINEARS}
-    y1["lm_head"] = torch.empty((1, VOCAB), dtype=torch.float32, device=dev)
-    yp = {name: torch.empty((PREFILL_M, N), dtype=torch.float32, device=dev)
-          for name, N, _ in LINEARS}
-    ws_bytes = max([nf4.nf4_workspace_bytes(M, N, K) for M in (1, PREFILL_M)
-                    for _, N, K in LINEARS] + [nf4.nf4_workspace_bytes(1, VOCAB, HIDDEN)])
-    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()  # inputs and the zeroed workspace are ready before stream s runs
+    launches = []
 
     decode_bytes = sum(packed_bytes(N, K) for _, N, K in LINEARS) * LAYERS \
         + packed_bytes(VOCAB, HIDDEN)
     prefill_flop = 2 * PREFILL_M * sum(N * K for _, N, K in LINEARS) * LAYERS
 
     def decode_step():
-        for lw in weights:
-            for name, N, K in LINEARS:
-                pw = lw[name]
-                nf4.nf4_gemv(x1[K], 1, pw.qweight, pw.absmax, cb, N, K, y1[name], ws, ws_bytes)
-        nf4.nf4_gemv(x1[HIDDEN], 1, lm_head.qweight, lm_head.absmax, cb, VOCAB, HIDDEN,
-                     y1["lm_head"], ws, ws_bytes)
+        for layer in range(LAYERS):
+            for name, _, _ in LINEARS:
+                mdl.gemv(name, layer)
+        mdl.gemv("lm_head", 0)
 
     def prefill_step():
-        for lw in weights:
-            for name, N, K in LINEARS:
-                pw = lw[name]
-                nf4.nf4_gemm(xp[K], PREFILL_M, pw.qweight, pw.absmax, cb, N, K, yp[name],
-                             ws, ws_bytes)
+        for layer in range(LAYERS):
+            for name, _, _ in LINEARS:
+                mdl.gemm(name, layer)
 
     # ---- capture each sequence once; replay it per step
     with torch.cuda.stream(s):
         decode_step()
         prefill_step()
     s.synchronize()
+    launches += [("gemv", n) for n in decode_labels()] + [("gemm", n) for n in prefill_labels()]
     g_dec, g_pre = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_dec, stream=s):
         decode_step()
@@ -200,12 +321,33 @@ def main():
             e2.record(s)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - w0) * 1e3 / args.steps
+    for _ in range(args.warmup + args.steps):
+        launches += [("gemv", n) for n in decode_labels()] + \
+                    [("gemm", n) for n in prefill_labels()]
     dec_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in ev]))
     pre_ms = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in ev]))
     log(f"[bench] {args.steps} timed steps: decode {dec_ms:.3f} ms, prefill {pre_ms:.3f} ms")
 
+    # ---- dominant kernels: the 28 gate|up launches back to back
+    name, N, K = DOMINANT
+    reps = args.dominant_replays
+    gemv_ms = graph_ms(torch, s, lambda: [mdl.gemv(name, l) for l in range(LAYERS)], reps)
+    gemv_us = gemv_ms * 1e3 / LAYERS
+    launches += [("gemv", name)] * (LAYERS * (reps + 1))
+    gemm_ms = graph_ms(torch, s, lambda: [mdl.gemm(name, l) for l in range(LAYERS)], reps)
+    gemm_us = gemm_ms * 1e3 / LAYERS
+    launches += [("gemm", name)] * (LAYERS * (reps + 1))
+    log(f"[bench] dominant {name}: gemv {gemv_us:.2f} us, gemm {gemm_us:.2f} us per launch")
+    if args.launch_log:
+        with open(args.launch_log, "w") as f:
+            json.dump(launches, f)
+
     dec_gbps = decode_bytes / (dec_ms * 1e-3) / 1e9
     pre_tflops = prefill_flop / (pre_ms * 1e-3) / 1e12
+    gv_bytes = packed_bytes(N, K)
+    gv_gbps = gv_bytes / (gemv_us * 1e-6) / 1e9
+    gm_flop = 2 * PREFILL_M * N * K
+    gm_tflops = gm_flop / (gemm_us * 1e-6) / 1e12
     out = {
         "metric": METRIC, "value": round(dec_gbps, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 3),
@@ -218,18 +360,108 @@ def main():
                    "block": 64, "scale_dtype": "fp32", "out_dtype": "fp32"},
         "decode_ms": round(dec_ms, 4),
         "prefill": {"value": round(pre_tflops, 2), "unit": "TFLOP/s", "ms": round(pre_ms, 3)},
-        "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "kernel": "nf4_gemv (113 launches per decode step)"},
-        "roofline_prefill": {"bound": "mfma", "achieved": round(pre_tflops, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gv_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gv_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_bytes("gemv"),
+                     "kernel": f"nf4_gemv gate|up N={N} K={K} M=1",
+                     "algorithmic_bytes": gv_bytes, "launch_us": round(gemv_us, 2)},
+        "roofline_prefill": {"bound": "mfma", "achieved": round(gm_tflops, 2),
                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                             "frac": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                             "traffic": None, "kernel": "nf4_gemm (112 launches per prefill step)"},
+                             "frac": round(gm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "traffic": traffic_bytes("gemm"),
+                             "kernel": f"nf4_gemm gate|up N={N} K={K} M={PREFILL_M}",
+                             "algorithmic_flop": gm_flop, "launch_us": round(gemm_us, 2)},
     }
     if not args.no_cpu:
         log("[bench] timing the CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def pmc_pass(torch, nf4, cb, seed, s):
+    """Counter workload, each step synchronized: a plain copy of 1 GiB
+    (counter calibration), then three gate|up GEMVs on distinct weights and
+    one gate|up GEMM."""
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    mdl = Model(torch, nf4, cb, seed, s, layers=3, with_head=False, only=("gate_up",))
+    with torch.cuda.stream(s):
+        for layer in range(3):
+            mdl.gemv("gate_up", layer)
+            s.synchronize()
+        mdl.gemm("gate_up", 0)
+        s.synchronize()
+    log("[bench] pmc pass: copy 1 GiB, 3 x gate|up gemv, 1 x gate|up gemm")
+
+
+def _kernel_short(name):
+    name = name.replace("void ", "").replace("nf4::(anonymous namespace)::", "")
+    return name.split("(")[0]
+
+
+def summarize(args):
+    """Markdown summary of rocprofv3 CSV output: kernel trace (per kernel and
+    linear, using the launch log to label nf4 launches in dispatch order) and
+    counter collection (per kernel, KiB per dispatch)."""
+    print(f"# {args.title}\n\nCommand (from the repository root, on one MI355X):\n\n```\n"
+          f"{args.command}\n```\n")
+    stats = glob.glob(os.path.join(args.summarize, "**", "*kernel_stats.csv"), recursive=True)
+    for st in stats:
+        print("rocprofv3 --stats, per kernel:\n")
+        print("| kernel | calls | total ms | mean us | min us | max us | % of GPU time |")
+        print("|---|---|---|---|---|---|---|")
+        for r in csv.DictReader(open(st)):
+            print(f"| `{_kernel_short(r['Name'])[:60]}` | {r['Calls']} | "
+                  f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['AverageNs']) / 1e3:.2f} | "
+                  f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                  f"{float(r['Percentage']):.2f} |")
+        print()
+    traces = glob.glob(os.path.join(args.summarize, "**", "*kernel_trace.csv"), recursive=True)
+    if traces:
+        rows = []
+        for t in traces:
+            rows += list(csv.DictReader(open(t)))
+        rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+        labels = json.load(open(args.launch_log)) if args.launch_log else None
+        nf4_rows = [r for r in rows if "nf4::" in r["Kernel_Name"] and
+                    ("gemv" in r["Kernel_Name"] or "gemm" in r["Kernel_Name"])]
+        if labels is not None:
+            assert len(labels) == len(nf4_rows), (len(labels), len(nf4_rows))
+        d = collections.defaultdict(list)
+        for i, r in enumerate(nf4_rows):
+            lab = labels[i][1] if labels else ""
+            d[(_kernel_short(r["Kernel_Name"]), lab)].append(
+                int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        print("Per kernel and linear (nf4 launches labelled in dispatch order from the "
+              "launch log):\n")
+        print("| kernel | linear | calls | mean us | median us | min us | total ms |")
+        print("|---|---|---|---|---|---|---|")
+        for (k, lab), v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
+            v.sort()
+            print(f"| `{k}` | {lab} | {len(v)} | {sum(v) / len(v) / 1e3:.2f} | "
+                  f"{v[len(v) // 2] / 1e3:.2f} | {v[0] / 1e3:.2f} | {sum(v) / 1e6:.3f} |")
+        print()
+    counters = glob.glob(os.path.join(args.summarize, "**", "*counter_collection.csv"),
+                         recursive=True)
+    if counters:
+        d = collections.defaultdict(list)
+        for c in counters:
+            for r in csv.DictReader(open(c)):
+                kn = r["Kernel_Name"]
+                if not ("copy" in kn.lower() or ("nf4::" in kn and ("gemv" in kn or "gemm" in kn))):
+                    continue
+                d[(_kernel_short(kn)[:60], r["Counter_Name"])].append(
+                    float(r["Counter_Value"]))
+        print("| kernel | counter | dispatches | values per dispatch |")
+        print("|---|---|---|---|")
+        for (k, cn), v in d.items():
+            print(f"| `{k}` | {cn} | {len(v)} | {', '.join(f'{x:.0f}' for x in v)} |")
+        print()
 
 
 if __name__ == "__main__":
