@@ -338,6 +338,23 @@ def main():
     gemm_us = gemm_ms * 1e3 / LAYERS
     launches += [("gemm", name)] * (LAYERS * (reps + 1))
     log(f"[bench] dominant {name}: gemv {gemv_us:.2f} us, gemm {gemm_us:.2f} us per launch")
+    # ---- lm_head: plain GEMV vs GEMV + on-device argmax (4 launches per replay)
+    amx_ws_bytes = nf4.nf4_gemv_argmax_workspace_bytes(1, VOCAB, HIDDEN)
+    amx_ws = torch.zeros(max(amx_ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    amx_idx = torch.zeros(8, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+
+    def lm_head_argmax():
+        pw = mdl.lm_head
+        nf4.nf4_gemv_argmax(mdl.x1[HIDDEN], 1, pw.qweight, pw.absmax, cb, VOCAB, HIDDEN,
+                            mdl.y1["lm_head"], amx_idx, amx_ws, amx_ws_bytes)
+
+    head_us = graph_ms(torch, s, lambda: [mdl.gemv("lm_head", 0) for _ in range(4)],
+                       reps) * 1e3 / 4
+    launches += [("gemv", "lm_head")] * (4 * (reps + 1))
+    head_amx_us = graph_ms(torch, s, lambda: [lm_head_argmax() for _ in range(4)], reps) * 1e3 / 4
+    launches += [("gemv", "lm_head_argmax")] * (4 * (reps + 1))
+    log(f"[bench] lm_head: gemv {head_us:.2f} us, gemv + argmax {head_amx_us:.2f} us")
     if args.launch_log:
         with open(args.launch_log, "w") as f:
             json.dump(launches, f)
@@ -365,6 +382,9 @@ def main():
                      "traffic": traffic_bytes("gemv"),
                      "kernel": f"nf4_gemv gate|up N={N} K={K} M=1",
                      "algorithmic_bytes": gv_bytes, "launch_us": round(gemv_us, 2)},
+        "lm_head_argmax": {"gemv_us": round(head_us, 2), "gemv_argmax_us": round(head_amx_us, 2),
+                           "host_copy_bytes": {"logits": 4 * VOCAB, "index": 4},
+                           "kernel": f"nf4_gemv_argmax N={VOCAB} K={HIDDEN} M=1"},
         "roofline_prefill": {"bound": "mfma", "achieved": round(gm_tflops, 2),
                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(gm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),

@@ -15,6 +15,7 @@
 // Lanes sharing a row combine with cross-lane shuffles, waves through LDS in
 // a fixed order, so the result is reproducible bit for bit.
 #include <atomic>
+#include <climits>
 
 #include "nf4_internal.h"
 
@@ -125,6 +126,150 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_generic_kernel(
 
 
 // ---------------------------------------------------------------------------
+// Argmax of y over n for every row m (the lm_head step that picks the next
+// token; vibevoice.c README, "The kernels that matter": the decode step ends
+// in one index per row instead of a copy of the logits).  Each workgroup
+// reduces its outputs to one candidate (value, n) per row m and stores it in
+// the workspace; the last workgroup to arrive (a device-scope counter, no
+// waiting on other workgroups) reduces the candidates and resets the counter
+// to zero.  Candidates are ordered by value, then by the lower n: a total
+// order, so any reduction tree picks the same winner, the first n that
+// holds the maximum.  NaN never wins; an all-NaN row gives index -1.
+// Workspace: [0, 4) arrival counter; from byte 256, P x M candidates of 8 B.
+// ---------------------------------------------------------------------------
+namespace amax {
+constexpr size_t kCandOffset = 256;
+__device__ inline bool better(float v, int n, float bv, int bn) {
+  return v > bv || (v == bv && n < bn);
+}
+__device__ inline uint64_t pack(float v, int n) {
+  return ((uint64_t)(uint32_t)n << 32) | (uint64_t)__float_as_uint(v);
+}
+__device__ inline void unpack(uint64_t c, float &v, int &n) {
+  v = __uint_as_float((uint32_t)c);
+  n = (int)(uint32_t)(c >> 32);
+}
+template <int M>
+__device__ inline void wave_reduce(float (&bv)[M], int (&bn)[M]) {
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv[m], off);
+      const int on = __shfl_xor(bn[m], off);
+      if (better(ov, on, bv[m], bn[m])) {
+        bv[m] = ov;
+        bn[m] = on;
+      }
+    }
+}
+// Reduce the workgroup's candidates across waves into lds[M] (threads < M
+// return them in v, n).  lds holds (waves x M) entries.
+template <int M>
+__device__ inline void block_reduce(float (&bv)[M], int (&bn)[M], uint64_t *lds, float &v,
+                                    int &n) {
+  wave_reduce<M>(bv, bn);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  if (lane == 0) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) lds[wave * M + m] = pack(bv[m], bn[m]);
+  }
+  __syncthreads();
+  v = -INFINITY;
+  n = INT_MAX;
+  if (threadIdx.x < M) {
+    for (int w = 0; w < nw; ++w) {
+      float ov;
+      int on;
+      unpack(lds[w * M + threadIdx.x], ov, on);
+      if (better(ov, on, v, n)) {
+        v = ov;
+        n = on;
+      }
+    }
+  }
+}
+// Every thread of the workgroup calls this with its own candidates.
+template <int M>
+__device__ void finish(float (&bv)[M], int (&bn)[M], int b, int P, uint32_t *counter,
+                       uint64_t *cand, int32_t *index, uint64_t *lds, int *flag) {
+  float v;
+  int n;
+  block_reduce<M>(bv, bn, lds, v, n);
+  if (threadIdx.x < M) {
+    __hip_atomic_store(cand + (size_t)b * M + threadIdx.x, pack(v, n), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    // the candidate is stored device-wide before the arrival is counted
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old =
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = old == (uint32_t)(P - 1);
+  }
+  __syncthreads();
+  if (!*flag) return;
+  // the last workgroup: every candidate is stored
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    bv[m] = -INFINITY;
+    bn[m] = INT_MAX;
+  }
+  for (int c = threadIdx.x; c < P; c += blockDim.x) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float ov;
+      int on;
+      unpack(__hip_atomic_load(cand + (size_t)c * M + m, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT),
+             ov, on);
+      if (better(ov, on, bv[m], bn[m])) {
+        bv[m] = ov;
+        bn[m] = on;
+      }
+    }
+  }
+  __syncthreads();  // lds is reused
+  block_reduce<M>(bv, bn, lds, v, n);
+  if (threadIdx.x < M) index[threadIdx.x] = n == INT_MAX ? -1 : n;
+  if (threadIdx.x == 0)
+    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+}  // namespace amax
+
+// Argmax over an already written y (the generic GEMV path): workgroup b
+// scans columns [N b / P, N (b + 1) / P).
+template <int M>
+__global__ __launch_bounds__(256) void argmax_kernel(const float *__restrict__ y, int N,
+                                                     uint32_t *counter, uint64_t *cand,
+                                                     int32_t *index) {
+  __shared__ uint64_t lds[4 * M];
+  __shared__ int flag;
+  const int P = gridDim.x, b = blockIdx.x;
+  const int n0 = (int)((int64_t)N * b / P), n1 = (int)((int64_t)N * (b + 1) / P);
+  float bv[M];
+  int bn[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    bv[m] = -INFINITY;
+    bn[m] = INT_MAX;
+  }
+  for (int n = n0 + (int)threadIdx.x; n < n1; n += blockDim.x) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float v = y[(int64_t)m * N + n];
+      if (amax::better(v, n, bv[m], bn[m])) {
+        bv[m] = v;
+        bn[m] = n;
+      }
+    }
+  }
+  amax::finish<M>(bv, bn, b, P, counter, cand, index, lds, &flag);
+}
+
+
+// ---------------------------------------------------------------------------
 // Fast path (codebook of bf16 values, x small enough for LDS).
 //
 // Work split: workgroup b owns the whole row groups [G*b/P, G*(b+1)/P), a
@@ -151,11 +296,11 @@ constexpr int kLdsBytes = 160 * 1024;                // LDS per workgroup on gfx
 // instructions may cross; vector memory instructions may not.
 constexpr int kSchedAllButGlobalLoads = 0x1 | 0x2 | 0x4 | 0x8 | 0x80 | 0x100 | 0x200 | 0x400;
 
-template <int M>
+template <int M, bool ARGMAX>
 __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
     const uint16_t *__restrict__ x, const uint4 *__restrict__ qw,
     const float2 *__restrict__ am, CodeTerms ct, int N, int K, int KT, int G, int P,
-    float *__restrict__ y) {
+    float *__restrict__ y, uint32_t *counter, uint64_t *cand, int32_t *index) {
   constexpr int D = kFastDepth;
   // The table is the kernel's only static LDS array, so it sits at address
   // 0 and a lookup address needs no base added; x and the partials follow in
@@ -327,12 +472,33 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
 
   // ---- every row group of the workgroup: sum the waves' partials in order
   __syncthreads();
-  for (int c = threadIdx.x; c < Gw * 16 * M; c += blockDim.x) {
-    const int jj = c / (16 * M), rem = c - jj * 16 * M, rr = rem / M, m = rem - rr * M;
-    float sum = 0.0f;
+  float bv[M];
+  int bn[M];
 #pragma unroll
-    for (int w = 0; w < kFastWaves; ++w) sum += red[((jj * kFastWaves + w) * 16 + rr) * M + m];
-    y[(int64_t)m * N + (int64_t)(g0 + jj) * 16 + rr] = sum;
+  for (int m = 0; m < M; ++m) {
+    bv[m] = -INFINITY;
+    bn[m] = INT_MAX;
+  }
+  for (int c = threadIdx.x; c < Gw * 16; c += blockDim.x) {
+    const int jj = c >> 4, rr = c & 15;
+    const int n = (g0 + jj) * 16 + rr;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kFastWaves; ++w) sum += red[((jj * kFastWaves + w) * 16 + rr) * M + m];
+      y[(int64_t)m * N + n] = sum;
+      if (ARGMAX && amax::better(sum, n, bv[m], bn[m])) {
+        bv[m] = sum;
+        bn[m] = n;
+      }
+    }
+  }
+  if constexpr (ARGMAX) {
+    // the table is no longer read: its first bytes hold the reduction
+    uint64_t *scratch = reinterpret_cast<uint64_t *>(table);
+    amax::finish<M>(bv, bn, blockIdx.x, P, counter, cand, index, scratch,
+                    reinterpret_cast<int *>(table) + 2 * kFastWaves * M);
   }
 }
 
@@ -364,20 +530,22 @@ bool fast_eligible(int M, int64_t N, int64_t K, int nterm) {
   return nterm == 1 && qbytes < (int64_t(1) << 32) && fast_dyn_bytes(M, K, 1) <= kDynMax;
 }
 
-template <int M>
+template <int M, bool ARGMAX>
 hipError_t launch_fast(const uint16_t *x, const uint4 *qw, const float2 *am, const CodeTerms &ct,
-                       int64_t N, int64_t K, float *y, hipStream_t s) {
+                       int64_t N, int64_t K, float *y, uint32_t *counter, uint64_t *cand,
+                       int32_t *index, hipStream_t s) {
   static std::atomic<bool> attr_set{false};
   if (!attr_set.load(std::memory_order_acquire)) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&gemv_fast_kernel<M>),
+        reinterpret_cast<const void *>(&gemv_fast_kernel<M, ARGMAX>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDynMax);
     if (e != hipSuccess) return e;
     attr_set.store(true, std::memory_order_release);
   }
   const FastPlan p = fast_plan(M, N, K);
-  hipLaunchKernelGGL((gemv_fast_kernel<M>), dim3(p.P), dim3(kFastWaves * 64), p.lds, s, x, qw,
-                     am, ct, (int)N, (int)K, (int)tiles_k(K), (int)(N / kTileRows), p.P, y);
+  hipLaunchKernelGGL((gemv_fast_kernel<M, ARGMAX>), dim3(p.P), dim3(kFastWaves * 64), p.lds, s, x,
+                     qw, am, ct, (int)N, (int)K, (int)tiles_k(K), (int)(N / kTileRows), p.P, y,
+                     counter, cand, index);
   return hipGetLastError();
 }
 
@@ -420,6 +588,55 @@ hipError_t launch_t(const uint16_t *x, int M, const uint4 *qw, const float2 *am,
 
 size_t gemv_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
 
+namespace {
+int argmax_grid(int64_t N) {
+  const int64_t cus = device_cu_count();
+  const int64_t want = (N + 1023) / 1024;
+  return (int)(want < cus ? want : cus);
+}
+template <int M>
+hipError_t launch_argmax_m(const uint16_t *x, const uint4 *q, const float2 *a, const CodeTerms &ct,
+                           int nterm, int64_t N, int64_t K, float *y, uint32_t *counter,
+                           uint64_t *cand, int32_t *index, hipStream_t s) {
+  if (fast_eligible(M, N, K, nterm))
+    return launch_fast<M, true>(x, q, a, ct, N, K, y, counter, cand, index, s);
+  const hipError_t e = nterm == 1 ? launch_m<M, 1>(x, q, a, ct, N, K, y, s)
+                                  : launch_m<M, 3>(x, q, a, ct, N, K, y, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(argmax_kernel<M>, dim3(argmax_grid(N)), dim3(256), 0, s, y, (int)N, counter,
+                     cand, index);
+  return hipGetLastError();
+}
+}  // namespace
+
+size_t gemv_argmax_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  // candidates for the larger of the two possible grids
+  int64_t P = argmax_grid(N);
+  const FastPlan fp = fast_plan((int)M, N, K);
+  if (fp.P > P) P = fp.P;
+  return amax::kCandOffset + (size_t)P * (size_t)M * sizeof(uint64_t);
+}
+
+hipError_t launch_gemv_argmax(const uint16_t *x, int M, const uint8_t *qw, const float *am,
+                              const CodeTerms &ct, int nterm, int64_t N, int64_t K, float *y,
+                              int32_t *index, void *ws, hipStream_t s) {
+  const uint4 *q = reinterpret_cast<const uint4 *>(qw);
+  const float2 *a = reinterpret_cast<const float2 *>(am);
+  uint32_t *counter = reinterpret_cast<uint32_t *>(ws);
+  uint64_t *cand = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(ws) + amax::kCandOffset);
+  switch (M) {
+    case 1: return launch_argmax_m<1>(x, q, a, ct, nterm, N, K, y, counter, cand, index, s);
+    case 2: return launch_argmax_m<2>(x, q, a, ct, nterm, N, K, y, counter, cand, index, s);
+    case 3: return launch_argmax_m<3>(x, q, a, ct, nterm, N, K, y, counter, cand, index, s);
+    case 4: return launch_argmax_m<4>(x, q, a, ct, nterm, N, K, y, counter, cand, index, s);
+    case 5: return launch_argmax_m<5>(x, q, a, ct, nterm, N, K, y, counter, cand, index, s);
+    case 6: return launch_argmax_m<6>(x, q, a, ct, nterm, N, K, y, counter, cand, index, s);
+    case 7: return launch_argmax_m<7>(x, q, a, ct, nterm, N, K, y, counter, cand, index, s);
+    case 8: return launch_argmax_m<8>(x, q, a, ct, nterm, N, K, y, counter, cand, index, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_gemv(const uint16_t *x, int M, const uint8_t *qw, const float *am,
                        const CodeTerms &ct, int nterm, int64_t N, int64_t K, float *y, void *ws,
                        hipStream_t s) {
@@ -427,14 +644,14 @@ hipError_t launch_gemv(const uint16_t *x, int M, const uint8_t *qw, const float 
   const float2 *a = reinterpret_cast<const float2 *>(am);
   if (fast_eligible(M, N, K, nterm)) {
     switch (M) {
-      case 1: return launch_fast<1>(x, q, a, ct, N, K, y, s);
-      case 2: return launch_fast<2>(x, q, a, ct, N, K, y, s);
-      case 3: return launch_fast<3>(x, q, a, ct, N, K, y, s);
-      case 4: return launch_fast<4>(x, q, a, ct, N, K, y, s);
-      case 5: return launch_fast<5>(x, q, a, ct, N, K, y, s);
-      case 6: return launch_fast<6>(x, q, a, ct, N, K, y, s);
-      case 7: return launch_fast<7>(x, q, a, ct, N, K, y, s);
-      case 8: return launch_fast<8>(x, q, a, ct, N, K, y, s);
+      case 1: return launch_fast<1, false>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s);
+      case 2: return launch_fast<2, false>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s);
+      case 3: return launch_fast<3, false>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s);
+      case 4: return launch_fast<4, false>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s);
+      case 5: return launch_fast<5, false>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s);
+      case 6: return launch_fast<6, false>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s);
+      case 7: return launch_fast<7, false>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s);
+      case 8: return launch_fast<8, false>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s);
       default: return hipErrorInvalidValue;
     }
   }

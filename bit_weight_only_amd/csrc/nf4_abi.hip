@@ -205,6 +205,27 @@ nf4_status nf4_gemv(const uint16_t *x, int64_t M, const uint8_t *qweight, const 
       nf4::launch_gemv(x, (int)M, qweight, absmax, ct, nterm, N, K, y, workspace, stream));
 }
 
+size_t nf4_gemv_argmax_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || M > kMaxGemvM || !shape_ok(N, K)) return 0;
+  return nf4::gemv_argmax_workspace_bytes(M, N, K);
+}
+
+nf4_status nf4_gemv_argmax(const uint16_t *x, int64_t M, const uint8_t *qweight,
+                           const float *absmax, const float codebook[16], int64_t N, int64_t K,
+                           float *y, int32_t *index, void *workspace, size_t ws_bytes,
+                           hipStream_t stream) {
+  nf4_status st = check_linear_args(x, M, qweight, absmax, codebook, N, K, y, kMaxGemvM);
+  if (st != NF4_OK) return st;
+  if (!index || !workspace) return NF4_ERR_NULL;
+  if (!aligned16(index) || !aligned16(workspace)) return NF4_ERR_ALIGN;
+  if (nf4::gemv_argmax_workspace_bytes(M, N, K) > ws_bytes) return NF4_ERR_WORKSPACE;
+  nf4::CodeTerms ct;
+  const int nterm = split_codebook(codebook, ct);
+  if (nterm == 0) return NF4_ERR_CODEBOOK;
+  return from_hip(nf4::launch_gemv_argmax(x, (int)M, qweight, absmax, ct, nterm, N, K, y, index,
+                                          workspace, stream));
+}
+
 nf4_status nf4_gemm(const uint16_t *x, int64_t M, const uint8_t *qweight, const float *absmax,
                     const float codebook[16], int64_t N, int64_t K, float *y, void *workspace,
                     size_t ws_bytes, hipStream_t stream) {

@@ -58,6 +58,11 @@ hipError_t launch_gemv(const uint16_t *x, int M, const uint8_t *qw, const float 
                        const CodeTerms &ct, int nterm, int64_t N, int64_t K, float *y, void *ws,
                        hipStream_t s);
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// GEMV followed by the row-wise argmax of y (fused into the fast kernel).
+hipError_t launch_gemv_argmax(const uint16_t *x, int M, const uint8_t *qw, const float *am,
+                              const CodeTerms &ct, int nterm, int64_t N, int64_t K, float *y,
+                              int32_t *index, void *ws, hipStream_t s);
+size_t gemv_argmax_workspace_bytes(int64_t M, int64_t N, int64_t K);
 // Compute units of the current device (queried once per device).
 int device_cu_count();
 hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, const float *am,

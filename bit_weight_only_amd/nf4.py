@@ -18,7 +18,8 @@ NF4_OK, NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_CODEBOOK, NF4_ERR_WO
     NF4_ERR_HIP = range(7)
 
 EXPORTS = ("nf4_status_string", "nf4_qweight_bytes", "nf4_absmax_bytes", "nf4_workspace_bytes",
-           "nf4_pack", "nf4_dequant", "nf4_repack", "nf4_unpack", "nf4_gemv", "nf4_gemm")
+           "nf4_pack", "nf4_dequant", "nf4_repack", "nf4_unpack", "nf4_gemv", "nf4_gemm",
+           "nf4_gemv_argmax_workspace_bytes", "nf4_gemv_argmax")
 
 _lib = None
 
@@ -56,6 +57,10 @@ def lib() -> ctypes.CDLL:
         for f in (L.nf4_gemv, L.nf4_gemm):
             f.restype = st
             f.argtypes = [vp, i64, vp, vp, fp, i64, i64, vp, vp, sz, vp]
+        L.nf4_gemv_argmax_workspace_bytes.restype = sz
+        L.nf4_gemv_argmax_workspace_bytes.argtypes = [i64, i64, i64]
+        L.nf4_gemv_argmax.restype = st
+        L.nf4_gemv_argmax.argtypes = [vp, i64, vp, vp, fp, i64, i64, vp, vp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -133,6 +138,17 @@ def nf4_gemm(x, M: int, qweight, absmax, codebook, N: int, K: int, y, workspace=
              ws_bytes: int = 0, stream=None) -> None:
     _check(lib().nf4_gemm(_ptr(x), M, _ptr(qweight), _ptr(absmax), _codebook(codebook), N, K,
                           _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)), "nf4_gemm")
+
+
+def nf4_gemv_argmax_workspace_bytes(M: int, N: int, K: int) -> int:
+    return lib().nf4_gemv_argmax_workspace_bytes(M, N, K)
+
+
+def nf4_gemv_argmax(x, M: int, qweight, absmax, codebook, N: int, K: int, y, index, workspace,
+                    ws_bytes: int, stream=None) -> None:
+    _check(lib().nf4_gemv_argmax(_ptr(x), M, _ptr(qweight), _ptr(absmax), _codebook(codebook),
+                                 N, K, _ptr(y), _ptr(index), _ptr(workspace), ws_bytes,
+                                 _stream(stream)), "nf4_gemv_argmax")
 
 
 # ------------------------------------------------------------ conveniences

@@ -120,6 +120,27 @@ nf4_status nf4_gemv(const uint16_t *x, int64_t M, const uint8_t *qweight, const 
                     const float codebook[16], int64_t N, int64_t K, float *y, void *workspace,
                     size_t ws_bytes, hipStream_t stream);
 
+/* Bytes of workspace nf4_gemv_argmax needs for an M x N x K call on the
+ * current device: an arrival counter and one 8-byte candidate per workgroup
+ * and row.  0 for shapes nf4_gemv rejects. */
+size_t nf4_gemv_argmax_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* Decode GEMV followed by the argmax of each output row: the step that turns
+ * lm_head logits into the next token on the device (vibevoice.c README, "The
+ * kernels that matter": the host then copies M indices instead of M x N
+ * logits).  y is computed and written exactly as by nf4_gemv with the same
+ * arguments; then index[m] = the smallest n with y[m][n] == max_n y[m][n],
+ * compared as fp32 (NaN never wins; a row of NaN gives -1).  index: device
+ * int32[M], 16-byte aligned.  workspace: at least
+ * nf4_gemv_argmax_workspace_bytes(M, N, K) bytes, zero-filled once at
+ * allocation; every call leaves its counter at zero, and calls sharing one
+ * workspace must be ordered.  Errors as nf4_gemv, plus NF4_ERR_NULL for a
+ * NULL index or workspace. */
+nf4_status nf4_gemv_argmax(const uint16_t *x, int64_t M, const uint8_t *qweight,
+                           const float *absmax, const float codebook[16], int64_t N, int64_t K,
+                           float *y, int32_t *index, void *workspace, size_t ws_bytes,
+                           hipStream_t stream);
+
 /* Prefill GEMM, any M >= 1: same result definition as nf4_gemv, computed on
  * bf16 matrix cores with the codes as exact bf16 operands and the fp32
  * scales applied outside the matrix product once per 64-block.  workspace:

@@ -131,6 +131,28 @@ def test_layout_entry_validation():
     assert d(A, A, cbarr(bad), 16, 64, A, None) == nf4.NF4_ERR_CODEBOOK
 
 
+def test_argmax_validation():
+    f = lambda *a: call("nf4_gemv_argmax", *a)
+    ok = [A, 1, A, A, cbarr(), 16, 64, A, A, A, 1 << 20, None]
+    for i, err in ((0, nf4.NF4_ERR_NULL), (2, nf4.NF4_ERR_NULL), (7, nf4.NF4_ERR_NULL),
+                   (8, nf4.NF4_ERR_NULL), (9, nf4.NF4_ERR_NULL)):
+        bad = list(ok)
+        bad[i] = None
+        assert f(*bad) == err, i
+    for M in (0, 9):
+        bad = list(ok)
+        bad[1] = M
+        assert f(*bad) == nf4.NF4_ERR_SHAPE
+    bad = list(ok)
+    bad[5] = 24
+    assert f(*bad) == nf4.NF4_ERR_SHAPE
+    bad = list(ok)
+    bad[8] = A + 4
+    assert f(*bad) == nf4.NF4_ERR_ALIGN
+    for M, N, K in ((0, 16, 64), (9, 16, 64), (1, 24, 64), (1, 16, 96)):
+        assert nf4.nf4_gemv_argmax_workspace_bytes(M, N, K) == 0
+
+
 def test_binding_raises_named_errors():
     with pytest.raises(nf4.NF4Error) as e:
         nf4.nf4_gemv(A, 9, A, A, CB, 16, 64, A, stream=0)
