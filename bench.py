@@ -51,6 +51,7 @@ HIDDEN, MLP, KV, VOCAB = 3584, 18944, 512, 152064
 LINEARS = [("qkv", HIDDEN + 2 * KV, HIDDEN), ("o", HIDDEN, HIDDEN),
            ("gate_up", 2 * MLP, HIDDEN), ("down", HIDDEN, MLP)]
 PREFILL_M = 1024
+TAIL_M = 113  # last chunk of the 14449-row long-audio prompt
 DOMINANT = ("gate_up", 2 * MLP, HIDDEN)
 
 # HBM traffic per launch of the dominant kernels, from rocprofv3 --pmc runs of
@@ -339,6 +340,17 @@ def main():
     head_amx_us = graph_ms(torch, s, lambda: [lm_head_argmax() for _ in range(4)], reps) * 1e3 / 4
     launches += [("gemv", "lm_head_argmax")] * (4 * (reps + 1))
     log(f"[bench] lm_head: gemv {head_us:.2f} us, gemv + argmax {head_amx_us:.2f} us")
+    # ---- the 113-row tail of the 14449-row long-audio prefill (14 x 1024 + 113)
+    def tail_step():
+        for layer in range(LAYERS):
+            for lname, _, _ in LINEARS:
+                pw = mdl.weights[layer][lname]
+                nf4.nf4_gemm(mdl.xp[pw.K], TAIL_M, pw.qweight, pw.absmax, cb, pw.N, pw.K,
+                             mdl.yp[lname], mdl.ws, mdl.ws_bytes)
+    tail_ms = graph_ms(torch, s, tail_step, reps)
+    launches += [("gemm", n) for _ in range(reps + 1) for n in prefill_labels()]
+    tail_flop = 2 * TAIL_M * sum(N_ * K_ for _, N_, K_ in LINEARS) * LAYERS
+    log(f"[bench] prefill tail M={TAIL_M}: {tail_ms:.3f} ms")
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -386,6 +398,9 @@ def main():
                      "traffic": traffic_bytes("gemv"),
                      "kernel": f"nf4_gemv gate|up N={N} K={K} M=1",
                      "algorithmic_bytes": gv_bytes, "launch_us": round(gemv_us, 2)},
+        "prefill_tail": {"M": TAIL_M, "ms": round(tail_ms, 3),
+                         "value": round(tail_flop / (tail_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                         "note": "28 layers x 4 fused linears at M=113 (skinny path for narrow N)"},
         "lm_head_argmax": {"gemv_us": round(head_us, 2), "gemv_argmax_us": round(head_amx_us, 2),
                            "host_copy_bytes": {"logits": 4 * VOCAB, "index": 4},
                            "kernel": f"nf4_gemv_argmax N={VOCAB} K={HIDDEN} M=1"},

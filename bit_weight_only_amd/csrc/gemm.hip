@@ -394,9 +394,213 @@ __global__ __launch_bounds__(128 * WM) void gemm_pipe_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Skinny path, M <= 64 (a decode batch, a short prefill chunk or the tail of
+// a long one).  There the weights dominate: the job is to stream them at the
+// memory rate, which a K loop synchronised at every step cannot do with few
+// tiles across N.  Instead each wave owns one row group and streams all of
+// its K on its own, like the decode GEMV, keeping kSkD weight tiles in
+// flight in registers; only x is shared, staged in LDS in 32 KB chunks
+// (double buffered, one barrier per chunk).  Per tile the lane's 16 code
+// bytes become the B fragments of four 32-k MFMA steps through the pair
+// table, and the MB m-blocks of x supply the A fragments.
+// Every output is computed with exactly the operations of gemm_pipe_kernel:
+// per 64-block P = MFMA(kk=0, zero) then MFMA(kk=1, P), acc = fmaf(s, P, acc)
+// in K order, with the same operand values in the same lanes, so the two
+// kernels give bit-identical rows and the choice between them (by M) does
+// not change any row.
+// ---------------------------------------------------------------------------
+namespace skinny {
+constexpr int kWaves = 4;        // row groups per workgroup
+constexpr int kXBuf = 32 * 1024; // bytes of one x chunk buffer
+}  // namespace skinny
+
+template <int MB, int D>
+__global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
+    const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ qw,
+    const float *__restrict__ am, CodeTerms ct, int N, int K, int KT, int G,
+    float *__restrict__ y) {
+  constexpr int XR = 16 * MB;                  // x rows held (m-blocks of 16)
+  constexpr int KX = skinny::kXBuf / (XR * 2); // k per chunk: 1024, 512, 256
+  constexpr int TC = KX / kTileK;              // tiles per chunk: 8, 4, 2
+  constexpr int CPR = KX / 8;                  // 16-byte chunks per x row
+  constexpr int XV = skinny::kXBuf / 16 / (64 * skinny::kWaves);  // loads per thread per chunk
+  static_assert(D % TC == 0, "the prefetch ring is a whole number of chunks");
+  __shared__ __attribute__((aligned(16))) char lds[2 * skinny::kXBuf + pipe::kTableBytes];
+  char *ldsT = lds + 2 * skinny::kXBuf;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, h = lane >> 4;
+  const int g = blockIdx.x * skinny::kWaves + wave;
+  const int gc = g < G ? g : G - 1;  // a wave past N re-reads the last row group, stores nothing
+  const int m0 = blockIdx.y * XR;    // first x row of this workgroup
+  const int NC = (KT + TC - 1) / TC;  // chunks
+  const bool half_tail = (K & (kTileK - 1)) != 0;  // last tile holds one 64-block
+
+  // ---- x chunk c -> registers (rows past M re-read row M-1; k past K is 0)
+  auto load_x = [&](int c, uint4 (&xv)[XV]) {
+#pragma unroll
+    for (int u = 0; u < XV; ++u) {
+      const int q = tid + u * 64 * skinny::kWaves;
+      const int R = q / CPR, cr = q - R * CPR;
+      const int k = c * KX + cr * 8;
+      const int m = m0 + R < M ? m0 + R : M - 1;
+      xv[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (c < NC && k < K) xv[u] = *reinterpret_cast<const uint4 *>(x + (int64_t)m * K + k);
+    }
+  };
+  // row R, 16-byte chunk cr stored at chunk cr ^ (R & 15): the 16 rows of an
+  // A fragment fall in 16 different bank groups
+  auto store_x = [&](int buf, const uint4 (&xv)[XV]) {
+#pragma unroll
+    for (int u = 0; u < XV; ++u) {
+      const int q = tid + u * 64 * skinny::kWaves;
+      const int R = q / CPR, cr = q - R * CPR;
+      *reinterpret_cast<uint4 *>(lds + buf * skinny::kXBuf + R * (KX * 2) +
+                                 ((cr ^ (R & 15)) * 16)) = xv[u];
+    }
+  };
+
+  // ---- pair table (32 copies), the codebook staged in x buffer 1 first
+  uint16_t *codes16 = reinterpret_cast<uint16_t *>(lds + skinny::kXBuf);
+  if (tid < 16) codes16[tid] = ct.t[0][tid];
+  // weight prefetch: tile i of this wave's row group
+  const char *qrow = reinterpret_cast<const char *>(qw) + (int64_t)gc * KT * kTileBytes + lane * 16;
+  const char *srow = reinterpret_cast<const char *>(am) + (int64_t)gc * KT * kTileScales * 4 + r * 8;
+  uint4 wb[D];
+  float2 sb[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    const int i = d < KT ? d : KT - 1;
+    wb[d] = *reinterpret_cast<const uint4 *>(qrow + (int64_t)i * kTileBytes);
+    sb[d] = *reinterpret_cast<const float2 *>(srow + (int64_t)i * kTileScales * 4);
+  }
+  uint4 xv[XV];
+  load_x(0, xv);
+  __syncthreads();
+  for (int c = tid; c < pipe::kTableBytes / 16; c += 64 * skinny::kWaves) {
+    const int e = c / (pipe::kCopies / 4);
+    const uint32_t v = (uint32_t)codes16[e & 15] | ((uint32_t)codes16[e >> 4] << 16);
+    reinterpret_cast<uint4 *>(ldsT)[c] = make_uint4(v, v, v, v);
+  }
+  store_x(0, xv);
+  load_x(1, xv);
+  __syncthreads();
+
+  const uint32_t tcopy = (uint32_t)(lane & (pipe::kCopies - 1)) * 4;
+  f32x4 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  // A fragment of row mb*16 + r, logical chunk `cl` of the chunk's row
+  const uint32_t arow = (uint32_t)(r * (KX * 2));
+  // B fragments of the four 32-k steps of a tile, from the lane's 16 code bytes
+  auto lookups = [&](const uint4 &w, bf16x8 (&B)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t wd = j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w;
+      uint32_t bb[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t e = (wd >> (8 * q)) & 0xFFu;
+        bb[q] = *reinterpret_cast<const uint32_t *>(ldsT + e * (pipe::kCopies * 4) + tcopy);
+      }
+      B[j] = __builtin_bit_cast(bf16x8, make_uint4(bb[0], bb[1], bb[2], bb[3]));
+    }
+  };
+  // The lookups run one tile ahead of the products (two sets chosen by tile
+  // parity, D even), so their LDS latency overlaps the matrix instructions.
+  static_assert(D % 2 == 0, "B sets alternate by tile parity");
+  bf16x8 Bs[2][4];
+  lookups(wb[0], Bs[0]);
+
+  for (int base = 0; base < NC * TC; base += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int i = base + d;                // tile
+      const int tl = d % TC, cbuf = (i / TC) & 1;
+      // Tiles past K run on clamped data and are not folded; neither is the
+      // empty second block of a half tile (selects, not branches).
+      const bool live0 = i < KT, live1 = live0 && !(half_tail && i == KT - 1);
+      lookups(wb[(d + 1) % D], Bs[(d + 1) & 1]);
+      const bf16x8 (&B)[4] = Bs[d & 1];
+      const char *xc = lds + cbuf * skinny::kXBuf + arow;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const char *xm = xc + mb * 16 * (KX * 2);
+        bf16x8 A[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          A[j] = *reinterpret_cast<const bf16x8 *>(xm + (((tl * 16 + j * 4 + h) ^ r) * 16));
+        f32x4 p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0], B[0], zero, 0, 0, 0);
+        p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1], B[1], p, 0, 0, 0);
+        f32x4 q2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[2], B[2], zero, 0, 0, 0);
+        q2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[3], B[3], q2, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float f0 = fmaf(sb[d].x, p[e], acc[mb][e]);
+          const float a0 = live0 ? f0 : acc[mb][e];
+          const float f1 = fmaf(sb[d].y, q2[e], a0);
+          acc[mb][e] = live1 ? f1 : a0;
+        }
+      }
+      // ---- refill this slot D tiles ahead (clamped: same loads every step)
+      {
+        const int ni = i + D < KT ? i + D : KT - 1;
+        wb[d] = *reinterpret_cast<const uint4 *>(qrow + (int64_t)ni * kTileBytes);
+        sb[d] = *reinterpret_cast<const float2 *>(srow + (int64_t)ni * kTileScales * 4);
+      }
+      // ---- chunk boundary: x of the next chunk into the other buffer (it
+      // held the chunk before this one, which every wave finished before the
+      // previous barrier), the loads of the chunk after, then the barrier
+      // that makes the next chunk visible
+      if (tl == TC - 1) {
+        const int cn = i / TC + 1;
+        store_x(cn & 1, xv);
+        load_x(cn + 1, xv);
+        __syncthreads();
+      }
+      // keep the next tiles' work from being hoisted across this one
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = m0 + mb * 16 + 4 * h + e;
+      if (g < G && m < M) y[(int64_t)m * N + (int64_t)g * 16 + r] = acc[mb][e];
+    }
+}
+
 }  // namespace
 
 size_t gemm_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+
+bool skinny_eligible(int64_t M, int64_t N, int64_t K, int nterm) {
+  // 32-bit tile indices and element offsets
+  return nterm == 1 && M >= 1 && M <= kSkinnyMaxM && M * K < (int64_t(1) << 31) &&
+         (N / kTileRows) * tiles_k(K) < (int64_t(1) << 31);
+}
+
+hipError_t launch_skinny(const uint16_t *x, int64_t M, const uint8_t *qw, const float *am,
+                         const CodeTerms &ct, int64_t N, int64_t K, float *y, hipStream_t s) {
+  const int64_t G = N / kTileRows;
+  const unsigned gx = (unsigned)((G + skinny::kWaves - 1) / skinny::kWaves);
+  const dim3 block(64 * skinny::kWaves);
+  const int KT = (int)tiles_k(K);
+  // up to 16 rows: one m-block per wave; otherwise 32-row groups of x along
+  // the grid's y (workgroups of one row-group block run side by side and
+  // share the weights through the caches)
+  if (M <= 16)
+    hipLaunchKernelGGL((gemm_skinny_kernel<1, 8>), dim3(gx), block, 0, s, x, (int)M, qw, am, ct,
+                       (int)N, (int)K, KT, (int)G, y);
+  else
+    hipLaunchKernelGGL((gemm_skinny_kernel<2, 8>), dim3(gx, (unsigned)((M + 31) / 32)), block, 0,
+                       s, x, (int)M, qw, am, ct, (int)N, (int)K, KT, (int)G, y);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, const float *am,
                        const CodeTerms &ct, int nterm, int64_t N, int64_t K, float *y, void *,
@@ -407,6 +611,14 @@ hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, const fl
   // 32-bit byte offsets into x and the code buffer for the copies
   const bool dma_ok = M * K * 2 < (int64_t(1) << 32) &&
                       (N / kTileRows) * KT * kTileBytes < (int64_t(1) << 32);
+  // The skinny and tiled kernels give bit-identical rows, so the choice is
+  // about speed only: skinny up to 64 rows, and up to 256 rows when the tiled
+  // grid would occupy less than half of the CUs (narrow N).
+  if (skinny_eligible(M, N, K, nterm)) {
+    const int64_t ntile = (N + BN - 1) / BN;
+    if (M <= 64 || ntile * ((M + 127) / 128) < device_cu_count() / 2)
+      return launch_skinny(x, M, qw, am, ct, N, K, y, s);
+  }
   if (nterm == 1 && dma_ok) {
     // 256-row tiles (8 waves) unless 128-row tiles (4 waves) need no more
     // rounds of workgroups over the CUs: a 128-row tile takes nearly as long

@@ -600,8 +600,12 @@ hipError_t launch_argmax_m(const uint16_t *x, const uint4 *q, const float2 *a, c
                            uint64_t *cand, int32_t *index, hipStream_t s) {
   if (fast_eligible(M, N, K, nterm))
     return launch_fast<M, true>(x, q, a, ct, N, K, y, counter, cand, index, s);
-  const hipError_t e = nterm == 1 ? launch_m<M, 1>(x, q, a, ct, N, K, y, s)
-                                  : launch_m<M, 3>(x, q, a, ct, N, K, y, s);
+  const hipError_t e =
+      skinny_eligible(M, N, K, nterm)
+          ? launch_skinny(x, M, reinterpret_cast<const uint8_t *>(q),
+                          reinterpret_cast<const float *>(a), ct, N, K, y, s)
+      : nterm == 1 ? launch_m<M, 1>(x, q, a, ct, N, K, y, s)
+                   : launch_m<M, 3>(x, q, a, ct, N, K, y, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(argmax_kernel<M>, dim3(argmax_grid(N)), dim3(256), 0, s, y, (int)N, counter,
                      cand, index);
@@ -655,6 +659,9 @@ hipError_t launch_gemv(const uint16_t *x, int M, const uint8_t *qw, const float 
       default: return hipErrorInvalidValue;
     }
   }
+  // x too long for the LDS of the fast path: the skinny GEMM streams the
+  // weights the same way and stages x in chunks
+  if (skinny_eligible(M, N, K, nterm)) return launch_skinny(x, M, qw, am, ct, N, K, y, s);
   if (nterm == 1) return launch_t<1>(x, M, q, a, ct, N, K, y, s);
   return launch_t<3>(x, M, q, a, ct, N, K, y, s);
 }

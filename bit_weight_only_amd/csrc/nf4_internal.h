@@ -69,5 +69,12 @@ hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, const fl
                        const CodeTerms &ct, int nterm, int64_t N, int64_t K, float *y,
                        void *ws, size_t ws_bytes, hipStream_t s);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// Skinny path of the GEMM (M <= kSkinnyMaxM, codebook of bf16 values): one
+// wave per row group streams all of K; also serves nf4_gemv when x does not
+// fit the GEMV's LDS.  Bit-identical to the tiled GEMM.
+constexpr int64_t kSkinnyMaxM = 256;
+bool skinny_eligible(int64_t M, int64_t N, int64_t K, int nterm);
+hipError_t launch_skinny(const uint16_t *x, int64_t M, const uint8_t *qw, const float *am,
+                         const CodeTerms &ct, int64_t N, int64_t K, float *y, hipStream_t s);
 
 }  // namespace nf4

@@ -148,6 +148,22 @@ def test_deterministic_and_batch_independent(side, cb, kind):
         np.testing.assert_array_equal(side.run(kind, x[m:m + 1], pw, cb), y1[m:m + 1])
 
 
+@pytest.mark.parametrize("N,K", [(512, 3584), (256, 18944), (272, 704)])
+def test_gemm_skinny_and_tiled_rows_identical(side, cb, N, K):
+    """nf4_gemm runs rows of a narrow batch on the skinny path (one wave per
+    row group streaming all of K) and a wide batch on the tiled path; both
+    perform the same operations per output, so rows agree bit for bit
+    whichever path the batch size selects (K = 704 ends in a half tile)."""
+    packed, absmax, pw = case(side, cb, N, K, mid=27)
+    x = synth.activations(0, 300, K, stream=3)
+    yt = side.run("gemm", x, pw, cb)            # 300 rows: tiled
+    for M, m0 in ((1, 0), (1, 299), (29, 17), (64, 200), (256, 40)):
+        np.testing.assert_array_equal(side.run("gemm", x[m0:m0 + M], pw, cb), yt[m0:m0 + M],
+                                      err_msg=f"M={M} rows {m0}..")
+    yr, b = oracle.linear(x[[0, 17, 299]], packed, absmax, cb)
+    assert_linear_ok(yt[[0, 17, 299]], yr, b, f"tiled N={N} K={K}")
+
+
 def test_gemv_and_gemm_agree(side, cb):
     N, K = 1024, 3584
     packed, absmax, pw = case(side, cb, N, K, mid=26)
