@@ -23,6 +23,8 @@ namespace nf4 {
 namespace {
 
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 __device__ inline float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
@@ -281,16 +283,27 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float *__restrict__ y
 // LDS; after one barrier the partials of every row group are summed in wave
 // order.  No workspace, no atomics, and a fixed summation order.
 //
+// A tile's products run on the matrix cores: per 32-k step one
+// v_mfma_f32_16x16x32_bf16 with the x rows as operand A (lane row = lane % 16,
+// clamped to M - 1; rows past M are computed and dropped) and the looked-up
+// weights as operand B, whose fragment is exactly the lane's 8 codes of that
+// step.  Two steps make one 64-block, which is scaled and folded into the
+// lane's accumulators: D row 4 (lane / 16) + i is output row m, D column
+// lane % 16 the weight row.  The cost per tile is four matrix instructions
+// whatever M (up to 8), and the vector ALU is left with the lookups.
+//
 // LDS (dynamic, sized per launch): the pair table in 64 copies with a
 // 256-byte entry stride, so the address (code byte << 8) | (lane << 2) is one
 // v_perm_b32 and the 64 lanes of a wave hit 64 different banks; x for all M
-// rows, each padded with zeros to a whole number of 128-k tiles; and the
-// partial sums [row group][wave][16 rows][M].
+// rows, each padded with zeros to a whole number of 128-k tiles and stored
+// with a 16-byte skew per row (so the M rows of one operand-A read fall in
+// different banks); and the partial sums [row group][wave][16 rows][M].
 // ---------------------------------------------------------------------------
 constexpr int kFastWaves = 8;
 constexpr int kFastCopies = 64;
 constexpr int kFastTableWords = 256 * kFastCopies;  // 64 KB
 constexpr int kFastDepth = 4;                        // tiles in flight per wave
+constexpr int kFastSkew = 8;                         // x row skew in LDS, elements
 constexpr int kLdsBytes = 160 * 1024;                // LDS per workgroup on gfx950
 // sched_barrier mask: ALU, VALU, SALU, MFMA, all LDS and transcendental
 // instructions may cross; vector memory instructions may not.
@@ -308,8 +321,9 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
   __shared__ __attribute__((aligned(16))) uint32_t table[kFastTableWords];
   extern __shared__ __attribute__((aligned(16))) uint32_t lds_dyn[];
   const int KP = KT * kTileK;                 // padded x row length
+  const int XS = KP + kFastSkew;              // x row stride in LDS
   uint16_t *xs = reinterpret_cast<uint16_t *>(lds_dyn);
-  float *red = reinterpret_cast<float *>(lds_dyn + M * KP / 2);
+  float *red = reinterpret_cast<float *>(lds_dyn + M * XS / 2);
   uint16_t *codes_lds = reinterpret_cast<uint16_t *>(red);  // until the table is built
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -361,7 +375,7 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
   for (int u = 0; u < kStage; ++u) {
     const int c = (int)threadIdx.x + u * (int)blockDim.x;
     const int m = c / cpr, k = (c - m * cpr) * 8;
-    if (c < chunks) *reinterpret_cast<uint4 *>(&xs[m * KP + k]) = xv0[u];
+    if (c < chunks) *reinterpret_cast<uint4 *>(&xs[m * XS + k]) = xv0[u];
   }
   for (int c0 = (int)threadIdx.x + kStage * (int)blockDim.x; c0 < chunks;
        c0 += kStage * (int)blockDim.x) {
@@ -377,7 +391,7 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
     for (int u = 0; u < kStage; ++u) {
       const int c = c0 + u * (int)blockDim.x;
       const int m = c / cpr, k = (c - m * cpr) * 8;
-      if (c < chunks) *reinterpret_cast<uint4 *>(&xs[m * KP + k]) = v[u];
+      if (c < chunks) *reinterpret_cast<uint4 *>(&xs[m * XS + k]) = v[u];
     }
   }
   __syncthreads();
@@ -389,9 +403,14 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
 
   const uint32_t lane4 = (uint32_t)lane << 2;
   const char *tabc = reinterpret_cast<const char *>(table);
-  float acc[M];
+  // D rows 4h + i (i < NA) of the lane that can be real output rows
+  constexpr int NA = M < 4 ? M : 4;
+  float acc[NA];
 #pragma unroll
-  for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+  for (int i = 0; i < NA; ++i) acc[i] = 0.0f;
+  // operand A: x row lane % 16 (clamped), k = 128t + 32jj + 8h + 0..7
+  const uint16_t *xrow = xs + (M == 1 ? 0 : (r < M ? r : M - 1) * XS) + 8 * h;
+  const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
 
   // consumed-tile position: local row group j, tile t within it
   const int q8 = kFastWaves / KT, r8 = kFastWaves % KT;
@@ -402,33 +421,29 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
     for (int d = 0; d < D; ++d) {
       const int i = base + d;
       const bool live = i < n;
-      // ---- one 16-row x 128-k tile: lane owns row r, k = 128t + 32j + 8h + 0..7
-      float p[2][M];
-#pragma unroll
-      for (int m = 0; m < M; ++m) p[0][m] = p[1][m] = 0.0f;
-      const uint16_t *xt = xs + t * kTileK + 8 * h;
+      // ---- one 16-row x 128-k tile: lane holds weight row r, k = 128t + 32jj + 8h + 0..7
+      const uint16_t *xt = xrow + t * kTileK;
+      f32x4 P[2];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const uint32_t wd = jj == 0 ? wb[d].x : jj == 1 ? wb[d].y : jj == 2 ? wb[d].z : wb[d].w;
-        uint4 xv[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) xv[m] = *reinterpret_cast<const uint4 *>(xt + m * KP + 32 * jj);
+        const uint4 xa = *reinterpret_cast<const uint4 *>(xt + 32 * jj);
+        uint32_t bb[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t addr = __builtin_amdgcn_perm(wd, lane4, 0x0c0c0400u + (q << 8));
-          const uint32_t pr = *reinterpret_cast<const uint32_t *>(tabc + addr);
-#pragma unroll
-          for (int m = 0; m < M; ++m) {
-            const uint32_t xp = q == 0 ? xv[m].x : q == 1 ? xv[m].y : q == 2 ? xv[m].z : xv[m].w;
-            p[jj >> 1][m] = dot2(pr, xp, p[jj >> 1][m]);
-          }
+          bb[q] = *reinterpret_cast<const uint32_t *>(tabc + addr);
         }
+        const bf16x8 A = __builtin_bit_cast(bf16x8, xa);
+        const bf16x8 B = __builtin_bit_cast(bf16x8, make_uint4(bb[0], bb[1], bb[2], bb[3]));
+        P[jj >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, (jj & 1) ? P[jj >> 1] : zero,
+                                                             0, 0, 0);
       }
       const float s0 = live ? sb[d].x : 0.0f, s1 = live ? sb[d].y : 0.0f;
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        acc[m] = fmaf(s0, p[0][m], acc[m]);
-        acc[m] = fmaf(s1, p[1][m], acc[m]);
+      for (int e = 0; e < NA; ++e) {
+        acc[e] = fmaf(s0, P[0][e], acc[e]);
+        acc[e] = fmaf(s1, P[1][e], acc[e]);
       }
       // ---- refill this slot (D tiles ahead).  The empty asm pins the
       // accumulation before this point and the barrier keeps the scheduler
@@ -437,7 +452,7 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
       // ALU and LDS instructions may still move across it, so the next
       // tile's table lookups overlap this tile's arithmetic.
 #pragma unroll
-      for (int m = 0; m < M; ++m) asm volatile("" ::"v"(acc[m]));
+      for (int e = 0; e < NA; ++e) asm volatile("" ::"v"(acc[e]));
       __builtin_amdgcn_sched_barrier(kSchedAllButGlobalLoads);
       {
         const uint32_t lt = ptau < tile_end ? ptau : (uint32_t)T0;
@@ -454,16 +469,11 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
       }
       if (live && (jn != j || i == n - 1)) {
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-          acc[m] += __shfl_xor(acc[m], 16);
-          acc[m] += __shfl_xor(acc[m], 32);
+        for (int e = 0; e < NA; ++e) {
+          const int m = 4 * h + e;
+          if (m < M) red[((j * kFastWaves + wave) * 16 + r) * M + m] = acc[e];
+          acc[e] = 0.0f;
         }
-        if (h == 0) {
-#pragma unroll
-          for (int m = 0; m < M; ++m) red[((j * kFastWaves + wave) * 16 + r) * M + m] = acc[m];
-        }
-#pragma unroll
-        for (int m = 0; m < M; ++m) acc[m] = 0.0f;
       }
       j = jn;
       t = tn;
@@ -509,7 +519,7 @@ struct FastPlan {
 
 // dynamic LDS bytes (x and partials); the 64 KB table is static
 size_t fast_dyn_bytes(int M, int64_t K, int64_t Gw) {
-  return (size_t)M * tiles_k(K) * kTileK * 2 + (size_t)Gw * kFastWaves * 16 * M * 4;
+  return (size_t)M * (tiles_k(K) * kTileK + kFastSkew) * 2 + (size_t)Gw * kFastWaves * 16 * M * 4;
 }
 constexpr size_t kDynMax = (size_t)kLdsBytes - (size_t)kFastTableWords * 4;
 
