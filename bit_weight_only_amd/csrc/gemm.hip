@@ -9,11 +9,12 @@
 // outside the matrix product: for every 64-block the MFMA sums
 // P = sum_k x*c in fp32 (exact products), then acc += s * P.
 //
-// Two kernels:
-//   gemm_pipe_kernel<WM>  codebooks whose values are bf16 (the default one):
-//     (64 WM) x 128 outputs per workgroup, WM x 2 waves of 64 x 64, copies
-//     straight from global memory into LDS rings, codes expanded once per
-//     workgroup;
+// Kernels:
+//   gemm_tile_kernel<RG>  codebooks whose values are bf16 (the default one):
+//     128 x 16 RG outputs per workgroup, RG waves of 64 x 32, copies straight
+//     from global memory into LDS rings, each wave expanding the code words
+//     of its own columns;
+//   gemm_skinny_kernel    few rows (below);
 //   gemm_kernel<3>        any finite codebook (each value split into three
 //     bf16 terms), and shapes whose byte offsets exceed 32 bits.
 // Within each kernel every output is the same sequence of operations
@@ -148,40 +149,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
 constexpr int kBK = 64;  // k per step of the pipelined kernel (one scale block)
 
 // ---------------------------------------------------------------------------
-// Pipelined kernel.  The 64-k step is split into two 32-k halves (kk = 0, 1),
-// each a separate LDS block laid out [row][32 bf16].  The four 16-byte chunks
-// of a row are stored at chunk ^ ((row >> 2) & 3): LDS serves 16 lanes at a
-// time, and a fragment's 16 lanes (16 rows, one chunk) then hit 16 different
-// bank groups instead of 4.  Rings:
-//   A (x)        2 stages x 2 halves, copied global->LDS one step ahead;
-//   B (codes)    2 stages x 2 halves, expanded by the workgroup one step ahead;
-//   code words   per-wave ring of 8 quarter-slots, copied two steps ahead;
-//   scales       ring of 4 steps, copied two steps ahead.
-// In step t every wave runs the kk=0 products of step t from fragments it
-// loaded during step t-1, loads the kk=0 fragments of step t+1 meanwhile, then
-// runs the kk=1 products; so the matrix unit starts right after the barrier.
-// One barrier per step.  All copies issued after barrier t land before
-// barrier t+1, except the code and scale copies, which may stay in flight one
-// more step: they are issued last, and each barrier waits until at most that
-// many copies are outstanding.  Copy sources past the end are clamped, so
-// every step issues the same number of copies.
+// Copies straight from global memory into LDS, shared by the tiled and the
+// skinny kernels, and the 32-copy pair table the skinny kernel uses.
 namespace pipe {
 constexpr int kHalfRow = 64;                    // bytes of one row in one 32-k half
 constexpr int kCopies = 32;                     // pair-table copies (lane % 32)
 constexpr int kTableBytes = 256 * kCopies * 4;
-constexpr int kCodeSlots = 8;                   // quarter-slots per row group
-constexpr int kScaleSlots = 4;
-template <int WM>
-struct Map {
-  static constexpr int kWaves = 2 * WM, kThreads = 64 * kWaves, kBM = 64 * WM;
-  static constexpr int kRgPerWave = 8 / kWaves;  // row groups each wave copies and expands
-  static constexpr int kAHalf = kBM * kHalfRow, kBHalf = 128 * kHalfRow;
-  static constexpr int kOffA = 0, kOffB = kOffA + 4 * kAHalf, kOffC = kOffB + 4 * kBHalf,
-                       kOffS = kOffC + 8 * kCodeSlots * 256, kOffT = kOffS + kScaleSlots * 512,
-                       kBytes = kOffT + kTableBytes;
-  // copies per step that may still be in flight at the next barrier
-  static constexpr int kLate = 3 * kRgPerWave;
-};
 
 typedef __attribute__((address_space(3))) void lds_void;
 __device__ inline uint32_t lds_addr(const void *p) {
@@ -196,185 +169,189 @@ __device__ inline void copy16(uint32_t m0, const void *base, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(base)
                : "memory");
 }
+__device__ inline void copy4(uint32_t m0, const void *base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0), "v"(voff), "s"(base)
+               : "memory");
+}
 // Wait until at most N of this wave's copies are in flight and its LDS
 // operations are done, then meet the other waves.
 template <int N>
 __device__ inline void wait_copies_and_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
-__device__ inline void copy4(uint32_t m0, const void *base, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0), "v"(voff), "s"(base)
-               : "memory");
-}
 }  // namespace pipe
 
-template <int WM>
-__global__ __launch_bounds__(128 * WM) void gemm_pipe_kernel(
+// ---------------------------------------------------------------------------
+// Tiled kernel: a workgroup computes 128 rows x 16 RG columns (RG row groups,
+// 8 or 16) with RG waves, each 64 rows x 32 columns (4 x 2 MFMA blocks), so
+// there are 2 or 4 waves per SIMD.  Each wave expands the B fragments of its
+// own two row groups straight from code words in LDS (no expanded copy of B
+// is stored), and the pair table has one copy per lane at a 256-byte stride:
+// the lookup address (code byte << 8) | (lane << 2) is one v_perm_b32 and the
+// 64 lanes hit 64 banks.  The 64-k step is split into two 32-k halves, each a
+// separate LDS block laid out [row][32 bf16], with the four 16-byte chunks of
+// a row stored at chunk ^ ((row >> 2) & 3) so that the 16 rows of a fragment
+// read fall in 16 different bank groups.  LDS (bytes): table 64 K at address
+// 0, x 2 stages x 2 halves x 8 K, code words RG x 8 quarter slots x 256,
+// scales 4 steps x RG x 64.  Rings, all filled by global->LDS copies issued
+// right after the barrier of step t: x of step t+1 (into the stage step t-1
+// read), code quarters 2t+6 and 2t+7 (into the slots of quarters 2t-2 and
+// 2t-1), scales of step t+2 (into the slot of step t-2).  Each wave issues
+// the same copies every step (sources past the end are clamped), x first, so
+// that waiting until at most the last three are in flight means x of the
+// coming step has landed.  Every output gets the operations of the other
+// kernels: per 64-block P = MFMA(kk=0, zero), MFMA(kk=1, P), acc = fmaf(s, P,
+// acc), in K order.
+namespace tile {
+constexpr int kBM = 128;
+constexpr int kTable = 256 * 64 * 4;            // one copy per lane
+constexpr int kAHalf = kBM * pipe::kHalfRow;    // 8 KB: 128 rows x 32 k
+constexpr int kSlots = 8;                       // code quarter slots per row group
+constexpr int kOffA = kTable, kOffC = kOffA + 4 * kAHalf;
+template <int RG>
+struct Map {
+  static constexpr int kWaves = RG, kThreads = 64 * RG, kWN = RG / 2;  // waves along N
+  static constexpr int kOffS = kOffC + RG * kSlots * 256, kBytes = kOffS + 4 * RG * 64;
+  static constexpr int kACopies = 16 / kWaves;  // x copies per wave per step
+};
+}  // namespace tile
+
+template <int RG>
+__global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
     const uint16_t *__restrict__ x, int64_t M, const uint8_t *__restrict__ qw,
     const float *__restrict__ am, CodeTerms ct, int64_t N, int64_t K, int64_t KT,
     float *__restrict__ y) {
-  using L = pipe::Map<WM>;
+  using L = tile::Map<RG>;
+  // the only static LDS array, so the table sits at LDS address 0
   __shared__ __attribute__((aligned(16))) char lds[L::kBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, h = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * L::kBM;
-  const int64_t gblk = (int64_t)blockIdx.x * 8;
+  const int wm = wave / L::kWN, wn = wave % L::kWN;
+  const int64_t m0 = (int64_t)blockIdx.y * tile::kBM;
+  const int64_t gblk = (int64_t)blockIdx.x * RG;
   const int64_t G = N / kTileRows;
-  const int S = (int)(K / kBK), U = 2 * S;  // steps, 32-k quarters
+  const int S = (int)(K / kBK), U = 2 * S;
   const uint32_t base = pipe::lds_addr(lds);
-  char *ldsA = lds + L::kOffA, *ldsB = lds + L::kOffB, *ldsC = lds + L::kOffC;
-  char *ldsS = lds + L::kOffS, *ldsT = lds + L::kOffT;
+  const char *ldsA = lds + tile::kOffA, *ldsC = lds + tile::kOffC, *ldsS = lds + L::kOffS;
 
-  // ---- per-lane copy offsets (bytes).  Rows past M and row groups past N
-  // re-read the last valid one; their outputs are never stored.
-  // A: copy i = 2 * wave + v fills rows 16i .. 16i+15 of a half block; lane l
-  // fills chunk slot l % 4 of row 16i + l/4, i.e. logical chunk
-  // (l % 4) ^ ((row >> 2) & 3) = (l % 4) ^ ((l >> 4) & 3).
-  uint32_t aoff[2];
+  // Copy assignment.  x: copy i (16 per step, 1 KB each) fills rows
+  // 16 (i % 8) .. + 15 of half i / 8; wave w issues i = w, w + RG, ...  Lane
+  // l fills chunk slot l % 4 of row 16 (i % 8) + l / 4, i.e. logical chunk
+  // (l % 4) ^ ((l >> 4) & 3).  Code words and scales: wave w copies those of
+  // row group w.  Rows past M and row groups past N re-read the last valid
+  // one; their outputs are never stored.
+  uint32_t aoff[L::kACopies], mA[L::kACopies];
 #pragma unroll
-  for (int v = 0; v < 2; ++v) {
-    const int R = 16 * (2 * wave + v) + (lane >> 2);
-    const int64_t gm = m0 + R < M ? m0 + R : M - 1;
+  for (int v = 0; v < L::kACopies; ++v) {
+    const int i = wave + v * RG, blk = i % 8, half = i / 8;
+    const int64_t R = m0 + 16 * blk + (lane >> 2);
+    const int64_t gm = R < M ? R : M - 1;
     const int c = (lane & 3) ^ ((lane >> 4) & 3);
-    aoff[v] = (uint32_t)((gm * K + c * 8) * 2);
+    aoff[v] = (uint32_t)((gm * K + half * 32 + c * 8) * 2);
+    mA[v] = base + tile::kOffA + half * tile::kAHalf + blk * 1024;
   }
-  uint32_t coff[L::kRgPerWave], soff[L::kRgPerWave];
-#pragma unroll
-  for (int v = 0; v < L::kRgPerWave; ++v) {
-    const int64_t rg = gblk + wave * L::kRgPerWave + v;
+  uint32_t coff, soff;
+  {
+    const int64_t rg = gblk + wave;
     const int64_t g = rg < G ? rg : G - 1;
-    coff[v] = (uint32_t)(g * KT * kTileBytes + lane * 16);
-    soff[v] = (uint32_t)((g * KT * kTileScales + 2 * r) * 4);
+    coff = (uint32_t)(g * KT * kTileBytes + lane * 16);
+    soff = (uint32_t)((g * KT * kTileScales + 2 * r) * 4);
   }
-  // half `half` of x columns [64 step, 64 step + 64) -> A stage step & 1
-  auto issue_a = [&](int step, int half) {
-    const int sc = step < S ? step : S - 1;
-    const uint16_t *src = x + (int64_t)sc * kBK + half * 32;
-    const uint32_t dst = base + L::kOffA + ((step & 1) * 2 + half) * L::kAHalf;
+  const uint32_t mC = base + tile::kOffC + wave * tile::kSlots * 256;
+  const uint32_t mS = base + L::kOffS + wave * 64;
+  auto copy_x = [&](int step) {
+    const uint32_t sc = (uint32_t)(step < S ? step : S - 1) * (kBK * 2);
 #pragma unroll
-    for (int v = 0; v < 2; ++v) pipe::copy16(dst + (2 * wave + v) * 1024, src, aoff[v]);
+    for (int v = 0; v < L::kACopies; ++v)
+      pipe::copy16(mA[v] + (step & 1) * 2 * tile::kAHalf, x, aoff[v] + sc);
   };
-  // quarter u = code dword u & 3 of device tile u >> 2 (k in [32u, 32u + 32))
-  auto issue_codes = [&](int u) {
+  auto copy_codes = [&](int u) {  // quarter u: code dword u & 3 of device tile u >> 2
     const int uc = u < U ? u : U - 1;
-    const uint8_t *src = qw + (int64_t)(uc >> 2) * kTileBytes + (uc & 3) * 4;
-#pragma unroll
-    for (int v = 0; v < L::kRgPerWave; ++v)
-      pipe::copy4(base + L::kOffC + ((wave * L::kRgPerWave + v) * pipe::kCodeSlots + (u & 7)) * 256,
-                  src, coff[v]);
+    pipe::copy4(mC + (u & 7) * 256, qw, coff + (uint32_t)((uc >> 2) * kTileBytes + (uc & 3) * 4));
   };
-  // scales of step `step` (one per row of each row group)
-  auto issue_scales = [&](int step) {
+  auto copy_scales = [&](int step) {
     const int sc = step < S ? step : S - 1;
-    const float *src = am + (int64_t)(sc >> 1) * kTileScales + (sc & 1);
-    if (lane < 16) {
-#pragma unroll
-      for (int v = 0; v < L::kRgPerWave; ++v)
-        pipe::copy4(base + L::kOffS + (step & 3) * 512 + (wave * L::kRgPerWave + v) * 64, src,
-                    soff[v]);
-    }
-  };
-  // expand quarter u of this wave's row groups into B stage (u >> 1) & 1, half u & 1
-  const uint32_t tcopy = (uint32_t)(lane & (pipe::kCopies - 1)) * 4;
-  // row r, logical chunk h within a 16-row block (rows differ by multiples of
-  // 16, so the swizzle only depends on r)
-  const uint32_t bsw = (uint32_t)(r * pipe::kHalfRow + ((h ^ ((r >> 2) & 3)) * 16));
-  auto dequant = [&](int u) {
-#pragma unroll
-    for (int v = 0; v < L::kRgPerWave; ++v) {
-      const int rgl = wave * L::kRgPerWave + v;
-      const uint32_t wd = *reinterpret_cast<const uint32_t *>(
-          ldsC + (rgl * pipe::kCodeSlots + (u & 7)) * 256 + lane * 4);
-      uint32_t bb[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t e = (wd >> (8 * q)) & 0xFFu;
-        bb[q] = *reinterpret_cast<const uint32_t *>(ldsT + e * (pipe::kCopies * 4) + tcopy);
-      }
-      *reinterpret_cast<uint4 *>(ldsB + (((u >> 1) & 1) * 2 + (u & 1)) * L::kBHalf + rgl * 1024 +
-                                 bsw) = make_uint4(bb[0], bb[1], bb[2], bb[3]);
-    }
-  };
-  // fragments: lane (r, h) holds row r of a 16-row block, bf16 8h .. 8h+7 of the half
-  const uint32_t afr = (uint32_t)(wm * 64 * pipe::kHalfRow) + bsw;
-  const uint32_t bfr = (uint32_t)(wn * 64 * pipe::kHalfRow) + bsw;
-  auto load_frags = [&](int st, int half, bf16x8(&A)[4], bf16x8(&B)[4]) {
-    const char *pa = ldsA + (st * 2 + half) * L::kAHalf + afr;
-    const char *pb = ldsB + (st * 2 + half) * L::kBHalf + bfr;
-#pragma unroll
-    for (int mm = 0; mm < 4; ++mm) A[mm] = *reinterpret_cast<const bf16x8 *>(pa + mm * 1024);
-#pragma unroll
-    for (int nn = 0; nn < 4; ++nn) B[nn] = *reinterpret_cast<const bf16x8 *>(pb + nn * 1024);
+    const uint32_t o = (uint32_t)(((sc >> 1) * kTileScales + (sc & 1)) * 4);
+    if (lane < 16) pipe::copy4(mS + (step & 3) * RG * 64, am, soff + o);
   };
 
-  // ---- prologue: pair table (from the codebook staged in B stage 1 half 1,
-  // which the prologue does not expand into), then the first copies
-  uint16_t *codes16 = reinterpret_cast<uint16_t *>(ldsB + 3 * L::kBHalf);
+  // the pair table, from the codebook staged in the scale ring (filled only
+  // after the second barrier)
+  uint16_t *codes16 = reinterpret_cast<uint16_t *>(lds + L::kOffS);
   if (tid < 16) codes16[tid] = ct.t[0][tid];
   __syncthreads();
-  for (int c = tid; c < pipe::kTableBytes / 16; c += L::kThreads) {
-    const int e = c / (pipe::kCopies / 4);
+  for (int c = tid; c < tile::kTable / 16; c += L::kThreads) {
+    const int e = c >> 4;  // 16 chunks of 4 copies per entry
     const uint32_t v = (uint32_t)codes16[e & 15] | ((uint32_t)codes16[e >> 4] << 16);
-    reinterpret_cast<uint4 *>(ldsT)[c] = make_uint4(v, v, v, v);
+    reinterpret_cast<uint4 *>(lds)[c] = make_uint4(v, v, v, v);
   }
-  issue_a(0, 0);
-  issue_a(0, 1);
-  issue_a(1, 0);
+  __syncthreads();
+  copy_x(0);
 #pragma unroll
-  for (int u = 0; u < 7; ++u) issue_codes(u);
-  issue_scales(0);
-  issue_scales(1);
-  pipe::wait_copies_and_barrier<0>();
-  dequant(0);
-  dequant(1);
-  dequant(2);
+  for (int u = 0; u < 6; ++u) copy_codes(u);
+  copy_scales(0);
+  copy_scales(1);
   pipe::wait_copies_and_barrier<0>();
 
-  bf16x8 A0[4], B0[4], A1[4], B1[4];
-  load_frags(0, 0, A0, B0);
-  f32x4 acc[4][4];
+  const uint32_t lane4 = (uint32_t)lane << 2;
+  // fragments: lane (r, h) holds row r of a 16-row block, bf16 8h .. 8h+7 of the half
+  const uint32_t afr = (uint32_t)(wm * 64 * pipe::kHalfRow + r * pipe::kHalfRow +
+                                  ((h ^ ((r >> 2) & 3)) * 16));
+  const char *cw = ldsC + (wn * 2) * tile::kSlots * 256 + lane * 4;
+  f32x4 acc[4][2];
 #pragma unroll
   for (int a2 = 0; a2 < 4; ++a2)
 #pragma unroll
-    for (int b2 = 0; b2 < 4; ++b2) acc[a2][b2] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b2 = 0; b2 < 2; ++b2) acc[a2][b2] = f32x4{0.f, 0.f, 0.f, 0.f};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
   for (int t = 0; t < S; ++t) {
-    // A copies of step t-1 have landed and B halves expanded in step t-1 are
-    // visible; every wave is done reading what this step's copies overwrite.
-    pipe::wait_copies_and_barrier<L::kLate>();
-    issue_a(t + 1, 1);
-    issue_a(t + 2, 0);
-    issue_codes(2 * t + 7);
-    issue_codes(2 * t + 8);
-    issue_scales(t + 2);
-
-    load_frags(t & 1, 1, A1, B1);
-    f32x4 p[4][4];
+    // Landed: x of step t (copied in step t-1), quarters 2t, 2t+1 (step
+    // t-3), scales of step t (step t-2); in flight at most the code and scale
+    // copies of step t-1.  Past the barrier no wave reads x of step t-1,
+    // quarters 2t-2, 2t-1 or the scales of step t-2 any more.
+    pipe::wait_copies_and_barrier<3>();
+    copy_x(t + 1);
+    copy_codes(2 * t + 6);
+    copy_codes(2 * t + 7);
+    copy_scales(t + 2);
+    const char *sp = ldsS + (t & 3) * RG * 64 + wn * 2 * 64 + r * 4;
+    const float s0 = *reinterpret_cast<const float *>(sp);
+    const float s1 = *reinterpret_cast<const float *>(sp + 64);
+    f32x4 p[4][2];
 #pragma unroll
-    for (int mm = 0; mm < 4; ++mm)
+    for (int hf = 0; hf < 2; ++hf) {
+      const char *pa = ldsA + ((t & 1) * 2 + hf) * tile::kAHalf + afr;
+      bf16x8 A[4], B[2];
 #pragma unroll
-      for (int nn = 0; nn < 4; ++nn)
-        p[mm][nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0[mm], B0[nn], zero, 0, 0, 0);
-    load_frags((t + 1) & 1, 0, A0, B0);
-    dequant(2 * t + 3);
-    dequant(2 * t + 4);
+      for (int mm = 0; mm < 4; ++mm) A[mm] = *reinterpret_cast<const bf16x8 *>(pa + mm * 1024);
 #pragma unroll
-    for (int mm = 0; mm < 4; ++mm)
+      for (int nn = 0; nn < 2; ++nn) {
+        const uint32_t wd = *reinterpret_cast<const uint32_t *>(
+            cw + (nn * tile::kSlots + ((2 * t + hf) & 7)) * 256);
+        uint32_t bb[4];
 #pragma unroll
-      for (int nn = 0; nn < 4; ++nn)
-        p[mm][nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[mm], B1[nn], p[mm][nn], 0, 0, 0);
-    const char *sp = ldsS + (t & 3) * 512 + wn * 4 * 64 + r * 4;
-#pragma unroll
-    for (int nn = 0; nn < 4; ++nn) {
-      const float s = *reinterpret_cast<const float *>(sp + nn * 64);
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t a = __builtin_amdgcn_perm(wd, lane4, 0x0c0c0400u + (q << 8));
+          bb[q] = *reinterpret_cast<const uint32_t *>(lds + a);
+        }
+        B[nn] = __builtin_bit_cast(bf16x8, make_uint4(bb[0], bb[1], bb[2], bb[3]));
+      }
 #pragma unroll
       for (int mm = 0; mm < 4; ++mm)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mm][nn][i] = fmaf(s, p[mm][nn][i], acc[mm][nn][i]);
+        for (int nn = 0; nn < 2; ++nn)
+          p[mm][nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mm], B[nn], hf ? p[mm][nn] : zero,
+                                                              0, 0, 0);
     }
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[mm][0][i] = fmaf(s0, p[mm][0][i], acc[mm][0][i]);
+        acc[mm][1][i] = fmaf(s1, p[mm][1][i], acc[mm][1][i]);
+      }
   }
   // the clamped copies of the last steps must land before the workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -382,8 +359,8 @@ __global__ __launch_bounds__(128 * WM) void gemm_pipe_kernel(
 #pragma unroll
   for (int mm = 0; mm < 4; ++mm)
 #pragma unroll
-    for (int nn = 0; nn < 4; ++nn) {
-      const int64_t g = gblk + wn * 4 + nn;
+    for (int nn = 0; nn < 2; ++nn) {
+      const int64_t g = gblk + wn * 2 + nn;
       if (g >= G) continue;
       const int64_t col = g * kTileRows + r;
 #pragma unroll
@@ -404,7 +381,7 @@ __global__ __launch_bounds__(128 * WM) void gemm_pipe_kernel(
 // (double buffered, one barrier per chunk).  Per tile the lane's 16 code
 // bytes become the B fragments of four 32-k MFMA steps through the pair
 // table, and the MB m-blocks of x supply the A fragments.
-// Every output is computed with exactly the operations of gemm_pipe_kernel:
+// Every output is computed with exactly the operations of gemm_tile_kernel:
 // per 64-block P = MFMA(kk=0, zero) then MFMA(kk=1, P), acc = fmaf(s, P, acc)
 // in K order, with the same operand values in the same lanes, so the two
 // kernels give bit-identical rows and the choice between them (by M) does
@@ -620,27 +597,23 @@ hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, const fl
       return launch_skinny(x, M, qw, am, ct, N, K, y, s);
   }
   if (nterm == 1 && dma_ok) {
-    // 256-row tiles (8 waves) unless 128-row tiles (4 waves) need no more
-    // rounds of workgroups over the CUs: a 128-row tile takes nearly as long
-    // as a 256-row one, so the short tiles only pay off when they fill CUs
-    // that would otherwise idle.
-    const int64_t ntile = (N + BN - 1) / BN;
-    const int64_t cus = device_cu_count();
-    const int64_t rounds_tall = (ntile * ((M + 255) / 256) + cus - 1) / cus;
-    const int64_t rounds_short = (ntile * ((M + 127) / 128) + cus - 1) / cus;
-    if (rounds_tall < rounds_short) {
-      const dim3 grid((unsigned)ntile, (unsigned)((M + 255) / 256));
-      hipLaunchKernelGGL(gemm_pipe_kernel<4>, grid, dim3(512), 0, s, x, M, qw, am, ct, N, K, KT,
-                         y);
+    // 16 row groups per workgroup (4 waves per SIMD) unless that grid would
+    // leave more than half of the CUs idle; then 8 (one workgroup per CU on
+    // twice as many CUs).
+    const int64_t G = N / kTileRows, mt = (M + tile::kBM - 1) / tile::kBM;
+    if (((G + 15) / 16) * mt >= device_cu_count() / 2) {
+      const dim3 grid((unsigned)((G + 15) / 16), (unsigned)mt);
+      hipLaunchKernelGGL(gemm_tile_kernel<16>, grid, dim3(64 * 16), 0, s, x, M, qw, am, ct, N, K,
+                         KT, y);
     } else {
-      const dim3 grid((unsigned)ntile, (unsigned)((M + 127) / 128));
-      hipLaunchKernelGGL(gemm_pipe_kernel<2>, grid, dim3(256), 0, s, x, M, qw, am, ct, N, K, KT,
+      const dim3 grid((unsigned)((G + 7) / 8), (unsigned)mt);
+      hipLaunchKernelGGL(gemm_tile_kernel<8>, grid, dim3(64 * 8), 0, s, x, M, qw, am, ct, N, K, KT,
                          y);
     }
-  } else {
-    const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM)), block(256);
-    hipLaunchKernelGGL(gemm_kernel<3>, grid, block, 0, s, x, M, q, a, ct, N, K, KT, y);
+    return hipGetLastError();
   }
+  const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM)), block(256);
+  hipLaunchKernelGGL(gemm_kernel<3>, grid, block, 0, s, x, M, q, a, ct, N, K, KT, y);
   return hipGetLastError();
 }
 
