@@ -23,6 +23,8 @@
 // the other rows in the batch, and a column slice of a fused matrix equals
 // the separate matrix's output.  K is therefore never split across
 // workgroups.
+#include <type_traits>
+
 #include "nf4_internal.h"
 
 namespace nf4 {
@@ -220,7 +222,7 @@ template <int RG>
 __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
     const uint16_t *__restrict__ x, int64_t M, const uint8_t *__restrict__ qw,
     const float *__restrict__ am, CodeTerms ct, int64_t N, int64_t K, int64_t KT,
-    float *__restrict__ y) {
+    float *__restrict__ y, int ntn, int ntm) {
   using L = tile::Map<RG>;
   // the only static LDS array, so the table sits at LDS address 0
   __shared__ __attribute__((aligned(16))) char lds[L::kBytes];
@@ -228,8 +230,17 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, h = lane >> 4;
   const int wm = wave / L::kWN, wn = wave % L::kWN;
-  const int64_t m0 = (int64_t)blockIdx.y * tile::kBM;
-  const int64_t gblk = (int64_t)blockIdx.x * RG;
+  // Tile order for the 8 XCDs, each with its own L2: consecutive workgroups
+  // go to consecutive XCDs, so workgroup b runs on XCD b % 8.  XCD k takes
+  // the N tiles k, k+8, ... and, for each, all M tiles one after the other,
+  // so the workgroups that expand one weight tile share an L2.  Workgroups
+  // past the last N tile (the grid is padded to a multiple of 8 N tiles)
+  // leave before any barrier.
+  const int xcd = (int)(blockIdx.x & 7), slot = (int)(blockIdx.x >> 3);
+  const int nt = (slot / ntm) * 8 + xcd, mt = slot % ntm;
+  if (nt >= ntn) return;
+  const int64_t m0 = (int64_t)mt * tile::kBM;
+  const int64_t gblk = (int64_t)nt * RG;
   const int64_t G = N / kTileRows;
   const int S = (int)(K / kBK), U = 2 * S;
   const uint32_t base = pipe::lds_addr(lds);
@@ -306,35 +317,59 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
     for (int b2 = 0; b2 < 2; ++b2) acc[a2][b2] = f32x4{0.f, 0.f, 0.f, 0.f};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
-  for (int t = 0; t < S; ++t) {
+  // Copy offsets as running bases: every source offset grows with the step,
+  // so min(offset, last offset) is the clamped one.  With 2 steps unrolled
+  // the x stage is a constant; code and scale slots shift by 4 and 2 every
+  // other pair of steps.
+  const uint32_t xlast = (uint32_t)(S - 1) * (kBK * 2);
+  const uint32_t clast = (uint32_t)(((U - 1) >> 2) * kTileBytes + ((U - 1) & 3) * 4);
+  const uint32_t slast = (uint32_t)((((S - 1) >> 1) * kTileScales + ((S - 1) & 1)) * 4);
+  auto step = [&](auto phc, int t) {
+    constexpr int PH = decltype(phc)::value;
+    const int q = (t >> 1) & 1;
     // Landed: x of step t (copied in step t-1), quarters 2t, 2t+1 (step
     // t-3), scales of step t (step t-2); in flight at most the code and scale
     // copies of step t-1.  Past the barrier no wave reads x of step t-1,
     // quarters 2t-2, 2t-1 or the scales of step t-2 any more.
+    __builtin_amdgcn_sched_barrier(0);
     pipe::wait_copies_and_barrier<3>();
-    copy_x(t + 1);
-    copy_codes(2 * t + 6);
-    copy_codes(2 * t + 7);
-    copy_scales(t + 2);
-    const char *sp = ldsS + (t & 3) * RG * 64 + wn * 2 * 64 + r * 4;
+    {
+      const uint32_t xo = min((uint32_t)(t + 1) * (kBK * 2), xlast);
+#pragma unroll
+      for (int v = 0; v < L::kACopies; ++v)
+        pipe::copy16(mA[v] + ((PH + 1) & 1) * 2 * tile::kAHalf, x, aoff[v] + xo);
+      // quarters u = 2t+6, 2t+7 with t = 2k + PH: device tile k + 1 + PH,
+      // dwords 2 - 2 PH and 3 - 2 PH
+      const uint32_t tb = (uint32_t)((t >> 1) + 1 + PH) * kTileBytes;
+      const uint32_t c0 = min(tb + (2 - 2 * PH) * 4, clast);
+      const uint32_t c1 = min(tb + (3 - 2 * PH) * 4, clast);
+      const uint32_t sl = (uint32_t)(2 * PH + 6 + 4 * q) & 7;
+      pipe::copy4(mC + sl * 256, qw, coff + c0);
+      pipe::copy4(mC + (sl + 1) * 256, qw, coff + c1);
+      // scales of step t+2: tile t/2 + 1, half PH
+      const uint32_t so = min((uint32_t)((t >> 1) + 1) * (kTileScales * 4) + PH * 4, slast);
+      if (lane < 16) pipe::copy4(mS + (uint32_t)((PH + 2 + 2 * q) & 3) * RG * 64, am, soff + so);
+    }
+    const char *sp = ldsS + (PH + 2 * q) * RG * 64 + wn * 2 * 64 + r * 4;
     const float s0 = *reinterpret_cast<const float *>(sp);
     const float s1 = *reinterpret_cast<const float *>(sp + 64);
+    const char *cwt = cw + ((2 * PH + 4 * q) & 7) * 256;
     f32x4 p[4][2];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      const char *pa = ldsA + ((t & 1) * 2 + hf) * tile::kAHalf + afr;
+      const char *pa = ldsA + (PH * 2 + hf) * tile::kAHalf + afr;
       bf16x8 A[4], B[2];
 #pragma unroll
       for (int mm = 0; mm < 4; ++mm) A[mm] = *reinterpret_cast<const bf16x8 *>(pa + mm * 1024);
 #pragma unroll
       for (int nn = 0; nn < 2; ++nn) {
-        const uint32_t wd = *reinterpret_cast<const uint32_t *>(
-            cw + (nn * tile::kSlots + ((2 * t + hf) & 7)) * 256);
+        const uint32_t wd =
+            *reinterpret_cast<const uint32_t *>(cwt + (nn * tile::kSlots + hf) * 256);
         uint32_t bb[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t a = __builtin_amdgcn_perm(wd, lane4, 0x0c0c0400u + (q << 8));
-          bb[q] = *reinterpret_cast<const uint32_t *>(lds + a);
+        for (int qq = 0; qq < 4; ++qq) {
+          const uint32_t a = __builtin_amdgcn_perm(wd, lane4, 0x0c0c0400u + (qq << 8));
+          bb[qq] = *reinterpret_cast<const uint32_t *>(lds + a);
         }
         B[nn] = __builtin_bit_cast(bf16x8, make_uint4(bb[0], bb[1], bb[2], bb[3]));
       }
@@ -352,7 +387,15 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
         acc[mm][0][i] = fmaf(s0, p[mm][0][i], acc[mm][0][i]);
         acc[mm][1][i] = fmaf(s1, p[mm][1][i], acc[mm][1][i]);
       }
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  int t = 0;
+  for (; t + 1 < S; t += 2) {
+    step(P0{}, t);
+    step(P1{}, t + 1);
   }
+  if (t < S) step(P0{}, t);
   // the clamped copies of the last steps must land before the workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -601,14 +644,16 @@ hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, const fl
     // leave more than half of the CUs idle; then 8 (one workgroup per CU on
     // twice as many CUs).
     const int64_t G = N / kTileRows, mt = (M + tile::kBM - 1) / tile::kBM;
+    // one-dimensional grid, N tiles padded to a multiple of 8 (see the kernel)
+    auto padded = [&](int64_t nt) { return (unsigned)((nt + 7) / 8 * 8 * mt); };
     if (((G + 15) / 16) * mt >= device_cu_count() / 2) {
-      const dim3 grid((unsigned)((G + 15) / 16), (unsigned)mt);
-      hipLaunchKernelGGL(gemm_tile_kernel<16>, grid, dim3(64 * 16), 0, s, x, M, qw, am, ct, N, K,
-                         KT, y);
+      const int64_t nt = (G + 15) / 16;
+      hipLaunchKernelGGL(gemm_tile_kernel<16>, dim3(padded(nt)), dim3(64 * 16), 0, s, x, M, qw,
+                         am, ct, N, K, KT, y, (int)nt, (int)mt);
     } else {
-      const dim3 grid((unsigned)((G + 7) / 8), (unsigned)mt);
-      hipLaunchKernelGGL(gemm_tile_kernel<8>, grid, dim3(64 * 8), 0, s, x, M, qw, am, ct, N, K, KT,
-                         y);
+      const int64_t nt = (G + 7) / 8;
+      hipLaunchKernelGGL(gemm_tile_kernel<8>, dim3(padded(nt)), dim3(64 * 8), 0, s, x, M, qw, am,
+                         ct, N, K, KT, y, (int)nt, (int)mt);
     }
     return hipGetLastError();
   }
