@@ -194,26 +194,26 @@ __device__ inline void wait_copies_and_barrier() {
 // separate LDS block laid out [row][32 bf16], with the four 16-byte chunks of
 // a row stored at chunk ^ ((row >> 2) & 3) so that the 16 rows of a fragment
 // read fall in 16 different bank groups.  LDS (bytes): table 64 K at address
-// 0, x 2 stages x 2 halves x 8 K, code words RG x 8 quarter slots x 256,
-// scales 4 steps x RG x 64.  Rings, all filled by global->LDS copies issued
-// right after the barrier of step t: x of step t+1 (into the stage step t-1
-// read), code quarters 2t+6 and 2t+7 (into the slots of quarters 2t-2 and
-// 2t-1), scales of step t+2 (into the slot of step t-2).  Each wave issues
-// the same copies every step (sources past the end are clamped), x first, so
-// that waiting until at most the last three are in flight means x of the
-// coming step has landed.  Every output gets the operations of the other
-// kernels: per 64-block P = MFMA(kk=0, zero), MFMA(kk=1, P), acc = fmaf(s, P,
-// acc), in K order.
+// 0, x 2 stages x 2 halves x 8 K, and per row group 2 device tiles of code
+// words (1 K each) and of scales (128 each).  Rings, filled by global->LDS
+// copies issued right after the barrier of step t: x of step t+1 (into the
+// stage step t-1 read); at odd t = 2k+1 also device tile k+2 of every row
+// group, code words and scales (into the slot of tile k, which step 2k read
+// into registers for both of its steps).  Sources past the end are clamped,
+// x is copied first, and a barrier waits until x of the coming step has
+// landed.  Every output gets the operations of the other kernels: per
+// 64-block P = MFMA(kk=0, zero), MFMA(kk=1, P), acc = fmaf(s, P, acc), in K
+// order.
 namespace tile {
 constexpr int kBM = 128;
 constexpr int kTable = 256 * 64 * 4;            // one copy per lane
 constexpr int kAHalf = kBM * pipe::kHalfRow;    // 8 KB: 128 rows x 32 k
-constexpr int kSlots = 8;                       // code quarter slots per row group
 constexpr int kOffA = kTable, kOffC = kOffA + 4 * kAHalf;
 template <int RG>
 struct Map {
   static constexpr int kWaves = RG, kThreads = 64 * RG, kWN = RG / 2;  // waves along N
-  static constexpr int kOffS = kOffC + RG * kSlots * 256, kBytes = kOffS + 4 * RG * 64;
+  static constexpr int kOffS = kOffC + RG * 2 * kTileBytes,
+                       kBytes = kOffS + RG * 2 * kTileScales * 4;
   static constexpr int kACopies = 16 / kWaves;  // x copies per wave per step
 };
 }  // namespace tile
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
   const int64_t m0 = (int64_t)mt * tile::kBM;
   const int64_t gblk = (int64_t)nt * RG;
   const int64_t G = N / kTileRows;
-  const int S = (int)(K / kBK), U = 2 * S;
+  const int S = (int)(K / kBK);
   const uint32_t base = pipe::lds_addr(lds);
   const char *ldsA = lds + tile::kOffA, *ldsC = lds + tile::kOffC, *ldsS = lds + L::kOffS;
 
@@ -267,24 +267,22 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
     const int64_t rg = gblk + wave;
     const int64_t g = rg < G ? rg : G - 1;
     coff = (uint32_t)(g * KT * kTileBytes + lane * 16);
-    soff = (uint32_t)((g * KT * kTileScales + 2 * r) * 4);
+    soff = (uint32_t)((g * KT * kTileScales) * 4 + lane * 16);  // lanes 0..7 copy
   }
-  const uint32_t mC = base + tile::kOffC + wave * tile::kSlots * 256;
-  const uint32_t mS = base + L::kOffS + wave * 64;
+  const uint32_t mC = base + tile::kOffC + wave * 2 * kTileBytes;
+  const uint32_t mS = base + L::kOffS + wave * 2 * kTileScales * 4;
   auto copy_x = [&](int step) {
     const uint32_t sc = (uint32_t)(step < S ? step : S - 1) * (kBK * 2);
 #pragma unroll
     for (int v = 0; v < L::kACopies; ++v)
       pipe::copy16(mA[v] + (step & 1) * 2 * tile::kAHalf, x, aoff[v] + sc);
   };
-  auto copy_codes = [&](int u) {  // quarter u: code dword u & 3 of device tile u >> 2
-    const int uc = u < U ? u : U - 1;
-    pipe::copy4(mC + (u & 7) * 256, qw, coff + (uint32_t)((uc >> 2) * kTileBytes + (uc & 3) * 4));
-  };
-  auto copy_scales = [&](int step) {
-    const int sc = step < S ? step : S - 1;
-    const uint32_t o = (uint32_t)(((sc >> 1) * kTileScales + (sc & 1)) * 4);
-    if (lane < 16) pipe::copy4(mS + (step & 3) * RG * 64, am, soff + o);
+  // device tile T (steps 2T, 2T+1) of the wave's row group: 1 KB of code
+  // words and 128 bytes of scales, into ring slot T & 1
+  auto copy_tile = [&](int T) {
+    const uint32_t tc = (uint32_t)(T < KT ? T : KT - 1);
+    pipe::copy16(mC + (T & 1) * kTileBytes, qw, coff + tc * kTileBytes);
+    if (lane < 8) pipe::copy16(mS + (T & 1) * kTileScales * 4, am, soff + tc * kTileScales * 4);
   };
 
   // the pair table, from the codebook staged in the scale ring (filled only
@@ -299,17 +297,17 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
   }
   __syncthreads();
   copy_x(0);
-#pragma unroll
-  for (int u = 0; u < 6; ++u) copy_codes(u);
-  copy_scales(0);
-  copy_scales(1);
+  copy_tile(0);
+  copy_tile(1);
   pipe::wait_copies_and_barrier<0>();
 
   const uint32_t lane4 = (uint32_t)lane << 2;
   // fragments: lane (r, h) holds row r of a 16-row block, bf16 8h .. 8h+7 of the half
   const uint32_t afr = (uint32_t)(wm * 64 * pipe::kHalfRow + r * pipe::kHalfRow +
                                   ((h ^ ((r >> 2) & 3)) * 16));
-  const char *cw = ldsC + (wn * 2) * tile::kSlots * 256 + lane * 4;
+  // this wave's two row groups: code words (16 bytes per lane) and scales
+  const char *cw = ldsC + (wn * 2) * 2 * kTileBytes + lane * 16;
+  const char *sw = ldsS + (wn * 2) * 2 * kTileScales * 4 + r * 8;
   f32x4 acc[4][2];
 #pragma unroll
   for (int a2 = 0; a2 < 4; ++a2)
@@ -317,43 +315,37 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
     for (int b2 = 0; b2 < 2; ++b2) acc[a2][b2] = f32x4{0.f, 0.f, 0.f, 0.f};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
-  // Copy offsets as running bases: every source offset grows with the step,
-  // so min(offset, last offset) is the clamped one.  With 2 steps unrolled
-  // the x stage is a constant; code and scale slots shift by 4 and 2 every
-  // other pair of steps.
+  // Two steps per iteration: the x stage is a constant, and the code words
+  // and scales of device tile k = t / 2 are read once, at the even step, for
+  // both steps.  Every source offset grows with the step, so min(offset,
+  // last offset) is the clamped one.
   const uint32_t xlast = (uint32_t)(S - 1) * (kBK * 2);
-  const uint32_t clast = (uint32_t)(((U - 1) >> 2) * kTileBytes + ((U - 1) & 3) * 4);
-  const uint32_t slast = (uint32_t)((((S - 1) >> 1) * kTileScales + ((S - 1) & 1)) * 4);
+  uint4 cv[2];
+  float2 sv[2];
   auto step = [&](auto phc, int t) {
     constexpr int PH = decltype(phc)::value;
-    const int q = (t >> 1) & 1;
-    // Landed: x of step t (copied in step t-1), quarters 2t, 2t+1 (step
-    // t-3), scales of step t (step t-2); in flight at most the code and scale
-    // copies of step t-1.  Past the barrier no wave reads x of step t-1,
-    // quarters 2t-2, 2t-1 or the scales of step t-2 any more.
+    // Landed: x of step t (copied in step t-1; at an even step the tile
+    // copies of step t-1 may still be in flight), and device tile t / 2 (two
+    // or more steps ago).  Past the barrier no wave reads x of step t-1, and
+    // at an odd step no wave reads device tile t / 2 from LDS any more.
     __builtin_amdgcn_sched_barrier(0);
-    pipe::wait_copies_and_barrier<3>();
+    pipe::wait_copies_and_barrier<PH == 0 ? 2 : 0>();
     {
       const uint32_t xo = min((uint32_t)(t + 1) * (kBK * 2), xlast);
 #pragma unroll
       for (int v = 0; v < L::kACopies; ++v)
         pipe::copy16(mA[v] + ((PH + 1) & 1) * 2 * tile::kAHalf, x, aoff[v] + xo);
-      // quarters u = 2t+6, 2t+7 with t = 2k + PH: device tile k + 1 + PH,
-      // dwords 2 - 2 PH and 3 - 2 PH
-      const uint32_t tb = (uint32_t)((t >> 1) + 1 + PH) * kTileBytes;
-      const uint32_t c0 = min(tb + (2 - 2 * PH) * 4, clast);
-      const uint32_t c1 = min(tb + (3 - 2 * PH) * 4, clast);
-      const uint32_t sl = (uint32_t)(2 * PH + 6 + 4 * q) & 7;
-      pipe::copy4(mC + sl * 256, qw, coff + c0);
-      pipe::copy4(mC + (sl + 1) * 256, qw, coff + c1);
-      // scales of step t+2: tile t/2 + 1, half PH
-      const uint32_t so = min((uint32_t)((t >> 1) + 1) * (kTileScales * 4) + PH * 4, slast);
-      if (lane < 16) pipe::copy4(mS + (uint32_t)((PH + 2 + 2 * q) & 3) * RG * 64, am, soff + so);
+      if (PH == 1) copy_tile((t >> 1) + 2);
     }
-    const char *sp = ldsS + (PH + 2 * q) * RG * 64 + wn * 2 * 64 + r * 4;
-    const float s0 = *reinterpret_cast<const float *>(sp);
-    const float s1 = *reinterpret_cast<const float *>(sp + 64);
-    const char *cwt = cw + ((2 * PH + 4 * q) & 7) * 256;
+    if (PH == 0) {
+      const int sl = (t >> 1) & 1;
+#pragma unroll
+      for (int nn = 0; nn < 2; ++nn) {
+        cv[nn] = *reinterpret_cast<const uint4 *>(cw + (nn * 2 + sl) * kTileBytes);
+        sv[nn] = *reinterpret_cast<const float2 *>(sw + (nn * 2 + sl) * kTileScales * 4);
+      }
+    }
+    const float s0 = PH ? sv[0].y : sv[0].x, s1 = PH ? sv[1].y : sv[1].x;
     f32x4 p[4][2];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
@@ -363,8 +355,9 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
       for (int mm = 0; mm < 4; ++mm) A[mm] = *reinterpret_cast<const bf16x8 *>(pa + mm * 1024);
 #pragma unroll
       for (int nn = 0; nn < 2; ++nn) {
-        const uint32_t wd =
-            *reinterpret_cast<const uint32_t *>(cwt + (nn * tile::kSlots + hf) * 256);
+        // quarter 2 PH + hf of the tile: code dword 2 PH + hf of the lane
+        const uint32_t wd = (2 * PH + hf) == 0 ? cv[nn].x : (2 * PH + hf) == 1 ? cv[nn].y
+                          : (2 * PH + hf) == 2 ? cv[nn].z : cv[nn].w;
         uint32_t bb[4];
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
