@@ -58,10 +58,10 @@ DOMINANT = ("gate_up", 2 * MLP, HIDDEN)
 # `python bench.py --pmc-pass` (profiles/hbm_traffic_gate_up.md): counter KiB
 # per dispatch and the calibration of each counter on a plain 1 GiB copy.
 TRAFFIC = {
-    "gemv": {"source": "gemv.hip", "fetch_kib": 37533, "write_kib": 148,
-             "sha256": "c4aa8ca97a42bd9cf9198e03b33d2b8c5161269b7fbfa1f52b6c683ecc1c70cc"},
-    "gemm": {"source": "gemm.hip", "fetch_kib": 206645, "write_kib": 151553,
-             "sha256": "c0f983011d51f4d5192906691df56c0c652e641d0ac15a155ddd3300d4209d06"},
+    "gemv": {"source": "gemv.hip", "fetch_kib": 37530, "write_kib": 148,
+             "sha256": "3fb2deb8a460ad9c2fb9428591ccc0b9f6758d677e834546e5852b4d0d4acde9"},
+    "gemm": {"source": "gemm.hip", "fetch_kib": 180720, "write_kib": 153684,
+             "sha256": "7ed7b44ddb1ac1e5979ad93d4f95dc2525845e72386aad7098830595578322f9"},
 }
 COPY_CALIBRATION = {"fetch_kib_per_gib": 524308, "write_kib_per_gib": 1048576}
 
