@@ -8,13 +8,16 @@ Qwen2-7B-shaped decoder (hidden 3584, MLP 18944, k/v 512, head 152064):
            launches, 13.364 TFLOP.
 Weights are seeded N(0, 0.02^2) fp32 drawn on the GPU and quantized there by
 nf4_pack (load time, untimed); activations are seeded N(0, 1) in bf16.  Each
-sequence is captured once in a HIP graph and replayed.  The JSON line's
+sequence is captured once in a HIP graph and replayed.  Every decode launch
+names the next one's matrix as its read-ahead hint (nf4_gemv_prefetch):
+a decoder knows its weights ahead of the activations.  The JSON line's
 `value` is decode packed-weight GB/s over the whole step (launch gaps
 included); prefill TFLOP/s sits beside it.
 
 `roofline` covers the dominant decode kernel (the gate|up GEMV, 28 launches
 per step): its 28 launches on distinct weights are replayed back to back in
-one graph, each replay timed with events on the launch stream; the median
+one graph, each naming the next as its hint as in the step, each replay
+timed with events on the launch stream; the median
 replay / 28 is the launch duration.  `roofline_prefill`
 does the same for the gate|up GEMM.  `traffic` is the HBM bytes per launch
 from rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, each scaled by what the
@@ -58,9 +61,9 @@ DOMINANT = ("gate_up", 2 * MLP, HIDDEN)
 # `python bench.py --pmc-pass` (profiles/hbm_traffic_gate_up.md): counter KiB
 # per dispatch and the calibration of each counter on a plain 1 GiB copy.
 TRAFFIC = {
-    "gemv": {"source": "gemv.hip", "fetch_kib": 37530, "write_kib": 148,
-             "sha256": "3fb2deb8a460ad9c2fb9428591ccc0b9f6758d677e834546e5852b4d0d4acde9"},
-    "gemm": {"source": "gemm.hip", "fetch_kib": 180720, "write_kib": 153684,
+    "gemv": {"source": "gemv.hip", "fetch_kib": 42727, "write_kib": 148,
+             "sha256": "61a295479b812add35f76dcdbe8184987c95604af965c7ff245d061849268203"},
+    "gemm": {"source": "gemm.hip", "fetch_kib": 180720, "write_kib": 153848,
              "sha256": "7ed7b44ddb1ac1e5979ad93d4f95dc2525845e72386aad7098830595578322f9"},
 }
 COPY_CALIBRATION = {"fetch_kib_per_gib": 524308, "write_kib_per_gib": 1048576}
@@ -181,13 +184,21 @@ class Model:
         self.ws = torch.zeros(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()  # inputs and the zeroed workspace are ready before stream s runs
 
-    def gemv(self, name, layer):
-        if name == "lm_head":
-            pw, K = self.lm_head, HIDDEN
+    def packed(self, name, layer):
+        return self.lm_head if name == "lm_head" else self.weights[layer][name]
+
+    def gemv(self, name, layer, nxt=None):
+        """One decode GEMV; nxt = (name, layer) of the next launch on the
+        stream, named as a read-ahead hint (nf4_gemv_prefetch)."""
+        pw = self.packed(name, layer)
+        if nxt is None:
+            self.nf4.nf4_gemv(self.x1[pw.K], 1, pw.qweight, pw.absmax, self.cb, pw.N, pw.K,
+                              self.y1[name], self.ws, self.ws_bytes)
         else:
-            pw, K = self.weights[layer][name], dict((n, k) for n, _, k in LINEARS)[name]
-        self.nf4.nf4_gemv(self.x1[K], 1, pw.qweight, pw.absmax, self.cb, pw.N, K, self.y1[name],
-                          self.ws, self.ws_bytes)
+            npw = self.packed(*nxt)
+            self.nf4.nf4_gemv_prefetch(self.x1[pw.K], 1, pw.qweight, pw.absmax, self.cb, pw.N,
+                                       pw.K, self.y1[name], self.ws, self.ws_bytes,
+                                       npw.qweight, npw.absmax, npw.N, npw.K)
 
     def gemm(self, name, layer):
         pw = self.weights[layer][name]
@@ -277,11 +288,14 @@ def main():
         + packed_bytes(VOCAB, HIDDEN)
     prefill_flop = 2 * PREFILL_M * sum(N * K for _, N, K in LINEARS) * LAYERS
 
+    # a decode step's launches in order; each names the next one as its
+    # read-ahead hint (the weights are known ahead, the activations are not)
+    decode_order = [(name, layer) for layer in range(LAYERS) for name, _, _ in LINEARS] + \
+        [("lm_head", 0)]
+
     def decode_step():
-        for layer in range(LAYERS):
-            for name, _, _ in LINEARS:
-                mdl.gemv(name, layer)
-        mdl.gemv("lm_head", 0)
+        for i, (name, layer) in enumerate(decode_order):
+            mdl.gemv(name, layer, decode_order[i + 1] if i + 1 < len(decode_order) else None)
 
     def prefill_step():
         for layer in range(LAYERS):
@@ -316,7 +330,10 @@ def main():
     # launches back to back
     name, N, K = DOMINANT
     reps = args.dominant_replays
-    gemv_ms = graph_ms(torch, s, lambda: [mdl.gemv(name, l) for l in range(LAYERS)], reps)
+    # (each launch hints the next layer's gate|up, as the launch before a
+    # gate|up in a decode step hints it)
+    gemv_ms = graph_ms(torch, s, lambda: [mdl.gemv(name, l, (name, (l + 1) % LAYERS))
+                                          for l in range(LAYERS)], reps)
     gemv_us = gemv_ms * 1e3 / LAYERS
     launches += [("gemv", name)] * (LAYERS * (reps + 1))
     gemm_ms = graph_ms(torch, s, lambda: [mdl.gemm(name, l) for l in range(LAYERS)], reps)
@@ -389,6 +406,7 @@ def main():
         "config": {"workload": "Qwen2-7B-shaped decoder layer linears (28 layers, fused q|k|v "
                                "and gate|up) + lm_head: decode M=1 then prefill M=1024",
                    "decode_M": 1, "prefill_M": PREFILL_M, "layers": LAYERS,
+                   "decode_read_ahead": "each nf4_gemv names the next launch's matrix",
                    "decode_packed_bytes": decode_bytes, "prefill_flop": prefill_flop,
                    "block": 64, "scale_dtype": "fp32", "out_dtype": "fp32"},
         "decode_ms": round(dec_ms, 4),
@@ -431,7 +449,7 @@ def pmc_pass(torch, nf4, cb, seed, s):
     mdl = Model(torch, nf4, cb, seed, s, layers=3, with_head=False, only=("gate_up",))
     with torch.cuda.stream(s):
         for layer in range(3):
-            mdl.gemv("gate_up", layer)
+            mdl.gemv("gate_up", layer, ("gate_up", (layer + 1) % 3))
             s.synchronize()
         mdl.gemm("gate_up", 0)
         s.synchronize()

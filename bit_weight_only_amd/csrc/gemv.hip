@@ -313,7 +313,8 @@ template <int M, bool ARGMAX>
 __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
     const uint16_t *__restrict__ x, const uint4 *__restrict__ qw,
     const float2 *__restrict__ am, CodeTerms ct, int N, int K, int KT, int G, int P,
-    float *__restrict__ y, uint32_t *counter, uint64_t *cand, int32_t *index) {
+    float *__restrict__ y, uint32_t *counter, uint64_t *cand, int32_t *index,
+    const char *__restrict__ nq, const char *__restrict__ nsb, int nG, int nKT, int nP) {
   constexpr int D = kFastDepth;
   // The table is the kernel's only static LDS array, so it sits at address
   // 0 and a lookup address needs no base added; x and the partials follow in
@@ -334,6 +335,18 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
   const char *qbase = reinterpret_cast<const char *>(qw);
   const char *sbase = reinterpret_cast<const char *>(am);
   const uint32_t tile_end = (uint32_t)(T0 + Twg);
+  // Refills past the end of a wave's share read ahead into the next launch's
+  // matrix when one is named (nq): the tiles this wave index of this
+  // workgroup index loads first in that launch, so they are in the caches
+  // when it starts.  Otherwise, and past that share, they re-read the
+  // workgroup's first tile.  Their data is never used.
+  uint32_t pn = 0, ntile_end = 0;
+  if (nq != nullptr && (int)blockIdx.x < nP) {
+    const int ng0 = (int)((int64_t)nG * blockIdx.x / nP);
+    const int ng1 = (int)((int64_t)nG * (blockIdx.x + 1) / nP);
+    pn = (uint32_t)(ng0 * nKT + wave);
+    ntile_end = (uint32_t)(ng1 * nKT);
+  }
 
   // Prefetch cursor; steps past the wave's share re-read the workgroup's
   // first tile so that every step issues the same loads.
@@ -422,43 +435,55 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
       const int i = base + d;
       const bool live = i < n;
       // ---- one 16-row x 128-k tile: lane holds weight row r, k = 128t + 32jj + 8h + 0..7
+      // The 16 lookup addresses and the two scales are all the slot's words
+      // are needed for, so the slot is refilled (D tiles ahead) as soon as
+      // they are formed, and the lookups and products run while that load
+      // is in flight.  The empty asm pins the addresses before the refill
+      // and the barrier keeps the scheduler from hoisting the global loads
+      // above them (either would rotate the slot registers and force a full
+      // wait per step); ALU and LDS instructions may still cross it.
+      uint32_t ad[16];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const uint32_t wd = jj == 0 ? wb[d].x : jj == 1 ? wb[d].y : jj == 2 ? wb[d].z : wb[d].w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          ad[4 * jj + q] = __builtin_amdgcn_perm(wd, lane4, 0x0c0c0400u + (q << 8));
+      }
+      const float s0 = live ? sb[d].x : 0.0f, s1 = live ? sb[d].y : 0.0f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) asm volatile("" ::"v"(ad[u]));
+      asm volatile("" ::"v"(s0), "v"(s1));
+      __builtin_amdgcn_sched_barrier(kSchedAllButGlobalLoads);
+      {
+        const bool dead = ptau >= tile_end;
+        const bool ahead = dead && pn < ntile_end;
+        const uint32_t lt = ahead ? pn : dead ? (uint32_t)T0 : ptau;
+        const char *qsrc = ahead ? nq : qbase;
+        const char *ssrc = ahead ? nsb : sbase;
+        wb[d] = *reinterpret_cast<const uint4 *>(qsrc + (lt * 1024u + lane * 16u));
+        sb[d] = *reinterpret_cast<const float2 *>(ssrc + (lt * 128u + r * 8u));
+        ptau += kFastWaves;
+        pn += dead ? kFastWaves : 0u;
+      }
       const uint16_t *xt = xrow + t * kTileK;
       f32x4 P[2];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const uint32_t wd = jj == 0 ? wb[d].x : jj == 1 ? wb[d].y : jj == 2 ? wb[d].z : wb[d].w;
         const uint4 xa = *reinterpret_cast<const uint4 *>(xt + 32 * jj);
         uint32_t bb[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t addr = __builtin_amdgcn_perm(wd, lane4, 0x0c0c0400u + (q << 8));
-          bb[q] = *reinterpret_cast<const uint32_t *>(tabc + addr);
-        }
+        for (int q = 0; q < 4; ++q)
+          bb[q] = *reinterpret_cast<const uint32_t *>(tabc + ad[4 * jj + q]);
         const bf16x8 A = __builtin_bit_cast(bf16x8, xa);
         const bf16x8 B = __builtin_bit_cast(bf16x8, make_uint4(bb[0], bb[1], bb[2], bb[3]));
         P[jj >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, (jj & 1) ? P[jj >> 1] : zero,
                                                              0, 0, 0);
       }
-      const float s0 = live ? sb[d].x : 0.0f, s1 = live ? sb[d].y : 0.0f;
 #pragma unroll
       for (int e = 0; e < NA; ++e) {
         acc[e] = fmaf(s0, P[0][e], acc[e]);
         acc[e] = fmaf(s1, P[1][e], acc[e]);
-      }
-      // ---- refill this slot (D tiles ahead).  The empty asm pins the
-      // accumulation before this point and the barrier keeps the scheduler
-      // from hoisting the global loads above the slot's last use (either
-      // would rotate the slot registers and force a full wait per step);
-      // ALU and LDS instructions may still move across it, so the next
-      // tile's table lookups overlap this tile's arithmetic.
-#pragma unroll
-      for (int e = 0; e < NA; ++e) asm volatile("" ::"v"(acc[e]));
-      __builtin_amdgcn_sched_barrier(kSchedAllButGlobalLoads);
-      {
-        const uint32_t lt = ptau < tile_end ? ptau : (uint32_t)T0;
-        wb[d] = *reinterpret_cast<const uint4 *>(qbase + (lt * 1024u + lane * 16u));
-        sb[d] = *reinterpret_cast<const float2 *>(sbase + (lt * 128u + r * 8u));
-        ptau += kFastWaves;
       }
       // ---- advance; when the row group changes (or the share ends), leave
       // this wave's partial for it in LDS
@@ -543,7 +568,7 @@ bool fast_eligible(int M, int64_t N, int64_t K, int nterm) {
 template <int M, bool ARGMAX>
 hipError_t launch_fast(const uint16_t *x, const uint4 *qw, const float2 *am, const CodeTerms &ct,
                        int64_t N, int64_t K, float *y, uint32_t *counter, uint64_t *cand,
-                       int32_t *index, hipStream_t s) {
+                       int32_t *index, hipStream_t s, const NextMatrix *next) {
   static std::atomic<bool> attr_set{false};
   if (!attr_set.load(std::memory_order_acquire)) {
     const hipError_t e = hipFuncSetAttribute(
@@ -553,9 +578,19 @@ hipError_t launch_fast(const uint16_t *x, const uint4 *qw, const float2 *am, con
     attr_set.store(true, std::memory_order_release);
   }
   const FastPlan p = fast_plan(M, N, K);
+  // the next launch's partition, if it takes this fast path with the same M
+  const char *nq = nullptr, *nsb = nullptr;
+  int nG = 0, nKT = 0, nP = 0;
+  if (next != nullptr && next->qw != nullptr && fast_eligible(M, next->N, next->K, 1)) {
+    nq = reinterpret_cast<const char *>(next->qw);
+    nsb = reinterpret_cast<const char *>(next->am);
+    nG = (int)(next->N / kTileRows);
+    nKT = (int)tiles_k(next->K);
+    nP = fast_plan(M, next->N, next->K).P;
+  }
   hipLaunchKernelGGL((gemv_fast_kernel<M, ARGMAX>), dim3(p.P), dim3(kFastWaves * 64), p.lds, s, x,
                      qw, am, ct, (int)N, (int)K, (int)tiles_k(K), (int)(N / kTileRows), p.P, y,
-                     counter, cand, index);
+                     counter, cand, index, nq, nsb, nG, nKT, nP);
   return hipGetLastError();
 }
 
@@ -609,7 +644,7 @@ hipError_t launch_argmax_m(const uint16_t *x, const uint4 *q, const float2 *a, c
                            int nterm, int64_t N, int64_t K, float *y, uint32_t *counter,
                            uint64_t *cand, int32_t *index, hipStream_t s) {
   if (fast_eligible(M, N, K, nterm))
-    return launch_fast<M, true>(x, q, a, ct, N, K, y, counter, cand, index, s);
+    return launch_fast<M, true>(x, q, a, ct, N, K, y, counter, cand, index, s, nullptr);
   const hipError_t e =
       skinny_eligible(M, N, K, nterm)
           ? launch_skinny(x, M, reinterpret_cast<const uint8_t *>(q),
@@ -653,19 +688,19 @@ hipError_t launch_gemv_argmax(const uint16_t *x, int M, const uint8_t *qw, const
 
 hipError_t launch_gemv(const uint16_t *x, int M, const uint8_t *qw, const float *am,
                        const CodeTerms &ct, int nterm, int64_t N, int64_t K, float *y, void *ws,
-                       hipStream_t s) {
+                       hipStream_t s, const NextMatrix *next) {
   const uint4 *q = reinterpret_cast<const uint4 *>(qw);
   const float2 *a = reinterpret_cast<const float2 *>(am);
   if (fast_eligible(M, N, K, nterm)) {
     switch (M) {
-      case 1: return launch_fast<1, false>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s);
-      case 2: return launch_fast<2, false>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s);
-      case 3: return launch_fast<3, false>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s);
-      case 4: return launch_fast<4, false>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s);
-      case 5: return launch_fast<5, false>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s);
-      case 6: return launch_fast<6, false>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s);
-      case 7: return launch_fast<7, false>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s);
-      case 8: return launch_fast<8, false>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s);
+      case 1: return launch_fast<1, false>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, next);
+      case 2: return launch_fast<2, false>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, next);
+      case 3: return launch_fast<3, false>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, next);
+      case 4: return launch_fast<4, false>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, next);
+      case 5: return launch_fast<5, false>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, next);
+      case 6: return launch_fast<6, false>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, next);
+      case 7: return launch_fast<7, false>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, next);
+      case 8: return launch_fast<8, false>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, next);
       default: return hipErrorInvalidValue;
     }
   }

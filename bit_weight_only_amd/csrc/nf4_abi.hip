@@ -205,6 +205,34 @@ nf4_status nf4_gemv(const uint16_t *x, int64_t M, const uint8_t *qweight, const 
       nf4::launch_gemv(x, (int)M, qweight, absmax, ct, nterm, N, K, y, workspace, stream));
 }
 
+nf4_status nf4_gemv_prefetch(const uint16_t *x, int64_t M, const uint8_t *qweight,
+                             const float *absmax, const float codebook[16], int64_t N, int64_t K,
+                             float *y, void *workspace, size_t ws_bytes,
+                             const uint8_t *next_qweight, const float *next_absmax,
+                             int64_t next_N, int64_t next_K, hipStream_t stream) {
+  nf4_status st = check_linear_args(x, M, qweight, absmax, codebook, N, K, y, kMaxGemvM);
+  if (st != NF4_OK) return st;
+  nf4::NextMatrix next;
+  if (next_qweight != nullptr) {
+    if (!next_absmax) return NF4_ERR_NULL;
+    if (!aligned16(next_qweight) || !aligned16(next_absmax)) return NF4_ERR_ALIGN;
+    if (!shape_ok(next_N, next_K)) return NF4_ERR_SHAPE;
+    next.qw = next_qweight;
+    next.am = next_absmax;
+    next.N = next_N;
+    next.K = next_K;
+  }
+  const size_t need = nf4::gemv_workspace_bytes(M, N, K);
+  if (need > 0 && !workspace) return NF4_ERR_NULL;
+  if (need > ws_bytes) return NF4_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return NF4_ERR_ALIGN;
+  nf4::CodeTerms ct;
+  const int nterm = split_codebook(codebook, ct);
+  if (nterm == 0) return NF4_ERR_CODEBOOK;
+  return from_hip(nf4::launch_gemv(x, (int)M, qweight, absmax, ct, nterm, N, K, y, workspace,
+                                   stream, next_qweight ? &next : nullptr));
+}
+
 size_t nf4_gemv_argmax_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || M > kMaxGemvM || !shape_ok(N, K)) return 0;
   return nf4::gemv_argmax_workspace_bytes(M, N, K);

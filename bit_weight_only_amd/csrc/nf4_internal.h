@@ -54,9 +54,16 @@ hipError_t launch_repack(const uint8_t *codes, const float *scales, int64_t N, i
                          uint8_t *qw, float *am, hipStream_t s);
 hipError_t launch_unpack(const uint8_t *qw, const float *am, int64_t N, int64_t K, uint8_t *codes,
                          float *scales, hipStream_t s);
+// The packed matrix of the next GEMV launch, named so that the current
+// launch can read its first tiles ahead (a hint: results never depend on it).
+struct NextMatrix {
+  const uint8_t *qw = nullptr;
+  const float *am = nullptr;
+  int64_t N = 0, K = 0;
+};
 hipError_t launch_gemv(const uint16_t *x, int M, const uint8_t *qw, const float *am,
                        const CodeTerms &ct, int nterm, int64_t N, int64_t K, float *y, void *ws,
-                       hipStream_t s);
+                       hipStream_t s, const NextMatrix *next = nullptr);
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K);
 // GEMV followed by the row-wise argmax of y (fused into the fast kernel).
 hipError_t launch_gemv_argmax(const uint16_t *x, int M, const uint8_t *qw, const float *am,

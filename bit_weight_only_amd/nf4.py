@@ -19,7 +19,7 @@ NF4_OK, NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_CODEBOOK, NF4_ERR_WO
 
 EXPORTS = ("nf4_status_string", "nf4_qweight_bytes", "nf4_absmax_bytes", "nf4_workspace_bytes",
            "nf4_pack", "nf4_dequant", "nf4_repack", "nf4_unpack", "nf4_gemv", "nf4_gemm",
-           "nf4_gemv_argmax_workspace_bytes", "nf4_gemv_argmax")
+           "nf4_gemv_argmax_workspace_bytes", "nf4_gemv_argmax", "nf4_gemv_prefetch")
 
 _lib = None
 
@@ -61,6 +61,9 @@ def lib() -> ctypes.CDLL:
         L.nf4_gemv_argmax_workspace_bytes.argtypes = [i64, i64, i64]
         L.nf4_gemv_argmax.restype = st
         L.nf4_gemv_argmax.argtypes = [vp, i64, vp, vp, fp, i64, i64, vp, vp, vp, sz, vp]
+        L.nf4_gemv_prefetch.restype = st
+        L.nf4_gemv_prefetch.argtypes = [vp, i64, vp, vp, fp, i64, i64, vp, vp, sz, vp, vp, i64,
+                                        i64, vp]
         _lib = L
     return _lib
 
@@ -132,6 +135,15 @@ def nf4_gemv(x, M: int, qweight, absmax, codebook, N: int, K: int, y, workspace=
              ws_bytes: int = 0, stream=None) -> None:
     _check(lib().nf4_gemv(_ptr(x), M, _ptr(qweight), _ptr(absmax), _codebook(codebook), N, K,
                           _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)), "nf4_gemv")
+
+
+def nf4_gemv_prefetch(x, M: int, qweight, absmax, codebook, N: int, K: int, y, workspace=None,
+                      ws_bytes: int = 0, next_qweight=None, next_absmax=None, next_N: int = 0,
+                      next_K: int = 0, stream=None) -> None:
+    _check(lib().nf4_gemv_prefetch(_ptr(x), M, _ptr(qweight), _ptr(absmax), _codebook(codebook),
+                                   N, K, _ptr(y), _ptr(workspace), ws_bytes, _ptr(next_qweight),
+                                   _ptr(next_absmax), next_N, next_K, _stream(stream)),
+           "nf4_gemv_prefetch")
 
 
 def nf4_gemm(x, M: int, qweight, absmax, codebook, N: int, K: int, y, workspace=None,

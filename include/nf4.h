@@ -77,11 +77,12 @@ size_t nf4_qweight_bytes(int64_t N, int64_t K);
 size_t nf4_absmax_bytes(int64_t N, int64_t K);
 
 /* Bytes of scratch that nf4_gemv / nf4_gemm need for an M x N x K call on
- * the current device (partial sums of row groups split across waves and
- * their arrival counters); the larger of the two needs.  A workspace must be
- * zero-filled once when it is allocated; every call leaves its counters at
- * zero again.  Calls sharing one workspace must be ordered (the same
- * stream, or synchronised). */
+ * the current device; the larger of the two needs.  Neither needs any on
+ * this build (the GEMV sums its partials in LDS and the GEMM never splits
+ * K), so this returns 0 and the workspace arguments may be NULL with 0
+ * bytes; a caller that passes a workspace anyway keeps working if a later
+ * build needs one (zero-filled once at allocation, calls sharing it
+ * ordered). */
 size_t nf4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Quantize fp32 W[N][K] (row-major) into the device layout.  Per block of
@@ -119,6 +120,27 @@ nf4_status nf4_unpack(const uint8_t *qweight, const float *absmax, int64_t N, in
 nf4_status nf4_gemv(const uint16_t *x, int64_t M, const uint8_t *qweight, const float *absmax,
                     const float codebook[16], int64_t N, int64_t K, float *y, void *workspace,
                     size_t ws_bytes, hipStream_t stream);
+
+/* nf4_gemv, plus a read-ahead hint naming the packed matrix of the next GEMV
+ * launch on the stream (next_qweight, next_absmax, next_N x next_K, in the
+ * device layout).  The pages put the shortfall of the small projections on
+ * a fixed cost per kernel (vibevoice.c README, "Quantization" > "Weights",
+ * the decode-GEMV bullet of the int4 GPU path: launch, ramp-up and tail); a
+ * decode step knows its linears in advance, and a matrix does not depend on
+ * activations, so this launch spends the loads it issues after its own
+ * weights are in flight on the first tiles the next launch will read (as
+ * planned for the same M), which then start from the caches.  y is computed
+ * exactly as by nf4_gemv: bit for bit the same, with or without the hint.
+ * next_qweight == NULL means no hint (next_absmax and the next shape are
+ * then ignored).  Otherwise next_absmax must not be NULL, both must be
+ * 16-byte aligned device buffers of an existing packed matrix whose shape
+ * nf4_gemv accepts (else NF4_ERR_NULL, NF4_ERR_ALIGN, NF4_ERR_SHAPE); the
+ * next matrix is only read.  Other arguments and errors as nf4_gemv. */
+nf4_status nf4_gemv_prefetch(const uint16_t *x, int64_t M, const uint8_t *qweight,
+                             const float *absmax, const float codebook[16], int64_t N, int64_t K,
+                             float *y, void *workspace, size_t ws_bytes,
+                             const uint8_t *next_qweight, const float *next_absmax,
+                             int64_t next_N, int64_t next_K, hipStream_t stream);
 
 /* Bytes of workspace nf4_gemv_argmax needs for an M x N x K call on the
  * current device: an arrival counter and one 8-byte candidate per workgroup

@@ -153,6 +153,32 @@ def test_argmax_validation():
         assert nf4.nf4_gemv_argmax_workspace_bytes(M, N, K) == 0
 
 
+def test_prefetch_validation():
+    """nf4_gemv_prefetch checks its own arguments as nf4_gemv does, and the
+    next matrix when one is named; only calls that fail before any HIP call
+    are made here."""
+    f = lambda *a: call("nf4_gemv_prefetch", *a)
+    ok = [A, 1, A, A, cbarr(), 16, 64, A, None, 0, A, A, 32, 128, None]
+    for i, err in ((0, nf4.NF4_ERR_NULL), (2, nf4.NF4_ERR_NULL), (7, nf4.NF4_ERR_NULL)):
+        bad = list(ok)
+        bad[i] = None
+        assert f(*bad) == err, i
+    bad = list(ok)
+    bad[1] = 9
+    assert f(*bad) == nf4.NF4_ERR_SHAPE
+    bad = list(ok)
+    bad[11] = None                      # next qweight without next absmax
+    assert f(*bad) == nf4.NF4_ERR_NULL
+    for i in (10, 11):
+        bad = list(ok)
+        bad[i] = A + 8
+        assert f(*bad) == nf4.NF4_ERR_ALIGN, i
+    for nN, nK in ((24, 128), (32, 96), (0, 64), (16, 0)):
+        bad = list(ok)
+        bad[12], bad[13] = nN, nK
+        assert f(*bad) == nf4.NF4_ERR_SHAPE, (nN, nK)
+
+
 def test_binding_raises_named_errors():
     with pytest.raises(nf4.NF4Error) as e:
         nf4.nf4_gemv(A, 9, A, A, CB, 16, 64, A, stream=0)
