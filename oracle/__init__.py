@@ -71,6 +71,15 @@ def lib():
         L.oracle_dequant.argtypes = [vp, vp, vp, i64, i64, vp]
         L.oracle_linear.restype = ctypes.c_int
         L.oracle_linear.argtypes = [vp, i64, vp, vp, vp, i64, i64, vp, i64, vp, vp, ctypes.c_int]
+        L.oracle_round_fp16.restype = d
+        L.oracle_round_fp16.argtypes = [d]
+        L.oracle_awq_quantize.restype = ctypes.c_int
+        L.oracle_awq_quantize.argtypes = [vp, i64, i64, vp, vp, vp, ctypes.c_int]
+        L.oracle_awq_dequant.restype = None
+        L.oracle_awq_dequant.argtypes = [vp, vp, vp, i64, i64, vp]
+        L.oracle_awq_linear.restype = ctypes.c_int
+        L.oracle_awq_linear.argtypes = [vp, i64, vp, vp, vp, i64, i64, vp, i64, vp, vp,
+                                        ctypes.c_int]
         _lib = L
     return _lib
 
@@ -184,6 +193,76 @@ def linear(x_bf16: np.ndarray, packed: np.ndarray, absmax: np.ndarray, cb: np.nd
                              nrows, _ptr(y), _ptr(bound), threads or default_threads())
     if rc != 0:
         raise ValueError("oracle_linear: bad arguments")
+    return y, bound
+
+
+# ---------------------------------------------------------------- second format
+# Asymmetric int4 in groups of 128 along K (vibevoice.c README, "Quantization"
+# > "Weights", the AWQ/GPTQ paragraph): w = (q - z) * s with an exact integer
+# zero point z per group and an FP16 scale s per group.  The pages give the
+# dequantization; the quantizer is the plain min-max round-to-nearest of that
+# form (a reading: the pages load quantized checkpoints).
+GROUP = 128
+
+
+def round_fp16(v: float) -> float:
+    """Nearest binary16 value (ties to even), as a float."""
+    return lib().oracle_round_fp16(float(v))
+
+
+def awq_quantize(W: np.ndarray, threads: int | None = None):
+    """Per row and group of 128: s = fp16(max(wmax - wmin, 1e-5) / 15),
+    z = clamp(rint(-wmin / s), 0, 15), q = clamp(rint(w / s) + z, 0, 15).
+
+    Returns (codes uint8 [N, K], scales float32 [N, K/128], zeros uint8
+    [N, K/128])."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    codes = np.empty((N, K), np.uint8)
+    scales = np.empty((N, K // GROUP), np.float32)
+    zeros = np.empty((N, K // GROUP), np.uint8)
+    rc = lib().oracle_awq_quantize(_ptr(W), N, K, _ptr(codes), _ptr(scales), _ptr(zeros),
+                                   threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_awq_quantize: K must be a positive multiple of 128")
+    return codes, scales, zeros
+
+
+def awq_dequant(packed: np.ndarray, scales: np.ndarray, zeros: np.ndarray) -> np.ndarray:
+    """W'[n, k] = fl32((q - z) * s): one binary32 multiply per weight."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
+    N, K2 = packed.shape
+    K = 2 * K2
+    assert scales.shape == (N, K // GROUP) and zeros.shape == (N, K // GROUP)
+    out = np.empty((N, K), np.float32)
+    lib().oracle_awq_dequant(_ptr(packed), _ptr(scales), _ptr(zeros), N, K, _ptr(out))
+    return out
+
+
+def awq_linear(x_bf16: np.ndarray, packed: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
+               rows=None, threads: int | None = None):
+    """y[m, n] = sum_k x[m, k] * W'[n, k] in double, natural k order, with the
+    second format's W'; returns (y, bound) as linear()."""
+    x_bf16 = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
+    M, K = x_bf16.shape
+    N = packed.shape[0]
+    assert packed.shape == (N, K // 2)
+    if rows is None:
+        rows_arr, nrows, rp = None, N, None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows, rp = rows_arr.size, _ptr(rows_arr)
+    y = np.empty((M, nrows), np.float64)
+    bound = np.empty((M, nrows), np.float64)
+    rc = lib().oracle_awq_linear(_ptr(x_bf16), M, _ptr(packed), _ptr(scales), _ptr(zeros), N, K,
+                                 rp, nrows, _ptr(y), _ptr(bound), threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_awq_linear: bad arguments")
     return y, bound
 
 

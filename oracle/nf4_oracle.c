@@ -285,3 +285,172 @@ int oracle_linear(const uint16_t *x, int64_t M, const uint8_t *packed, const flo
   for (int t = 1; t < nthreads; ++t) pthread_join(th[t], NULL);
   return 0;
 }
+
+/* ======================================================================== */
+/* Second format: asymmetric int4 in groups of 128 along K (vibevoice.c     */
+/* README, "Quantization" > "Weights", the AWQ/GPTQ paragraph): a weight is */
+/* (q - z) * s with a 4-bit integer q, an exact integer zero point z per    */
+/* group and an FP16 scale s per group.                                     */
+/* ======================================================================== */
+#define ORACLE_GROUP 128
+
+/* Nearest binary16 value of a double, ties to even; the result as a double.
+ * Written from the IEEE 754 binary16 format: 11 significant bits for
+ * normal values (exponent -14..15), a fixed quantum of 2^-24 below 2^-14,
+ * and overflow past the largest finite value 65504 to infinity. */
+double oracle_round_fp16(double v) {
+  if (v != v || v == 0.0) return v;
+  const double a = fabs(v);
+  if (a >= 65520.0) return v > 0 ? INFINITY : -INFINITY;  /* halfway to 2^16 and above */
+  int e;
+  frexp(a, &e);                      /* a = f * 2^e with f in [0.5, 1) */
+  int q_exp = e - 11;                /* quantum of an 11-bit significand */
+  if (q_exp < -24) q_exp = -24;      /* subnormal range: fixed quantum */
+  const double quantum = ldexp(1.0, q_exp);
+  const double r = nearbyint(a / quantum) * quantum;  /* a / quantum is exact */
+  return v > 0 ? r : -r;
+}
+
+/* Per row and group of 128: wmin, wmax; s = fp16(max(wmax - wmin, 1e-5) / 15);
+ * z = clamp(rint(-wmin / s), 0, 15); q = clamp(rint(w / s) + z, 0, 15), all
+ * in double with round-half-even (the rounding mode in force).  codes: one
+ * per byte [N][K]; scales fp32 [N][K/128] (each fp16-exact); zeros uint8
+ * [N][K/128].  Returns -1 on a bad shape. */
+typedef struct {
+  const float *W;
+  int64_t N, K;
+  uint8_t *codes;
+  float *scales;
+  uint8_t *zeros;
+  int64_t r0, r1;
+} awq_job;
+
+static void awq_rows(const awq_job *j) {
+  const int64_t ng = j->K / ORACLE_GROUP;
+  for (int64_t n = j->r0; n < j->r1; ++n)
+    for (int64_t g = 0; g < ng; ++g) {
+      const float *w = j->W + n * j->K + g * ORACLE_GROUP;
+      uint8_t *q = j->codes + n * j->K + g * ORACLE_GROUP;
+      float lo = w[0], hi = w[0];
+      for (int k = 1; k < ORACLE_GROUP; ++k) {
+        if (w[k] < lo) lo = w[k];
+        if (w[k] > hi) hi = w[k];
+      }
+      double range = (double)hi - (double)lo;
+      if (range < 1e-5) range = 1e-5;
+      const double s = oracle_round_fp16(range / 15.0);
+      double z = nearbyint(-(double)lo / s);
+      if (z < 0) z = 0;
+      if (z > 15) z = 15;
+      j->scales[n * ng + g] = (float)s;
+      j->zeros[n * ng + g] = (uint8_t)z;
+      for (int k = 0; k < ORACLE_GROUP; ++k) {
+        double v = nearbyint((double)w[k] / s) + z;
+        if (v < 0) v = 0;
+        if (v > 15) v = 15;
+        q[k] = (uint8_t)v;
+      }
+    }
+}
+
+static void *awq_thread(void *arg) {
+  awq_rows((const awq_job *)arg);
+  return NULL;
+}
+
+int oracle_awq_quantize(const float *W, int64_t N, int64_t K, uint8_t *codes, float *scales,
+                        uint8_t *zeros, int nthreads) {
+  if (N < 1 || K < ORACLE_GROUP || K % ORACLE_GROUP) return -1;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  if ((int64_t)nthreads > N) nthreads = (int)N;
+  pthread_t th[256];
+  awq_job jobs[256];
+  for (int t = 0; t < nthreads; ++t)
+    jobs[t] = (awq_job){W, N, K, codes, scales, zeros, N * t / nthreads, N * (t + 1) / nthreads};
+  for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], NULL, awq_thread, &jobs[t]);
+  awq_rows(&jobs[0]);
+  for (int t = 1; t < nthreads; ++t) pthread_join(th[t], NULL);
+  return 0;
+}
+
+/* W'[n,k] = fl32((q - z) * s): the integer q - z (exact in binary32) times s,
+ * one binary32 multiply.  packed: canonical bytes [N][K/2]. */
+static void awq_dequant_row(const uint8_t *packed, const float *scales, const uint8_t *zeros,
+                            int64_t K, int64_t n, float *out_row) {
+  const int64_t ng = K / ORACLE_GROUP;
+  for (int64_t k = 0; k < K; ++k) {
+    const int q = code_at(packed, K, n, k);
+    const int z = zeros[n * ng + k / ORACLE_GROUP];
+    const float d = (float)(q - z);
+    const float s = scales[n * ng + k / ORACLE_GROUP];
+    out_row[k] = d * s;
+  }
+}
+
+void oracle_awq_dequant(const uint8_t *packed, const float *scales, const uint8_t *zeros,
+                        int64_t N, int64_t K, float *W_out) {
+  for (int64_t n = 0; n < N; ++n) awq_dequant_row(packed, scales, zeros, K, n, W_out + n * K);
+}
+
+/* y[m,n] = sum_k x[m,k] * W'[n,k] in double, natural k order, and
+ * bound[m,n] = sum_k |x[m,k] * W'[n,k]|, as oracle_linear. */
+typedef struct {
+  const uint16_t *x;
+  int64_t M;
+  const uint8_t *packed;
+  const float *scales;
+  const uint8_t *zeros;
+  int64_t N, K;
+  const int64_t *rows;
+  int64_t nrows;
+  double *y, *bound;
+  int64_t r0, r1;
+} awq_linear_job;
+
+static void awq_linear_part(const awq_linear_job *j) {
+  float *w = (float *)malloc(sizeof(float) * (size_t)j->K);
+  if (!w) return;
+  for (int64_t r = j->r0; r < j->r1; ++r) {
+    int64_t n = j->rows ? j->rows[r] : r;
+    awq_dequant_row(j->packed, j->scales, j->zeros, j->K, n, w);
+    for (int64_t m = 0; m < j->M; ++m) {
+      const uint16_t *xr = j->x + m * j->K;
+      double acc = 0.0, b = 0.0;
+      for (int64_t k = 0; k < j->K; ++k) {
+        double p = bf16_to_double(xr[k]) * (double)w[k];
+        acc += p;
+        b += fabs(p);
+      }
+      j->y[m * j->nrows + r] = acc;
+      if (j->bound) j->bound[m * j->nrows + r] = b;
+    }
+  }
+  free(w);
+}
+
+static void *awq_linear_thread(void *arg) {
+  awq_linear_part((const awq_linear_job *)arg);
+  return NULL;
+}
+
+int oracle_awq_linear(const uint16_t *x, int64_t M, const uint8_t *packed, const float *scales,
+                      const uint8_t *zeros, int64_t N, int64_t K, const int64_t *rows,
+                      int64_t nrows, double *y, double *bound, int nthreads) {
+  if (M < 1 || N < 1 || K < ORACLE_GROUP || K % ORACLE_GROUP) return -1;
+  if (!rows) nrows = N;
+  for (int64_t r = 0; rows && r < nrows; ++r)
+    if (rows[r] < 0 || rows[r] >= N) return -1;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  if ((int64_t)nthreads > nrows) nthreads = (int)nrows;
+  pthread_t th[256];
+  awq_linear_job jobs[256];
+  for (int t = 0; t < nthreads; ++t)
+    jobs[t] = (awq_linear_job){x, M, packed, scales, zeros, N, K, rows, nrows,
+                               y, bound, nrows * t / nthreads, nrows * (t + 1) / nthreads};
+  for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], NULL, awq_linear_thread, &jobs[t]);
+  awq_linear_part(&jobs[0]);
+  for (int t = 1; t < nthreads; ++t) pthread_join(th[t], NULL);
+  return 0;
+}
