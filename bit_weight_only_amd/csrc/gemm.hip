@@ -204,26 +204,43 @@ __device__ inline void wait_copies_and_barrier() {
 // landed.  Every output gets the operations of the other kernels: per
 // 64-block P = MFMA(kk=0, zero), MFMA(kk=1, P), acc = fmaf(s, P, acc), in K
 // order.
+//
+// Affine variant (AFF, the asymmetric int4 format in groups of 128 k, codes
+// 0..15 in the table): the scale ring holds the params dword per row
+// (binary16 s | z << 16, 64 bytes per tile) and a third ring
+// holds the tile's x sums X[t][m0 .. m0 + 127] (512 bytes, copied from the
+// pre-pass result with the code words; every wave copies 512 / RG bytes of
+// it).  Per device tile and output: P = -z X, four MFMAs over the tile's
+// 32-k quarters (two steps), then acc = fmaf(s, P, acc).
 namespace tile {
 constexpr int kBM = 128;
 constexpr int kTable = 256 * 64 * 4;            // one copy per lane
 constexpr int kAHalf = kBM * pipe::kHalfRow;    // 8 KB: 128 rows x 32 k
 constexpr int kOffA = kTable, kOffC = kOffA + 4 * kAHalf;
-template <int RG>
+constexpr int kXSum = kBM * 4;                  // x sums of one tile, bytes
+template <int RG, bool AFF>
 struct Map {
   static constexpr int kWaves = RG, kThreads = 64 * RG, kWN = RG / 2;  // waves along N
   static constexpr int kOffS = kOffC + RG * 2 * kTileBytes,
-                       kBytes = kOffS + RG * 2 * kTileScales * 4;
+                       kOffX = kOffS + RG * 2 * kTileScales * 4,
+                       kBytes = kOffX + (AFF ? 2 * kXSum : 0);
   static constexpr int kACopies = 16 / kWaves;  // x copies per wave per step
+  static constexpr int kXLanes = kXSum / 16 / kWaves;  // lanes per wave copying x sums
+  // copies a wave may leave in flight past the barrier of an even step: the
+  // tile copies of the step before
+  static constexpr int kTileCopies = AFF ? 3 : 2;
+  // bytes of scales (params) per device tile in global memory; the LDS slot
+  // keeps 128
+  static constexpr int kScaleBytes = AFF ? kTileRows * 4 : kTileScales * 4;
 };
 }  // namespace tile
 
-template <int RG>
+template <int RG, bool AFF>
 __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
     const uint16_t *__restrict__ x, int64_t M, const uint8_t *__restrict__ qw,
     const float *__restrict__ am, CodeTerms ct, int64_t N, int64_t K, int64_t KT,
-    float *__restrict__ y, int ntn, int ntm) {
-  using L = tile::Map<RG>;
+    float *__restrict__ y, int ntn, int ntm, const float *__restrict__ xsum, int64_t Mp) {
+  using L = tile::Map<RG, AFF>;
   // the only static LDS array, so the table sits at LDS address 0
   __shared__ __attribute__((aligned(16))) char lds[L::kBytes];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -267,10 +284,13 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
     const int64_t rg = gblk + wave;
     const int64_t g = rg < G ? rg : G - 1;
     coff = (uint32_t)(g * KT * kTileBytes + lane * 16);
-    soff = (uint32_t)((g * KT * kTileScales) * 4 + lane * 16);  // lanes 0..7 copy
+    soff = (uint32_t)(g * KT * L::kScaleBytes + lane * 16);  // lanes 0..7 (0..3) copy
   }
   const uint32_t mC = base + tile::kOffC + wave * 2 * kTileBytes;
   const uint32_t mS = base + L::kOffS + wave * 2 * kTileScales * 4;
+  // x sums (affine): wave w copies bytes [w, w + 1) * 512 / RG of a tile's 512
+  const uint32_t mX = base + L::kOffX + wave * (tile::kXSum / RG);
+  const uint32_t xoff = (uint32_t)(m0 * 4) + (uint32_t)(wave * L::kXLanes + lane) * 16u;
   auto copy_x = [&](int step) {
     const uint32_t sc = (uint32_t)(step < S ? step : S - 1) * (kBK * 2);
 #pragma unroll
@@ -282,7 +302,12 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
   auto copy_tile = [&](int T) {
     const uint32_t tc = (uint32_t)(T < KT ? T : KT - 1);
     pipe::copy16(mC + (T & 1) * kTileBytes, qw, coff + tc * kTileBytes);
-    if (lane < 8) pipe::copy16(mS + (T & 1) * kTileScales * 4, am, soff + tc * kTileScales * 4);
+    if (lane < L::kScaleBytes / 16)
+      pipe::copy16(mS + (T & 1) * kTileScales * 4, am, soff + tc * L::kScaleBytes);
+    if constexpr (AFF) {
+      if (lane < L::kXLanes)
+        pipe::copy16(mX + (T & 1) * tile::kXSum, xsum, xoff + tc * (uint32_t)(Mp * 4));
+    }
   };
 
   // the pair table, from the codebook staged in the scale ring (filled only
@@ -307,7 +332,9 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
                                   ((h ^ ((r >> 2) & 3)) * 16));
   // this wave's two row groups: code words (16 bytes per lane) and scales
   const char *cw = ldsC + (wn * 2) * 2 * kTileBytes + lane * 16;
-  const char *sw = ldsS + (wn * 2) * 2 * kTileScales * 4 + r * 8;
+  const char *sw = ldsS + (wn * 2) * 2 * kTileScales * 4 + r * (AFF ? 4 : 8);
+  // x sums of D rows wm 64 + mm 16 + 4h + i (affine)
+  const char *xw = lds + L::kOffX + (wm * 64 + 4 * h) * 4;
   f32x4 acc[4][2];
 #pragma unroll
   for (int a2 = 0; a2 < 4; ++a2)
@@ -322,6 +349,7 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
   const uint32_t xlast = (uint32_t)(S - 1) * (kBK * 2);
   uint4 cv[2];
   float2 sv[2];
+  f32x4 pz[4][2];  // affine: the tile's product, carried from the even step to the odd one
   auto step = [&](auto phc, int t) {
     constexpr int PH = decltype(phc)::value;
     // Landed: x of step t (copied in step t-1; at an even step the tile
@@ -329,7 +357,7 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
     // or more steps ago).  Past the barrier no wave reads x of step t-1, and
     // at an odd step no wave reads device tile t / 2 from LDS any more.
     __builtin_amdgcn_sched_barrier(0);
-    pipe::wait_copies_and_barrier<PH == 0 ? 2 : 0>();
+    pipe::wait_copies_and_barrier<PH == 0 ? L::kTileCopies : 0>();
     {
       const uint32_t xo = min((uint32_t)(t + 1) * (kBK * 2), xlast);
 #pragma unroll
@@ -342,11 +370,34 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
 #pragma unroll
       for (int nn = 0; nn < 2; ++nn) {
         cv[nn] = *reinterpret_cast<const uint4 *>(cw + (nn * 2 + sl) * kTileBytes);
-        sv[nn] = *reinterpret_cast<const float2 *>(sw + (nn * 2 + sl) * kTileScales * 4);
+        if constexpr (AFF)
+          sv[nn] = make_float2(__uint_as_float(*reinterpret_cast<const uint32_t *>(
+                                   sw + (nn * 2 + sl) * kTileScales * 4)),
+                               0.0f);
+        else
+          sv[nn] = *reinterpret_cast<const float2 *>(sw + (nn * 2 + sl) * kTileScales * 4);
       }
     }
-    const float s0 = PH ? sv[0].y : sv[0].x, s1 = PH ? sv[1].y : sv[1].x;
+    // block scales, or (affine) s from the params dword
+    auto f16lo = [](float v) {
+      return (float)__builtin_bit_cast(_Float16, (uint16_t)(__float_as_uint(v) & 0xFFFFu));
+    };
+    const float s0 = AFF ? f16lo(sv[0].x) : PH ? sv[0].y : sv[0].x;
+    const float s1 = AFF ? f16lo(sv[1].x) : PH ? sv[1].y : sv[1].x;
     f32x4 p[4][2];
+    if constexpr (AFF) {
+      if (PH == 0) {
+        const int sl = (t >> 1) & 1;
+        const float nz0 = -(float)(__float_as_uint(sv[0].x) >> 16);
+        const float nz1 = -(float)(__float_as_uint(sv[1].x) >> 16);
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+          const f32x4 xz = *reinterpret_cast<const f32x4 *>(xw + sl * tile::kXSum + mm * 64);
+          pz[mm][0] = f32x4{nz0 * xz[0], nz0 * xz[1], nz0 * xz[2], nz0 * xz[3]};
+          pz[mm][1] = f32x4{nz1 * xz[0], nz1 * xz[1], nz1 * xz[2], nz1 * xz[3]};
+        }
+      }
+    }
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const char *pa = ldsA + (PH * 2 + hf) * tile::kAHalf + afr;
@@ -369,17 +420,23 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
 #pragma unroll
       for (int mm = 0; mm < 4; ++mm)
 #pragma unroll
-        for (int nn = 0; nn < 2; ++nn)
-          p[mm][nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mm], B[nn], hf ? p[mm][nn] : zero,
-                                                              0, 0, 0);
+        for (int nn = 0; nn < 2; ++nn) {
+          if constexpr (AFF)
+            pz[mm][nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mm], B[nn], pz[mm][nn], 0, 0, 0);
+          else
+            p[mm][nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mm], B[nn],
+                                                                hf ? p[mm][nn] : zero, 0, 0, 0);
+        }
     }
+    if (!AFF || PH == 1) {
 #pragma unroll
-    for (int mm = 0; mm < 4; ++mm)
+      for (int mm = 0; mm < 4; ++mm)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[mm][0][i] = fmaf(s0, p[mm][0][i], acc[mm][0][i]);
-        acc[mm][1][i] = fmaf(s1, p[mm][1][i], acc[mm][1][i]);
-      }
+        for (int i = 0; i < 4; ++i) {
+          acc[mm][0][i] = fmaf(s0, AFF ? pz[mm][0][i] : p[mm][0][i], acc[mm][0][i]);
+          acc[mm][1][i] = fmaf(s1, AFF ? pz[mm][1][i] : p[mm][1][i], acc[mm][1][i]);
+        }
+    }
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
@@ -587,9 +644,81 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Pre-pass of the affine GEMM: X[t][m] = sum of x[m][128 t .. 128 t + 127]
+// for m < Mp (zero past M), 16 lanes per (t, m): each lane adds its 8
+// values in k order, then a butterfly over the 16 lanes (xor 1, 2, 4, 8).
+// Consecutive 16-lane groups take consecutive m, so a wave writes 16
+// consecutive bytes of X.
+__global__ __launch_bounds__(256) void xsum_kernel(const uint16_t *__restrict__ x, int64_t M,
+                                                   int64_t K, int64_t Mp, int64_t ngroups,
+                                                   float *__restrict__ X) {
+  const int64_t gi = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+  const int q = threadIdx.x & 15;
+  const bool ok = gi < ngroups;
+  const int64_t g = ok ? gi : ngroups - 1;
+  const int64_t t = g / Mp, m = g - t * Mp;
+  const int64_t mr = m < M ? m : M - 1;
+  const uint4 c = *reinterpret_cast<const uint4 *>(x + mr * K + t * kTileK + 8 * q);
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  float v = __uint_as_float(w[0] << 16);
+  v += __uint_as_float(w[0] & 0xFFFF0000u);
+#pragma unroll
+  for (int i = 1; i < 4; ++i) {
+    v += __uint_as_float(w[i] << 16);
+    v += __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 8);
+  if (ok && q == 0) X[g] = m < M ? v : 0.0f;
+}
+
 }  // namespace
 
 size_t gemm_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+
+namespace {
+int64_t awq_rows_padded(int64_t M) { return (M + tile::kBM - 1) / tile::kBM * tile::kBM; }
+}  // namespace
+
+bool awq_gemm_supported(int64_t M, int64_t N, int64_t K) {
+  // 32-bit byte offsets for the copies into LDS: x, code words, x sums
+  const int64_t KT = K / kTileK, Mp = awq_rows_padded(M);
+  return M >= 1 && K % kTileK == 0 && M * K * 2 < (int64_t(1) << 32) &&
+         (N / kTileRows) * KT * kTileBytes < (int64_t(1) << 32) &&
+         KT * Mp * 4 < (int64_t(1) << 32);
+}
+
+size_t awq_gemm_workspace_bytes(int64_t M, int64_t, int64_t K) {
+  return (size_t)(K / kTileK) * (size_t)awq_rows_padded(M) * sizeof(float);
+}
+
+hipError_t launch_awq_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, const uint32_t *pr,
+                           int64_t N, int64_t K, float *y, void *ws, hipStream_t s) {
+  const int64_t KT = K / kTileK, Mp = awq_rows_padded(M), mt = Mp / tile::kBM;
+  float *X = reinterpret_cast<float *>(ws);
+  const int64_t ngroups = KT * Mp;
+  hipLaunchKernelGGL(xsum_kernel, dim3((unsigned)((ngroups * 16 + 255) / 256)), dim3(256), 0, s,
+                     x, M, K, Mp, ngroups, X);
+  const CodeTerms ct = identity_terms();
+  const int64_t G = N / kTileRows;
+  auto padded = [&](int64_t nt) { return (unsigned)((nt + 7) / 8 * 8 * mt); };
+  // the same choice of workgroup width as the codebook GEMM
+  if (((G + 15) / 16) * mt >= device_cu_count() / 2) {
+    const int64_t nt = (G + 15) / 16;
+    hipLaunchKernelGGL((gemm_tile_kernel<16, true>), dim3(padded(nt)), dim3(64 * 16), 0, s, x, M,
+                       qw, reinterpret_cast<const float *>(pr), ct, N, K, KT, y, (int)nt,
+                       (int)mt, X, Mp);
+  } else {
+    const int64_t nt = (G + 7) / 8;
+    hipLaunchKernelGGL((gemm_tile_kernel<8, true>), dim3(padded(nt)), dim3(64 * 8), 0, s, x, M, qw,
+                       reinterpret_cast<const float *>(pr), ct, N, K, KT, y, (int)nt, (int)mt, X,
+                       Mp);
+  }
+  return hipGetLastError();
+}
 
 bool skinny_eligible(int64_t M, int64_t N, int64_t K, int nterm) {
   // 32-bit tile indices and element offsets
@@ -641,12 +770,12 @@ hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, const fl
     auto padded = [&](int64_t nt) { return (unsigned)((nt + 7) / 8 * 8 * mt); };
     if (((G + 15) / 16) * mt >= device_cu_count() / 2) {
       const int64_t nt = (G + 15) / 16;
-      hipLaunchKernelGGL(gemm_tile_kernel<16>, dim3(padded(nt)), dim3(64 * 16), 0, s, x, M, qw,
-                         am, ct, N, K, KT, y, (int)nt, (int)mt);
+      hipLaunchKernelGGL((gemm_tile_kernel<16, false>), dim3(padded(nt)), dim3(64 * 16), 0, s, x,
+                         M, qw, am, ct, N, K, KT, y, (int)nt, (int)mt, nullptr, (int64_t)0);
     } else {
       const int64_t nt = (G + 7) / 8;
-      hipLaunchKernelGGL(gemm_tile_kernel<8>, dim3(padded(nt)), dim3(64 * 8), 0, s, x, M, qw, am,
-                         ct, N, K, KT, y, (int)nt, (int)mt);
+      hipLaunchKernelGGL((gemm_tile_kernel<8, false>), dim3(padded(nt)), dim3(64 * 8), 0, s, x, M,
+                         qw, am, ct, N, K, KT, y, (int)nt, (int)mt, nullptr, (int64_t)0);
     }
     return hipGetLastError();
   }

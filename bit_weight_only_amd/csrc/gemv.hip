@@ -298,6 +298,14 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float *__restrict__ y
 // rows, each padded with zeros to a whole number of 128-k tiles and stored
 // with a 16-byte skew per row (so the M rows of one operand-A read fall in
 // different banks); and the partial sums [row group][wave][16 rows][M].
+//
+// Affine variant (AFF, the asymmetric int4 format in groups of 128 k): the
+// codebook is 0..15, a tile row is one group with scale s and zero point z
+// (one params dword per row: binary16 s | z << 16), and the workgroup first
+// sums x over every tile, X[t][m] (in LDS after the partials, 8 floats per
+// tile).  A tile's four products then chain into one
+// accumulator that starts at -z X: P = -z X + sum x q = sum x (q - z), and
+// acc = fmaf(s, P, acc).
 // ---------------------------------------------------------------------------
 constexpr int kFastWaves = 8;
 constexpr int kFastCopies = 64;
@@ -309,7 +317,27 @@ constexpr int kLdsBytes = 160 * 1024;                // LDS per workgroup on gfx
 // instructions may cross; vector memory instructions may not.
 constexpr int kSchedAllButGlobalLoads = 0x1 | 0x2 | 0x4 | 0x8 | 0x80 | 0x100 | 0x200 | 0x400;
 
-template <int M, bool ARGMAX>
+// Sum of one 128-k tile row of bf16 x: 16 lanes (a 16-aligned group) each
+// add the 8 values of their 16-byte chunk in k order, then a butterfly over
+// the group (xor 1, 2, 4, 8) leaves the total in all 16 lanes.  Every lane
+// of the wave must take part.  The GEMM's pre-pass sums the same way.
+__device__ inline float tile_row_sum(uint4 c) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  float v = __uint_as_float(w[0] << 16);
+  v += __uint_as_float(w[0] & 0xFFFF0000u);
+#pragma unroll
+  for (int i = 1; i < 4; ++i) {
+    v += __uint_as_float(w[i] << 16);
+    v += __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 8);
+  return v;
+}
+
+template <int M, bool ARGMAX, bool AFF>
 __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
     const uint16_t *__restrict__ x, const uint4 *__restrict__ qw,
     const float2 *__restrict__ am, CodeTerms ct, int N, int K, int KT, int G, int P,
@@ -348,6 +376,15 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
     ntile_end = (uint32_t)(ng1 * nKT);
   }
 
+  // The lane's scales of tile lt: two block scales, or (affine) the params
+  // dword in .x.
+  auto load_scales = [&](const char *src, uint32_t lt) -> float2 {
+    if constexpr (AFF)
+      return make_float2(
+          __uint_as_float(*reinterpret_cast<const uint32_t *>(src + (lt * 64u + r * 4u))), 0.0f);
+    else
+      return *reinterpret_cast<const float2 *>(src + (lt * 128u + r * 8u));
+  };
   // Prefetch cursor; steps past the wave's share re-read the workgroup's
   // first tile so that every step issues the same loads.
   uint32_t ptau = (uint32_t)(T0 + wave);
@@ -357,7 +394,7 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
   for (int d = 0; d < D; ++d) {
     const uint32_t lt = ptau < tile_end ? ptau : (uint32_t)T0;
     wb[d] = *reinterpret_cast<const uint4 *>(qbase + (lt * 1024u + lane * 16u));
-    sb[d] = *reinterpret_cast<const float2 *>(sbase + (lt * 128u + r * 8u));
+    sb[d] = load_scales(sbase, lt);
     ptau += kFastWaves;
   }
 
@@ -412,6 +449,19 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
   // when a row group has fewer than 8 tiles).  The codes' words are reused
   // here, after the barrier above.
   for (int c = threadIdx.x; c < Gw * kFastWaves * 16 * M; c += blockDim.x) red[c] = 0.0f;
+  // x sums per tile (affine variant): X[t][m] for m < 8, zero past M
+  float *Xl = red + Gw * kFastWaves * 16 * M;
+  if constexpr (AFF) {
+    const int grp = (int)(threadIdx.x >> 4), ngrp = (int)(blockDim.x >> 4);
+    for (int b = 0; b < KT * 8; b += ngrp) {
+      const int pr = b + grp < KT * 8 ? b + grp : KT * 8 - 1;
+      const int tt = pr >> 3, m = pr & 7;
+      const int mr = m < M ? m : M - 1;
+      const uint4 c = *reinterpret_cast<const uint4 *>(&xs[mr * XS + tt * kTileK + 8 * (lane & 15)]);
+      const float v = tile_row_sum(c);
+      if ((lane & 15) == 0 && b + grp < KT * 8) Xl[pr] = m < M ? v : 0.0f;
+    }
+  }
   __syncthreads();
 
   const uint32_t lane4 = (uint32_t)lane << 2;
@@ -450,7 +500,16 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
         for (int q = 0; q < 4; ++q)
           ad[4 * jj + q] = __builtin_amdgcn_perm(wd, lane4, 0x0c0c0400u + (q << 8));
       }
-      const float s0 = live ? sb[d].x : 0.0f, s1 = live ? sb[d].y : 0.0f;
+      // block scales, or (affine) the scale and minus the zero point
+      float s0, s1;
+      if constexpr (AFF) {
+        const uint32_t pv = __float_as_uint(sb[d].x);
+        s0 = live ? (float)__builtin_bit_cast(_Float16, (uint16_t)(pv & 0xFFFFu)) : 0.0f;
+        s1 = -(float)(pv >> 16);
+      } else {
+        s0 = live ? sb[d].x : 0.0f;
+        s1 = live ? sb[d].y : 0.0f;
+      }
 #pragma unroll
       for (int u = 0; u < 16; ++u) asm volatile("" ::"v"(ad[u]));
       asm volatile("" ::"v"(s0), "v"(s1));
@@ -462,12 +521,17 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
         const char *qsrc = ahead ? nq : qbase;
         const char *ssrc = ahead ? nsb : sbase;
         wb[d] = *reinterpret_cast<const uint4 *>(qsrc + (lt * 1024u + lane * 16u));
-        sb[d] = *reinterpret_cast<const float2 *>(ssrc + (lt * 128u + r * 8u));
+        sb[d] = load_scales(ssrc, lt);
         ptau += kFastWaves;
         pn += dead ? kFastWaves : 0u;
       }
       const uint16_t *xt = xrow + t * kTileK;
       f32x4 P[2];
+      if constexpr (AFF) {
+        // D rows 4h + e: x sums of rows 4 (h & 1) + e (rows past M are dropped)
+        const f32x4 xz = *reinterpret_cast<const f32x4 *>(Xl + t * 8 + 4 * (h & 1));
+        P[0] = f32x4{s1 * xz[0], s1 * xz[1], s1 * xz[2], s1 * xz[3]};
+      }
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const uint4 xa = *reinterpret_cast<const uint4 *>(xt + 32 * jj);
@@ -477,13 +541,16 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
           bb[q] = *reinterpret_cast<const uint32_t *>(tabc + ad[4 * jj + q]);
         const bf16x8 A = __builtin_bit_cast(bf16x8, xa);
         const bf16x8 B = __builtin_bit_cast(bf16x8, make_uint4(bb[0], bb[1], bb[2], bb[3]));
-        P[jj >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, (jj & 1) ? P[jj >> 1] : zero,
-                                                             0, 0, 0);
+        if constexpr (AFF)
+          P[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, P[0], 0, 0, 0);
+        else
+          P[jj >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              A, B, (jj & 1) ? P[jj >> 1] : zero, 0, 0, 0);
       }
 #pragma unroll
       for (int e = 0; e < NA; ++e) {
         acc[e] = fmaf(s0, P[0][e], acc[e]);
-        acc[e] = fmaf(s1, P[1][e], acc[e]);
+        if constexpr (!AFF) acc[e] = fmaf(s1, P[1][e], acc[e]);
       }
       // ---- advance; when the row group changes (or the share ends), leave
       // this wave's partial for it in LDS
@@ -542,42 +609,44 @@ struct FastPlan {
   size_t lds;
 };
 
-// dynamic LDS bytes (x and partials); the 64 KB table is static
-size_t fast_dyn_bytes(int M, int64_t K, int64_t Gw) {
-  return (size_t)M * (tiles_k(K) * kTileK + kFastSkew) * 2 + (size_t)Gw * kFastWaves * 16 * M * 4;
+// dynamic LDS bytes (x, partials and, affine, the x sums); the 64 KB table
+// is static
+size_t fast_dyn_bytes(int M, int64_t K, int64_t Gw, bool aff) {
+  return (size_t)M * (tiles_k(K) * kTileK + kFastSkew) * 2 + (size_t)Gw * kFastWaves * 16 * M * 4 +
+         (aff ? (size_t)tiles_k(K) * 8 * 4 : 0);
 }
 constexpr size_t kDynMax = (size_t)kLdsBytes - (size_t)kFastTableWords * 4;
 
-FastPlan fast_plan(int M, int64_t N, int64_t K) {
+FastPlan fast_plan(int M, int64_t N, int64_t K, bool aff = false) {
   const int64_t G = N / kTileRows;
   int64_t P = device_cu_count();
   if (P > G) P = G;
   // more workgroups when the partial slots of ceil(G/P) row groups do not fit
-  while (fast_dyn_bytes(M, K, (G + P - 1) / P) > kDynMax && P < G) P += P / 4 + 1;
+  while (fast_dyn_bytes(M, K, (G + P - 1) / P, aff) > kDynMax && P < G) P += P / 4 + 1;
   if (P > G) P = G;
-  return FastPlan{(int)P, fast_dyn_bytes(M, K, (G + P - 1) / P)};
+  return FastPlan{(int)P, fast_dyn_bytes(M, K, (G + P - 1) / P, aff)};
 }
 
-bool fast_eligible(int M, int64_t N, int64_t K, int nterm) {
+bool fast_eligible(int M, int64_t N, int64_t K, int nterm, bool aff = false) {
   // 32-bit tile indices and byte offsets into the code buffer, and LDS room
   // for x plus one row group's partials
   const int64_t qbytes = (N / kTileRows) * tiles_k(K) * kTileBytes;
-  return nterm == 1 && qbytes < (int64_t(1) << 32) && fast_dyn_bytes(M, K, 1) <= kDynMax;
+  return nterm == 1 && qbytes < (int64_t(1) << 32) && fast_dyn_bytes(M, K, 1, aff) <= kDynMax;
 }
 
-template <int M, bool ARGMAX>
+template <int M, bool ARGMAX, bool AFF = false>
 hipError_t launch_fast(const uint16_t *x, const uint4 *qw, const float2 *am, const CodeTerms &ct,
                        int64_t N, int64_t K, float *y, uint32_t *counter, uint64_t *cand,
                        int32_t *index, hipStream_t s, const NextMatrix *next) {
   static std::atomic<bool> attr_set{false};
   if (!attr_set.load(std::memory_order_acquire)) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&gemv_fast_kernel<M, ARGMAX>),
+        reinterpret_cast<const void *>(&gemv_fast_kernel<M, ARGMAX, AFF>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDynMax);
     if (e != hipSuccess) return e;
     attr_set.store(true, std::memory_order_release);
   }
-  const FastPlan p = fast_plan(M, N, K);
+  const FastPlan p = fast_plan(M, N, K, AFF);
   // the next launch's partition, if it takes this fast path with the same M
   const char *nq = nullptr, *nsb = nullptr;
   int nG = 0, nKT = 0, nP = 0;
@@ -588,7 +657,7 @@ hipError_t launch_fast(const uint16_t *x, const uint4 *qw, const float2 *am, con
     nKT = (int)tiles_k(next->K);
     nP = fast_plan(M, next->N, next->K).P;
   }
-  hipLaunchKernelGGL((gemv_fast_kernel<M, ARGMAX>), dim3(p.P), dim3(kFastWaves * 64), p.lds, s, x,
+  hipLaunchKernelGGL((gemv_fast_kernel<M, ARGMAX, AFF>), dim3(p.P), dim3(kFastWaves * 64), p.lds, s, x,
                      qw, am, ct, (int)N, (int)K, (int)tiles_k(K), (int)(N / kTileRows), p.P, y,
                      counter, cand, index, nq, nsb, nG, nKT, nP);
   return hipGetLastError();
@@ -709,6 +778,28 @@ hipError_t launch_gemv(const uint16_t *x, int M, const uint8_t *qw, const float 
   if (skinny_eligible(M, N, K, nterm)) return launch_skinny(x, M, qw, am, ct, N, K, y, s);
   if (nterm == 1) return launch_t<1>(x, M, q, a, ct, N, K, y, s);
   return launch_t<3>(x, M, q, a, ct, N, K, y, s);
+}
+
+bool awq_gemv_fast_eligible(int64_t M, int64_t N, int64_t K) {
+  return M >= 1 && M <= 8 && fast_eligible((int)M, N, K, 1, true);
+}
+
+hipError_t launch_awq_gemv_fast(const uint16_t *x, int M, const uint8_t *qw, const uint32_t *pr,
+                                int64_t N, int64_t K, float *y, hipStream_t s) {
+  const uint4 *q = reinterpret_cast<const uint4 *>(qw);
+  const float2 *a = reinterpret_cast<const float2 *>(pr);
+  const CodeTerms ct = identity_terms();
+  switch (M) {
+    case 1: return launch_fast<1, false, true>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, nullptr);
+    case 2: return launch_fast<2, false, true>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, nullptr);
+    case 3: return launch_fast<3, false, true>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, nullptr);
+    case 4: return launch_fast<4, false, true>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, nullptr);
+    case 5: return launch_fast<5, false, true>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, nullptr);
+    case 6: return launch_fast<6, false, true>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, nullptr);
+    case 7: return launch_fast<7, false, true>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, nullptr);
+    case 8: return launch_fast<8, false, true>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, nullptr);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace nf4

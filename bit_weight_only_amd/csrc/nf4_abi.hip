@@ -77,6 +77,9 @@ int split_codebook(const float *cb, nf4::CodeTerms &ct) {
 
 nf4_status from_hip(hipError_t e) { return e == hipSuccess ? NF4_OK : NF4_ERR_HIP; }
 
+// Shapes of the asymmetric int4 format: one group of 128 k per tile row.
+bool awq_shape_ok(int64_t N, int64_t K) { return shape_ok(N, K) && K % nf4::kTileK == 0; }
+
 nf4_status check_linear_args(const uint16_t *x, int64_t M, const uint8_t *qw, const float *am,
                              const float *cb, int64_t N, int64_t K, const float *y,
                              int64_t max_m) {
@@ -268,6 +271,101 @@ nf4_status nf4_gemm(const uint16_t *x, int64_t M, const uint8_t *qweight, const 
   if (nterm == 0) return NF4_ERR_CODEBOOK;
   return from_hip(nf4::launch_gemm(x, M, qweight, absmax, ct, nterm, N, K, y, workspace,
                                    ws_bytes, stream));
+}
+
+// ---------------------------------------------------------------------------
+// Asymmetric int4, groups of 128 along K: w = (q - z) * s.
+
+size_t nf4_awq_params_bytes(int64_t N, int64_t K) {
+  if (!awq_shape_ok(N, K)) return 0;
+  return (size_t)(N / nf4::kTileRows) * (size_t)nf4::tiles_k(K) * nf4::kAwqParamBytes;
+}
+
+size_t nf4_awq_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || M > kMaxGemmM || !awq_shape_ok(N, K) || !nf4::awq_gemm_supported(M, N, K))
+    return 0;
+  return nf4::awq_gemm_workspace_bytes(M, N, K);
+}
+
+nf4_status nf4_awq_pack(const float *W, int64_t N, int64_t K, uint8_t *qweight,
+                        uint32_t *params, hipStream_t stream) {
+  if (!W || !qweight || !params) return NF4_ERR_NULL;
+  if (!awq_shape_ok(N, K)) return NF4_ERR_SHAPE;
+  if (!aligned16(W) || !aligned16(qweight) || !aligned16(params)) return NF4_ERR_ALIGN;
+  return from_hip(nf4::launch_awq_pack(W, N, K, qweight, params, stream));
+}
+
+nf4_status nf4_awq_repack(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                          int64_t N, int64_t K, uint8_t *qweight, uint32_t *params,
+                          hipStream_t stream) {
+  if (!codes || !scales || !zeros || !qweight || !params) return NF4_ERR_NULL;
+  if (!awq_shape_ok(N, K)) return NF4_ERR_SHAPE;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(zeros) || !aligned16(qweight) ||
+      !aligned16(params))
+    return NF4_ERR_ALIGN;
+  return from_hip(nf4::launch_awq_repack(codes, scales, zeros, N, K, qweight, params, stream));
+}
+
+nf4_status nf4_awq_unpack(const uint8_t *qweight, const uint32_t *params, int64_t N, int64_t K,
+                          uint8_t *codes, uint16_t *scales, uint8_t *zeros, hipStream_t stream) {
+  if (!codes || !scales || !zeros || !qweight || !params) return NF4_ERR_NULL;
+  if (!awq_shape_ok(N, K)) return NF4_ERR_SHAPE;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(zeros) || !aligned16(qweight) ||
+      !aligned16(params))
+    return NF4_ERR_ALIGN;
+  return from_hip(nf4::launch_awq_unpack(qweight, params, N, K, codes, scales, zeros, stream));
+}
+
+nf4_status nf4_awq_dequant(const uint8_t *qweight, const uint32_t *params, int64_t N, int64_t K,
+                           float *W_out, hipStream_t stream) {
+  if (!qweight || !params || !W_out) return NF4_ERR_NULL;
+  if (!awq_shape_ok(N, K)) return NF4_ERR_SHAPE;
+  if (!aligned16(qweight) || !aligned16(params) || !aligned16(W_out)) return NF4_ERR_ALIGN;
+  return from_hip(nf4::launch_awq_dequant(qweight, params, N, K, W_out, stream));
+}
+
+}  // extern "C"
+
+namespace {
+nf4_status check_awq_linear(const uint16_t *x, int64_t M, const uint8_t *qw, const uint32_t *pr,
+                            int64_t N, int64_t K, const float *y, int64_t max_m) {
+  if (!x || !qw || !pr || !y) return NF4_ERR_NULL;
+  if (M < 1 || M > max_m || !awq_shape_ok(N, K)) return NF4_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(qw) || !aligned16(pr) || !aligned16(y)) return NF4_ERR_ALIGN;
+  return NF4_OK;
+}
+nf4_status check_awq_workspace(int64_t M, int64_t N, int64_t K, const void *ws, size_t ws_bytes) {
+  if (!nf4::awq_gemm_supported(M, N, K)) return NF4_ERR_SHAPE;
+  if (!ws) return NF4_ERR_NULL;
+  if (nf4::awq_gemm_workspace_bytes(M, N, K) > ws_bytes) return NF4_ERR_WORKSPACE;
+  if (!aligned16(ws)) return NF4_ERR_ALIGN;
+  return NF4_OK;
+}
+}  // namespace
+
+extern "C" {
+
+nf4_status nf4_awq_gemv(const uint16_t *x, int64_t M, const uint8_t *qweight,
+                        const uint32_t *params, int64_t N, int64_t K, float *y, void *workspace,
+                        size_t ws_bytes, hipStream_t stream) {
+  nf4_status st = check_awq_linear(x, M, qweight, params, N, K, y, kMaxGemvM);
+  if (st != NF4_OK) return st;
+  if (nf4::awq_gemv_fast_eligible(M, N, K))
+    return from_hip(nf4::launch_awq_gemv_fast(x, (int)M, qweight, params, N, K, y, stream));
+  // x too long for LDS: the tiled GEMM, which sums x in the workspace
+  st = check_awq_workspace(M, N, K, workspace, ws_bytes);
+  if (st != NF4_OK) return st;
+  return from_hip(nf4::launch_awq_gemm(x, M, qweight, params, N, K, y, workspace, stream));
+}
+
+nf4_status nf4_awq_gemm(const uint16_t *x, int64_t M, const uint8_t *qweight,
+                        const uint32_t *params, int64_t N, int64_t K, float *y, void *workspace,
+                        size_t ws_bytes, hipStream_t stream) {
+  nf4_status st = check_awq_linear(x, M, qweight, params, N, K, y, kMaxGemmM);
+  if (st != NF4_OK) return st;
+  st = check_awq_workspace(M, N, K, workspace, ws_bytes);
+  if (st != NF4_OK) return st;
+  return from_hip(nf4::launch_awq_gemm(x, M, qweight, params, N, K, y, workspace, stream));
 }
 
 }  // extern "C"

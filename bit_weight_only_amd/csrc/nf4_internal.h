@@ -46,6 +46,14 @@ struct Codebook {
 
 inline int64_t tiles_k(int64_t K) { return (K + kTileK - 1) / kTileK; }
 
+// The codebook 0, 1, ..., 15 as bf16 (exact): the codes of the asymmetric
+// int4 format enter the products as their integer values.
+inline CodeTerms identity_terms() {
+  CodeTerms ct{};
+  for (int i = 0; i < 16; ++i) ct.t[0][i] = (uint16_t)(__builtin_bit_cast(uint32_t, (float)i) >> 16);
+  return ct;
+}
+
 hipError_t launch_pack(const float *W, int64_t N, int64_t K, const PackConsts &pc, uint8_t *qw,
                        float *am, hipStream_t s);
 hipError_t launch_dequant(const uint8_t *qw, const float *am, const Codebook &cb, int64_t N,
@@ -54,6 +62,18 @@ hipError_t launch_repack(const uint8_t *codes, const float *scales, int64_t N, i
                          uint8_t *qw, float *am, hipStream_t s);
 hipError_t launch_unpack(const uint8_t *qw, const float *am, int64_t N, int64_t K, uint8_t *codes,
                          float *scales, hipStream_t s);
+// Second format (asymmetric int4, group 128 = one device tile row): codes in
+// the device layout; params 16 dwords per tile, dword r = binary16 bits of s
+// | z << 16 for row r.  K % 128 == 0.
+constexpr int kAwqParamBytes = kTileRows * 4;  // params of one tile
+hipError_t launch_awq_pack(const float *W, int64_t N, int64_t K, uint8_t *qw, uint32_t *pr,
+                           hipStream_t s);
+hipError_t launch_awq_repack(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                             int64_t N, int64_t K, uint8_t *qw, uint32_t *pr, hipStream_t s);
+hipError_t launch_awq_unpack(const uint8_t *qw, const uint32_t *pr, int64_t N, int64_t K,
+                             uint8_t *codes, uint16_t *scales, uint8_t *zeros, hipStream_t s);
+hipError_t launch_awq_dequant(const uint8_t *qw, const uint32_t *pr, int64_t N, int64_t K,
+                              float *out, hipStream_t s);
 // The packed matrix of the next GEMV launch, named so that the current
 // launch can read its first tiles ahead (a hint: results never depend on it).
 struct NextMatrix {
@@ -83,5 +103,18 @@ constexpr int64_t kSkinnyMaxM = 256;
 bool skinny_eligible(int64_t M, int64_t N, int64_t K, int nterm);
 hipError_t launch_skinny(const uint16_t *x, int64_t M, const uint8_t *qw, const float *am,
                          const CodeTerms &ct, int64_t N, int64_t K, float *y, hipStream_t s);
+
+
+// Linear layers of the asymmetric int4 format.  The GEMV keeps x and its
+// per-tile sums in LDS (M <= 8 and x small enough); the GEMM sums x per tile
+// in a pre-pass into the workspace ([K/128][M rounded up to 128] floats) and
+// runs the tiled kernel with the affine fold.
+bool awq_gemv_fast_eligible(int64_t M, int64_t N, int64_t K);
+hipError_t launch_awq_gemv_fast(const uint16_t *x, int M, const uint8_t *qw, const uint32_t *pr,
+                                int64_t N, int64_t K, float *y, hipStream_t s);
+bool awq_gemm_supported(int64_t M, int64_t N, int64_t K);
+size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_awq_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, const uint32_t *pr,
+                           int64_t N, int64_t K, float *y, void *ws, hipStream_t s);
 
 }  // namespace nf4

@@ -177,6 +177,144 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint4 *__restrict__ q
   }
 }
 
+// ---------------------------------------------------------------------------
+// Second format: asymmetric int4, one group per device tile row (128 k):
+// w = (q - z) * s with a binary16 scale s and an integer zero point z per
+// group (vibevoice.c README, "Quantization" > "Weights", the AWQ/GPTQ
+// paragraph).  The codes use the device layout above; a tile's params are
+// 16 dwords, dword r = binary16 bits of s | z << 16 for row r (s is a
+// binary16 value by construction, so nothing is lost).
+
+// Nearest binary16 value of a positive finite double, ties to even, as a
+// double: the significand is cut to 11 bits (10 stored) by integer
+// arithmetic on the binary64 encoding; below 2^-14 the quantum is 2^-24.
+__device__ inline double awq_fp16_of_positive(double a) {
+  if (a < 0x1p-14) return rint(a * 0x1p24) * 0x1p-24;  // exact scaling; rint ties to even
+  const uint64_t u = (uint64_t)__double_as_longlong(a);
+  const uint64_t drop = 42;                             // 52 - 10 fraction bits
+  const uint64_t keep = u >> drop, rest = u & ((1ull << drop) - 1), half = 1ull << (drop - 1);
+  const uint64_t up = (rest > half || (rest == half && (keep & 1))) ? 1u : 0u;
+  const double r = __longlong_as_double((long long)((keep + up) << drop));
+  return r >= 65520.0 ? __longlong_as_double(0x7FF0000000000000ll) : r;
+}
+
+// Quantizer of the second format, one group per (tile, row): lanes r, r+16,
+// r+32, r+48 share the row; min and max over their 32 values each.
+__global__ __launch_bounds__(256) void awq_pack_kernel(const float *__restrict__ W, int64_t K,
+                                                       int64_t KT, int64_t ntiles,
+                                                       uint4 *__restrict__ qw,
+                                                       uint32_t *__restrict__ pr) {
+  TileCoord c;
+  if (!tile_coord(ntiles, KT, c)) return;
+  const float *row = W + (c.g * kTileRows + c.r) * K;
+  float w[4][8];
+  float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t k0 = (int64_t)c.t * kTileK + 32 * j + 8 * c.h;
+    const float4 a = *reinterpret_cast<const float4 *>(row + k0);
+    const float4 b = *reinterpret_cast<const float4 *>(row + k0 + 4);
+    w[j][0] = a.x; w[j][1] = a.y; w[j][2] = a.z; w[j][3] = a.w;
+    w[j][4] = b.x; w[j][5] = b.y; w[j][6] = b.z; w[j][7] = b.w;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      lo = fminf(lo, w[j][i]);
+      hi = fmaxf(hi, w[j][i]);
+    }
+  }
+  lo = fminf(lo, __shfl_xor(lo, 16));
+  lo = fminf(lo, __shfl_xor(lo, 32));
+  hi = fmaxf(hi, __shfl_xor(hi, 16));
+  hi = fmaxf(hi, __shfl_xor(hi, 32));
+  double range = (double)hi - (double)lo;
+  if (range < 1e-5) range = 1e-5;
+  const double sd = awq_fp16_of_positive(range / 15.0);
+  const double zd = fmin(fmax(rint(-(double)lo / sd), 0.0), 15.0);
+  uint32_t out[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const double v = fmin(fmax(rint((double)w[j][i] / sd) + zd, 0.0), 15.0);
+      word |= (uint32_t)v << (4 * i);
+    }
+    out[j] = word;
+  }
+  qw[c.tile * 64 + c.lane] = make_uint4(out[0], out[1], out[2], out[3]);
+  if (c.h == 0)
+    pr[c.tile * kTileRows + c.r] =
+        (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(float)sd) | ((uint32_t)zd << 16);
+}
+
+// Canonical codes [N][K/2], scales [N][K/128] (binary16 bits) and zero
+// points [N][K/128] (bytes) -> device layout.
+__global__ __launch_bounds__(256) void awq_repack_kernel(const uint32_t *__restrict__ codes,
+                                                         const uint16_t *__restrict__ scales,
+                                                         const uint8_t *__restrict__ zeros,
+                                                         int64_t K, int64_t KT, int64_t ntiles,
+                                                         uint4 *__restrict__ qw,
+                                                         uint32_t *__restrict__ pr) {
+  TileCoord c;
+  if (!tile_coord(ntiles, KT, c)) return;
+  const int64_t n = c.g * kTileRows + c.r;
+  const uint32_t *row = codes + n * (K / 8);
+  uint32_t wd[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) wd[j] = row[((int64_t)c.t * kTileK + 32 * j + 8 * c.h) / 8];
+  qw[c.tile * 64 + c.lane] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  if (c.h == 0)
+    pr[c.tile * kTileRows + c.r] =
+        (uint32_t)scales[n * KT + c.t] | ((uint32_t)(zeros[n * KT + c.t] & 15) << 16);
+}
+
+// Device layout -> canonical codes, scales (binary16 bits) and zero points.
+__global__ __launch_bounds__(256) void awq_unpack_kernel(const uint4 *__restrict__ qw,
+                                                         const uint32_t *__restrict__ pr,
+                                                         int64_t K, int64_t KT, int64_t ntiles,
+                                                         uint32_t *__restrict__ codes,
+                                                         uint16_t *__restrict__ scales,
+                                                         uint8_t *__restrict__ zeros) {
+  TileCoord c;
+  if (!tile_coord(ntiles, KT, c)) return;
+  const int64_t n = c.g * kTileRows + c.r;
+  const uint4 q = qw[c.tile * 64 + c.lane];
+  uint32_t *row = codes + n * (K / 8);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    row[((int64_t)c.t * kTileK + 32 * j + 8 * c.h) / 8] =
+        j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
+  if (c.h == 0) {
+    const uint32_t v = pr[c.tile * kTileRows + c.r];
+    scales[n * KT + c.t] = (uint16_t)(v & 0xFFFFu);
+    zeros[n * KT + c.t] = (uint8_t)(v >> 16);
+  }
+}
+
+// Debug dequant of the second format: W'[n][k] = fl32((q - z) * s).
+__global__ __launch_bounds__(256) void awq_dequant_kernel(const uint4 *__restrict__ qw,
+                                                          const uint32_t *__restrict__ pr,
+                                                          int64_t K, int64_t KT, int64_t ntiles,
+                                                          float *__restrict__ out) {
+  TileCoord c;
+  if (!tile_coord(ntiles, KT, c)) return;
+  const uint32_t v = pr[c.tile * kTileRows + c.r];
+  const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
+  const float z = (float)(v >> 16);
+  const uint4 q = qw[c.tile * 64 + c.lane];
+  float *row = out + (c.g * kTileRows + c.r) * K;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t word = j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
+    const int64_t k0 = (int64_t)c.t * kTileK + 32 * j + 8 * c.h;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = ((float)((word >> (4 * i)) & 15u) - z) * s;
+    *reinterpret_cast<float4 *>(row + k0) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4 *>(row + k0 + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
 inline dim3 tile_grid(int64_t ntiles) {
   return dim3((unsigned)((ntiles + kWavesPerBlock - 1) / kWavesPerBlock));
 }
@@ -214,6 +352,40 @@ hipError_t launch_unpack(const uint8_t *qw, const float *am, int64_t N, int64_t 
   hipLaunchKernelGGL(unpack_kernel, tile_grid(ntiles), dim3(256), 0, s,
                      reinterpret_cast<const uint4 *>(qw), am, K, KT, ntiles,
                      reinterpret_cast<uint32_t *>(codes), scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_awq_pack(const float *W, int64_t N, int64_t K, uint8_t *qw, uint32_t *pr,
+                           hipStream_t s) {
+  const int64_t KT = tiles_k(K), ntiles = (N / kTileRows) * KT;
+  hipLaunchKernelGGL(awq_pack_kernel, tile_grid(ntiles), dim3(256), 0, s, W, K, KT, ntiles,
+                     reinterpret_cast<uint4 *>(qw), pr);
+  return hipGetLastError();
+}
+
+hipError_t launch_awq_repack(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                             int64_t N, int64_t K, uint8_t *qw, uint32_t *pr, hipStream_t s) {
+  const int64_t KT = tiles_k(K), ntiles = (N / kTileRows) * KT;
+  hipLaunchKernelGGL(awq_repack_kernel, tile_grid(ntiles), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t *>(codes), scales, zeros, K, KT, ntiles,
+                     reinterpret_cast<uint4 *>(qw), pr);
+  return hipGetLastError();
+}
+
+hipError_t launch_awq_unpack(const uint8_t *qw, const uint32_t *pr, int64_t N, int64_t K,
+                             uint8_t *codes, uint16_t *scales, uint8_t *zeros, hipStream_t s) {
+  const int64_t KT = tiles_k(K), ntiles = (N / kTileRows) * KT;
+  hipLaunchKernelGGL(awq_unpack_kernel, tile_grid(ntiles), dim3(256), 0, s,
+                     reinterpret_cast<const uint4 *>(qw), pr, K, KT, ntiles,
+                     reinterpret_cast<uint32_t *>(codes), scales, zeros);
+  return hipGetLastError();
+}
+
+hipError_t launch_awq_dequant(const uint8_t *qw, const uint32_t *pr, int64_t N, int64_t K,
+                              float *out, hipStream_t s) {
+  const int64_t KT = tiles_k(K), ntiles = (N / kTileRows) * KT;
+  hipLaunchKernelGGL(awq_dequant_kernel, tile_grid(ntiles), dim3(256), 0, s,
+                     reinterpret_cast<const uint4 *>(qw), pr, K, KT, ntiles, out);
   return hipGetLastError();
 }
 

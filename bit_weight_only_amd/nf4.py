@@ -19,7 +19,9 @@ NF4_OK, NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_CODEBOOK, NF4_ERR_WO
 
 EXPORTS = ("nf4_status_string", "nf4_qweight_bytes", "nf4_absmax_bytes", "nf4_workspace_bytes",
            "nf4_pack", "nf4_dequant", "nf4_repack", "nf4_unpack", "nf4_gemv", "nf4_gemm",
-           "nf4_gemv_argmax_workspace_bytes", "nf4_gemv_argmax", "nf4_gemv_prefetch")
+           "nf4_gemv_argmax_workspace_bytes", "nf4_gemv_argmax", "nf4_gemv_prefetch",
+           "nf4_awq_params_bytes", "nf4_awq_workspace_bytes", "nf4_awq_pack", "nf4_awq_repack",
+           "nf4_awq_unpack", "nf4_awq_dequant", "nf4_awq_gemv", "nf4_awq_gemm")
 
 _lib = None
 
@@ -64,6 +66,21 @@ def lib() -> ctypes.CDLL:
         L.nf4_gemv_prefetch.restype = st
         L.nf4_gemv_prefetch.argtypes = [vp, i64, vp, vp, fp, i64, i64, vp, vp, sz, vp, vp, i64,
                                         i64, vp]
+        L.nf4_awq_params_bytes.restype = sz
+        L.nf4_awq_params_bytes.argtypes = [i64, i64]
+        L.nf4_awq_workspace_bytes.restype = sz
+        L.nf4_awq_workspace_bytes.argtypes = [i64, i64, i64]
+        L.nf4_awq_pack.restype = st
+        L.nf4_awq_pack.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.nf4_awq_repack.restype = st
+        L.nf4_awq_repack.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp]
+        L.nf4_awq_unpack.restype = st
+        L.nf4_awq_unpack.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp]
+        L.nf4_awq_dequant.restype = st
+        L.nf4_awq_dequant.argtypes = [vp, vp, i64, i64, vp, vp]
+        for f in (L.nf4_awq_gemv, L.nf4_awq_gemm):
+            f.restype = st
+            f.argtypes = [vp, i64, vp, vp, i64, i64, vp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -163,6 +180,46 @@ def nf4_gemv_argmax(x, M: int, qweight, absmax, codebook, N: int, K: int, y, ind
                                  _stream(stream)), "nf4_gemv_argmax")
 
 
+def nf4_awq_params_bytes(N: int, K: int) -> int:
+    return lib().nf4_awq_params_bytes(N, K)
+
+
+def nf4_awq_workspace_bytes(M: int, N: int, K: int) -> int:
+    return lib().nf4_awq_workspace_bytes(M, N, K)
+
+
+def nf4_awq_pack(W, N: int, K: int, qweight, params, stream=None) -> None:
+    _check(lib().nf4_awq_pack(_ptr(W), N, K, _ptr(qweight), _ptr(params), _stream(stream)),
+           "nf4_awq_pack")
+
+
+def nf4_awq_repack(codes, scales, zeros, N: int, K: int, qweight, params, stream=None) -> None:
+    _check(lib().nf4_awq_repack(_ptr(codes), _ptr(scales), _ptr(zeros), N, K, _ptr(qweight),
+                                _ptr(params), _stream(stream)), "nf4_awq_repack")
+
+
+def nf4_awq_unpack(qweight, params, N: int, K: int, codes, scales, zeros, stream=None) -> None:
+    _check(lib().nf4_awq_unpack(_ptr(qweight), _ptr(params), N, K, _ptr(codes), _ptr(scales),
+                                _ptr(zeros), _stream(stream)), "nf4_awq_unpack")
+
+
+def nf4_awq_dequant(qweight, params, N: int, K: int, W_out, stream=None) -> None:
+    _check(lib().nf4_awq_dequant(_ptr(qweight), _ptr(params), N, K, _ptr(W_out),
+                                 _stream(stream)), "nf4_awq_dequant")
+
+
+def nf4_awq_gemv(x, M: int, qweight, params, N: int, K: int, y, workspace=None,
+                 ws_bytes: int = 0, stream=None) -> None:
+    _check(lib().nf4_awq_gemv(_ptr(x), M, _ptr(qweight), _ptr(params), N, K, _ptr(y),
+                              _ptr(workspace), ws_bytes, _stream(stream)), "nf4_awq_gemv")
+
+
+def nf4_awq_gemm(x, M: int, qweight, params, N: int, K: int, y, workspace=None,
+                 ws_bytes: int = 0, stream=None) -> None:
+    _check(lib().nf4_awq_gemm(_ptr(x), M, _ptr(qweight), _ptr(params), N, K, _ptr(y),
+                              _ptr(workspace), ws_bytes, _stream(stream)), "nf4_awq_gemm")
+
+
 # ------------------------------------------------------------ conveniences
 class PackedWeight:
     """Device-layout codes and scales of one N x K weight (torch uint8/fp32)."""
@@ -188,3 +245,29 @@ def pack_weight(W, codebook, stream=None) -> PackedWeight:
     pw = PackedWeight(N, K, device=W.device)
     nf4_pack(W, N, K, codebook, pw.qweight, pw.absmax, stream)
     return pw
+
+
+class AwqWeight:
+    """Device-layout codes and (s, z) params (int32 dwords) of one N x K int4 weight."""
+
+    def __init__(self, N: int, K: int, device="cuda"):
+        import torch
+        qb, pb = nf4_qweight_bytes(N, K), nf4_awq_params_bytes(N, K)
+        if qb == 0 or pb == 0:
+            raise NF4Error(NF4_ERR_SHAPE, "AwqWeight")
+        self.N, self.K = N, K
+        self.qweight = torch.empty(qb, dtype=torch.uint8, device=device)
+        self.params = torch.empty(pb // 4, dtype=torch.int32, device=device)
+
+    @property
+    def nbytes(self) -> int:
+        """Algorithmic bytes a full read moves: 4-bit codes plus one 4-byte (s, z) per group."""
+        return self.N * self.K // 2 + 4 * self.N * (self.K // 128)
+
+
+def awq_pack_weight(W, stream=None) -> AwqWeight:
+    """Quantize a device fp32 [N, K] tensor into a new AwqWeight."""
+    N, K = W.shape
+    aw = AwqWeight(N, K, device=W.device)
+    nf4_awq_pack(W, N, K, aw.qweight, aw.params, stream)
+    return aw

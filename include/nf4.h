@@ -172,6 +172,85 @@ nf4_status nf4_gemm(const uint16_t *x, int64_t M, const uint8_t *qweight, const 
                     const float codebook[16], int64_t N, int64_t K, float *y, void *workspace,
                     size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Second weight format: asymmetric int4 in groups of 128 along K, with an
+ * exact integer zero point per group (vibevoice.c README, "Quantization" >
+ * "Weights": the INT4 option of the load-time quantizer, AWQ's own form, and
+ * the AWQ/GPTQ repack paragraph, which reads a weight back as (q - z) * s
+ * and keeps scale and zero point together, 4 bytes per group).  A weight
+ * reads back as w = (q - z) * s with code q in 0..15, zero point z in 0..15
+ * and a scale s that is a binary16 value, one (s, z) per row and group.
+ * Here the product is exact (it always fits binary32); the pages' GPU
+ * kernels round it to FP16.
+ *
+ * Shapes: as above, and K % 128 == 0 (one group per device tile row).
+ * Device layout: the codes as in the NF4 layout above (dword j of lane l:
+ * codes q of k = 128t + 32j + 8(l / 16) + i); params: for tile (g, t), 16
+ * dwords at dword offset (g * KT + t) * 16, dword r = (binary16 bits of s)
+ * | z << 16 for row 16g + r, group t.
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of the params buffer: (N/16) * (K/128) * 64, or 0 when K % 128 != 0
+ * or the shape is rejected.  The code buffer is nf4_qweight_bytes(N, K). */
+size_t nf4_awq_params_bytes(int64_t N, int64_t K);
+
+/* Bytes of workspace nf4_awq_gemm (and nf4_awq_gemv when x does not fit its
+ * on-chip path) needs: K/128 x (M rounded up to 128) floats, the sums of x
+ * over every 128-k group.  0 for shapes these calls reject.  The workspace
+ * is overwritten by every call; calls sharing one must be ordered. */
+size_t nf4_awq_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* Quantize fp32 W[N][K] (row-major, finite) into the device layout.  Per row
+ * and group of 128 (lo = min w, hi = max w, computed in double):
+ * s = fp16(max(hi - lo, 1e-5) / 15) (nearest binary16, ties to even;
+ * +inf past the binary16 range), z = clamp(rint(-lo / s), 0, 15),
+ * q = clamp(rint(w / s) + z, 0, 15), with rint rounding ties to even and
+ * every division in double.  qweight: nf4_qweight_bytes(N, K) bytes; params:
+ * nf4_awq_params_bytes(N, K) bytes. */
+nf4_status nf4_awq_pack(const float *W, int64_t N, int64_t K, uint8_t *qweight,
+                        uint32_t *params, hipStream_t stream);
+
+/* Layout conversion for weights quantized elsewhere: codes[N][K/2] (byte j =
+ * q[2j] | q[2j+1] << 4), scales[N][K/128] binary16 bit patterns, zeros
+ * [N][K/128] bytes (the low 4 bits are used), all row-major device arrays
+ * (16-byte aligned), into the device layout.  Values are taken as given. */
+nf4_status nf4_awq_repack(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                          int64_t N, int64_t K, uint8_t *qweight, uint32_t *params,
+                          hipStream_t stream);
+
+/* Inverse of nf4_awq_repack: device layout back to codes, scales (binary16
+ * bits) and zero points, same arrays and alignment. */
+nf4_status nf4_awq_unpack(const uint8_t *qweight, const uint32_t *params, int64_t N, int64_t K,
+                          uint8_t *codes, uint16_t *scales, uint8_t *zeros, hipStream_t stream);
+
+/* Debug path: W_out[n][k] = fl32((q - z) * s) (exact), fp32 [N][K]
+ * row-major. */
+nf4_status nf4_awq_dequant(const uint8_t *qweight, const uint32_t *params, int64_t N, int64_t K,
+                           float *W_out, hipStream_t stream);
+
+/* Decode GEMV of the int4 format, 1 <= M <= 8:
+ * y[m][n] = sum_t s[n][t] * sum_{k in group t} x[m][k] * (q[n][k] - z[n][t]),
+ * fp32 accumulation: per group the matrix cores add the exact products
+ * x * q to -z * X (X = the group's sum of x, fp32), and the scale multiplies
+ * that once.  workspace: may be NULL with 0 bytes when x fits the on-chip
+ * path (M * K * 2 bytes up to about 90 KB); otherwise the call runs the
+ * tiled GEMM of nf4_awq_gemm and needs nf4_awq_workspace_bytes(M, N, K)
+ * bytes (else NF4_ERR_NULL or NF4_ERR_WORKSPACE).  Bitwise reproducible run
+ * to run. */
+nf4_status nf4_awq_gemv(const uint16_t *x, int64_t M, const uint8_t *qweight,
+                        const uint32_t *params, int64_t N, int64_t K, float *y, void *workspace,
+                        size_t ws_bytes, hipStream_t stream);
+
+/* Prefill GEMM of the int4 format, any M >= 1: the result definition of
+ * nf4_awq_gemv on the tiled matrix-core kernel, after a pre-pass that writes
+ * the group sums of x into the workspace (nf4_awq_workspace_bytes(M, N, K)
+ * bytes, required).  Rows of y do not depend on the other rows of x.  Shapes
+ * whose byte offsets into x, qweight or the workspace reach 2^32 give
+ * NF4_ERR_SHAPE.  Bitwise reproducible run to run. */
+nf4_status nf4_awq_gemm(const uint16_t *x, int64_t M, const uint8_t *qweight,
+                        const uint32_t *params, int64_t N, int64_t K, float *y, void *workspace,
+                        size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

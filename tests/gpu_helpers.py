@@ -101,6 +101,73 @@ class Side:
         return self.linear(kind, self.x_dev(x_bits), M, pw, cb).cpu().numpy()
 
 
+    # ---- asymmetric int4, groups of 128
+    def awq_pack(self, W: np.ndarray):
+        N, K = W.shape
+        Wd = self.to_dev(W.astype(np.float32))
+        aw = self.nf4.AwqWeight(N, K)
+        self.nf4.nf4_awq_pack(Wd, N, K, aw.qweight, aw.params, stream=self.stream)
+        self.sync()
+        del Wd
+        return aw
+
+    def awq_repack(self, packed: np.ndarray, scales: np.ndarray, zeros: np.ndarray):
+        """Canonical codes, fp32 scales (binary16 values) and zero points."""
+        N, K2 = packed.shape
+        K = 2 * K2
+        aw = self.nf4.AwqWeight(N, K)
+        s16 = np.ascontiguousarray(scales, np.float32).astype(np.float16)
+        assert np.array_equal(s16.astype(np.float32), scales), "scales must be binary16 values"
+        c, s, z = self.to_dev(packed), self.to_dev(s16.view(np.int16)), self.to_dev(zeros)
+        self.nf4.nf4_awq_repack(c, s, z, N, K, aw.qweight, aw.params, stream=self.stream)
+        self.sync()
+        return aw
+
+    def awq_unpack(self, aw):
+        """-> (canonical codes [N, K/2], scales float32 [N, K/128], zeros [N, K/128])."""
+        t = self.torch
+        G = aw.K // 128
+        codes = t.empty((aw.N, aw.K // 2), dtype=t.uint8, device="cuda")
+        scales = t.empty((aw.N, G), dtype=t.int16, device="cuda")
+        zeros = t.empty((aw.N, G), dtype=t.uint8, device="cuda")
+        self.nf4.nf4_awq_unpack(aw.qweight, aw.params, aw.N, aw.K, codes, scales, zeros,
+                                stream=self.stream)
+        self.sync()
+        s16 = scales.cpu().numpy().view(np.float16)
+        return codes.cpu().numpy(), s16.astype(np.float32), zeros.cpu().numpy()
+
+    def awq_dequant(self, aw):
+        t = self.torch
+        out = t.empty((aw.N, aw.K), dtype=t.float32, device="cuda")
+        self.nf4.nf4_awq_dequant(aw.qweight, aw.params, aw.N, aw.K, out, stream=self.stream)
+        self.sync()
+        return out.cpu().numpy()
+
+    def awq_linear(self, kind: str, xd, M: int, aw, y=None):
+        t = self.torch
+        if y is None:
+            y = t.empty((M, aw.N), dtype=t.float32, device="cuda")
+        fn = self.nf4.nf4_awq_gemv if kind == "gemv" else self.nf4.nf4_awq_gemm
+        ws_bytes = self.nf4.nf4_awq_workspace_bytes(M, aw.N, aw.K)
+        ws = t.empty(max(ws_bytes, 16), dtype=t.uint8, device="cuda")
+        self.stream.wait_stream(t.cuda.current_stream())
+        fn(xd, M, aw.qweight, aw.params, aw.N, aw.K, y, ws, ws_bytes, stream=self.stream)
+        self.sync()
+        return y
+
+    def awq_run(self, kind: str, x_bits: np.ndarray, aw) -> np.ndarray:
+        M = x_bits.shape[0]
+        return self.awq_linear(kind, self.x_dev(x_bits), M, aw).cpu().numpy()
+
+
+def oracle_awq_layer(cfg, layer, mid, N, K, rows=None):
+    """Oracle int4 quantization of the seeded weight (all rows or selected rows):
+    (W, canonical codes, scales, zeros)."""
+    W = synth.weights(cfg, layer, mid, N, K, rows=rows)
+    codes, scales, zeros = oracle.awq_quantize(W)
+    return W, oracle.pack(codes), scales, zeros
+
+
 def oracle_layer(cfg, layer, mid, N, K, cb, rows=None):
     """Oracle quantization of the seeded weight (all rows or selected rows)."""
     W = synth.weights(cfg, layer, mid, N, K, rows=rows)

@@ -183,3 +183,78 @@ def test_binding_raises_named_errors():
     with pytest.raises(nf4.NF4Error) as e:
         nf4.nf4_gemv(A, 9, A, A, CB, 16, 64, A, stream=0)
     assert e.value.status == nf4.NF4_ERR_SHAPE and "NF4_ERR_SHAPE" in str(e.value)
+
+
+# ----------------------------------------------- asymmetric int4, group 128
+@pytest.mark.parametrize("N,K", [(16, 128), (48, 256), (4608, 3584), (3584, 18944)])
+def test_awq_size_queries(N, K):
+    assert nf4.nf4_awq_params_bytes(N, K) == (N // 16) * (K // 128) * 64 == 4 * N * K // 128
+    for M in (1, 8, 127, 128, 129, 14449):
+        Mp = -(-M // 128) * 128
+        assert nf4.nf4_awq_workspace_bytes(M, N, K) == (K // 128) * Mp * 4
+
+
+@pytest.mark.parametrize("N,K", [(16, 64), (16, 192), (24, 128), (0, 128), (16, 0)])
+def test_awq_size_queries_reject_bad_shapes(N, K):
+    assert nf4.nf4_awq_params_bytes(N, K) == 0
+    assert nf4.nf4_awq_workspace_bytes(1, N, K) == 0
+
+
+def test_awq_layout_validation():
+    p = lambda *a: call("nf4_awq_pack", *a)
+    assert p(None, 16, 128, A, A, None) == nf4.NF4_ERR_NULL
+    assert p(A, 16, 128, None, A, None) == nf4.NF4_ERR_NULL
+    assert p(A, 16, 128, A, None, None) == nf4.NF4_ERR_NULL
+    assert p(A, 16, 64, A, A, None) == nf4.NF4_ERR_SHAPE       # K % 128 != 0
+    assert p(A, 24, 128, A, A, None) == nf4.NF4_ERR_SHAPE
+    assert p(A + 4, 16, 128, A, A, None) == nf4.NF4_ERR_ALIGN
+    assert p(A, 16, 128, A, A + 8, None) == nf4.NF4_ERR_ALIGN
+    for name in ("nf4_awq_repack", "nf4_awq_unpack"):
+        f = lambda *a: call(name, *a)
+        ok = [A, A, A, 16, 128, A, A, None] if name == "nf4_awq_repack" else \
+             [A, A, 16, 128, A, A, A, None]
+        ptrs = [i for i, v in enumerate(ok) if v == A]
+        for i in ptrs:
+            bad = list(ok)
+            bad[i] = None
+            assert f(*bad) == nf4.NF4_ERR_NULL, (name, i)
+            bad[i] = A + 2
+            assert f(*bad) == nf4.NF4_ERR_ALIGN, (name, i)
+        bad = list(ok)
+        k_at = 4 if name == "nf4_awq_repack" else 3
+        bad[k_at] = 192
+        assert f(*bad) == nf4.NF4_ERR_SHAPE
+    d = lambda *a: call("nf4_awq_dequant", *a)
+    assert d(A, None, 16, 128, A, None) == nf4.NF4_ERR_NULL
+    assert d(A, A, 16, 320, A, None) == nf4.NF4_ERR_SHAPE
+    assert d(A, A, 16, 128, A + 4, None) == nf4.NF4_ERR_ALIGN
+
+
+def test_awq_linear_validation():
+    g = lambda *a: call("nf4_awq_gemv", *a)
+    m = lambda *a: call("nf4_awq_gemm", *a)
+    ok = [A, 1, A, A, 16, 128, A, A, 1 << 20, None]
+    for f in (g, m):
+        for i in (0, 2, 3, 6):
+            bad = list(ok)
+            bad[i] = None
+            assert f(*bad) == nf4.NF4_ERR_NULL, i
+            bad[i] = A + 8
+            assert f(*bad) == nf4.NF4_ERR_ALIGN, i
+        for M, N, K in ((0, 16, 128), (1, 24, 128), (1, 16, 64), (1, 16, 192)):
+            bad = list(ok)
+            bad[1], bad[4], bad[5] = M, N, K
+            assert f(*bad) == nf4.NF4_ERR_SHAPE, (M, N, K)
+    assert g(*([A, 9] + ok[2:])) == nf4.NF4_ERR_SHAPE
+    # the GEMM always needs the x sums in the workspace
+    assert m(A, 1, A, A, 16, 128, A, None, 0, None) == nf4.NF4_ERR_NULL
+    assert m(A, 1, A, A, 16, 128, A, A, 511, None) == nf4.NF4_ERR_WORKSPACE
+    assert m(A, 1, A, A, 16, 128, A, A + 4, 512, None) == nf4.NF4_ERR_ALIGN
+    # x of 8 x 8192 bf16 (128 KB) does not fit the GEMV's LDS: it needs the
+    # workspace of the GEMM it falls back on
+    need = nf4.nf4_awq_workspace_bytes(8, 16, 8192)
+    assert need == 64 * 128 * 4
+    assert g(A, 8, A, A, 16, 8192, A, None, 0, None) == nf4.NF4_ERR_NULL
+    assert g(A, 8, A, A, 16, 8192, A, A, need - 1, None) == nf4.NF4_ERR_WORKSPACE
+    # byte offsets past 32 bits
+    assert m(A, 1 << 17, A, A, 16, 1 << 14, A, A, 1 << 40, None) == nf4.NF4_ERR_SHAPE
