@@ -207,11 +207,12 @@ __device__ inline void wait_copies_and_barrier() {
 //
 // Affine variant (AFF, the asymmetric int4 format in groups of 128 k, codes
 // 0..15 in the table): the scale ring holds the params dword per row
-// (binary16 s | z << 16, 64 bytes per tile) and a third ring
-// holds the tile's x sums X[t][m0 .. m0 + 127] (512 bytes, copied from the
-// pre-pass result with the code words; every wave copies 512 / RG bytes of
-// it).  Per device tile and output: P = -z X, four MFMAs over the tile's
-// 32-k quarters (two steps), then acc = fmaf(s, P, acc).
+// (binary16 s | z << 16, 64 bytes per tile) and a 2-slot ring holds the
+// x sums X[t][m0 .. m0 + 127] of a tile (512 bytes of the pre-pass result;
+// every wave copies 512 / RG bytes of it), tile T + 1's copied at the even
+// step of tile T into the slot tile T - 1 used.  Per device tile and
+// output: P = four MFMAs over the tile's 32-k quarters from zero (two
+// steps), g = fmaf(-z, X, P), acc = fmaf(s, g, acc).
 namespace tile {
 constexpr int kBM = 128;
 constexpr int kTable = 256 * 64 * 4;            // one copy per lane
@@ -228,7 +229,7 @@ struct Map {
   static constexpr int kXLanes = kXSum / 16 / kWaves;  // lanes per wave copying x sums
   // copies a wave may leave in flight past the barrier of an even step: the
   // tile copies of the step before
-  static constexpr int kTileCopies = AFF ? 3 : 2;
+  static constexpr int kTileCopies = 2;
   // bytes of scales (params) per device tile in global memory; the LDS slot
   // keeps 128
   static constexpr int kScaleBytes = AFF ? kTileRows * 4 : kTileScales * 4;
@@ -304,7 +305,11 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
     pipe::copy16(mC + (T & 1) * kTileBytes, qw, coff + tc * kTileBytes);
     if (lane < L::kScaleBytes / 16)
       pipe::copy16(mS + (T & 1) * kTileScales * 4, am, soff + tc * L::kScaleBytes);
+  };
+  // x sums of device tile T (affine) into ring slot T & 1
+  auto copy_xsum = [&](int T) {
     if constexpr (AFF) {
+      const uint32_t tc = (uint32_t)(T < KT ? T : KT - 1);
       if (lane < L::kXLanes)
         pipe::copy16(mX + (T & 1) * tile::kXSum, xsum, xoff + tc * (uint32_t)(Mp * 4));
     }
@@ -324,6 +329,7 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
   copy_x(0);
   copy_tile(0);
   copy_tile(1);
+  copy_xsum(0);
   pipe::wait_copies_and_barrier<0>();
 
   const uint32_t lane4 = (uint32_t)lane << 2;
@@ -364,6 +370,7 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
       for (int v = 0; v < L::kACopies; ++v)
         pipe::copy16(mA[v] + ((PH + 1) & 1) * 2 * tile::kAHalf, x, aoff[v] + xo);
       if (PH == 1) copy_tile((t >> 1) + 2);
+      if (PH == 0) copy_xsum((t >> 1) + 1);
     }
     if (PH == 0) {
       const int sl = (t >> 1) & 1;
@@ -385,19 +392,6 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
     const float s0 = AFF ? f16lo(sv[0].x) : PH ? sv[0].y : sv[0].x;
     const float s1 = AFF ? f16lo(sv[1].x) : PH ? sv[1].y : sv[1].x;
     f32x4 p[4][2];
-    if constexpr (AFF) {
-      if (PH == 0) {
-        const int sl = (t >> 1) & 1;
-        const float nz0 = -(float)(__float_as_uint(sv[0].x) >> 16);
-        const float nz1 = -(float)(__float_as_uint(sv[1].x) >> 16);
-#pragma unroll
-        for (int mm = 0; mm < 4; ++mm) {
-          const f32x4 xz = *reinterpret_cast<const f32x4 *>(xw + sl * tile::kXSum + mm * 64);
-          pz[mm][0] = f32x4{nz0 * xz[0], nz0 * xz[1], nz0 * xz[2], nz0 * xz[3]};
-          pz[mm][1] = f32x4{nz1 * xz[0], nz1 * xz[1], nz1 * xz[2], nz1 * xz[3]};
-        }
-      }
-    }
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const char *pa = ldsA + (PH * 2 + hf) * tile::kAHalf + afr;
@@ -422,19 +416,35 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
 #pragma unroll
         for (int nn = 0; nn < 2; ++nn) {
           if constexpr (AFF)
-            pz[mm][nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mm], B[nn], pz[mm][nn], 0, 0, 0);
+            pz[mm][nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                A[mm], B[nn], (PH == 0 && hf == 0) ? zero : pz[mm][nn], 0, 0, 0);
           else
             p[mm][nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mm], B[nn],
                                                                 hf ? p[mm][nn] : zero, 0, 0, 0);
         }
     }
-    if (!AFF || PH == 1) {
+    if constexpr (AFF) {
+      if (PH == 1) {
+        const int sl = (t >> 1) & 1;
+        const float nz0 = -(float)(__float_as_uint(sv[0].x) >> 16);
+        const float nz1 = -(float)(__float_as_uint(sv[1].x) >> 16);
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+          const f32x4 xz = *reinterpret_cast<const f32x4 *>(xw + sl * tile::kXSum + mm * 64);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[mm][0][i] = fmaf(s0, fmaf(nz0, xz[i], pz[mm][0][i]), acc[mm][0][i]);
+            acc[mm][1][i] = fmaf(s1, fmaf(nz1, xz[i], pz[mm][1][i]), acc[mm][1][i]);
+          }
+        }
+      }
+    } else {
 #pragma unroll
       for (int mm = 0; mm < 4; ++mm)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          acc[mm][0][i] = fmaf(s0, AFF ? pz[mm][0][i] : p[mm][0][i], acc[mm][0][i]);
-          acc[mm][1][i] = fmaf(s1, AFF ? pz[mm][1][i] : p[mm][1][i], acc[mm][1][i]);
+          acc[mm][0][i] = fmaf(s0, p[mm][0][i], acc[mm][0][i]);
+          acc[mm][1][i] = fmaf(s1, p[mm][1][i], acc[mm][1][i]);
         }
     }
   };
@@ -478,26 +488,33 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
 // per 64-block P = MFMA(kk=0, zero) then MFMA(kk=1, P), acc = fmaf(s, P, acc)
 // in K order, with the same operand values in the same lanes, so the two
 // kernels give bit-identical rows and the choice between them (by M) does
-// not change any row.
+// not change any row.  Affine variant (AFF): the x sums of a chunk's tiles
+// and rows (TC x XR floats from the pre-pass) are staged in LDS with the x
+// chunk, and a tile's output is P = four MFMAs from zero, g = fmaf(-z, X,
+// P), acc = fmaf(s, g, acc), as in the tiled kernel's affine variant.
 // ---------------------------------------------------------------------------
 namespace skinny {
 constexpr int kWaves = 4;        // row groups per workgroup
 constexpr int kXBuf = 32 * 1024; // bytes of one x chunk buffer
 }  // namespace skinny
 
-template <int MB, int D>
+template <int MB, int D, bool AFF>
 __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ qw,
     const float *__restrict__ am, CodeTerms ct, int N, int K, int KT, int G,
-    float *__restrict__ y) {
+    float *__restrict__ y, const float *__restrict__ xsum, int Mp) {
   constexpr int XR = 16 * MB;                  // x rows held (m-blocks of 16)
   constexpr int KX = skinny::kXBuf / (XR * 2); // k per chunk: 1024, 512, 256
   constexpr int TC = KX / kTileK;              // tiles per chunk: 8, 4, 2
   constexpr int CPR = KX / 8;                  // 16-byte chunks per x row
   constexpr int XV = skinny::kXBuf / 16 / (64 * skinny::kWaves);  // loads per thread per chunk
   static_assert(D % TC == 0, "the prefetch ring is a whole number of chunks");
-  __shared__ __attribute__((aligned(16))) char lds[2 * skinny::kXBuf + pipe::kTableBytes];
+  constexpr int XSB = TC * XR * 4;             // x sums of a chunk, bytes (512)
+  static_assert(XSB / 16 <= 64 * skinny::kWaves, "one 16-byte load per thread");
+  __shared__ __attribute__((aligned(16))) char
+      lds[2 * skinny::kXBuf + pipe::kTableBytes + (AFF ? 2 * XSB : 0)];
   char *ldsT = lds + 2 * skinny::kXBuf;
+  char *ldsX = ldsT + pipe::kTableBytes;  // affine: x sums [buffer][tile][row]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, h = lane >> 4;
@@ -507,7 +524,10 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
   const int NC = (KT + TC - 1) / TC;  // chunks
   const bool half_tail = (K & (kTileK - 1)) != 0;  // last tile holds one 64-block
 
-  // ---- x chunk c -> registers (rows past M re-read row M-1; k past K is 0)
+  // ---- x chunk c -> registers (rows past M re-read row M-1; k past K is 0);
+  // affine: also 16 bytes of the chunk's x sums per thread below XSB / 16
+  // (thread i: tile i / (XR / 4), rows m0 + 4 (i % (XR / 4)) .. + 3)
+  uint4 xsv = make_uint4(0u, 0u, 0u, 0u);
   auto load_x = [&](int c, uint4 (&xv)[XV]) {
 #pragma unroll
     for (int u = 0; u < XV; ++u) {
@@ -517,6 +537,12 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
       const int m = m0 + R < M ? m0 + R : M - 1;
       xv[u] = make_uint4(0u, 0u, 0u, 0u);
       if (c < NC && k < K) xv[u] = *reinterpret_cast<const uint4 *>(x + (int64_t)m * K + k);
+    }
+    if constexpr (AFF) {
+      xsv = make_uint4(0u, 0u, 0u, 0u);
+      const int tl = tid / (XR / 4), part = tid % (XR / 4), t = c * TC + tl;
+      if (tid < XSB / 16 && c < NC && t < KT)
+        xsv = *reinterpret_cast<const uint4 *>(xsum + (int64_t)t * Mp + m0 + part * 4);
     }
   };
   // row R, 16-byte chunk cr stored at chunk cr ^ (R & 15): the 16 rows of an
@@ -529,6 +555,9 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
       *reinterpret_cast<uint4 *>(lds + buf * skinny::kXBuf + R * (KX * 2) +
                                  ((cr ^ (R & 15)) * 16)) = xv[u];
     }
+    if constexpr (AFF) {
+      if (tid < XSB / 16) *reinterpret_cast<uint4 *>(ldsX + buf * XSB + tid * 16) = xsv;
+    }
   };
 
   // ---- pair table (32 copies), the codebook staged in x buffer 1 first
@@ -536,14 +565,23 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
   if (tid < 16) codes16[tid] = ct.t[0][tid];
   // weight prefetch: tile i of this wave's row group
   const char *qrow = reinterpret_cast<const char *>(qw) + (int64_t)gc * KT * kTileBytes + lane * 16;
-  const char *srow = reinterpret_cast<const char *>(am) + (int64_t)gc * KT * kTileScales * 4 + r * 8;
+  // scales of a tile: two block scales, or (affine) the params dword in .x
+  constexpr int SB = AFF ? kTileRows * 4 : kTileScales * 4;  // bytes per tile
+  const char *srow = reinterpret_cast<const char *>(am) + (int64_t)gc * KT * SB + r * (AFF ? 4 : 8);
+  auto load_s = [&](int i) -> float2 {
+    if constexpr (AFF)
+      return make_float2(
+          __uint_as_float(*reinterpret_cast<const uint32_t *>(srow + (int64_t)i * SB)), 0.0f);
+    else
+      return *reinterpret_cast<const float2 *>(srow + (int64_t)i * SB);
+  };
   uint4 wb[D];
   float2 sb[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
     const int i = d < KT ? d : KT - 1;
     wb[d] = *reinterpret_cast<const uint4 *>(qrow + (int64_t)i * kTileBytes);
-    sb[d] = *reinterpret_cast<const float2 *>(srow + (int64_t)i * kTileScales * 4);
+    sb[d] = load_s(i);
   }
   uint4 xv[XV];
   load_x(0, xv);
@@ -602,6 +640,23 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           A[j] = *reinterpret_cast<const bf16x8 *>(xm + (((tl * 16 + j * 4 + h) ^ r) * 16));
+        if constexpr (AFF) {
+          const uint32_t pv = __float_as_uint(sb[d].x);
+          const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(pv & 0xFFFFu));
+          const float nz = -(float)(pv >> 16);
+          const f32x4 xz = *reinterpret_cast<const f32x4 *>(ldsX + cbuf * XSB +
+                                                            (tl * XR + mb * 16 + 4 * h) * 4);
+          f32x4 P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0], B[0], zero, 0, 0, 0);
+#pragma unroll
+          for (int j = 1; j < 4; ++j)
+            P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[j], B[j], P, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float f = fmaf(sc, fmaf(nz, xz[e], P[e]), acc[mb][e]);
+            acc[mb][e] = live0 ? f : acc[mb][e];
+          }
+          continue;
+        }
         f32x4 p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0], B[0], zero, 0, 0, 0);
         p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1], B[1], p, 0, 0, 0);
         f32x4 q2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[2], B[2], zero, 0, 0, 0);
@@ -618,7 +673,7 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
       {
         const int ni = i + D < KT ? i + D : KT - 1;
         wb[d] = *reinterpret_cast<const uint4 *>(qrow + (int64_t)ni * kTileBytes);
-        sb[d] = *reinterpret_cast<const float2 *>(srow + (int64_t)ni * kTileScales * 4);
+        sb[d] = load_s(ni);
       }
       // ---- chunk boundary: x of the next chunk into the other buffer (it
       // held the chunk before this one, which every wave finished before the
@@ -646,8 +701,8 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
 
 // ---------------------------------------------------------------------------
 // Pre-pass of the affine GEMM: X[t][m] = sum of x[m][128 t .. 128 t + 127]
-// for m < Mp (zero past M), 16 lanes per (t, m): each lane adds its 8
-// values in k order, then a butterfly over the 16 lanes (xor 1, 2, 4, 8).
+// for m < Mp (zero past M), 16 lanes (a DPP row) per (t, m): each lane adds
+// its 8 values in k order, then row16_sum; the GEMV sums the same way.
 // Consecutive 16-lane groups take consecutive m, so a wave writes 16
 // consecutive bytes of X.
 __global__ __launch_bounds__(256) void xsum_kernel(const uint16_t *__restrict__ x, int64_t M,
@@ -660,18 +715,7 @@ __global__ __launch_bounds__(256) void xsum_kernel(const uint16_t *__restrict__ 
   const int64_t t = g / Mp, m = g - t * Mp;
   const int64_t mr = m < M ? m : M - 1;
   const uint4 c = *reinterpret_cast<const uint4 *>(x + mr * K + t * kTileK + 8 * q);
-  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-  float v = __uint_as_float(w[0] << 16);
-  v += __uint_as_float(w[0] & 0xFFFF0000u);
-#pragma unroll
-  for (int i = 1; i < 4; ++i) {
-    v += __uint_as_float(w[i] << 16);
-    v += __uint_as_float(w[i] & 0xFFFF0000u);
-  }
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
+  const float v = row16_sum(chunk_sum8(c));
   if (ok && q == 0) X[g] = m < M ? v : 0.0f;
 }
 
@@ -704,8 +748,23 @@ hipError_t launch_awq_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, cons
                      x, M, K, Mp, ngroups, X);
   const CodeTerms ct = identity_terms();
   const int64_t G = N / kTileRows;
+  const float *prf = reinterpret_cast<const float *>(pr);
+  // the codebook GEMM's choices: skinny for few rows (bit-identical rows),
+  // then the workgroup width of the tiled kernel
+  if (skinny_eligible(M, N, K, 1) &&
+      (M <= 64 || ((N + BN - 1) / BN) * mt < device_cu_count() / 2)) {
+    const unsigned gx = (unsigned)((G + skinny::kWaves - 1) / skinny::kWaves);
+    const dim3 block(64 * skinny::kWaves);
+    if (M <= 16)
+      hipLaunchKernelGGL((gemm_skinny_kernel<1, 8, true>), dim3(gx), block, 0, s, x, (int)M, qw,
+                         prf, ct, (int)N, (int)K, (int)KT, (int)G, y, X, (int)Mp);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<2, 8, true>), dim3(gx, (unsigned)((M + 31) / 32)),
+                         block, 0, s, x, (int)M, qw, prf, ct, (int)N, (int)K, (int)KT, (int)G, y,
+                         X, (int)Mp);
+    return hipGetLastError();
+  }
   auto padded = [&](int64_t nt) { return (unsigned)((nt + 7) / 8 * 8 * mt); };
-  // the same choice of workgroup width as the codebook GEMM
   if (((G + 15) / 16) * mt >= device_cu_count() / 2) {
     const int64_t nt = (G + 15) / 16;
     hipLaunchKernelGGL((gemm_tile_kernel<16, true>), dim3(padded(nt)), dim3(64 * 16), 0, s, x, M,
@@ -736,11 +795,12 @@ hipError_t launch_skinny(const uint16_t *x, int64_t M, const uint8_t *qw, const 
   // the grid's y (workgroups of one row-group block run side by side and
   // share the weights through the caches)
   if (M <= 16)
-    hipLaunchKernelGGL((gemm_skinny_kernel<1, 8>), dim3(gx), block, 0, s, x, (int)M, qw, am, ct,
-                       (int)N, (int)K, KT, (int)G, y);
+    hipLaunchKernelGGL((gemm_skinny_kernel<1, 8, false>), dim3(gx), block, 0, s, x, (int)M, qw, am,
+                       ct, (int)N, (int)K, KT, (int)G, y, nullptr, 0);
   else
-    hipLaunchKernelGGL((gemm_skinny_kernel<2, 8>), dim3(gx, (unsigned)((M + 31) / 32)), block, 0,
-                       s, x, (int)M, qw, am, ct, (int)N, (int)K, KT, (int)G, y);
+    hipLaunchKernelGGL((gemm_skinny_kernel<2, 8, false>), dim3(gx, (unsigned)((M + 31) / 32)),
+                       block, 0, s, x, (int)M, qw, am, ct, (int)N, (int)K, KT, (int)G, y, nullptr,
+                       0);
   return hipGetLastError();
 }
 

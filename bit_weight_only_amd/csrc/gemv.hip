@@ -303,9 +303,9 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float *__restrict__ y
 // codebook is 0..15, a tile row is one group with scale s and zero point z
 // (one params dword per row: binary16 s | z << 16), and the workgroup first
 // sums x over every tile, X[t][m] (in LDS after the partials, 8 floats per
-// tile).  A tile's four products then chain into one
-// accumulator that starts at -z X: P = -z X + sum x q = sum x (q - z), and
-// acc = fmaf(s, P, acc).
+// tile).  A tile's four products then chain into one sum P = sum x q (from
+// zero), the zero point enters as g = fmaf(-z, X, P) = sum x (q - z) with
+// one rounding, and acc = fmaf(s, g, acc).
 // ---------------------------------------------------------------------------
 constexpr int kFastWaves = 8;
 constexpr int kFastCopies = 64;
@@ -316,26 +316,6 @@ constexpr int kLdsBytes = 160 * 1024;                // LDS per workgroup on gfx
 // sched_barrier mask: ALU, VALU, SALU, MFMA, all LDS and transcendental
 // instructions may cross; vector memory instructions may not.
 constexpr int kSchedAllButGlobalLoads = 0x1 | 0x2 | 0x4 | 0x8 | 0x80 | 0x100 | 0x200 | 0x400;
-
-// Sum of one 128-k tile row of bf16 x: 16 lanes (a 16-aligned group) each
-// add the 8 values of their 16-byte chunk in k order, then a butterfly over
-// the group (xor 1, 2, 4, 8) leaves the total in all 16 lanes.  Every lane
-// of the wave must take part.  The GEMM's pre-pass sums the same way.
-__device__ inline float tile_row_sum(uint4 c) {
-  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-  float v = __uint_as_float(w[0] << 16);
-  v += __uint_as_float(w[0] & 0xFFFF0000u);
-#pragma unroll
-  for (int i = 1; i < 4; ++i) {
-    v += __uint_as_float(w[i] << 16);
-    v += __uint_as_float(w[i] & 0xFFFF0000u);
-  }
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
-  return v;
-}
 
 template <int M, bool ARGMAX, bool AFF>
 __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
@@ -401,10 +381,23 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
   // Setup.  The 16 codes go through LDS (indexing the kernel-argument block
   // with a per-thread index would be one memory round trip per use); the x
   // loads are issued before the first barrier and stored after the table is
-  // built, so their latency hides behind it.
+  // built, so their latency hides behind it.  Affine: a row has a whole
+  // number of 128-k tiles, so the 16 lanes of a DPP row hold the 16 chunks
+  // of one tile row of x, and their sum goes to X as x is stored (the
+  // chunk sums in k order, then row16_sum).
   if (threadIdx.x < 16) codes_lds[threadIdx.x] = ct.t[0][threadIdx.x];
   const int chunks = M * KP / 8, cpr = KP / 8;
   constexpr int kStage = 4;
+  float *Xl = red + Gw * kFastWaves * 16 * M;  // affine: X[t][m], 8 floats per tile
+  auto store_xsum = [&](int c, uint4 v) {
+    if constexpr (AFF) {
+      const float sum = row16_sum(chunk_sum8(v));
+      if ((lane & 15) == 0 && c < chunks) {
+        const int m = c / cpr;
+        Xl[((c - m * cpr) >> 4) * 8 + m] = sum;
+      }
+    }
+  };
   uint4 xv0[kStage];
 #pragma unroll
   for (int u = 0; u < kStage; ++u) {
@@ -426,6 +419,7 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
     const int c = (int)threadIdx.x + u * (int)blockDim.x;
     const int m = c / cpr, k = (c - m * cpr) * 8;
     if (c < chunks) *reinterpret_cast<uint4 *>(&xs[m * XS + k]) = xv0[u];
+    store_xsum(c, xv0[u]);
   }
   for (int c0 = (int)threadIdx.x + kStage * (int)blockDim.x; c0 < chunks;
        c0 += kStage * (int)blockDim.x) {
@@ -442,6 +436,7 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
       const int c = c0 + u * (int)blockDim.x;
       const int m = c / cpr, k = (c - m * cpr) * 8;
       if (c < chunks) *reinterpret_cast<uint4 *>(&xs[m * XS + k]) = v[u];
+      store_xsum(c, v[u]);
     }
   }
   __syncthreads();
@@ -449,18 +444,10 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
   // when a row group has fewer than 8 tiles).  The codes' words are reused
   // here, after the barrier above.
   for (int c = threadIdx.x; c < Gw * kFastWaves * 16 * M; c += blockDim.x) red[c] = 0.0f;
-  // x sums per tile (affine variant): X[t][m] for m < 8, zero past M
-  float *Xl = red + Gw * kFastWaves * 16 * M;
-  if constexpr (AFF) {
-    const int grp = (int)(threadIdx.x >> 4), ngrp = (int)(blockDim.x >> 4);
-    for (int b = 0; b < KT * 8; b += ngrp) {
-      const int pr = b + grp < KT * 8 ? b + grp : KT * 8 - 1;
-      const int tt = pr >> 3, m = pr & 7;
-      const int mr = m < M ? m : M - 1;
-      const uint4 c = *reinterpret_cast<const uint4 *>(&xs[mr * XS + tt * kTileK + 8 * (lane & 15)]);
-      const float v = tile_row_sum(c);
-      if ((lane & 15) == 0 && b + grp < KT * 8) Xl[pr] = m < M ? v : 0.0f;
-    }
+  // the x sums of rows M .. 7 (read by lanes whose output rows are dropped)
+  if constexpr (AFF && M < 8) {
+    for (int c = threadIdx.x; c < KT * 8; c += blockDim.x)
+      if ((c & 7) >= M) Xl[c] = 0.0f;
   }
   __syncthreads();
 
@@ -527,11 +514,6 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
       }
       const uint16_t *xt = xrow + t * kTileK;
       f32x4 P[2];
-      if constexpr (AFF) {
-        // D rows 4h + e: x sums of rows 4 (h & 1) + e (rows past M are dropped)
-        const f32x4 xz = *reinterpret_cast<const f32x4 *>(Xl + t * 8 + 4 * (h & 1));
-        P[0] = f32x4{s1 * xz[0], s1 * xz[1], s1 * xz[2], s1 * xz[3]};
-      }
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const uint4 xa = *reinterpret_cast<const uint4 *>(xt + 32 * jj);
@@ -542,15 +524,22 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
         const bf16x8 A = __builtin_bit_cast(bf16x8, xa);
         const bf16x8 B = __builtin_bit_cast(bf16x8, make_uint4(bb[0], bb[1], bb[2], bb[3]));
         if constexpr (AFF)
-          P[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, P[0], 0, 0, 0);
+          P[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, jj ? P[0] : zero, 0, 0, 0);
         else
           P[jj >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               A, B, (jj & 1) ? P[jj >> 1] : zero, 0, 0, 0);
       }
+      if constexpr (AFF) {
+        // D rows 4h + e: x sums of rows 4 (h & 1) + e (rows past M are dropped)
+        const f32x4 xz = *reinterpret_cast<const f32x4 *>(Xl + t * 8 + 4 * (h & 1));
 #pragma unroll
-      for (int e = 0; e < NA; ++e) {
-        acc[e] = fmaf(s0, P[0][e], acc[e]);
-        if constexpr (!AFF) acc[e] = fmaf(s1, P[1][e], acc[e]);
+        for (int e = 0; e < NA; ++e) acc[e] = fmaf(s0, fmaf(s1, xz[e], P[0][e]), acc[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < NA; ++e) {
+          acc[e] = fmaf(s0, P[0][e], acc[e]);
+          acc[e] = fmaf(s1, P[1][e], acc[e]);
+        }
       }
       // ---- advance; when the row group changes (or the share ends), leave
       // this wave's partial for it in LDS

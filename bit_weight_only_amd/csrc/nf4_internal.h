@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace nf4 {
 
 // Quantization block along K (vibevoice.c README, "Quantization" >
@@ -104,6 +106,36 @@ bool skinny_eligible(int64_t M, int64_t N, int64_t K, int nterm);
 hipError_t launch_skinny(const uint16_t *x, int64_t M, const uint8_t *qw, const float *am,
                          const CodeTerms &ct, int64_t N, int64_t K, float *y, hipStream_t s);
 
+
+// Sum of the 8 bf16 values of a 16-byte chunk, in k order.
+__device__ inline float chunk_sum8(uint4 c) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  float v = __uint_as_float(w[0] << 16);
+  v += __uint_as_float(w[0] & 0xFFFF0000u);
+#pragma unroll
+  for (int i = 1; i < 4; ++i) {
+    v += __uint_as_float(w[i] << 16);
+    v += __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+  return v;
+}
+
+// Sum over the 16 lanes of a row (lanes 16i .. 16i + 15) left in every lane
+// of it: neighbours (lane ^ 1), then pairs (lane ^ 2), then quads (lane i of
+// a half-row with lane 7 - i), then halves (lane i with 15 - i), each step a
+// DPP add.  A balanced tree, so every lane of the row gets the same bits.
+// Every lane of the wave must execute it.
+__device__ inline float row16_sum(float v) {
+  auto dpp = [](float x, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value,
+                                                      0xF, 0xF, false));
+  };
+  v += dpp(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1, 0, 3, 2]
+  v += dpp(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2, 3, 0, 1]
+  v += dpp(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  v += dpp(v, std::integral_constant<int, 0x140>{});  // row_mirror
+  return v;
+}
 
 // Linear layers of the asymmetric int4 format.  The GEMV keeps x and its
 // per-tile sums in LDS (M <= 8 and x small enough); the GEMM sums x per tile
