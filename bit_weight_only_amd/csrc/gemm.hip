@@ -205,23 +205,27 @@ __device__ inline void wait_copies_and_barrier() {
 // 64-block P = MFMA(kk=0, zero), MFMA(kk=1, P), acc = fmaf(s, P, acc), in K
 // order.
 //
-// Affine variant (AFF, the asymmetric int4 format in groups of 128 k, codes
-// 0..15 in the table): the scale ring holds the params dword per row
-// (binary16 s | z << 16, 64 bytes per tile) and a 2-slot ring holds the
-// x sums X[t][m0 .. m0 + 127] of a tile (512 bytes of the pre-pass result;
-// every wave copies 512 / RG bytes of it), tile T + 1's copied at the even
-// step of tile T into the slot tile T - 1 used.  Per device tile and
-// output: P = four MFMAs over the tile's 32-k quarters from zero (two
-// steps), g = fmaf(-z, X, P), acc = fmaf(s, g, acc).
+// Affine variant (AFF, the asymmetric int4 format in groups of 128 k): no
+// pair table (x starts at LDS 0); a B pair is a shift and a mask of the
+// interleaved code word, bf16 (1 + c/16, 1 + c'/16).  The scale ring holds
+// the params dword per row (binary16 s | z << 16, 64 bytes per tile) and a
+// 2-slot ring the x sums X[t][m0 .. m0 + 127] of a tile (512 bytes of the
+// pre-pass result; every wave copies 512 / RG bytes of it), tile T + 1's
+// copied at the even step of tile T into the slot tile T - 1 used.  Per
+// device tile and output: P = four MFMAs over the tile's 32-k quarters from
+// zero (two steps; P = sum x (1 + q/16)), g = fmaf(-(16 + z)/16, X, P),
+// acc = fmaf(16 s, g, acc).
 namespace tile {
 constexpr int kBM = 128;
 constexpr int kTable = 256 * 64 * 4;            // one copy per lane
 constexpr int kAHalf = kBM * pipe::kHalfRow;    // 8 KB: 128 rows x 32 k
-constexpr int kOffA = kTable, kOffC = kOffA + 4 * kAHalf;
+
 constexpr int kXSum = kBM * 4;                  // x sums of one tile, bytes
 template <int RG, bool AFF>
 struct Map {
   static constexpr int kWaves = RG, kThreads = 64 * RG, kWN = RG / 2;  // waves along N
+  // the affine variant has no pair table
+  static constexpr int kOffA = AFF ? 0 : kTable, kOffC = kOffA + 4 * kAHalf;
   static constexpr int kOffS = kOffC + RG * 2 * kTileBytes,
                        kOffX = kOffS + RG * 2 * kTileScales * 4,
                        kBytes = kOffX + (AFF ? 2 * kXSum : 0);
@@ -262,7 +266,7 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
   const int64_t G = N / kTileRows;
   const int S = (int)(K / kBK);
   const uint32_t base = pipe::lds_addr(lds);
-  const char *ldsA = lds + tile::kOffA, *ldsC = lds + tile::kOffC, *ldsS = lds + L::kOffS;
+  const char *ldsA = lds + L::kOffA, *ldsC = lds + L::kOffC, *ldsS = lds + L::kOffS;
 
   // Copy assignment.  x: copy i (16 per step, 1 KB each) fills rows
   // 16 (i % 8) .. + 15 of half i / 8; wave w issues i = w, w + RG, ...  Lane
@@ -278,7 +282,7 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
     const int64_t gm = R < M ? R : M - 1;
     const int c = (lane & 3) ^ ((lane >> 4) & 3);
     aoff[v] = (uint32_t)((gm * K + half * 32 + c * 8) * 2);
-    mA[v] = base + tile::kOffA + half * tile::kAHalf + blk * 1024;
+    mA[v] = base + L::kOffA + half * tile::kAHalf + blk * 1024;
   }
   uint32_t coff, soff;
   {
@@ -287,7 +291,7 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
     coff = (uint32_t)(g * KT * kTileBytes + lane * 16);
     soff = (uint32_t)(g * KT * L::kScaleBytes + lane * 16);  // lanes 0..7 (0..3) copy
   }
-  const uint32_t mC = base + tile::kOffC + wave * 2 * kTileBytes;
+  const uint32_t mC = base + L::kOffC + wave * 2 * kTileBytes;
   const uint32_t mS = base + L::kOffS + wave * 2 * kTileScales * 4;
   // x sums (affine): wave w copies bytes [w, w + 1) * 512 / RG of a tile's 512
   const uint32_t mX = base + L::kOffX + wave * (tile::kXSum / RG);
@@ -318,9 +322,9 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
   // the pair table, from the codebook staged in the scale ring (filled only
   // after the second barrier)
   uint16_t *codes16 = reinterpret_cast<uint16_t *>(lds + L::kOffS);
-  if (tid < 16) codes16[tid] = ct.t[0][tid];
+  if (!AFF && tid < 16) codes16[tid] = ct.t[0][tid];
   __syncthreads();
-  for (int c = tid; c < tile::kTable / 16; c += L::kThreads) {
+  for (int c = tid; c < (AFF ? 0 : tile::kTable / 16); c += L::kThreads) {
     const int e = c >> 4;  // 16 chunks of 4 copies per entry
     const uint32_t v = (uint32_t)codes16[e & 15] | ((uint32_t)codes16[e >> 4] << 16);
     reinterpret_cast<uint4 *>(lds)[c] = make_uint4(v, v, v, v);
@@ -385,9 +389,9 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
           sv[nn] = *reinterpret_cast<const float2 *>(sw + (nn * 2 + sl) * kTileScales * 4);
       }
     }
-    // block scales, or (affine) s from the params dword
+    // block scales, or (affine) 16 s from the params dword: P sums x (1 + q/16)
     auto f16lo = [](float v) {
-      return (float)__builtin_bit_cast(_Float16, (uint16_t)(__float_as_uint(v) & 0xFFFFu));
+      return 16.0f * (float)__builtin_bit_cast(_Float16, (uint16_t)(__float_as_uint(v) & 0xFFFFu));
     };
     const float s0 = AFF ? f16lo(sv[0].x) : PH ? sv[0].y : sv[0].x;
     const float s1 = AFF ? f16lo(sv[1].x) : PH ? sv[1].y : sv[1].x;
@@ -406,8 +410,13 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
         uint32_t bb[4];
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
-          const uint32_t a = __builtin_amdgcn_perm(wd, lane4, 0x0c0c0400u + (qq << 8));
-          bb[qq] = *reinterpret_cast<const uint32_t *>(lds + a);
+          if constexpr (AFF) {
+            // bf16 (1 + c/16) of codes 2qq, 2qq + 1 (interleaved nibbles)
+            bb[qq] = awq_pair(wd, qq, 0x3F803F80u);
+          } else {
+            const uint32_t a = __builtin_amdgcn_perm(wd, lane4, 0x0c0c0400u + (qq << 8));
+            bb[qq] = *reinterpret_cast<const uint32_t *>(lds + a);
+          }
         }
         B[nn] = __builtin_bit_cast(bf16x8, make_uint4(bb[0], bb[1], bb[2], bb[3]));
       }
@@ -426,8 +435,9 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
     if constexpr (AFF) {
       if (PH == 1) {
         const int sl = (t >> 1) & 1;
-        const float nz0 = -(float)(__float_as_uint(sv[0].x) >> 16);
-        const float nz1 = -(float)(__float_as_uint(sv[1].x) >> 16);
+        // -(16 + z) / 16, exact
+        const float nz0 = -(float)(16u + (__float_as_uint(sv[0].x) >> 16)) * 0.0625f;
+        const float nz1 = -(float)(16u + (__float_as_uint(sv[1].x) >> 16)) * 0.0625f;
 #pragma unroll
         for (int mm = 0; mm < 4; ++mm) {
           const f32x4 xz = *reinterpret_cast<const f32x4 *>(xw + sl * tile::kXSum + mm * 64);
@@ -488,10 +498,11 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
 // per 64-block P = MFMA(kk=0, zero) then MFMA(kk=1, P), acc = fmaf(s, P, acc)
 // in K order, with the same operand values in the same lanes, so the two
 // kernels give bit-identical rows and the choice between them (by M) does
-// not change any row.  Affine variant (AFF): the x sums of a chunk's tiles
-// and rows (TC x XR floats from the pre-pass) are staged in LDS with the x
-// chunk, and a tile's output is P = four MFMAs from zero, g = fmaf(-z, X,
-// P), acc = fmaf(s, g, acc), as in the tiled kernel's affine variant.
+// not change any row.  Affine variant (AFF): no table (B pairs from the
+// interleaved code words by shift and mask), the x sums of a chunk's tiles
+// and rows (TC x XR floats from the pre-pass) staged in LDS with the x
+// chunk, and per tile P = four MFMAs from zero, g = fmaf(-(16 + z)/16, X,
+// P), acc = fmaf(16 s, g, acc), as in the tiled kernel's affine variant.
 // ---------------------------------------------------------------------------
 namespace skinny {
 constexpr int kWaves = 4;        // row groups per workgroup
@@ -511,10 +522,10 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
   static_assert(D % TC == 0, "the prefetch ring is a whole number of chunks");
   constexpr int XSB = TC * XR * 4;             // x sums of a chunk, bytes (512)
   static_assert(XSB / 16 <= 64 * skinny::kWaves, "one 16-byte load per thread");
-  __shared__ __attribute__((aligned(16))) char
-      lds[2 * skinny::kXBuf + pipe::kTableBytes + (AFF ? 2 * XSB : 0)];
+  constexpr int TB = AFF ? 0 : pipe::kTableBytes;  // the affine variant has no table
+  __shared__ __attribute__((aligned(16))) char lds[2 * skinny::kXBuf + TB + (AFF ? 2 * XSB : 0)];
   char *ldsT = lds + 2 * skinny::kXBuf;
-  char *ldsX = ldsT + pipe::kTableBytes;  // affine: x sums [buffer][tile][row]
+  char *ldsX = ldsT + TB;  // affine: x sums [buffer][tile][row]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, h = lane >> 4;
@@ -562,7 +573,7 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
 
   // ---- pair table (32 copies), the codebook staged in x buffer 1 first
   uint16_t *codes16 = reinterpret_cast<uint16_t *>(lds + skinny::kXBuf);
-  if (tid < 16) codes16[tid] = ct.t[0][tid];
+  if (!AFF && tid < 16) codes16[tid] = ct.t[0][tid];
   // weight prefetch: tile i of this wave's row group
   const char *qrow = reinterpret_cast<const char *>(qw) + (int64_t)gc * KT * kTileBytes + lane * 16;
   // scales of a tile: two block scales, or (affine) the params dword in .x
@@ -586,7 +597,7 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
   uint4 xv[XV];
   load_x(0, xv);
   __syncthreads();
-  for (int c = tid; c < pipe::kTableBytes / 16; c += 64 * skinny::kWaves) {
+  for (int c = tid; c < TB / 16; c += 64 * skinny::kWaves) {
     const int e = c / (pipe::kCopies / 4);
     const uint32_t v = (uint32_t)codes16[e & 15] | ((uint32_t)codes16[e >> 4] << 16);
     reinterpret_cast<uint4 *>(ldsT)[c] = make_uint4(v, v, v, v);
@@ -610,8 +621,12 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
       uint32_t bb[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint32_t e = (wd >> (8 * q)) & 0xFFu;
-        bb[q] = *reinterpret_cast<const uint32_t *>(ldsT + e * (pipe::kCopies * 4) + tcopy);
+        if constexpr (AFF) {
+          bb[q] = awq_pair(wd, q, 0x3F803F80u);
+        } else {
+          const uint32_t e = (wd >> (8 * q)) & 0xFFu;
+          bb[q] = *reinterpret_cast<const uint32_t *>(ldsT + e * (pipe::kCopies * 4) + tcopy);
+        }
       }
       B[j] = __builtin_bit_cast(bf16x8, make_uint4(bb[0], bb[1], bb[2], bb[3]));
     }
@@ -642,8 +657,8 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
           A[j] = *reinterpret_cast<const bf16x8 *>(xm + (((tl * 16 + j * 4 + h) ^ r) * 16));
         if constexpr (AFF) {
           const uint32_t pv = __float_as_uint(sb[d].x);
-          const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(pv & 0xFFFFu));
-          const float nz = -(float)(pv >> 16);
+          const float sc = 16.0f * (float)__builtin_bit_cast(_Float16, (uint16_t)(pv & 0xFFFFu));
+          const float nz = -(float)(16u + (pv >> 16)) * 0.0625f;
           const f32x4 xz = *reinterpret_cast<const f32x4 *>(ldsX + cbuf * XSB +
                                                             (tl * XR + mb * 16 + 4 * h) * 4);
           f32x4 P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0], B[0], zero, 0, 0, 0);

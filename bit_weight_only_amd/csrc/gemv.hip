@@ -299,13 +299,17 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float *__restrict__ y
 // with a 16-byte skew per row (so the M rows of one operand-A read fall in
 // different banks); and the partial sums [row group][wave][16 rows][M].
 //
-// Affine variant (AFF, the asymmetric int4 format in groups of 128 k): the
-// codebook is 0..15, a tile row is one group with scale s and zero point z
-// (one params dword per row: binary16 s | z << 16), and the workgroup first
-// sums x over every tile, X[t][m] (in LDS after the partials, 8 floats per
-// tile).  A tile's four products then chain into one sum P = sum x q (from
-// zero), the zero point enters as g = fmaf(-z, X, P) = sum x (q - z) with
-// one rounding, and acc = fmaf(s, g, acc).
+// Affine variant (AFF, the asymmetric int4 format in groups of 128 k): a
+// tile row is one group with scale s and zero point z (one params dword per
+// row: binary16 s | z << 16), and the workgroup first sums x over every
+// tile, X[t][m] (in LDS after the partials, 8 floats per tile).  There is
+// no table: the code words interleave their nibbles so that a shift and a
+// mask put codes 2p, 2p + 1 into the mantissas of the bf16 pair
+// (1 + c/16, 1 + c'/16) (0x3F80 is bf16 1.0), the B operand as it stands.
+// A tile's four products form two sums of 64 k each (as in the codebook
+// variant, so two MFMA chains overlap), P = P0 + P1 = sum x (1 + q/16), then
+// g = fmaf(-(16 + z)/16, X, P) = sum x (q - z) / 16 with one rounding, and
+// acc = fmaf(16 s, g, acc) (both constants exact).
 // ---------------------------------------------------------------------------
 constexpr int kFastWaves = 8;
 constexpr int kFastCopies = 64;
@@ -327,7 +331,7 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
   // The table is the kernel's only static LDS array, so it sits at address
   // 0 and a lookup address needs no base added; x and the partials follow in
   // dynamic LDS.
-  __shared__ __attribute__((aligned(16))) uint32_t table[kFastTableWords];
+  __shared__ __attribute__((aligned(16))) uint32_t table[AFF ? 4 : kFastTableWords];
   extern __shared__ __attribute__((aligned(16))) uint32_t lds_dyn[];
   const int KP = KT * kTileK;                 // padded x row length
   const int XS = KP + kFastSkew;              // x row stride in LDS
@@ -385,7 +389,7 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
   // number of 128-k tiles, so the 16 lanes of a DPP row hold the 16 chunks
   // of one tile row of x, and their sum goes to X as x is stored (the
   // chunk sums in k order, then row16_sum).
-  if (threadIdx.x < 16) codes_lds[threadIdx.x] = ct.t[0][threadIdx.x];
+  if (!AFF && threadIdx.x < 16) codes_lds[threadIdx.x] = ct.t[0][threadIdx.x];
   const int chunks = M * KP / 8, cpr = KP / 8;
   constexpr int kStage = 4;
   float *Xl = red + Gw * kFastWaves * 16 * M;  // affine: X[t][m], 8 floats per tile
@@ -409,7 +413,7 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
   __syncthreads();
   // Pair table: consecutive lanes fill consecutive 16-byte chunks (four
   // copies of one entry each), so the stores are free of bank conflicts.
-  for (int c = threadIdx.x; c < kFastTableWords / 4; c += blockDim.x) {
+  for (int c = threadIdx.x; c < (AFF ? 0 : kFastTableWords / 4); c += blockDim.x) {
     const int e = c / (kFastCopies / 4);
     const uint32_t v = (uint32_t)codes_lds[e & 15] | ((uint32_t)codes_lds[e >> 4] << 16);
     reinterpret_cast<uint4 *>(table)[c] = make_uint4(v, v, v, v);
@@ -453,6 +457,7 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
 
   const uint32_t lane4 = (uint32_t)lane << 2;
   const char *tabc = reinterpret_cast<const char *>(table);
+  const uint32_t magic = 0x3F803F80u;  // bf16 pair (1.0, 1.0), affine B operands
   // D rows 4h + i (i < NA) of the lane that can be real output rows
   constexpr int NA = M < 4 ? M : 4;
   float acc[NA];
@@ -479,31 +484,37 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
       // and the barrier keeps the scheduler from hoisting the global loads
       // above them (either would rotate the slot registers and force a full
       // wait per step); ALU and LDS instructions may still cross it.
-      uint32_t ad[16];
+      // Affine: no table; the slot's four code words are kept (pinned like
+      // the addresses) and the B pairs are formed next to their products.
+      uint32_t ad[AFF ? 4 : 16];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const uint32_t wd = jj == 0 ? wb[d].x : jj == 1 ? wb[d].y : jj == 2 ? wb[d].z : wb[d].w;
+        if constexpr (AFF) {
+          ad[jj] = wd;
+        } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          ad[4 * jj + q] = __builtin_amdgcn_perm(wd, lane4, 0x0c0c0400u + (q << 8));
+          for (int q = 0; q < 4; ++q)
+            ad[4 * jj + q] = __builtin_amdgcn_perm(wd, lane4, 0x0c0c0400u + (q << 8));
+        }
       }
-      // block scales, or (affine) the scale and minus the zero point
+      // block scales, or (affine) 16 s and -(16 + z) / 16: P sums x (1 + q/16)
       float s0, s1;
       if constexpr (AFF) {
         const uint32_t pv = __float_as_uint(sb[d].x);
-        s0 = live ? (float)__builtin_bit_cast(_Float16, (uint16_t)(pv & 0xFFFFu)) : 0.0f;
-        s1 = -(float)(pv >> 16);
+        s0 = live ? 16.0f * (float)__builtin_bit_cast(_Float16, (uint16_t)(pv & 0xFFFFu)) : 0.0f;
+        s1 = -(float)(16u + (pv >> 16)) * 0.0625f;
       } else {
         s0 = live ? sb[d].x : 0.0f;
         s1 = live ? sb[d].y : 0.0f;
       }
 #pragma unroll
-      for (int u = 0; u < 16; ++u) asm volatile("" ::"v"(ad[u]));
+      for (int u = 0; u < (AFF ? 4 : 16); ++u) asm volatile("" ::"v"(ad[u]));
       asm volatile("" ::"v"(s0), "v"(s1));
       __builtin_amdgcn_sched_barrier(kSchedAllButGlobalLoads);
       {
         const bool dead = ptau >= tile_end;
-        const bool ahead = dead && pn < ntile_end;
+        const bool ahead = !AFF && dead && pn < ntile_end;  // no read-ahead in the affine variant
         const uint32_t lt = ahead ? pn : dead ? (uint32_t)T0 : ptau;
         const char *qsrc = ahead ? nq : qbase;
         const char *ssrc = ahead ? nsb : sbase;
@@ -519,21 +530,26 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
         const uint4 xa = *reinterpret_cast<const uint4 *>(xt + 32 * jj);
         uint32_t bb[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          bb[q] = *reinterpret_cast<const uint32_t *>(tabc + ad[4 * jj + q]);
+        for (int q = 0; q < 4; ++q) {
+          if constexpr (AFF) {
+            // bf16 (1 + c/16) of codes 2q and 2q + 1: their nibbles sit at
+            // bits 4q and 16 + 4q of the interleaved code word
+            bb[q] = awq_pair(ad[jj], q, magic);
+          } else {
+            bb[q] = *reinterpret_cast<const uint32_t *>(tabc + ad[4 * jj + q]);
+          }
+        }
         const bf16x8 A = __builtin_bit_cast(bf16x8, xa);
         const bf16x8 B = __builtin_bit_cast(bf16x8, make_uint4(bb[0], bb[1], bb[2], bb[3]));
-        if constexpr (AFF)
-          P[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, jj ? P[0] : zero, 0, 0, 0);
-        else
-          P[jj >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              A, B, (jj & 1) ? P[jj >> 1] : zero, 0, 0, 0);
+        P[jj >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, (jj & 1) ? P[jj >> 1] : zero,
+                                                             0, 0, 0);
       }
       if constexpr (AFF) {
         // D rows 4h + e: x sums of rows 4 (h & 1) + e (rows past M are dropped)
         const f32x4 xz = *reinterpret_cast<const f32x4 *>(Xl + t * 8 + 4 * (h & 1));
 #pragma unroll
-        for (int e = 0; e < NA; ++e) acc[e] = fmaf(s0, fmaf(s1, xz[e], P[0][e]), acc[e]);
+        for (int e = 0; e < NA; ++e)
+          acc[e] = fmaf(s0, fmaf(s1, xz[e], P[0][e] + P[1][e]), acc[e]);
       } else {
 #pragma unroll
         for (int e = 0; e < NA; ++e) {
@@ -605,13 +621,15 @@ size_t fast_dyn_bytes(int M, int64_t K, int64_t Gw, bool aff) {
          (aff ? (size_t)tiles_k(K) * 8 * 4 : 0);
 }
 constexpr size_t kDynMax = (size_t)kLdsBytes - (size_t)kFastTableWords * 4;
+constexpr size_t kDynMaxAff = (size_t)kLdsBytes - 256;  // no pair table
+inline size_t dyn_max(bool aff) { return aff ? kDynMaxAff : kDynMax; }
 
 FastPlan fast_plan(int M, int64_t N, int64_t K, bool aff = false) {
   const int64_t G = N / kTileRows;
   int64_t P = device_cu_count();
   if (P > G) P = G;
   // more workgroups when the partial slots of ceil(G/P) row groups do not fit
-  while (fast_dyn_bytes(M, K, (G + P - 1) / P, aff) > kDynMax && P < G) P += P / 4 + 1;
+  while (fast_dyn_bytes(M, K, (G + P - 1) / P, aff) > dyn_max(aff) && P < G) P += P / 4 + 1;
   if (P > G) P = G;
   return FastPlan{(int)P, fast_dyn_bytes(M, K, (G + P - 1) / P, aff)};
 }
@@ -620,7 +638,7 @@ bool fast_eligible(int M, int64_t N, int64_t K, int nterm, bool aff = false) {
   // 32-bit tile indices and byte offsets into the code buffer, and LDS room
   // for x plus one row group's partials
   const int64_t qbytes = (N / kTileRows) * tiles_k(K) * kTileBytes;
-  return nterm == 1 && qbytes < (int64_t(1) << 32) && fast_dyn_bytes(M, K, 1, aff) <= kDynMax;
+  return nterm == 1 && qbytes < (int64_t(1) << 32) && fast_dyn_bytes(M, K, 1, aff) <= dyn_max(aff);
 }
 
 template <int M, bool ARGMAX, bool AFF = false>
@@ -631,7 +649,7 @@ hipError_t launch_fast(const uint16_t *x, const uint4 *qw, const float2 *am, con
   if (!attr_set.load(std::memory_order_acquire)) {
     const hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&gemv_fast_kernel<M, ARGMAX, AFF>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDynMax);
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_max(AFF));
     if (e != hipSuccess) return e;
     attr_set.store(true, std::memory_order_release);
   }

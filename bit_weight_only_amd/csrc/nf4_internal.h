@@ -137,6 +137,19 @@ __device__ inline float row16_sum(float v) {
   return v;
 }
 
+// B pair of the asymmetric int4 format: bf16 (1 + c/16) of codes 2q and
+// 2q + 1 of an interleaved code word (nibble positions q and q + 4), i.e.
+// the nibbles moved to mantissa bits 3..6 of each half and or-ed with bf16
+// 1.0 (0x3F80).  One shift and one v_and_or_b32 whose mask comes from a
+// scalar register and whose magic word from a vector register (the
+// three-operand encoding takes neither a literal nor two scalar operands).
+__device__ inline uint32_t awq_pair(uint32_t wd, int q, uint32_t magic_v) {
+  const uint32_t sh = q ? wd >> (4 * q - 3) : wd << 3;
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(sh), "s"(0x00780078u), "v"(magic_v));
+  return d;
+}
+
 // Linear layers of the asymmetric int4 format.  The GEMV keeps x and its
 // per-tile sums in LDS (M <= 8 and x small enough); the GEMM sums x per tile
 // in a pre-pass into the workspace ([K/128][M rounded up to 128] floats) and

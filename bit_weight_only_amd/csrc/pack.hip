@@ -181,9 +181,28 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint4 *__restrict__ q
 // Second format: asymmetric int4, one group per device tile row (128 k):
 // w = (q - z) * s with a binary16 scale s and an integer zero point z per
 // group (vibevoice.c README, "Quantization" > "Weights", the AWQ/GPTQ
-// paragraph).  The codes use the device layout above; a tile's params are
-// 16 dwords, dword r = binary16 bits of s | z << 16 for row r (s is a
-// binary16 value by construction, so nothing is lost).
+// paragraph).  The codes use the device layout above with the nibbles of
+// every dword interleaved: code i (k = k0 + i) sits at nibble position
+// (i >> 1) + 4 (i & 1), so codes 2p and 2p + 1 share the bit positions of
+// the two halves of a bf16 pair (the pages permute nibbles inside 16-byte
+// runs for the same reason: one logic operation with a magic constant
+// yields the pair).  A tile's params are 16 dwords, dword r = binary16 bits
+// of s | z << 16 for row r (s is a binary16 value by construction, so
+// nothing is lost).
+__device__ inline int awq_nibble_pos(int i) { return (i >> 1) + 4 * (i & 1); }
+// canonical dword (code i at nibble i) <-> interleaved dword
+__device__ inline uint32_t awq_interleave(uint32_t w) {
+  uint32_t o = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o |= ((w >> (4 * i)) & 15u) << (4 * awq_nibble_pos(i));
+  return o;
+}
+__device__ inline uint32_t awq_deinterleave(uint32_t w) {
+  uint32_t o = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o |= ((w >> (4 * awq_nibble_pos(i))) & 15u) << (4 * i);
+  return o;
+}
 
 // Nearest binary16 value of a positive finite double, ties to even, as a
 // double: the significand is cut to 11 bits (10 stored) by integer
@@ -237,7 +256,7 @@ __global__ __launch_bounds__(256) void awq_pack_kernel(const float *__restrict__
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const double v = fmin(fmax(rint((double)w[j][i] / sd) + zd, 0.0), 15.0);
-      word |= (uint32_t)v << (4 * i);
+      word |= (uint32_t)v << (4 * awq_nibble_pos(i));
     }
     out[j] = word;
   }
@@ -261,7 +280,8 @@ __global__ __launch_bounds__(256) void awq_repack_kernel(const uint32_t *__restr
   const uint32_t *row = codes + n * (K / 8);
   uint32_t wd[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) wd[j] = row[((int64_t)c.t * kTileK + 32 * j + 8 * c.h) / 8];
+  for (int j = 0; j < 4; ++j)
+    wd[j] = awq_interleave(row[((int64_t)c.t * kTileK + 32 * j + 8 * c.h) / 8]);
   qw[c.tile * 64 + c.lane] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
   if (c.h == 0)
     pr[c.tile * kTileRows + c.r] =
@@ -283,7 +303,7 @@ __global__ __launch_bounds__(256) void awq_unpack_kernel(const uint4 *__restrict
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     row[((int64_t)c.t * kTileK + 32 * j + 8 * c.h) / 8] =
-        j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
+        awq_deinterleave(j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w);
   if (c.h == 0) {
     const uint32_t v = pr[c.tile * kTileRows + c.r];
     scales[n * KT + c.t] = (uint16_t)(v & 0xFFFFu);
@@ -309,7 +329,7 @@ __global__ __launch_bounds__(256) void awq_dequant_kernel(const uint4 *__restric
     const int64_t k0 = (int64_t)c.t * kTileK + 32 * j + 8 * c.h;
     float v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = ((float)((word >> (4 * i)) & 15u) - z) * s;
+    for (int i = 0; i < 8; ++i) v[i] = ((float)((word >> (4 * awq_nibble_pos(i))) & 15u) - z) * s;
     *reinterpret_cast<float4 *>(row + k0) = make_float4(v[0], v[1], v[2], v[3]);
     *reinterpret_cast<float4 *>(row + k0 + 4) = make_float4(v[4], v[5], v[6], v[7]);
   }

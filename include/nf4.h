@@ -233,10 +233,10 @@ nf4_status nf4_awq_dequant(const uint8_t *qweight, const uint32_t *params, int64
  * fp32 accumulation: per group the matrix cores add the exact products
  * x * q to -z * X (X = the group's sum of x, fp32), and the scale multiplies
  * that once.  workspace: may be NULL with 0 bytes when x fits the on-chip
- * path (M * K * 2 bytes up to about 90 KB); otherwise the call runs the
- * tiled GEMM of nf4_awq_gemm and needs nf4_awq_workspace_bytes(M, N, K)
- * bytes (else NF4_ERR_NULL or NF4_ERR_WORKSPACE).  Bitwise reproducible run
- * to run. */
+ * path (M * K * 2 bytes of x plus K/4 bytes of sums within a workgroup's
+ * 160 KB of LDS, about M * K <= 78000); otherwise the call runs the GEMM of
+ * nf4_awq_gemm and needs nf4_awq_workspace_bytes(M, N, K) bytes (else
+ * NF4_ERR_NULL or NF4_ERR_WORKSPACE).  Bitwise reproducible run to run. */
 nf4_status nf4_awq_gemv(const uint16_t *x, int64_t M, const uint8_t *qweight,
                         const uint32_t *params, int64_t N, int64_t K, float *y, void *workspace,
                         size_t ws_bytes, hipStream_t stream);

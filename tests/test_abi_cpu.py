@@ -250,11 +250,11 @@ def test_awq_linear_validation():
     assert m(A, 1, A, A, 16, 128, A, None, 0, None) == nf4.NF4_ERR_NULL
     assert m(A, 1, A, A, 16, 128, A, A, 511, None) == nf4.NF4_ERR_WORKSPACE
     assert m(A, 1, A, A, 16, 128, A, A + 4, 512, None) == nf4.NF4_ERR_ALIGN
-    # x of 8 x 8192 bf16 (128 KB) does not fit the GEMV's LDS: it needs the
+    # x of 8 x 18944 bf16 (303 KB) does not fit the GEMV's LDS: it needs the
     # workspace of the GEMM it falls back on
-    need = nf4.nf4_awq_workspace_bytes(8, 16, 8192)
-    assert need == 64 * 128 * 4
-    assert g(A, 8, A, A, 16, 8192, A, None, 0, None) == nf4.NF4_ERR_NULL
-    assert g(A, 8, A, A, 16, 8192, A, A, need - 1, None) == nf4.NF4_ERR_WORKSPACE
+    need = nf4.nf4_awq_workspace_bytes(8, 16, 18944)
+    assert need == 148 * 128 * 4
+    assert g(A, 8, A, A, 16, 18944, A, None, 0, None) == nf4.NF4_ERR_NULL
+    assert g(A, 8, A, A, 16, 18944, A, A, need - 1, None) == nf4.NF4_ERR_WORKSPACE
     # byte offsets past 32 bits
     assert m(A, 1 << 17, A, A, 16, 1 << 14, A, A, 1 << 40, None) == nf4.NF4_ERR_SHAPE
