@@ -14,6 +14,11 @@ a decoder knows its weights ahead of the activations.  The JSON line's
 `value` is decode packed-weight GB/s over the whole step (launch gaps
 included); prefill TFLOP/s sits beside it.
 
+`int4_group128` repeats decode, prefill and both rooflines with the same
+seeded weights quantized to the second format, asymmetric int4 in groups of
+128 (nf4_awq_pack; nf4_awq_gemv / nf4_awq_gemm; algorithmic bytes N K / 2 +
+4 N K / 128: codes and one 4-byte (s, z) per group).
+
 `roofline` covers the dominant decode kernel (the gate|up GEMV, 28 launches
 per step): its 28 launches on distinct weights are replayed back to back in
 one graph, each naming the next as its hint as in the step, each replay
@@ -24,7 +29,7 @@ from rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, each scaled by what the
 counter reads for a plain 1 GiB copy), recorded below together with a hash of
 the kernel source they were taken on; it is null when the source differs.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu] [--no-int4]
     python bench.py --pmc-pass          # workload for rocprofv3 --pmc runs
     python bench.py --summarize DIR --launch-log FILE --title T --command C
 """
@@ -61,16 +66,25 @@ DOMINANT = ("gate_up", 2 * MLP, HIDDEN)
 # `python bench.py --pmc-pass` (profiles/hbm_traffic_gate_up.md): counter KiB
 # per dispatch and the calibration of each counter on a plain 1 GiB copy.
 TRAFFIC = {
-    "gemv": {"source": "gemv.hip", "fetch_kib": 42727, "write_kib": 148,
-             "sha256": "61a295479b812add35f76dcdbe8184987c95604af965c7ff245d061849268203"},
-    "gemm": {"source": "gemm.hip", "fetch_kib": 180720, "write_kib": 153848,
-             "sha256": "7ed7b44ddb1ac1e5979ad93d4f95dc2525845e72386aad7098830595578322f9"},
+    "gemv": {"source": "gemv.hip", "fetch_kib": 42731, "write_kib": 148,
+             "sha256": "6376bb178b9be91a2dce5ee4b73091ccda54ebbdf43941092678f94087a9c7fe"},
+    "gemm": {"source": "gemm.hip", "fetch_kib": 180720, "write_kib": 153694,
+             "sha256": "9c0581cd848c56dce6dbccf425c0622202cd7fa028f23a8938544c4501dc2575"},
+    "awq_gemv": {"source": "gemv.hip", "fetch_kib": 35460, "write_kib": 148,
+                 "sha256": "6376bb178b9be91a2dce5ee4b73091ccda54ebbdf43941092678f94087a9c7fe"},
+    "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180885, "write_kib": 153636,
+                 "sha256": "9c0581cd848c56dce6dbccf425c0622202cd7fa028f23a8938544c4501dc2575"},
 }
 COPY_CALIBRATION = {"fetch_kib_per_gib": 524308, "write_kib_per_gib": 1048576}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def awq_packed_bytes(N, K):
+    """Algorithmic bytes of an int4 (group 128) matrix: codes + 4 B per group."""
+    return N * K // 2 + 4 * N * (K // 128)
 
 
 def packed_bytes(N, K):
@@ -94,6 +108,8 @@ def traffic_bytes(kind):
     """HBM bytes per launch from the recorded counters, or None when they
     were not taken or the kernel source changed since."""
     t, cal = TRAFFIC[kind], COPY_CALIBRATION
+    if t is None:
+        return None
     if None in (t["sha256"], t["fetch_kib"], t["write_kib"], cal["fetch_kib_per_gib"],
                 cal["write_kib_per_gib"]):
         return None
@@ -207,6 +223,54 @@ class Model:
                           self.yp[name], self.ws, self.ws_bytes)
 
 
+class AwqModel:
+    """The same seeded weights quantized to the int4 group-128 format; shares
+    the activation and output buffers of `base`."""
+
+    def __init__(self, torch, nf4, seed, stream, base, layers=LAYERS, with_head=True, only=None):
+        dev = "cuda"
+        self.torch, self.nf4, self.s, self.base = torch, nf4, stream, base
+        gen = torch.Generator(device=dev)
+        self.weights = []
+        with torch.cuda.stream(stream):
+            for layer in range(layers):
+                lw = {}
+                for i, (name, N, K) in enumerate(LINEARS):
+                    if only is not None and name not in only:
+                        continue
+                    gen.manual_seed(seed + 16 * layer + i)
+                    W = torch.randn((N, K), generator=gen, device=dev, dtype=torch.float32) * 0.02
+                    lw[name] = nf4.awq_pack_weight(W, stream=stream)
+                    del W
+                self.weights.append(lw)
+            self.lm_head = None
+            if with_head:
+                gen.manual_seed(seed + 16 * LAYERS)
+                W = torch.randn((VOCAB, HIDDEN), generator=gen, device=dev,
+                                dtype=torch.float32) * 0.02
+                self.lm_head = nf4.awq_pack_weight(W, stream=stream)
+                del W
+        stream.synchronize()
+        torch.cuda.empty_cache()
+        self.ws_bytes = max(nf4.nf4_awq_workspace_bytes(M, N, K)
+                            for M in (1, TAIL_M, PREFILL_M) for _, N, K in LINEARS)
+        self.ws = torch.zeros(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def packed(self, name, layer):
+        return self.lm_head if name == "lm_head" else self.weights[layer][name]
+
+    def gemv(self, name, layer):
+        aw, b = self.packed(name, layer), self.base
+        self.nf4.nf4_awq_gemv(b.x1[aw.K], 1, aw.qweight, aw.params, aw.N, aw.K, b.y1[name],
+                              self.ws, self.ws_bytes)
+
+    def gemm(self, name, layer, M=PREFILL_M):
+        aw, b = self.weights[layer][name], self.base
+        self.nf4.nf4_awq_gemm(b.xp[aw.K], M, aw.qweight, aw.params, aw.N, aw.K, b.yp[name],
+                              self.ws, self.ws_bytes)
+
+
 def decode_labels():
     return [name for _ in range(LAYERS) for name, _, _ in LINEARS] + ["lm_head"]
 
@@ -244,6 +308,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-int4", action="store_true",
+                    help="skip the int4 group-128 format's decode and prefill measurements")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--seed", type=int, default=0x4E4634)
     ap.add_argument("--dominant-replays", type=int, default=9)
@@ -429,10 +495,110 @@ def main():
                              "kernel": f"nf4_gemm gate|up N={N} K={K} M={PREFILL_M}",
                              "algorithmic_flop": gm_flop, "launch_us": round(gemm_us, 2)},
     }
+    if not args.no_int4:
+        del g_dec, g_pre
+        out["int4_group128"] = int4_leg(torch, nf4, args, s, mdl, launches)
+        if args.launch_log:
+            with open(args.launch_log, "w") as f:
+                json.dump(launches, f)
     if not args.no_cpu:
         log("[bench] timing the CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def int4_leg(torch, nf4, args, s, mdl, launches):
+    """Decode (M=1) and prefill (M=1024) steps and the gate|up rooflines for
+    the int4 group-128 format; launch labels go to `launches` as int4:<linear>."""
+    import numpy as np
+    t0 = time.perf_counter()
+    amdl = AwqModel(torch, nf4, args.seed, s, mdl)
+    log(f"[bench] int4: packed {LAYERS} layers + lm_head in {time.perf_counter() - t0:.1f} s")
+    dec_labels = ["int4:" + n for n in decode_labels()]
+    pre_labels = ["int4:" + n for n in prefill_labels()]
+    decode_bytes = sum(awq_packed_bytes(N, K) for _, N, K in LINEARS) * LAYERS \
+        + awq_packed_bytes(VOCAB, HIDDEN)
+    prefill_flop = 2 * PREFILL_M * sum(N * K for _, N, K in LINEARS) * LAYERS
+
+    def decode_step():
+        for layer in range(LAYERS):
+            for name, _, _ in LINEARS:
+                amdl.gemv(name, layer)
+        amdl.gemv("lm_head", 0)
+
+    def prefill_step():
+        for layer in range(LAYERS):
+            for name, _, _ in LINEARS:
+                amdl.gemm(name, layer)
+
+    with torch.cuda.stream(s):
+        decode_step()
+        prefill_step()
+    s.synchronize()
+    launches += [("gemv", n) for n in dec_labels] + [("gemm", n) for n in pre_labels]
+    g_dec, g_pre = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_dec, stream=s):
+        decode_step()
+    with torch.cuda.graph(g_pre, stream=s):
+        prefill_step()
+    s.synchronize()
+    with torch.cuda.stream(s):
+        for _ in range(args.warmup):
+            g_dec.replay()
+            g_pre.replay()
+    s.synchronize()
+    launches += ([("gemv", n) for n in dec_labels] + [("gemm", n) for n in pre_labels]) \
+        * args.warmup
+    name, N, K = DOMINANT
+    reps = args.dominant_replays
+    gemv_us = graph_ms(torch, s, lambda: [amdl.gemv(name, l) for l in range(LAYERS)],
+                       reps) * 1e3 / LAYERS
+    launches += [("gemv", "int4:" + name)] * (LAYERS * (reps + 1))
+    gemm_us = graph_ms(torch, s, lambda: [amdl.gemm(name, l) for l in range(LAYERS)],
+                       reps) * 1e3 / LAYERS
+    launches += [("gemm", "int4:" + name)] * (LAYERS * (reps + 1))
+    log(f"[bench] int4 dominant {name}: gemv {gemv_us:.2f} us, gemm {gemm_us:.2f} us per launch")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        for e0, e1, e2 in ev:
+            e0.record(s)
+            g_dec.replay()
+            e1.record(s)
+            g_pre.replay()
+            e2.record(s)
+    torch.cuda.synchronize()
+    launches += ([("gemv", n) for n in dec_labels] + [("gemm", n) for n in pre_labels]) \
+        * args.steps
+    dec_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in ev]))
+    pre_ms = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in ev]))
+    log(f"[bench] int4 {args.steps} timed steps: decode {dec_ms:.3f} ms, prefill {pre_ms:.3f} ms")
+    gv_bytes = awq_packed_bytes(N, K)
+    gv_gbps = gv_bytes / (gemv_us * 1e-6) / 1e9
+    gm_flop = 2 * PREFILL_M * N * K
+    gm_tflops = gm_flop / (gemm_us * 1e-6) / 1e12
+    del g_dec, g_pre, amdl
+    torch.cuda.empty_cache()
+    return {
+        "format": "asymmetric int4, groups of 128 along K, w = (q - z) * s, fp16 s",
+        "decode": {"value": round(decode_bytes / (dec_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                   "ms": round(dec_ms, 4), "packed_bytes": decode_bytes},
+        "prefill": {"value": round(prefill_flop / (pre_ms * 1e-3) / 1e12, 2),
+                    "unit": "TFLOP/s", "ms": round(pre_ms, 3),
+                    "note": "each nf4_awq_gemm = x-sum pre-pass + GEMM kernel"},
+        "roofline": {"bound": "hbm", "achieved": round(gv_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gv_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_bytes("awq_gemv"),
+                     "kernel": f"nf4_awq_gemv gate|up N={N} K={K} M=1",
+                     "algorithmic_bytes": gv_bytes, "launch_us": round(gemv_us, 2)},
+        "roofline_prefill": {"bound": "mfma", "achieved": round(gm_tflops, 2),
+                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(gm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "traffic": traffic_bytes("awq_gemm"),
+                             "kernel": f"nf4_awq_gemm gate|up N={N} K={K} M={PREFILL_M}",
+                             "algorithmic_flop": gm_flop, "launch_us": round(gemm_us, 2)},
+    }
 
 
 def pmc_pass(torch, nf4, cb, seed, s):
@@ -453,7 +619,14 @@ def pmc_pass(torch, nf4, cb, seed, s):
             s.synchronize()
         mdl.gemm("gate_up", 0)
         s.synchronize()
-    log("[bench] pmc pass: copy 1 GiB, 3 x gate|up gemv, 1 x gate|up gemm")
+    amdl = AwqModel(torch, nf4, seed, s, mdl, layers=3, with_head=False, only=("gate_up",))
+    with torch.cuda.stream(s):
+        for layer in range(3):
+            amdl.gemv("gate_up", layer)
+            s.synchronize()
+        amdl.gemm("gate_up", 0)
+        s.synchronize()
+    log("[bench] pmc pass: copy 1 GiB, 3 x gate|up gemv, 1 x gate|up gemm, both formats")
 
 
 def _kernel_short(name):
