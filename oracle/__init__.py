@@ -266,6 +266,24 @@ def awq_linear(x_bf16: np.ndarray, packed: np.ndarray, scales: np.ndarray, zeros
     return y, bound
 
 
+# Act-order checkpoints (vibevoice.c README, "Quantization" > "Weights", the
+# GPTQ act-order bullet): the input channels were quantized in order of
+# importance, so a group's channels are scattered over K.  The loader sorts
+# the channels by group, which makes every group a contiguous run of 128, and
+# keeps that order; the decoder gathers the activations through it before the
+# product: y = sum_j x[perm[j]] * W[n][perm[j]].
+def act_order_perm(g_idx: np.ndarray) -> np.ndarray:
+    """Channel order sorted by group, channels of one group in ascending
+    order (a stable sort of the group index): perm[j] = the j-th channel."""
+    g_idx = np.asarray(g_idx)
+    return np.argsort(g_idx, kind="stable").astype(np.int32)
+
+
+def gather_columns(x: np.ndarray, perm: np.ndarray) -> np.ndarray:
+    """x_out[m][j] = x[m][perm[j]]."""
+    return np.ascontiguousarray(np.asarray(x)[:, np.asarray(perm)])
+
+
 # ---------------------------------------------------------------- acceptance
 REL_L2 = 1e-5
 ELEM = 1e-4

@@ -114,3 +114,59 @@ def test_codes_round_trip_through_the_canonical_packing():
 def test_rejects_k_not_a_multiple_of_128():
     with pytest.raises(ValueError):
         oracle.awq_quantize(np.zeros((16, 192), np.float32))
+
+
+# ------------------------------------------------------ act-order gather
+def test_act_order_perm_sorts_channels_by_group_stably():
+    g_idx = np.array([1, 0, 1, 0, 2, 1, 0, 2])
+    perm = oracle.act_order_perm(g_idx)
+    np.testing.assert_array_equal(perm, [1, 3, 6, 0, 2, 5, 4, 7])
+    assert perm.dtype == np.int32
+
+
+def test_act_order_perm_makes_groups_contiguous():
+    rng = np.random.default_rng(11)
+    K = 1024
+    g_idx = rng.permutation(np.repeat(np.arange(K // G), G))  # scattered groups of 128
+    perm = oracle.act_order_perm(g_idx)
+    assert sorted(perm.tolist()) == list(range(K))
+    np.testing.assert_array_equal(g_idx[perm], np.repeat(np.arange(K // G), G))
+    for g in range(K // G):
+        run = perm[g * G:(g + 1) * G]
+        assert np.all(np.diff(run) > 0)  # ascending within a group
+
+
+def test_gather_columns_by_hand_and_inverse():
+    x = np.arange(12, dtype=np.uint16).reshape(2, 6)
+    perm = np.array([5, 0, 3, 1, 4, 2], np.int32)
+    np.testing.assert_array_equal(oracle.gather_columns(x, perm),
+                                  [[5, 0, 3, 1, 4, 2], [11, 6, 9, 7, 10, 8]])
+    rng = np.random.default_rng(12)
+    x = rng.integers(0, 1 << 16, (3, 256), dtype=np.uint16)
+    p = rng.permutation(256).astype(np.int32)
+    inv = np.empty_like(p)
+    inv[p] = np.arange(256, dtype=np.int32)
+    np.testing.assert_array_equal(oracle.gather_columns(oracle.gather_columns(x, p), inv), x)
+    ident = np.arange(256, dtype=np.int32)
+    np.testing.assert_array_equal(oracle.gather_columns(x, ident), x)
+
+
+def test_act_order_pipeline_computes_x_times_w():
+    """Quantize the channel-sorted weight, gather x through the same order:
+    the oracle's linear equals x @ W'^T with W' the dequantized weight put
+    back into the checkpoint's channel order (numpy float64; only the order
+    of the sum differs)."""
+    rng = np.random.default_rng(13)
+    N, K, M = 48, 512, 3
+    g_idx = rng.permutation(np.repeat(np.arange(K // G), G))
+    perm = oracle.act_order_perm(g_idx)
+    W = synth.weights(0, 4, 1, N, K)
+    codes, scales, zeros = oracle.awq_quantize(oracle.gather_columns(W, perm))
+    packed = oracle.pack(codes)
+    x = synth.activations(0, M, K, stream=4)
+    y, _ = oracle.awq_linear(oracle.gather_columns(x, perm), packed, scales, zeros)
+    deq_sorted = oracle.awq_dequant(packed, scales, zeros).astype(np.float64)
+    Wp = np.empty_like(deq_sorted)
+    Wp[:, perm] = deq_sorted
+    xf = synth.bf16_bits_to_fp32(x).astype(np.float64)
+    np.testing.assert_allclose(y, xf @ Wp.T, rtol=1e-12, atol=1e-12)
