@@ -324,6 +324,15 @@ nf4_status nf4_awq_dequant(const uint8_t *qweight, const uint32_t *params, int64
   return from_hip(nf4::launch_awq_dequant(qweight, params, N, K, W_out, stream));
 }
 
+nf4_status nf4_gather_columns(const uint16_t *x, int64_t M, int64_t K, const int32_t *perm,
+                              uint16_t *x_out, hipStream_t stream) {
+  if (!x || !perm || !x_out) return NF4_ERR_NULL;
+  if (M < 1 || M > kMaxGemmM || K < 8 || K % 8 != 0 || K > kMaxDim || M * K > kMaxElems)
+    return NF4_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(perm) || !aligned16(x_out)) return NF4_ERR_ALIGN;
+  return from_hip(nf4::launch_gather_columns(x, M, K, perm, x_out, stream));
+}
+
 }  // extern "C"
 
 namespace {

@@ -76,6 +76,9 @@ hipError_t launch_awq_unpack(const uint8_t *qw, const uint32_t *pr, int64_t N, i
                              uint8_t *codes, uint16_t *scales, uint8_t *zeros, hipStream_t s);
 hipError_t launch_awq_dequant(const uint8_t *qw, const uint32_t *pr, int64_t N, int64_t K,
                               float *out, hipStream_t s);
+// out[m][j] = x[m][perm[j]] (bf16 bits), K % 8 == 0; perm clamped to [0, K).
+hipError_t launch_gather_columns(const uint16_t *x, int64_t M, int64_t K, const int32_t *perm,
+                                 uint16_t *out, hipStream_t s);
 // The packed matrix of the next GEMV launch, named so that the current
 // launch can read its first tiles ahead (a hint: results never depend on it).
 struct NextMatrix {

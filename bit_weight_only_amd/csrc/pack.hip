@@ -335,6 +335,36 @@ __global__ __launch_bounds__(256) void awq_dequant_kernel(const uint4 *__restric
   }
 }
 
+// Activation gather of act-order checkpoints (vibevoice.c README,
+// "Quantization" > "Weights", the GPTQ act-order bullet: the loader sorts
+// the input channels by group and the decoder gathers x through that order
+// before the product): out[m][j] = x[m][perm[j]].  One thread writes 8
+// consecutive outputs as one 16-byte store; perm values outside [0, K) are
+// clamped into it.
+__global__ __launch_bounds__(256) void gather_columns_kernel(const uint16_t *__restrict__ x,
+                                                             int64_t K,
+                                                             const int32_t *__restrict__ perm,
+                                                             uint16_t *__restrict__ out,
+                                                             int64_t nchunks) {
+  const int64_t kc = K / 8;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nchunks;
+       c += (int64_t)gridDim.x * 256) {
+    const int64_t m = c / kc, j0 = (c - m * kc) * 8;
+    const int4 p0 = *reinterpret_cast<const int4 *>(perm + j0);
+    const int4 p1 = *reinterpret_cast<const int4 *>(perm + j0 + 4);
+    const int p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    const uint16_t *row = x + m * K;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t a = p[2 * i] < 0 ? 0 : p[2 * i] >= K ? K - 1 : p[2 * i];
+      const int64_t b = p[2 * i + 1] < 0 ? 0 : p[2 * i + 1] >= K ? K - 1 : p[2 * i + 1];
+      w[i] = (uint32_t)row[a] | ((uint32_t)row[b] << 16);
+    }
+    *reinterpret_cast<uint4 *>(out + m * K + j0) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 inline dim3 tile_grid(int64_t ntiles) {
   return dim3((unsigned)((ntiles + kWavesPerBlock - 1) / kWavesPerBlock));
 }
@@ -406,6 +436,16 @@ hipError_t launch_awq_dequant(const uint8_t *qw, const uint32_t *pr, int64_t N, 
   const int64_t KT = tiles_k(K), ntiles = (N / kTileRows) * KT;
   hipLaunchKernelGGL(awq_dequant_kernel, tile_grid(ntiles), dim3(256), 0, s,
                      reinterpret_cast<const uint4 *>(qw), pr, K, KT, ntiles, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_columns(const uint16_t *x, int64_t M, int64_t K, const int32_t *perm,
+                                 uint16_t *out, hipStream_t s) {
+  const int64_t nchunks = M * (K / 8);
+  int64_t blocks = (nchunks + 255) / 256;
+  if (blocks > (int64_t(1) << 20)) blocks = int64_t(1) << 20;  // grid-stride beyond
+  hipLaunchKernelGGL(gather_columns_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, K, perm,
+                     out, nchunks);
   return hipGetLastError();
 }
 

@@ -21,7 +21,7 @@ EXPORTS = ("nf4_status_string", "nf4_qweight_bytes", "nf4_absmax_bytes", "nf4_wo
            "nf4_pack", "nf4_dequant", "nf4_repack", "nf4_unpack", "nf4_gemv", "nf4_gemm",
            "nf4_gemv_argmax_workspace_bytes", "nf4_gemv_argmax", "nf4_gemv_prefetch",
            "nf4_awq_params_bytes", "nf4_awq_workspace_bytes", "nf4_awq_pack", "nf4_awq_repack",
-           "nf4_awq_unpack", "nf4_awq_dequant", "nf4_awq_gemv", "nf4_awq_gemm")
+           "nf4_awq_unpack", "nf4_awq_dequant", "nf4_gather_columns", "nf4_awq_gemv", "nf4_awq_gemm")
 
 _lib = None
 
@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.nf4_awq_unpack.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp]
         L.nf4_awq_dequant.restype = st
         L.nf4_awq_dequant.argtypes = [vp, vp, i64, i64, vp, vp]
+        L.nf4_gather_columns.restype = st
+        L.nf4_gather_columns.argtypes = [vp, i64, i64, vp, vp, vp]
         for f in (L.nf4_awq_gemv, L.nf4_awq_gemm):
             f.restype = st
             f.argtypes = [vp, i64, vp, vp, i64, i64, vp, vp, sz, vp]
@@ -206,6 +208,11 @@ def nf4_awq_unpack(qweight, params, N: int, K: int, codes, scales, zeros, stream
 def nf4_awq_dequant(qweight, params, N: int, K: int, W_out, stream=None) -> None:
     _check(lib().nf4_awq_dequant(_ptr(qweight), _ptr(params), N, K, _ptr(W_out),
                                  _stream(stream)), "nf4_awq_dequant")
+
+
+def nf4_gather_columns(x, M: int, K: int, perm, x_out, stream=None) -> None:
+    _check(lib().nf4_gather_columns(_ptr(x), M, K, _ptr(perm), _ptr(x_out), _stream(stream)),
+           "nf4_gather_columns")
 
 
 def nf4_awq_gemv(x, M: int, qweight, params, N: int, K: int, y, workspace=None,

@@ -228,6 +228,20 @@ nf4_status nf4_awq_unpack(const uint8_t *qweight, const uint32_t *params, int64_
 nf4_status nf4_awq_dequant(const uint8_t *qweight, const uint32_t *params, int64_t N, int64_t K,
                            float *W_out, hipStream_t stream);
 
+/* Activation gather for act-order checkpoints (vibevoice.c README,
+ * "Quantization" > "Weights", the GPTQ act-order bullet): such checkpoints
+ * quantized the input channels in order of importance, so a group's channels
+ * are scattered over K.  Sorting the channels by group at load (a stable sort
+ * of the per-channel group index; perm[j] = the j-th channel) makes every
+ * group a contiguous run that nf4_awq_pack / nf4_awq_repack and the linears
+ * take as is, and the decoder then gathers x through the same order before
+ * the product: x_out[m][j] = x[m][perm[j]] (bf16 bit patterns, [M][K]
+ * row-major).  perm: device int32[K]; values outside [0, K) are clamped into
+ * it.  1 <= M <= 2^23, K % 8 == 0 (else NF4_ERR_SHAPE); x, perm and x_out
+ * 16-byte aligned device buffers; x_out must not overlap x. */
+nf4_status nf4_gather_columns(const uint16_t *x, int64_t M, int64_t K, const int32_t *perm,
+                              uint16_t *x_out, hipStream_t stream);
+
 /* Decode GEMV of the int4 format, 1 <= M <= 8:
  * y[m][n] = sum_t s[n][t] * sum_{k in group t} x[m][k] * (q[n][k] - z[n][t]),
  * fp32 accumulation: per group the matrix cores add the exact products

@@ -258,3 +258,16 @@ def test_awq_linear_validation():
     assert g(A, 8, A, A, 16, 18944, A, A, need - 1, None) == nf4.NF4_ERR_WORKSPACE
     # byte offsets past 32 bits
     assert m(A, 1 << 17, A, A, 16, 1 << 14, A, A, 1 << 40, None) == nf4.NF4_ERR_SHAPE
+
+
+def test_gather_validation():
+    f = lambda *a: call("nf4_gather_columns", *a)
+    ok = [A, 4, 3584, A, A, None]
+    for i in (0, 3, 4):
+        bad = list(ok)
+        bad[i] = None
+        assert f(*bad) == nf4.NF4_ERR_NULL, i
+        bad[i] = A + 4
+        assert f(*bad) == nf4.NF4_ERR_ALIGN, i
+    for M, K in ((0, 128), (1, 0), (1, 4), (1, 100), (1 << 24, 128)):
+        assert f(A, M, K, A, A, None) == nf4.NF4_ERR_SHAPE, (M, K)

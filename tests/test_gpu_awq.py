@@ -271,3 +271,56 @@ def test_awq_long_prefill_one_call(side):
     picks = np.concatenate([np.arange(14336, M)] + [[c, c + 1023] for c in range(0, 14336, 1024)])
     yr, b = oracle.awq_linear(x[picks], packed, scales, zeros)
     assert_linear_ok(y[picks][:, rows], yr, b, "awq long prefill")
+
+
+# ------------------------------------------------------------ act-order gather
+def gather_dev(side, x_bits, perm):
+    t = side.torch
+    M, K = x_bits.shape
+    xd = side.x_dev(x_bits)
+    pd = side.to_dev(np.ascontiguousarray(perm, np.int32))
+    out = t.empty((M, K), dtype=t.int16, device="cuda")
+    side.stream.wait_stream(t.cuda.current_stream())
+    side.nf4.nf4_gather_columns(xd, M, K, pd, out, stream=side.stream)
+    side.sync()
+    return out
+
+
+@pytest.mark.parametrize("M,K", [(1, 8), (3, 128), (1, 3584), (5, 18944), (1024, 3584)])
+def test_gather_columns_bit_exact(side, M, K):
+    say(f"[gather] M={M} K={K}")
+    rng = np.random.default_rng(K + M)
+    perm = rng.permutation(K).astype(np.int32)
+    x = synth.activations(0, M, K, stream=21)
+    got = gather_dev(side, x, perm).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, oracle.gather_columns(x, perm))
+
+
+def test_gather_columns_clamps_out_of_range(side):
+    K = 256
+    perm = np.arange(K, dtype=np.int32)[::-1].copy()
+    perm[[0, 7, 100]] = [-5, K, 1 << 30]
+    x = synth.activations(0, 2, K, stream=22)
+    got = gather_dev(side, x, perm).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, oracle.gather_columns(x, np.clip(perm, 0, K - 1)))
+
+
+@pytest.mark.parametrize("kind,M", [("gemv", 1), ("gemv", 2), ("gemm", 64), ("gemm", 300)])
+def test_act_order_pipeline(side, kind, M):
+    """Scattered groups: the channel order sorted by group on the host (the
+    loader's step), the sorted weight packed on the GPU, x gathered on the GPU
+    through the same order, then the int4 linear; against the oracle's
+    pipeline on the same seeded inputs."""
+    N, K = 512, 3584
+    say(f"[act-order {kind}] M={M} N={N} K={K}")
+    rng = np.random.default_rng(31)
+    g_idx = rng.permutation(np.repeat(np.arange(K // 128), 128))
+    perm = oracle.act_order_perm(g_idx)
+    W = synth.weights(0, 5, 2, N, K)
+    Ws = oracle.gather_columns(W, perm)
+    aw, packed, scales, zeros = check_pack(side, Ws)
+    x = synth.activations(0, M, K, stream=23)
+    xg = gather_dev(side, x, perm)
+    y = side.awq_linear(kind, xg, M, aw).cpu().numpy()
+    yr, b = oracle.awq_linear(oracle.gather_columns(x, perm), packed, scales, zeros)
+    assert_linear_ok(y, yr, b, f"act-order {kind} M={M}")
