@@ -16,8 +16,9 @@ included); prefill TFLOP/s sits beside it.
 
 `int4_group128` repeats decode, prefill and both rooflines with the same
 seeded weights quantized to the second format, asymmetric int4 in groups of
-128 (nf4_awq_pack; nf4_awq_gemv / nf4_awq_gemm; algorithmic bytes N K / 2 +
-4 N K / 128: codes and one 4-byte (s, z) per group).
+128 (nf4_awq_pack; nf4_awq_gemv_prefetch with the same read-ahead hints /
+nf4_awq_gemm; algorithmic bytes N K / 2 + 4 N K / 128: codes and one 4-byte
+(s, z) per group).
 
 `roofline` covers the dominant decode kernel (the gate|up GEMV, 28 launches
 per step): its 28 launches on distinct weights are replayed back to back in
@@ -66,13 +67,13 @@ DOMINANT = ("gate_up", 2 * MLP, HIDDEN)
 # `python bench.py --pmc-pass` (profiles/hbm_traffic_gate_up.md): counter KiB
 # per dispatch and the calibration of each counter on a plain 1 GiB copy.
 TRAFFIC = {
-    "gemv": {"source": "gemv.hip", "fetch_kib": 42731, "write_kib": 148,
-             "sha256": "6376bb178b9be91a2dce5ee4b73091ccda54ebbdf43941092678f94087a9c7fe"},
-    "gemm": {"source": "gemm.hip", "fetch_kib": 180720, "write_kib": 153694,
+    "gemv": {"source": "gemv.hip", "fetch_kib": 42729, "write_kib": 148,
+             "sha256": "4865fef77e624e1aac6e1b49863fe8ac5766ee26b1b65a189a0c0e0ce9226844"},
+    "gemm": {"source": "gemm.hip", "fetch_kib": 180721, "write_kib": 153259,
              "sha256": "9c0581cd848c56dce6dbccf425c0622202cd7fa028f23a8938544c4501dc2575"},
-    "awq_gemv": {"source": "gemv.hip", "fetch_kib": 35460, "write_kib": 148,
-                 "sha256": "6376bb178b9be91a2dce5ee4b73091ccda54ebbdf43941092678f94087a9c7fe"},
-    "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180885, "write_kib": 153636,
+    "awq_gemv": {"source": "gemv.hip", "fetch_kib": 40366, "write_kib": 148,
+                 "sha256": "4865fef77e624e1aac6e1b49863fe8ac5766ee26b1b65a189a0c0e0ce9226844"},
+    "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180882, "write_kib": 152888,
                  "sha256": "9c0581cd848c56dce6dbccf425c0622202cd7fa028f23a8938544c4501dc2575"},
 }
 COPY_CALIBRATION = {"fetch_kib_per_gib": 524308, "write_kib_per_gib": 1048576}
@@ -260,10 +261,18 @@ class AwqModel:
     def packed(self, name, layer):
         return self.lm_head if name == "lm_head" else self.weights[layer][name]
 
-    def gemv(self, name, layer):
+    def gemv(self, name, layer, nxt=None):
+        """One decode GEMV; nxt = (name, layer) of the next launch, named as
+        a read-ahead hint (nf4_awq_gemv_prefetch)."""
         aw, b = self.packed(name, layer), self.base
-        self.nf4.nf4_awq_gemv(b.x1[aw.K], 1, aw.qweight, aw.params, aw.N, aw.K, b.y1[name],
-                              self.ws, self.ws_bytes)
+        if nxt is None:
+            self.nf4.nf4_awq_gemv(b.x1[aw.K], 1, aw.qweight, aw.params, aw.N, aw.K, b.y1[name],
+                                  self.ws, self.ws_bytes)
+        else:
+            na = self.packed(*nxt)
+            self.nf4.nf4_awq_gemv_prefetch(b.x1[aw.K], 1, aw.qweight, aw.params, aw.N, aw.K,
+                                           b.y1[name], self.ws, self.ws_bytes, na.qweight,
+                                           na.params, na.N, na.K)
 
     def gemm(self, name, layer, M=PREFILL_M):
         aw, b = self.weights[layer][name], self.base
@@ -520,11 +529,12 @@ def int4_leg(torch, nf4, args, s, mdl, launches):
         + awq_packed_bytes(VOCAB, HIDDEN)
     prefill_flop = 2 * PREFILL_M * sum(N * K for _, N, K in LINEARS) * LAYERS
 
+    order = [(name, layer) for layer in range(LAYERS) for name, _, _ in LINEARS] + \
+        [("lm_head", 0)]
+
     def decode_step():
-        for layer in range(LAYERS):
-            for name, _, _ in LINEARS:
-                amdl.gemv(name, layer)
-        amdl.gemv("lm_head", 0)
+        for i, (name, layer) in enumerate(order):
+            amdl.gemv(name, layer, order[i + 1] if i + 1 < len(order) else None)
 
     def prefill_step():
         for layer in range(LAYERS):
@@ -551,8 +561,8 @@ def int4_leg(torch, nf4, args, s, mdl, launches):
         * args.warmup
     name, N, K = DOMINANT
     reps = args.dominant_replays
-    gemv_us = graph_ms(torch, s, lambda: [amdl.gemv(name, l) for l in range(LAYERS)],
-                       reps) * 1e3 / LAYERS
+    gemv_us = graph_ms(torch, s, lambda: [amdl.gemv(name, l, (name, (l + 1) % LAYERS))
+                                          for l in range(LAYERS)], reps) * 1e3 / LAYERS
     launches += [("gemv", "int4:" + name)] * (LAYERS * (reps + 1))
     gemm_us = graph_ms(torch, s, lambda: [amdl.gemm(name, l) for l in range(LAYERS)],
                        reps) * 1e3 / LAYERS
@@ -622,7 +632,7 @@ def pmc_pass(torch, nf4, cb, seed, s):
     amdl = AwqModel(torch, nf4, seed, s, mdl, layers=3, with_head=False, only=("gate_up",))
     with torch.cuda.stream(s):
         for layer in range(3):
-            amdl.gemv("gate_up", layer)
+            amdl.gemv("gate_up", layer, ("gate_up", (layer + 1) % 3))
             s.synchronize()
         amdl.gemm("gate_up", 0)
         s.synchronize()

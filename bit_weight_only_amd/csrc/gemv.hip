@@ -339,7 +339,10 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
   float *red = reinterpret_cast<float *>(lds_dyn + M * XS / 2);
   uint16_t *codes_lds = reinterpret_cast<uint16_t *>(red);  // until the table is built
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index as a scalar: every per-wave quantity below (tile cursor,
+  // share end, read-ahead cursor, trip count) stays in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
   const int r = lane & 15, h = lane >> 4;
   const int g0 = (int)((int64_t)G * blockIdx.x / P), g1 = (int)((int64_t)G * (blockIdx.x + 1) / P);
   const int Gw = g1 - g0, T0 = g0 * KT, Twg = Gw * KT;
@@ -514,7 +517,7 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
       __builtin_amdgcn_sched_barrier(kSchedAllButGlobalLoads);
       {
         const bool dead = ptau >= tile_end;
-        const bool ahead = !AFF && dead && pn < ntile_end;  // no read-ahead in the affine variant
+        const bool ahead = dead && pn < ntile_end;
         const uint32_t lt = ahead ? pn : dead ? (uint32_t)T0 : ptau;
         const char *qsrc = ahead ? nq : qbase;
         const char *ssrc = ahead ? nsb : sbase;
@@ -657,12 +660,12 @@ hipError_t launch_fast(const uint16_t *x, const uint4 *qw, const float2 *am, con
   // the next launch's partition, if it takes this fast path with the same M
   const char *nq = nullptr, *nsb = nullptr;
   int nG = 0, nKT = 0, nP = 0;
-  if (next != nullptr && next->qw != nullptr && fast_eligible(M, next->N, next->K, 1)) {
+  if (next != nullptr && next->qw != nullptr && fast_eligible(M, next->N, next->K, 1, AFF)) {
     nq = reinterpret_cast<const char *>(next->qw);
     nsb = reinterpret_cast<const char *>(next->am);
     nG = (int)(next->N / kTileRows);
     nKT = (int)tiles_k(next->K);
-    nP = fast_plan(M, next->N, next->K).P;
+    nP = fast_plan(M, next->N, next->K, AFF).P;
   }
   hipLaunchKernelGGL((gemv_fast_kernel<M, ARGMAX, AFF>), dim3(p.P), dim3(kFastWaves * 64), p.lds, s, x,
                      qw, am, ct, (int)N, (int)K, (int)tiles_k(K), (int)(N / kTileRows), p.P, y,
@@ -792,19 +795,20 @@ bool awq_gemv_fast_eligible(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_awq_gemv_fast(const uint16_t *x, int M, const uint8_t *qw, const uint32_t *pr,
-                                int64_t N, int64_t K, float *y, hipStream_t s) {
+                                int64_t N, int64_t K, float *y, hipStream_t s,
+                                const NextMatrix *next) {
   const uint4 *q = reinterpret_cast<const uint4 *>(qw);
   const float2 *a = reinterpret_cast<const float2 *>(pr);
   const CodeTerms ct = identity_terms();
   switch (M) {
-    case 1: return launch_fast<1, false, true>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, nullptr);
-    case 2: return launch_fast<2, false, true>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, nullptr);
-    case 3: return launch_fast<3, false, true>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, nullptr);
-    case 4: return launch_fast<4, false, true>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, nullptr);
-    case 5: return launch_fast<5, false, true>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, nullptr);
-    case 6: return launch_fast<6, false, true>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, nullptr);
-    case 7: return launch_fast<7, false, true>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, nullptr);
-    case 8: return launch_fast<8, false, true>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, nullptr);
+    case 1: return launch_fast<1, false, true>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, next);
+    case 2: return launch_fast<2, false, true>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, next);
+    case 3: return launch_fast<3, false, true>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, next);
+    case 4: return launch_fast<4, false, true>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, next);
+    case 5: return launch_fast<5, false, true>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, next);
+    case 6: return launch_fast<6, false, true>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, next);
+    case 7: return launch_fast<7, false, true>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, next);
+    case 8: return launch_fast<8, false, true>(x, q, a, ct, N, K, y, nullptr, nullptr, nullptr, s, next);
     default: return hipErrorInvalidValue;
   }
 }

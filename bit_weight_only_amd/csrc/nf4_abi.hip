@@ -367,6 +367,31 @@ nf4_status nf4_awq_gemv(const uint16_t *x, int64_t M, const uint8_t *qweight,
   return from_hip(nf4::launch_awq_gemm(x, M, qweight, params, N, K, y, workspace, stream));
 }
 
+nf4_status nf4_awq_gemv_prefetch(const uint16_t *x, int64_t M, const uint8_t *qweight,
+                                 const uint32_t *params, int64_t N, int64_t K, float *y,
+                                 void *workspace, size_t ws_bytes, const uint8_t *next_qweight,
+                                 const uint32_t *next_params, int64_t next_N, int64_t next_K,
+                                 hipStream_t stream) {
+  nf4_status st = check_awq_linear(x, M, qweight, params, N, K, y, kMaxGemvM);
+  if (st != NF4_OK) return st;
+  nf4::NextMatrix next;
+  if (next_qweight != nullptr) {
+    if (!next_params) return NF4_ERR_NULL;
+    if (!aligned16(next_qweight) || !aligned16(next_params)) return NF4_ERR_ALIGN;
+    if (!awq_shape_ok(next_N, next_K)) return NF4_ERR_SHAPE;
+    next.qw = next_qweight;
+    next.am = reinterpret_cast<const float *>(next_params);
+    next.N = next_N;
+    next.K = next_K;
+  }
+  if (nf4::awq_gemv_fast_eligible(M, N, K))
+    return from_hip(nf4::launch_awq_gemv_fast(x, (int)M, qweight, params, N, K, y, stream,
+                                              next_qweight ? &next : nullptr));
+  st = check_awq_workspace(M, N, K, workspace, ws_bytes);
+  if (st != NF4_OK) return st;
+  return from_hip(nf4::launch_awq_gemm(x, M, qweight, params, N, K, y, workspace, stream));
+}
+
 nf4_status nf4_awq_gemm(const uint16_t *x, int64_t M, const uint8_t *qweight,
                         const uint32_t *params, int64_t N, int64_t K, float *y, void *workspace,
                         size_t ws_bytes, hipStream_t stream) {

@@ -159,7 +159,8 @@ __device__ inline uint32_t awq_pair(uint32_t wd, int q, uint32_t magic_v) {
 // runs the tiled kernel with the affine fold.
 bool awq_gemv_fast_eligible(int64_t M, int64_t N, int64_t K);
 hipError_t launch_awq_gemv_fast(const uint16_t *x, int M, const uint8_t *qw, const uint32_t *pr,
-                                int64_t N, int64_t K, float *y, hipStream_t s);
+                                int64_t N, int64_t K, float *y, hipStream_t s,
+                                const NextMatrix *next = nullptr);
 bool awq_gemm_supported(int64_t M, int64_t N, int64_t K);
 size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_awq_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, const uint32_t *pr,

@@ -21,7 +21,7 @@ EXPORTS = ("nf4_status_string", "nf4_qweight_bytes", "nf4_absmax_bytes", "nf4_wo
            "nf4_pack", "nf4_dequant", "nf4_repack", "nf4_unpack", "nf4_gemv", "nf4_gemm",
            "nf4_gemv_argmax_workspace_bytes", "nf4_gemv_argmax", "nf4_gemv_prefetch",
            "nf4_awq_params_bytes", "nf4_awq_workspace_bytes", "nf4_awq_pack", "nf4_awq_repack",
-           "nf4_awq_unpack", "nf4_awq_dequant", "nf4_gather_columns", "nf4_awq_gemv", "nf4_awq_gemm")
+           "nf4_awq_unpack", "nf4_awq_dequant", "nf4_gather_columns", "nf4_awq_gemv_prefetch", "nf4_awq_gemv", "nf4_awq_gemm")
 
 _lib = None
 
@@ -78,6 +78,9 @@ def lib() -> ctypes.CDLL:
         L.nf4_awq_unpack.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp]
         L.nf4_awq_dequant.restype = st
         L.nf4_awq_dequant.argtypes = [vp, vp, i64, i64, vp, vp]
+        L.nf4_awq_gemv_prefetch.restype = st
+        L.nf4_awq_gemv_prefetch.argtypes = [vp, i64, vp, vp, i64, i64, vp, vp, sz, vp, vp, i64,
+                                            i64, vp]
         L.nf4_gather_columns.restype = st
         L.nf4_gather_columns.argtypes = [vp, i64, i64, vp, vp, vp]
         for f in (L.nf4_awq_gemv, L.nf4_awq_gemm):
@@ -219,6 +222,15 @@ def nf4_awq_gemv(x, M: int, qweight, params, N: int, K: int, y, workspace=None,
                  ws_bytes: int = 0, stream=None) -> None:
     _check(lib().nf4_awq_gemv(_ptr(x), M, _ptr(qweight), _ptr(params), N, K, _ptr(y),
                               _ptr(workspace), ws_bytes, _stream(stream)), "nf4_awq_gemv")
+
+
+def nf4_awq_gemv_prefetch(x, M: int, qweight, params, N: int, K: int, y, workspace=None,
+                          ws_bytes: int = 0, next_qweight=None, next_params=None,
+                          next_N: int = 0, next_K: int = 0, stream=None) -> None:
+    _check(lib().nf4_awq_gemv_prefetch(_ptr(x), M, _ptr(qweight), _ptr(params), N, K, _ptr(y),
+                                       _ptr(workspace), ws_bytes, _ptr(next_qweight),
+                                       _ptr(next_params), next_N, next_K, _stream(stream)),
+           "nf4_awq_gemv_prefetch")
 
 
 def nf4_awq_gemm(x, M: int, qweight, params, N: int, K: int, y, workspace=None,

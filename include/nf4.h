@@ -255,6 +255,20 @@ nf4_status nf4_awq_gemv(const uint16_t *x, int64_t M, const uint8_t *qweight,
                         const uint32_t *params, int64_t N, int64_t K, float *y, void *workspace,
                         size_t ws_bytes, hipStream_t stream);
 
+/* nf4_awq_gemv plus the read-ahead hint of nf4_gemv_prefetch: the packed
+ * int4 matrix of the next GEMV launch on the stream (next_qweight,
+ * next_params, next_N x next_K), whose first tiles this launch loads after
+ * its own weights are in flight.  y is bit for bit that of nf4_awq_gemv.
+ * next_qweight == NULL means no hint; otherwise next_params must not be NULL,
+ * both 16-byte aligned, and the next shape one that nf4_awq_gemv accepts
+ * (else NF4_ERR_NULL, NF4_ERR_ALIGN, NF4_ERR_SHAPE).  The hint is ignored
+ * when this call runs the GEMM path. */
+nf4_status nf4_awq_gemv_prefetch(const uint16_t *x, int64_t M, const uint8_t *qweight,
+                                 const uint32_t *params, int64_t N, int64_t K, float *y,
+                                 void *workspace, size_t ws_bytes, const uint8_t *next_qweight,
+                                 const uint32_t *next_params, int64_t next_N, int64_t next_K,
+                                 hipStream_t stream);
+
 /* Prefill GEMM of the int4 format, any M >= 1: the result definition of
  * nf4_awq_gemv on the tiled matrix-core kernel, after a pre-pass that writes
  * the group sums of x into the workspace (nf4_awq_workspace_bytes(M, N, K)

@@ -271,3 +271,26 @@ def test_gather_validation():
         assert f(*bad) == nf4.NF4_ERR_ALIGN, i
     for M, K in ((0, 128), (1, 0), (1, 4), (1, 100), (1 << 24, 128)):
         assert f(A, M, K, A, A, None) == nf4.NF4_ERR_SHAPE, (M, K)
+
+
+def test_awq_prefetch_validation():
+    f = lambda *a: call("nf4_awq_gemv_prefetch", *a)
+    ok = [A, 1, A, A, 16, 128, A, None, 0, A, A, 32, 256, None]
+    for i in (0, 2, 3, 6):
+        bad = list(ok)
+        bad[i] = None
+        assert f(*bad) == nf4.NF4_ERR_NULL, i
+    bad = list(ok)
+    bad[1] = 9
+    assert f(*bad) == nf4.NF4_ERR_SHAPE
+    bad = list(ok)
+    bad[10] = None                      # next qweight without next params
+    assert f(*bad) == nf4.NF4_ERR_NULL
+    for i in (9, 10):
+        bad = list(ok)
+        bad[i] = A + 8
+        assert f(*bad) == nf4.NF4_ERR_ALIGN, i
+    for nN, nK in ((24, 128), (32, 64), (32, 192), (0, 128)):
+        bad = list(ok)
+        bad[11], bad[12] = nN, nK
+        assert f(*bad) == nf4.NF4_ERR_SHAPE, (nN, nK)

@@ -324,3 +324,43 @@ def test_act_order_pipeline(side, kind, M):
     y = side.awq_linear(kind, xg, M, aw).cpu().numpy()
     yr, b = oracle.awq_linear(oracle.gather_columns(x, perm), packed, scales, zeros)
     assert_linear_ok(y, yr, b, f"act-order {kind} M={M}")
+
+
+# ------------------------------------------------------------ read-ahead hint
+@pytest.mark.parametrize("M", [1, 2, 8])
+def test_awq_prefetch_hint_keeps_results_bitwise(side, M):
+    """A decode chain over the fused Qwen2-7B linears, each launch naming the
+    next one's matrix (and the last naming the first): y equals the plain
+    nf4_awq_gemv bit for bit, and the oracle's within the bar."""
+    t = side.torch
+    names = list(QWEN_FUSED)
+    rows = {n: sample_rows(QWEN_FUSED[n][0], 40 + i) for i, n in enumerate(names)}
+    aws, refs = {}, {}
+    for i, n in enumerate(names):
+        N, K = QWEN_FUSED[n]
+        W = synth.weights(2, 1, 70 + i, N, K)
+        aws[n] = side.awq_pack(W)
+        codes, scales, zeros = oracle.awq_quantize(W[rows[n]])
+        refs[n] = (oracle.pack(codes), scales, zeros)
+        del W
+    for i, n in enumerate(names):
+        N, K = QWEN_FUSED[n]
+        say(f"[awq prefetch] M={M} {n}")
+        aw, nx = aws[n], aws[names[(i + 1) % len(names)]]
+        x = synth.activations(2, M, K, stream=30 + i)
+        xd = side.x_dev(x)
+        ws_bytes = side.nf4.nf4_awq_workspace_bytes(M, N, K)
+        ws = t.empty(max(ws_bytes, 16), dtype=t.uint8, device="cuda")
+        y0 = t.empty((M, N), dtype=t.float32, device="cuda")
+        y1 = t.empty((M, N), dtype=t.float32, device="cuda")
+        side.stream.wait_stream(t.cuda.current_stream())
+        side.nf4.nf4_awq_gemv(xd, M, aw.qweight, aw.params, N, K, y0, ws, ws_bytes,
+                              stream=side.stream)
+        side.nf4.nf4_awq_gemv_prefetch(xd, M, aw.qweight, aw.params, N, K, y1, ws, ws_bytes,
+                                       nx.qweight, nx.params, nx.N, nx.K, stream=side.stream)
+        side.sync()
+        a, b = y0.cpu().numpy(), y1.cpu().numpy()
+        np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+        packed, scales, zeros = refs[n]
+        yr, bd = oracle.awq_linear(x, packed, scales, zeros)
+        assert_linear_ok(b[:, rows[n]], yr, bd, f"awq prefetch {n} M={M}")
