@@ -12,6 +12,9 @@
  * the product) both read one shared repacked weight layout (same README,
  * "Quantization" > "Weights": one row-major layout permuted inside each
  * 16-byte run so one load feeds both the GEMV and the matrix-core operand).
+ * A second 4-bit format, asymmetric int4 in groups of 128 with an integer
+ * zero point (the nf4_awq_* entry points at the end), shares the layout and
+ * the kernels.
  *
  * Conventions shared by every entry point
  *  - Every pointer except `codebook` is DEVICE memory owned by the caller.
