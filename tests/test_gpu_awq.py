@@ -12,7 +12,7 @@ Linear path (nf4_awq_gemv, nf4_awq_gemm): rel-L2 <= 1e-5 per call and every
 element within 1e-4 * sum_k |x*w|; exact where the arithmetic is exact
 (one-hot x); rows of the GEMM independent of the batch; shapes of Qwen2-7B
 (hidden 3584, MLP 18944, head 152064) at decode, M = 1024 prefill and a long
-M = 14449 prefill.
+M = 14449 prefill; the Voxtral decoder's fused linears at decode.
 """
 import numpy as np
 import pytest
@@ -20,7 +20,8 @@ import pytest
 import oracle
 from bit_weight_only_amd import synth
 
-from gpu_helpers import QWEN, QWEN_FUSED, Side, assert_linear_ok, oracle_awq_layer, say
+from gpu_helpers import (QWEN, QWEN_FUSED, VOXTRAL_FUSED, Side, assert_linear_ok,
+                         oracle_awq_layer, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -237,6 +238,20 @@ def test_awq_qwen_decode_full_size(side, name, M):
     y = side.awq_run("gemv", x, aw)
     yr, b = oracle.awq_linear(x, packed, scales, zeros)
     assert_linear_ok(y[:, rows], yr, b, f"awq qwen {name} M={M}")
+    assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("name", list(VOXTRAL_FUSED))
+def test_awq_voxtral_decode_full_size(side, name):
+    N, K = VOXTRAL_FUSED[name]
+    say(f"[awq gemv] voxtral {name} N={N} K={K}")
+    rows = sample_rows(N, 24)
+    aw, packed, scales, zeros = full_awq_case(side, 1, 110 + list(VOXTRAL_FUSED).index(name),
+                                              N, K, rows)
+    x = synth.activations(1, 1, K)
+    y = side.awq_run("gemv", x, aw)
+    yr, b = oracle.awq_linear(x, packed, scales, zeros)
+    assert_linear_ok(y[:, rows], yr, b, f"awq voxtral {name}")
     assert np.all(np.isfinite(y))
 
 
