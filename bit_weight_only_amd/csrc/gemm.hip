@@ -10,11 +10,12 @@
 // P = sum_k x*c in fp32 (exact products), then acc += s * P.
 //
 // Kernels:
-//   gemm_tile_kernel<RG>  codebooks whose values are bf16 (the default one):
-//     128 x 16 RG outputs per workgroup, RG waves of 64 x 32, copies straight
-//     from global memory into LDS rings, each wave expanding the code words
-//     of its own columns;
-//   gemm_skinny_kernel    few rows (below);
+//   gemm_tile_kernel<RG, AFF>  codebooks whose values are bf16 (the default
+//     one) and the asymmetric int4 format (AFF): 128 x 16 RG outputs per
+//     workgroup, RG waves of 64 x 32, copies straight from global memory
+//     into LDS rings, each wave expanding the code words of its own columns;
+//   gemm_skinny_kernel<MB, D, AFF>  few rows (below);
+//   xsum_kernel           the int4 format's per-group sums of x (pre-pass);
 //   gemm_kernel<3>        any finite codebook (each value split into three
 //     bf16 terms), and shapes whose byte offsets exceed 32 bits.
 // Within each kernel every output is the same sequence of operations

@@ -6,14 +6,20 @@
 // into the multiply-accumulate and the weights stay 4-bit up to the product;
 // 128-bit loads; split over K when the rows alone would not cover the GPU.
 //
-// Mapping on gfx950: one workgroup per 16-row group, its waves splitting the
-// K tiles.  A lane's 16-byte load holds 32 codes of one row.  Each byte (two
-// codes) indexes a replicated LDS table of bf16 code pairs, and
-// v_dot2_f32_bf16 multiplies that pair by the matching pair of bf16
-// activations with fp32 accumulation (the codes are bf16 values, so every
-// product is exact).  The fp32 block scale multiplies each 64-block's sum.
-// Lanes sharing a row combine with cross-lane shuffles, waves through LDS in
-// a fixed order, so the result is reproducible bit for bit.
+// Kernels on gfx950 (a lane's 16-byte load holds 32 codes of one row; each
+// byte, two codes, indexes a replicated LDS table of bf16 code pairs; the
+// codes are bf16 values, so every product is exact in fp32, and the fp32
+// block scale multiplies each 64-block's sum):
+//   gemv_fast_kernel<M, ARGMAX, AFF>  workgroups own runs of whole row
+//     groups, their 8 waves split the tiles; x and the partial sums live in
+//     LDS; the products run on the matrix cores (below); optional argmax of
+//     y (ARGMAX) and the asymmetric int4 format (AFF, no table); loads past
+//     a wave's share read ahead into the next launch's matrix when named;
+//   gemv_generic_kernel  codebooks needing three bf16 terms, v_dot2_f32_bf16
+//     products, one workgroup per row group, lanes combined by shuffles;
+//   argmax_kernel  the argmax of y after the generic path.
+// Partial sums combine in a fixed order, so results are reproducible bit for
+// bit.
 #include <atomic>
 #include <climits>
 

@@ -1,5 +1,7 @@
 // pack.hip -- load-time kernels: quantize fp32 weights into the device
-// layout, the debug dequant, and the canonical <-> device layout copies.
+// layout, the debug dequant, and the canonical <-> device layout copies, for
+// the NF4 format and the asymmetric int4 format; and the activation gather
+// of act-order checkpoints.
 //
 // Method (vibevoice.c README, "Quantization" > "Weights"): every projection
 // is quantized once as it is loaded, before placement, deterministically;
