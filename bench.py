@@ -68,13 +68,13 @@ DOMINANT = ("gate_up", 2 * MLP, HIDDEN)
 # per dispatch and the calibration of each counter on a plain 1 GiB copy.
 TRAFFIC = {
     "gemv": {"source": "gemv.hip", "fetch_kib": 42729, "write_kib": 148,
-             "sha256": "4865fef77e624e1aac6e1b49863fe8ac5766ee26b1b65a189a0c0e0ce9226844"},
-    "gemm": {"source": "gemm.hip", "fetch_kib": 180721, "write_kib": 153259,
-             "sha256": "9c0581cd848c56dce6dbccf425c0622202cd7fa028f23a8938544c4501dc2575"},
+             "sha256": "5f77a7ec2181f4cf3a6616c5591104233b07a441586fca9cda18542272ac5a99"},
+    "gemm": {"source": "gemm.hip", "fetch_kib": 180722, "write_kib": 153549,
+             "sha256": "f0a37143ae6b452ca2d19c1e4aef292a61ae51ba33a00d56d243352b08234831"},
     "awq_gemv": {"source": "gemv.hip", "fetch_kib": 40366, "write_kib": 148,
-                 "sha256": "4865fef77e624e1aac6e1b49863fe8ac5766ee26b1b65a189a0c0e0ce9226844"},
-    "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180882, "write_kib": 152888,
-                 "sha256": "9c0581cd848c56dce6dbccf425c0622202cd7fa028f23a8938544c4501dc2575"},
+                 "sha256": "5f77a7ec2181f4cf3a6616c5591104233b07a441586fca9cda18542272ac5a99"},
+    "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180888, "write_kib": 153287,
+                 "sha256": "f0a37143ae6b452ca2d19c1e4aef292a61ae51ba33a00d56d243352b08234831"},
 }
 COPY_CALIBRATION = {"fetch_kib_per_gib": 524308, "write_kib_per_gib": 1048576}
 
