@@ -190,6 +190,11 @@ class Model:
                 torch.int16)
 
         self.x1 = {K: bf16_randn(1, K, seed + 1000 + K) for K in (HIDDEN, MLP)}
+        # two decode slots (M = 2)
+        self.x2 = {K: bf16_randn(2, K, seed + 3000 + K) for K in (HIDDEN, MLP)}
+        self.y2 = {name: torch.empty((2, N), dtype=torch.float32, device=dev)
+                   for name, N, _ in LINEARS}
+        self.y2["lm_head"] = torch.empty((2, VOCAB), dtype=torch.float32, device=dev)
         self.xp = {K: bf16_randn(PREFILL_M, K, seed + 2000 + K) for K in (HIDDEN, MLP)}
         self.y1 = {name: torch.empty((1, N), dtype=torch.float32, device=dev)
                    for name, N, _ in LINEARS}
@@ -204,18 +209,19 @@ class Model:
     def packed(self, name, layer):
         return self.lm_head if name == "lm_head" else self.weights[layer][name]
 
-    def gemv(self, name, layer, nxt=None):
-        """One decode GEMV; nxt = (name, layer) of the next launch on the
-        stream, named as a read-ahead hint (nf4_gemv_prefetch)."""
+    def gemv(self, name, layer, nxt=None, M=1):
+        """One decode GEMV (M = 1 or 2 rows); nxt = (name, layer) of the next
+        launch on the stream, named as a read-ahead hint (nf4_gemv_prefetch)."""
         pw = self.packed(name, layer)
+        x, y = (self.x1[pw.K], self.y1[name]) if M == 1 else (self.x2[pw.K], self.y2[name])
         if nxt is None:
-            self.nf4.nf4_gemv(self.x1[pw.K], 1, pw.qweight, pw.absmax, self.cb, pw.N, pw.K,
-                              self.y1[name], self.ws, self.ws_bytes)
+            self.nf4.nf4_gemv(x, M, pw.qweight, pw.absmax, self.cb, pw.N, pw.K, y, self.ws,
+                              self.ws_bytes)
         else:
             npw = self.packed(*nxt)
-            self.nf4.nf4_gemv_prefetch(self.x1[pw.K], 1, pw.qweight, pw.absmax, self.cb, pw.N,
-                                       pw.K, self.y1[name], self.ws, self.ws_bytes,
-                                       npw.qweight, npw.absmax, npw.N, npw.K)
+            self.nf4.nf4_gemv_prefetch(x, M, pw.qweight, pw.absmax, self.cb, pw.N, pw.K, y,
+                                       self.ws, self.ws_bytes, npw.qweight, npw.absmax, npw.N,
+                                       npw.K)
 
     def gemm(self, name, layer):
         pw = self.weights[layer][name]
@@ -415,6 +421,14 @@ def main():
     gemm_us = gemm_ms * 1e3 / LAYERS
     launches += [("gemm", name)] * (LAYERS * (reps + 1))
     log(f"[bench] dominant {name}: gemv {gemv_us:.2f} us, gemm {gemm_us:.2f} us per launch")
+    # ---- the decode step with two slots (M = 2), same read-ahead hints
+    def decode_step_m2():
+        for i, (nm, layer) in enumerate(decode_order):
+            mdl.gemv(nm, layer, decode_order[i + 1] if i + 1 < len(decode_order) else None, M=2)
+
+    dec2_ms = graph_ms(torch, s, decode_step_m2, max(args.steps, 5))
+    launches += [("gemv", "m2:" + n) for n in decode_labels()] * (max(args.steps, 5) + 1)
+    log(f"[bench] decode M=2: {dec2_ms:.3f} ms per step")
     # ---- lm_head: plain GEMV vs GEMV + on-device argmax (4 launches per replay)
     amx_ws_bytes = nf4.nf4_gemv_argmax_workspace_bytes(1, VOCAB, HIDDEN)
     amx_ws = torch.zeros(max(amx_ws_bytes, 16), dtype=torch.uint8, device="cuda")
@@ -485,6 +499,9 @@ def main():
                    "decode_packed_bytes": decode_bytes, "prefill_flop": prefill_flop,
                    "block": 64, "scale_dtype": "fp32", "out_dtype": "fp32"},
         "decode_ms": round(dec_ms, 4),
+        "decode_m2": {"value": round(decode_bytes / (dec2_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                      "ms": round(dec2_ms, 4),
+                      "note": "the same 113 launches with two activation rows (two server slots)"},
         "prefill": {"value": round(pre_tflops, 2), "unit": "TFLOP/s", "ms": round(pre_ms, 3)},
         "roofline": {"bound": "hbm", "achieved": round(gv_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gv_gbps / HBM_PEAK_GBPS, 4),
