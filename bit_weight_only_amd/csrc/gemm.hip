@@ -10,9 +10,9 @@
 // P = sum_k x*c in fp32 (exact products), then acc += s * P.
 //
 // Kernels:
-//   gemm_tile_kernel<RG, AFF>  codebooks whose values are bf16 (the default
-//     one) and the asymmetric int4 format (AFF): 128 x 16 RG outputs per
-//     workgroup, RG waves of 64 x 32, copies straight from global memory
+//   gemm_tile_kernel<RG, AFF, MB>  codebooks whose values are bf16 (the
+//     default one) and the asymmetric int4 format (AFF): 128 x 16 RG outputs
+//     per workgroup, waves of 16 MB x 32, copies straight from global memory
 //     into LDS rings, each wave expanding the code words of its own columns;
 //   gemm_skinny_kernel<MB, D, AFF>  few rows (below);
 //   xsum_kernel           the int4 format's per-group sums of x (pre-pass);
@@ -150,6 +150,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
 
 
 constexpr int kBK = 64;  // k per step of the pipelined kernel (one scale block)
+// 16-row m-blocks per wave of the tiled kernel: 8 waves per workgroup either
+// way, of 128 x 32 outputs for 16 row groups (each B fragment feeds 8
+// MFMAs: half the lookup-address VALU per MFMA of 64-row waves) and of
+// 64 x 32 for 8 row groups (two waves per SIMD keep latency hidden there)
+constexpr int kTileMB = 8, kTileMB8 = 4;
 
 // ---------------------------------------------------------------------------
 // Copies straight from global memory into LDS, shared by the tiled and the
@@ -186,8 +191,8 @@ __device__ inline void wait_copies_and_barrier() {
 
 // ---------------------------------------------------------------------------
 // Tiled kernel: a workgroup computes 128 rows x 16 RG columns (RG row groups,
-// 8 or 16) with RG waves, each 64 rows x 32 columns (4 x 2 MFMA blocks), so
-// there are 2 or 4 waves per SIMD.  Each wave expands the B fragments of its
+// 8 or 16) with 4 RG / MB waves, each 16 MB rows x 32 columns (MB x 2 MFMA
+// blocks; MB = 8 for RG = 16 and 4 for RG = 8, so 8 waves, 2 per SIMD).  Each wave expands the B fragments of its
 // own two row groups straight from code words in LDS (no expanded copy of B
 // is stored), and the pair table has one copy per lane at a 256-byte stride:
 // the lookup address (code byte << 8) | (lane << 2) is one v_perm_b32 and the
@@ -222,9 +227,12 @@ constexpr int kTable = 256 * 64 * 4;            // one copy per lane
 constexpr int kAHalf = kBM * pipe::kHalfRow;    // 8 KB: 128 rows x 32 k
 
 constexpr int kXSum = kBM * 4;                  // x sums of one tile, bytes
-template <int RG, bool AFF>
+template <int RG, bool AFF, int MB>
 struct Map {
-  static constexpr int kWaves = RG, kThreads = 64 * RG, kWN = RG / 2;  // waves along N
+  // MB 16-row m-blocks per wave: waves of 16 MB x 32, 8 / MB along M and
+  // RG / 2 along N
+  static constexpr int kWaves = 4 * RG / MB, kThreads = 64 * kWaves, kWN = RG / 2;
+  static constexpr int kRGW = RG / kWaves;  // row groups each wave copies (1 or 2)
   // the affine variant has no pair table
   static constexpr int kOffA = AFF ? 0 : kTable, kOffC = kOffA + 4 * kAHalf;
   static constexpr int kOffS = kOffC + RG * 2 * kTileBytes,
@@ -234,19 +242,19 @@ struct Map {
   static constexpr int kXLanes = kXSum / 16 / kWaves;  // lanes per wave copying x sums
   // copies a wave may leave in flight past the barrier of an even step: the
   // tile copies of the step before
-  static constexpr int kTileCopies = 2;
+  static constexpr int kTileCopies = 2 * kRGW;
   // bytes of scales (params) per device tile in global memory; the LDS slot
   // keeps 128
   static constexpr int kScaleBytes = AFF ? kTileRows * 4 : kTileScales * 4;
 };
 }  // namespace tile
 
-template <int RG, bool AFF>
-__global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
+template <int RG, bool AFF, int MB>
+__global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
     const uint16_t *__restrict__ x, int64_t M, const uint8_t *__restrict__ qw,
     const float *__restrict__ am, CodeTerms ct, int64_t N, int64_t K, int64_t KT,
     float *__restrict__ y, int ntn, int ntm, const float *__restrict__ xsum, int64_t Mp) {
-  using L = tile::Map<RG, AFF>;
+  using L = tile::Map<RG, AFF, MB>;
   // the only static LDS array, so the table sits at LDS address 0
   __shared__ __attribute__((aligned(16))) char lds[L::kBytes];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -269,33 +277,35 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
   const uint32_t base = pipe::lds_addr(lds);
   const char *ldsA = lds + L::kOffA, *ldsC = lds + L::kOffC, *ldsS = lds + L::kOffS;
 
-  // Copy assignment.  x: copy i (16 per step, 1 KB each) fills rows
-  // 16 (i % 8) .. + 15 of half i / 8; wave w issues i = w, w + RG, ...  Lane
-  // l fills chunk slot l % 4 of row 16 (i % 8) + l / 4, i.e. logical chunk
-  // (l % 4) ^ ((l >> 4) & 3).  Code words and scales: wave w copies those of
-  // row group w.  Rows past M and row groups past N re-read the last valid
-  // one; their outputs are never stored.
+  // Copy assignment (W waves).  x: copy i (16 per step, 1 KB each) fills
+  // rows 16 (i % 8) .. + 15 of half i / 8; wave w issues i = w, w + W, ...
+  // Lane l fills chunk slot l % 4 of row 16 (i % 8) + l / 4, i.e. logical
+  // chunk (l % 4) ^ ((l >> 4) & 3).  Code words and scales: wave w copies
+  // those of row groups w, w + W, ...  Rows past M and row groups past N
+  // re-read the last valid one; their outputs are never stored.
   uint32_t aoff[L::kACopies], mA[L::kACopies];
 #pragma unroll
   for (int v = 0; v < L::kACopies; ++v) {
-    const int i = wave + v * RG, blk = i % 8, half = i / 8;
+    const int i = wave + v * L::kWaves, blk = i % 8, half = i / 8;
     const int64_t R = m0 + 16 * blk + (lane >> 2);
     const int64_t gm = R < M ? R : M - 1;
     const int c = (lane & 3) ^ ((lane >> 4) & 3);
     aoff[v] = (uint32_t)((gm * K + half * 32 + c * 8) * 2);
     mA[v] = base + L::kOffA + half * tile::kAHalf + blk * 1024;
   }
-  uint32_t coff, soff;
-  {
-    const int64_t rg = gblk + wave;
+  uint32_t coff[L::kRGW], soff[L::kRGW], mC[L::kRGW], mS[L::kRGW];
+#pragma unroll
+  for (int u = 0; u < L::kRGW; ++u) {
+    const int q = wave + u * L::kWaves;  // row group of the tile
+    const int64_t rg = gblk + q;
     const int64_t g = rg < G ? rg : G - 1;
-    coff = (uint32_t)(g * KT * kTileBytes + lane * 16);
-    soff = (uint32_t)(g * KT * L::kScaleBytes + lane * 16);  // lanes 0..7 (0..3) copy
+    coff[u] = (uint32_t)(g * KT * kTileBytes + lane * 16);
+    soff[u] = (uint32_t)(g * KT * L::kScaleBytes + lane * 16);  // lanes 0..7 (0..3) copy
+    mC[u] = base + L::kOffC + q * 2 * kTileBytes;
+    mS[u] = base + L::kOffS + q * 2 * kTileScales * 4;
   }
-  const uint32_t mC = base + L::kOffC + wave * 2 * kTileBytes;
-  const uint32_t mS = base + L::kOffS + wave * 2 * kTileScales * 4;
-  // x sums (affine): wave w copies bytes [w, w + 1) * 512 / RG of a tile's 512
-  const uint32_t mX = base + L::kOffX + wave * (tile::kXSum / RG);
+  // x sums (affine): wave w copies bytes [w, w + 1) * 512 / W of a tile's 512
+  const uint32_t mX = base + L::kOffX + wave * (tile::kXSum / L::kWaves);
   const uint32_t xoff = (uint32_t)(m0 * 4) + (uint32_t)(wave * L::kXLanes + lane) * 16u;
   auto copy_x = [&](int step) {
     const uint32_t sc = (uint32_t)(step < S ? step : S - 1) * (kBK * 2);
@@ -307,9 +317,12 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
   // words and 128 bytes of scales, into ring slot T & 1
   auto copy_tile = [&](int T) {
     const uint32_t tc = (uint32_t)(T < KT ? T : KT - 1);
-    pipe::copy16(mC + (T & 1) * kTileBytes, qw, coff + tc * kTileBytes);
-    if (lane < L::kScaleBytes / 16)
-      pipe::copy16(mS + (T & 1) * kTileScales * 4, am, soff + tc * L::kScaleBytes);
+#pragma unroll
+    for (int u = 0; u < L::kRGW; ++u) {
+      pipe::copy16(mC[u] + (T & 1) * kTileBytes, qw, coff[u] + tc * kTileBytes);
+      if (lane < L::kScaleBytes / 16)
+        pipe::copy16(mS[u] + (T & 1) * kTileScales * 4, am, soff[u] + tc * L::kScaleBytes);
+    }
   };
   // x sums of device tile T (affine) into ring slot T & 1
   auto copy_xsum = [&](int T) {
@@ -339,16 +352,16 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
 
   const uint32_t lane4 = (uint32_t)lane << 2;
   // fragments: lane (r, h) holds row r of a 16-row block, bf16 8h .. 8h+7 of the half
-  const uint32_t afr = (uint32_t)(wm * 64 * pipe::kHalfRow + r * pipe::kHalfRow +
+  const uint32_t afr = (uint32_t)(wm * 16 * MB * pipe::kHalfRow + r * pipe::kHalfRow +
                                   ((h ^ ((r >> 2) & 3)) * 16));
   // this wave's two row groups: code words (16 bytes per lane) and scales
   const char *cw = ldsC + (wn * 2) * 2 * kTileBytes + lane * 16;
   const char *sw = ldsS + (wn * 2) * 2 * kTileScales * 4 + r * (AFF ? 4 : 8);
   // x sums of D rows wm 64 + mm 16 + 4h + i (affine)
-  const char *xw = lds + L::kOffX + (wm * 64 + 4 * h) * 4;
-  f32x4 acc[4][2];
+  const char *xw = lds + L::kOffX + (wm * 16 * MB + 4 * h) * 4;
+  f32x4 acc[MB][2];
 #pragma unroll
-  for (int a2 = 0; a2 < 4; ++a2)
+  for (int a2 = 0; a2 < MB; ++a2)
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2) acc[a2][b2] = f32x4{0.f, 0.f, 0.f, 0.f};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -360,7 +373,7 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
   const uint32_t xlast = (uint32_t)(S - 1) * (kBK * 2);
   uint4 cv[2];
   float2 sv[2];
-  f32x4 pz[4][2];  // affine: the tile's product, carried from the even step to the odd one
+  f32x4 pz[MB][2];  // affine: the tile's product, carried from the even step to the odd one
   auto step = [&](auto phc, int t) {
     constexpr int PH = decltype(phc)::value;
     // Landed: x of step t (copied in step t-1; at an even step the tile
@@ -396,13 +409,13 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
     };
     const float s0 = AFF ? f16lo(sv[0].x) : PH ? sv[0].y : sv[0].x;
     const float s1 = AFF ? f16lo(sv[1].x) : PH ? sv[1].y : sv[1].x;
-    f32x4 p[4][2];
+    f32x4 p[MB][2];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const char *pa = ldsA + (PH * 2 + hf) * tile::kAHalf + afr;
-      bf16x8 A[4], B[2];
+      bf16x8 A[MB], B[2];
 #pragma unroll
-      for (int mm = 0; mm < 4; ++mm) A[mm] = *reinterpret_cast<const bf16x8 *>(pa + mm * 1024);
+      for (int mm = 0; mm < MB; ++mm) A[mm] = *reinterpret_cast<const bf16x8 *>(pa + mm * 1024);
 #pragma unroll
       for (int nn = 0; nn < 2; ++nn) {
         // quarter 2 PH + hf of the tile: code dword 2 PH + hf of the lane
@@ -422,7 +435,7 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
         B[nn] = __builtin_bit_cast(bf16x8, make_uint4(bb[0], bb[1], bb[2], bb[3]));
       }
 #pragma unroll
-      for (int mm = 0; mm < 4; ++mm)
+      for (int mm = 0; mm < MB; ++mm)
 #pragma unroll
         for (int nn = 0; nn < 2; ++nn) {
           if constexpr (AFF)
@@ -440,7 +453,7 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
         const float nz0 = -(float)(16u + (__float_as_uint(sv[0].x) >> 16)) * 0.0625f;
         const float nz1 = -(float)(16u + (__float_as_uint(sv[1].x) >> 16)) * 0.0625f;
 #pragma unroll
-        for (int mm = 0; mm < 4; ++mm) {
+        for (int mm = 0; mm < MB; ++mm) {
           const f32x4 xz = *reinterpret_cast<const f32x4 *>(xw + sl * tile::kXSum + mm * 64);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -451,7 +464,7 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
       }
     } else {
 #pragma unroll
-      for (int mm = 0; mm < 4; ++mm)
+      for (int mm = 0; mm < MB; ++mm)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           acc[mm][0][i] = fmaf(s0, p[mm][0][i], acc[mm][0][i]);
@@ -471,7 +484,7 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
 #pragma unroll
-  for (int mm = 0; mm < 4; ++mm)
+  for (int mm = 0; mm < MB; ++mm)
 #pragma unroll
     for (int nn = 0; nn < 2; ++nn) {
       const int64_t g = gblk + wn * 2 + nn;
@@ -479,7 +492,7 @@ __global__ __launch_bounds__(64 * RG) void gemm_tile_kernel(
       const int64_t col = g * kTileRows + r;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t row = m0 + wm * 64 + mm * 16 + 4 * h + i;
+        const int64_t row = m0 + wm * 16 * MB + mm * 16 + 4 * h + i;
         if (row < M) y[row * N + col] = acc[mm][nn][i];
       }
     }
@@ -783,12 +796,13 @@ hipError_t launch_awq_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, cons
   auto padded = [&](int64_t nt) { return (unsigned)((nt + 7) / 8 * 8 * mt); };
   if (((G + 15) / 16) * mt >= device_cu_count() / 2) {
     const int64_t nt = (G + 15) / 16;
-    hipLaunchKernelGGL((gemm_tile_kernel<16, true>), dim3(padded(nt)), dim3(64 * 16), 0, s, x, M,
+    hipLaunchKernelGGL((gemm_tile_kernel<16, true, kTileMB>), dim3(padded(nt)),
+                       dim3(256 * 16 / kTileMB), 0, s, x, M,
                        qw, reinterpret_cast<const float *>(pr), ct, N, K, KT, y, (int)nt,
                        (int)mt, X, Mp);
   } else {
     const int64_t nt = (G + 7) / 8;
-    hipLaunchKernelGGL((gemm_tile_kernel<8, true>), dim3(padded(nt)), dim3(64 * 8), 0, s, x, M, qw,
+    hipLaunchKernelGGL((gemm_tile_kernel<8, true, 4>), dim3(padded(nt)), dim3(64 * 8), 0, s, x, M, qw,
                        reinterpret_cast<const float *>(pr), ct, N, K, KT, y, (int)nt, (int)mt, X,
                        Mp);
   }
@@ -846,12 +860,14 @@ hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, const fl
     auto padded = [&](int64_t nt) { return (unsigned)((nt + 7) / 8 * 8 * mt); };
     if (((G + 15) / 16) * mt >= device_cu_count() / 2) {
       const int64_t nt = (G + 15) / 16;
-      hipLaunchKernelGGL((gemm_tile_kernel<16, false>), dim3(padded(nt)), dim3(64 * 16), 0, s, x,
-                         M, qw, am, ct, N, K, KT, y, (int)nt, (int)mt, nullptr, (int64_t)0);
+      hipLaunchKernelGGL((gemm_tile_kernel<16, false, kTileMB>), dim3(padded(nt)),
+                         dim3(256 * 16 / kTileMB), 0, s, x, M, qw, am, ct, N, K, KT, y, (int)nt,
+                         (int)mt, nullptr, (int64_t)0);
     } else {
       const int64_t nt = (G + 7) / 8;
-      hipLaunchKernelGGL((gemm_tile_kernel<8, false>), dim3(padded(nt)), dim3(64 * 8), 0, s, x, M,
-                         qw, am, ct, N, K, KT, y, (int)nt, (int)mt, nullptr, (int64_t)0);
+      hipLaunchKernelGGL((gemm_tile_kernel<8, false, kTileMB8>), dim3(padded(nt)),
+                         dim3(256 * 8 / kTileMB8), 0, s, x, M, qw, am, ct, N, K, KT, y, (int)nt,
+                         (int)mt, nullptr, (int64_t)0);
     }
     return hipGetLastError();
   }
