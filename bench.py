@@ -473,8 +473,9 @@ def main():
     for _ in range(args.steps):
         launches += [("gemv", n) for n in decode_labels()] + \
                     [("gemm", n) for n in prefill_labels()]
-    dec_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in ev]))
-    pre_ms = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in ev]))
+    dec_all = [e0.elapsed_time(e1) for e0, e1, _ in ev]
+    pre_all = [e1.elapsed_time(e2) for _, e1, e2 in ev]
+    dec_ms, pre_ms = float(np.mean(dec_all)), float(np.mean(pre_all))
     log(f"[bench] {args.steps} timed steps: decode {dec_ms:.3f} ms, prefill {pre_ms:.3f} ms")
 
     if args.launch_log:
@@ -499,10 +500,14 @@ def main():
                    "decode_packed_bytes": decode_bytes, "prefill_flop": prefill_flop,
                    "block": 64, "scale_dtype": "fp32", "out_dtype": "fp32"},
         "decode_ms": round(dec_ms, 4),
+        "decode_ms_median": round(float(np.median(dec_all)), 4),
+        "decode_ms_min": round(float(np.min(dec_all)), 4),
         "decode_m2": {"value": round(decode_bytes / (dec2_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
                       "ms": round(dec2_ms, 4),
                       "note": "the same 113 launches with two activation rows (two server slots)"},
-        "prefill": {"value": round(pre_tflops, 2), "unit": "TFLOP/s", "ms": round(pre_ms, 3)},
+        "prefill": {"value": round(pre_tflops, 2), "unit": "TFLOP/s", "ms": round(pre_ms, 3),
+                    "ms_median": round(float(np.median(pre_all)), 3),
+                    "ms_min": round(float(np.min(pre_all)), 3)},
         "roofline": {"bound": "hbm", "achieved": round(gv_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gv_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_bytes("gemv"),
