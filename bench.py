@@ -69,12 +69,12 @@ DOMINANT = ("gate_up", 2 * MLP, HIDDEN)
 TRAFFIC = {
     "gemv": {"source": "gemv.hip", "fetch_kib": 42729, "write_kib": 148,
              "sha256": "5f77a7ec2181f4cf3a6616c5591104233b07a441586fca9cda18542272ac5a99"},
-    "gemm": {"source": "gemm.hip", "fetch_kib": 180756, "write_kib": 151999,
-             "sha256": "bd8d02c34b70d2a267629e0e4f953ccb56da336a2897531211530559945d462d"},
+    "gemm": {"source": "gemm.hip", "fetch_kib": 180754, "write_kib": 151931,
+             "sha256": "e9f716650e6cef0f4dd051301ff858a2d6bb98bed3d73b1ec43b204852f90039"},
     "awq_gemv": {"source": "gemv.hip", "fetch_kib": 40366, "write_kib": 148,
                  "sha256": "5f77a7ec2181f4cf3a6616c5591104233b07a441586fca9cda18542272ac5a99"},
-    "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180912, "write_kib": 151858,
-                 "sha256": "bd8d02c34b70d2a267629e0e4f953ccb56da336a2897531211530559945d462d"},
+    "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180912, "write_kib": 151918,
+                 "sha256": "e9f716650e6cef0f4dd051301ff858a2d6bb98bed3d73b1ec43b204852f90039"},
 }
 COPY_CALIBRATION = {"fetch_kib_per_gib": 524308, "write_kib_per_gib": 1048576}
 

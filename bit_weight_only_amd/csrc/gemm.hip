@@ -10,11 +10,11 @@
 // P = sum_k x*c in fp32 (exact products), then acc += s * P.
 //
 // Kernels:
-//   gemm_tile_kernel<RG, AFF, MB>  codebooks whose values are bf16 (the
+//   gemm_tile_kernel<RG, AFF, MB, SPLIT>  codebooks whose values are bf16 (the
 //     default one) and the asymmetric int4 format (AFF): 128 x 16 RG outputs
 //     per workgroup, waves of 16 MB x 32, copies straight from global memory
 //     into LDS rings, each wave expanding the code words of its own columns;
-//   gemm_skinny_kernel<MB, D, AFF>  few rows (below);
+//   gemm_skinny_kernel<MB, D, AFF, SPLIT>  few rows (below);
 //   xsum_kernel           the int4 format's per-group sums of x (pre-pass);
 //   gemm_kernel<3>        any finite codebook (each value split into three
 //     bf16 terms), and shapes whose byte offsets exceed 32 bits.
@@ -22,8 +22,11 @@
 // whatever the tile shape or M: the K order, the MFMA k-split and the
 // per-block fold never depend on the launch, so a row of y does not depend on
 // the other rows in the batch, and a column slice of a fused matrix equals
-// the separate matrix's output.  K is therefore never split across
-// workgroups.
+// the separate matrix's output.  The one split of K is fixed by K alone
+// (split_tiles: two halves for K >= 8192, each folded from zero, then added
+// once): the tiled kernel runs the halves on two workgroups that meet
+// through the workspace, the skinny and generic kernels one after the other
+// in a wave.
 #include <type_traits>
 
 #include "nf4_internal.h"
@@ -42,7 +45,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
                                                    const uint4 *__restrict__ qw,
                                                    const float2 *__restrict__ am, CodeTerms ct,
                                                    int64_t N, int64_t K, int64_t KT,
-                                                   float *__restrict__ y) {
+                                                   float *__restrict__ y, int kh) {
   __shared__ uint32_t table[NTERM * kPairWords];
   __shared__ __attribute__((aligned(16))) uint16_t xs[BM * XS];
 
@@ -60,13 +63,23 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
   const int64_t G = N / kTileRows;
   const uint32_t *tab = table + (lane & (kPairCopies - 1));
 
-  f32x4 acc[4][4];
+  // acc1: the sums of the first part of K when K is in two parts (kh > 0)
+  f32x4 acc[4][4], acc1[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < 4; ++b) acc[a][b] = acc1[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int64_t t = 0; t < KT; ++t) {
+    if (kh > 0 && t == kh) {  // the second part of K starts from zero
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          acc1[a][b] = acc[a][b];
+          acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
     __syncthreads();  // previous x tile fully consumed (and table built)
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -143,7 +156,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t row = m0 + wm * 64 + mm * 16 + 4 * h + i;
-        if (row < M) y[row * N + col] = acc[mm][nn][i];
+        const float v = kh ? acc1[mm][nn][i] + acc[mm][nn][i] : acc[mm][nn][i];
+        if (row < M) y[row * N + col] = v;
       }
     }
 }
@@ -221,6 +235,12 @@ __device__ inline void wait_copies_and_barrier() {
 // device tile and output: P = four MFMAs over the tile's 32-k quarters from
 // zero (two steps; P = sum x (1 + q/16)), g = fmaf(-(16 + z)/16, X, P),
 // acc = fmaf(16 s, g, acc).
+//
+// K in two parts (SPLIT, K >= 8192): the grid holds two workgroups per
+// output tile, one per half of K, each summing its half from zero; they meet
+// through the workspace (sums stored, arrival counted, the second adds the
+// first's sums to its own and stores y), which costs one extra write and read
+// of the tile but fills the CUs with wide tiles where N alone would not.
 namespace tile {
 constexpr int kBM = 128;
 constexpr int kTable = 256 * 64 * 4;            // one copy per lane
@@ -249,12 +269,15 @@ struct Map {
 };
 }  // namespace tile
 
-template <int RG, bool AFF, int MB>
+template <int RG, bool AFF, int MB, bool SPLIT>
 __global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
     const uint16_t *__restrict__ x, int64_t M, const uint8_t *__restrict__ qw,
     const float *__restrict__ am, CodeTerms ct, int64_t N, int64_t K, int64_t KT,
-    float *__restrict__ y, int ntn, int ntm, const float *__restrict__ xsum, int64_t Mp) {
+    float *__restrict__ y, int ntn, int ntm, const float *__restrict__ xsum, int64_t Mp,
+    int kh_arg, uint32_t *__restrict__ cnt, uint64_t *__restrict__ part) {
   using L = tile::Map<RG, AFF, MB>;
+  // K in two parts (SPLIT, kh > 0 device tiles in the first) or in one
+  const int kh = SPLIT ? kh_arg : 0;
   // the only static LDS array, so the table sits at LDS address 0
   __shared__ __attribute__((aligned(16))) char lds[L::kBytes];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -266,14 +289,25 @@ __global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
   // the N tiles k, k+8, ... and, for each, all M tiles one after the other,
   // so the workgroups that expand one weight tile share an L2.  Workgroups
   // past the last N tile (the grid is padded to a multiple of 8 N tiles)
-  // leave before any barrier.
-  const int xcd = (int)(blockIdx.x & 7), slot = (int)(blockIdx.x >> 3);
+  // leave before any barrier.  With K in two parts (kh > 0) the two
+  // workgroups of an output tile are neighbours in that order, part kc.
+  const int ns = kh ? 2 : 1;
+  const int xcd = (int)(blockIdx.x & 7), sl = (int)(blockIdx.x >> 3);
+  const int kc = sl % ns, slot = sl / ns;
   const int nt = (slot / ntm) * 8 + xcd, mt = slot % ntm;
   if (nt >= ntn) return;
   const int64_t m0 = (int64_t)mt * tile::kBM;
   const int64_t gblk = (int64_t)nt * RG;
   const int64_t G = N / kTileRows;
-  const int S = (int)(K / kBK);
+  // this workgroup's part of K: device tiles [t0, t0 + KTp), S 64-k steps;
+  // every source is addressed from the part's first tile
+  const int t0 = kc ? kh : 0;
+  const int64_t KTp = kh ? (kc ? KT - kh : kh) : KT;
+  const int S = kh ? (kc ? (int)(K / kBK) - 2 * kh : 2 * kh) : (int)(K / kBK);
+  x += (int64_t)t0 * kTileK;
+  qw += (int64_t)t0 * kTileBytes;
+  am += (int64_t)t0 * (L::kScaleBytes / 4);
+  if (AFF) xsum += (int64_t)t0 * Mp;
   const uint32_t base = pipe::lds_addr(lds);
   const char *ldsA = lds + L::kOffA, *ldsC = lds + L::kOffC, *ldsS = lds + L::kOffS;
 
@@ -316,7 +350,7 @@ __global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
   // device tile T (steps 2T, 2T+1) of the wave's row group: 1 KB of code
   // words and 128 bytes of scales, into ring slot T & 1
   auto copy_tile = [&](int T) {
-    const uint32_t tc = (uint32_t)(T < KT ? T : KT - 1);
+    const uint32_t tc = (uint32_t)(T < KTp ? T : KTp - 1);
 #pragma unroll
     for (int u = 0; u < L::kRGW; ++u) {
       pipe::copy16(mC[u] + (T & 1) * kTileBytes, qw, coff[u] + tc * kTileBytes);
@@ -327,7 +361,7 @@ __global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
   // x sums of device tile T (affine) into ring slot T & 1
   auto copy_xsum = [&](int T) {
     if constexpr (AFF) {
-      const uint32_t tc = (uint32_t)(T < KT ? T : KT - 1);
+      const uint32_t tc = (uint32_t)(T < KTp ? T : KTp - 1);
       if (lane < L::kXLanes)
         pipe::copy16(mX + (T & 1) * tile::kXSum, xsum, xoff + tc * (uint32_t)(Mp * 4));
     }
@@ -474,6 +508,11 @@ __global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
+  // The workspace pointers are first needed after the loop; taking them into
+  // scalar registers here keeps their loads from being in flight through the
+  // loop, where the waits for LDS reads would otherwise have to wait for
+  // everything (scalar loads return out of order).
+  if constexpr (SPLIT) asm volatile("" ::"s"(cnt), "s"(part));
   int t = 0;
   for (; t + 1 < S; t += 2) {
     step(P0{}, t);
@@ -482,6 +521,50 @@ __global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
   if (t < S) step(P0{}, t);
   // the clamped copies of the last steps must land before the workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  if (SPLIT) {
+    // K in two parts: each workgroup of the output tile stores its sums
+    // (thread-major, 8 bytes per lane and store) device-wide, then counts its
+    // arrival; the second to arrive adds the other part to its own and
+    // stores y, then sets the counter back to zero.  Both orders give the
+    // same bits: one fp32 addition commutes.
+    constexpr int NV = MB * 4;  // 8-byte pairs of sums per thread
+    const int64_t tile_id = (int64_t)nt * ntm + mt;
+    uint64_t *mine = part + (tile_id * 2 + kc) * (int64_t)(L::kThreads * NV) + tid;
+    const uint64_t *other = part + (tile_id * 2 + (kc ^ 1)) * (int64_t)(L::kThreads * NV) + tid;
+#pragma unroll
+    for (int mm = 0; mm < MB; ++mm)
+#pragma unroll
+      for (int nn = 0; nn < 2; ++nn)
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2) {
+          const uint64_t v = (uint64_t)__float_as_uint(acc[mm][nn][2 * i2]) |
+                             ((uint64_t)__float_as_uint(acc[mm][nn][2 * i2 + 1]) << 32);
+          __hip_atomic_store(mine + ((mm * 2 + nn) * 2 + i2) * L::kThreads, v, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+    // the sums are stored device-wide before the arrival is counted
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // also: no wave reads LDS any more
+    int *flag = reinterpret_cast<int *>(lds);
+    if (tid == 0)
+      *flag = (int)__hip_atomic_fetch_add(cnt + tile_id, 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (*flag == 0) return;
+#pragma unroll
+    for (int mm = 0; mm < MB; ++mm)
+#pragma unroll
+      for (int nn = 0; nn < 2; ++nn)
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2) {
+          const uint64_t v = __hip_atomic_load(other + ((mm * 2 + nn) * 2 + i2) * L::kThreads,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          acc[mm][nn][2 * i2] += __uint_as_float((uint32_t)v);
+          acc[mm][nn][2 * i2 + 1] += __uint_as_float((uint32_t)(v >> 32));
+        }
+    if (tid == 0) __hip_atomic_store(cnt + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 
 #pragma unroll
   for (int mm = 0; mm < MB; ++mm)
@@ -523,11 +606,13 @@ constexpr int kWaves = 4;        // row groups per workgroup
 constexpr int kXBuf = 32 * 1024; // bytes of one x chunk buffer
 }  // namespace skinny
 
-template <int MB, int D, bool AFF>
+template <int MB, int D, bool AFF, bool SPLIT>
 __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ qw,
     const float *__restrict__ am, CodeTerms ct, int N, int K, int KT, int G,
-    float *__restrict__ y, const float *__restrict__ xsum, int Mp) {
+    float *__restrict__ y, const float *__restrict__ xsum, int Mp, int kh_arg) {
+  // K in two parts (SPLIT, kh > 0 device tiles in the first) or in one
+  const int kh = SPLIT ? kh_arg : 0;
   constexpr int XR = 16 * MB;                  // x rows held (m-blocks of 16)
   constexpr int KX = skinny::kXBuf / (XR * 2); // k per chunk: 1024, 512, 256
   constexpr int TC = KX / kTileK;              // tiles per chunk: 8, 4, 2
@@ -621,9 +706,10 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
   __syncthreads();
 
   const uint32_t tcopy = (uint32_t)(lane & (pipe::kCopies - 1)) * 4;
-  f32x4 acc[MB];
+  // acc1: the sums of the first part of K when K is in two parts (kh > 0)
+  f32x4 acc[MB], acc1[MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = acc1[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   // A fragment of row mb*16 + r, logical chunk `cl` of the chunk's row
   const uint32_t arow = (uint32_t)(r * (KX * 2));
@@ -659,6 +745,13 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
       // Tiles past K run on clamped data and are not folded; neither is the
       // empty second block of a half tile (selects, not branches).
       const bool live0 = i < KT, live1 = live0 && !(half_tail && i == KT - 1);
+      if (SPLIT && i == kh) {  // the second part of K starts from zero
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          acc1[mb] = acc[mb];
+          acc[mb] = zero;
+        }
+      }
       lookups(wb[(d + 1) % D], Bs[(d + 1) & 1]);
       const bf16x8 (&B)[4] = Bs[d & 1];
       const char *xc = lds + cbuf * skinny::kXBuf + arow;
@@ -724,7 +817,8 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int m = m0 + mb * 16 + 4 * h + e;
-      if (g < G && m < M) y[(int64_t)m * N + (int64_t)g * 16 + r] = acc[mb][e];
+      const float v = SPLIT ? acc1[mb][e] + acc[mb][e] : acc[mb][e];
+      if (g < G && m < M) y[(int64_t)m * N + (int64_t)g * 16 + r] = v;
     }
 }
 
@@ -733,10 +827,14 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
 // for m < Mp (zero past M), 16 lanes (a DPP row) per (t, m): each lane adds
 // its 8 values in k order, then row16_sum; the GEMV sums the same way.
 // Consecutive 16-lane groups take consecutive m, so a wave writes 16
-// consecutive bytes of X.
+// consecutive bytes of X.  Also sets the ncnt arrival counters of a tiled
+// launch with K in two parts to zero.
 __global__ __launch_bounds__(256) void xsum_kernel(const uint16_t *__restrict__ x, int64_t M,
                                                    int64_t K, int64_t Mp, int64_t ngroups,
-                                                   float *__restrict__ X) {
+                                                   float *__restrict__ X, uint32_t *__restrict__ cnt,
+                                                   int64_t ncnt) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < ncnt; i += (int64_t)gridDim.x * 256)
+    cnt[i] = 0u;
   const int64_t gi = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
   const int q = threadIdx.x & 15;
   const bool ok = gi < ngroups;
@@ -748,64 +846,140 @@ __global__ __launch_bounds__(256) void xsum_kernel(const uint16_t *__restrict__ 
   if (ok && q == 0) X[g] = m < M ? v : 0.0f;
 }
 
+// ---------------------------------------------------------------------------
+// Launch choices, shared by both formats.
+
+// 32-bit byte offsets into x and the code buffer for the copies into LDS
+bool tile_dma_ok(int64_t M, int64_t N, int64_t K) {
+  return M * K * 2 < (int64_t(1) << 32) &&
+         (N / kTileRows) * tiles_k(K) * kTileBytes < (int64_t(1) << 32);
+}
+
+// The skinny kernel rather than the tiled one (bit-identical rows, so the
+// choice is about speed only): up to 64 rows, and up to 256 rows when the
+// tiled grid would occupy less than half of the CUs (narrow N).
+bool prefer_skinny(int64_t M, int64_t N, int64_t K, int nterm, int cus) {
+  if (!skinny_eligible(M, N, K, nterm)) return false;
+  return M <= 64 || ((N + BN - 1) / BN) * ((M + tile::kBM - 1) / tile::kBM) < cus / 2;
+}
+
+// Tiled launch: 16 row groups per workgroup unless that grid would leave
+// more than half of the CUs idle, then 8 (one workgroup per CU on twice as
+// many CUs); kh > 0 doubles the grid (two parts of K per output tile).
+struct TilePlan {
+  int rg;
+  int64_t nt, mt;
+  int kh;
+};
+TilePlan tile_plan(int64_t M, int64_t N, int64_t K, int cus) {
+  const int64_t G = N / kTileRows, mt = (M + tile::kBM - 1) / tile::kBM;
+  const int kh = split_tiles(K);
+  if (((G + 15) / 16) * mt * (kh ? 2 : 1) >= cus / 2) return {16, (G + 15) / 16, mt, kh};
+  return {8, (G + 7) / 8, mt, kh};
+}
+
+// Workspace of a tiled launch with K in two parts: one 4-byte arrival counter
+// per output tile (a 256-byte aligned block), then per output tile the sums
+// of both parts (128 x 16 RG floats each).
+size_t split_counter_bytes(int64_t ntiles) { return (size_t)((ntiles * 4 + 255) / 256 * 256); }
+size_t split_bytes(int rg, int64_t ntiles) {
+  return split_counter_bytes(ntiles) +
+         (size_t)ntiles * 2 * (size_t)(tile::kBM * kTileRows * rg) * sizeof(float);
+}
+// the larger of the two widths (the choice between them depends on the CU count)
+size_t split_bytes_max(int64_t M, int64_t N, int64_t K) {
+  if (!split_tiles(K)) return 0;
+  const int64_t G = N / kTileRows, mt = (M + tile::kBM - 1) / tile::kBM;
+  const size_t a = split_bytes(16, ((G + 15) / 16) * mt), b = split_bytes(8, ((G + 7) / 8) * mt);
+  return a > b ? a : b;
+}
+
+template <bool AFF>
+void launch_tile(const TilePlan &p, const uint16_t *x, int64_t M, const uint8_t *qw,
+                 const float *am, const CodeTerms &ct, int64_t N, int64_t K, float *y,
+                 const float *xsum, int64_t Mp, void *split_ws, hipStream_t s) {
+  const int64_t KT = tiles_k(K);
+  // one-dimensional grid, N tiles padded to a multiple of 8 (see the kernel)
+  const unsigned grid = (unsigned)((p.nt + 7) / 8 * 8 * p.mt * (p.kh ? 2 : 1));
+  uint32_t *cnt = p.kh ? reinterpret_cast<uint32_t *>(split_ws) : nullptr;
+  uint64_t *part = p.kh ? reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(split_ws) +
+                                                       split_counter_bytes(p.nt * p.mt))
+                        : nullptr;
+  auto go = [&](auto kern, int threads) {
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, x, M, qw, am, ct, N, K, KT, y,
+                       (int)p.nt, (int)p.mt, xsum, Mp, p.kh, cnt, part);
+  };
+  if (p.rg == 16)
+    p.kh ? go(gemm_tile_kernel<16, AFF, kTileMB, true>, 256 * 16 / kTileMB)
+         : go(gemm_tile_kernel<16, AFF, kTileMB, false>, 256 * 16 / kTileMB);
+  else
+    p.kh ? go(gemm_tile_kernel<8, AFF, kTileMB8, true>, 256 * 8 / kTileMB8)
+         : go(gemm_tile_kernel<8, AFF, kTileMB8, false>, 256 * 8 / kTileMB8);
+}
+
 }  // namespace
 
-size_t gemm_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  // only the tiled kernel with K in two parts needs one; the skinny kernel
+  // (up to 64 rows) and the generic kernel do not
+  if (!split_tiles(K) || !tile_dma_ok(M, N, K)) return 0;
+  if (M <= 64 && skinny_eligible(M, N, K, 1)) return 0;
+  return split_bytes_max(M, N, K);
+}
 
 namespace {
 int64_t awq_rows_padded(int64_t M) { return (M + tile::kBM - 1) / tile::kBM * tile::kBM; }
+size_t awq_xsum_bytes(int64_t M, int64_t K) {
+  return (size_t)(K / kTileK) * (size_t)awq_rows_padded(M) * sizeof(float);
+}
 }  // namespace
 
 bool awq_gemm_supported(int64_t M, int64_t N, int64_t K) {
   // 32-bit byte offsets for the copies into LDS: x, code words, x sums
   const int64_t KT = K / kTileK, Mp = awq_rows_padded(M);
-  return M >= 1 && K % kTileK == 0 && M * K * 2 < (int64_t(1) << 32) &&
-         (N / kTileRows) * KT * kTileBytes < (int64_t(1) << 32) &&
-         KT * Mp * 4 < (int64_t(1) << 32);
+  return M >= 1 && K % kTileK == 0 && tile_dma_ok(M, N, K) && KT * Mp * 4 < (int64_t(1) << 32);
 }
 
-size_t awq_gemm_workspace_bytes(int64_t M, int64_t, int64_t K) {
-  return (size_t)(K / kTileK) * (size_t)awq_rows_padded(M) * sizeof(float);
+size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  // the x sums, then what a tiled launch with K in two parts needs
+  const bool skinny_only = M <= 64 && skinny_eligible(M, N, K, 1);
+  return awq_xsum_bytes(M, K) + (skinny_only ? 0 : split_bytes_max(M, N, K));
 }
 
 hipError_t launch_awq_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, const uint32_t *pr,
                            int64_t N, int64_t K, float *y, void *ws, hipStream_t s) {
-  const int64_t KT = K / kTileK, Mp = awq_rows_padded(M), mt = Mp / tile::kBM;
+  const int64_t KT = K / kTileK, Mp = awq_rows_padded(M);
   float *X = reinterpret_cast<float *>(ws);
+  char *split_ws = reinterpret_cast<char *>(ws) + awq_xsum_bytes(M, K);
+  const int cus = device_cu_count();
+  // the codebook GEMM's choices: skinny for few rows, else the tiled kernel
+  const bool skinny = prefer_skinny(M, N, K, 1, cus);
+  const TilePlan p = tile_plan(M, N, K, cus);
   const int64_t ngroups = KT * Mp;
   hipLaunchKernelGGL(xsum_kernel, dim3((unsigned)((ngroups * 16 + 255) / 256)), dim3(256), 0, s,
-                     x, M, K, Mp, ngroups, X);
+                     x, M, K, Mp, ngroups, X, reinterpret_cast<uint32_t *>(split_ws),
+                     (!skinny && p.kh) ? p.nt * p.mt : (int64_t)0);
   const CodeTerms ct = identity_terms();
   const int64_t G = N / kTileRows;
   const float *prf = reinterpret_cast<const float *>(pr);
-  // the codebook GEMM's choices: skinny for few rows (bit-identical rows),
-  // then the workgroup width of the tiled kernel
-  if (skinny_eligible(M, N, K, 1) &&
-      (M <= 64 || ((N + BN - 1) / BN) * mt < device_cu_count() / 2)) {
+  if (skinny) {
     const unsigned gx = (unsigned)((G + skinny::kWaves - 1) / skinny::kWaves);
     const dim3 block(64 * skinny::kWaves);
+    const int kh = split_tiles(K);
+    auto go = [&](auto kern, dim3 grid) {
+      hipLaunchKernelGGL(kern, grid, block, 0, s, x, (int)M, qw, prf, ct, (int)N, (int)K, (int)KT,
+                         (int)G, y, X, (int)Mp, kh);
+    };
+    const dim3 g2(gx, (unsigned)((M + 31) / 32));
     if (M <= 16)
-      hipLaunchKernelGGL((gemm_skinny_kernel<1, 8, true>), dim3(gx), block, 0, s, x, (int)M, qw,
-                         prf, ct, (int)N, (int)K, (int)KT, (int)G, y, X, (int)Mp);
+      kh ? go(gemm_skinny_kernel<1, 8, true, true>, dim3(gx))
+         : go(gemm_skinny_kernel<1, 8, true, false>, dim3(gx));
     else
-      hipLaunchKernelGGL((gemm_skinny_kernel<2, 8, true>), dim3(gx, (unsigned)((M + 31) / 32)),
-                         block, 0, s, x, (int)M, qw, prf, ct, (int)N, (int)K, (int)KT, (int)G, y,
-                         X, (int)Mp);
+      kh ? go(gemm_skinny_kernel<2, 8, true, true>, g2)
+         : go(gemm_skinny_kernel<2, 8, true, false>, g2);
     return hipGetLastError();
   }
-  auto padded = [&](int64_t nt) { return (unsigned)((nt + 7) / 8 * 8 * mt); };
-  if (((G + 15) / 16) * mt >= device_cu_count() / 2) {
-    const int64_t nt = (G + 15) / 16;
-    hipLaunchKernelGGL((gemm_tile_kernel<16, true, kTileMB>), dim3(padded(nt)),
-                       dim3(256 * 16 / kTileMB), 0, s, x, M,
-                       qw, reinterpret_cast<const float *>(pr), ct, N, K, KT, y, (int)nt,
-                       (int)mt, X, Mp);
-  } else {
-    const int64_t nt = (G + 7) / 8;
-    hipLaunchKernelGGL((gemm_tile_kernel<8, true, 4>), dim3(padded(nt)), dim3(64 * 8), 0, s, x, M, qw,
-                       reinterpret_cast<const float *>(pr), ct, N, K, KT, y, (int)nt, (int)mt, X,
-                       Mp);
-  }
+  launch_tile<true>(p, x, M, qw, prf, ct, N, K, y, X, Mp, split_ws, s);
   return hipGetLastError();
 }
 
@@ -821,58 +995,41 @@ hipError_t launch_skinny(const uint16_t *x, int64_t M, const uint8_t *qw, const 
   const unsigned gx = (unsigned)((G + skinny::kWaves - 1) / skinny::kWaves);
   const dim3 block(64 * skinny::kWaves);
   const int KT = (int)tiles_k(K);
+  const int kh = split_tiles(K);
   // up to 16 rows: one m-block per wave; otherwise 32-row groups of x along
   // the grid's y (workgroups of one row-group block run side by side and
   // share the weights through the caches)
+  auto go = [&](auto kern, dim3 grid) {
+    hipLaunchKernelGGL(kern, grid, block, 0, s, x, (int)M, qw, am, ct, (int)N, (int)K, KT, (int)G, y,
+                       nullptr, 0, kh);
+  };
+  const dim3 g2(gx, (unsigned)((M + 31) / 32));
   if (M <= 16)
-    hipLaunchKernelGGL((gemm_skinny_kernel<1, 8, false>), dim3(gx), block, 0, s, x, (int)M, qw, am,
-                       ct, (int)N, (int)K, KT, (int)G, y, nullptr, 0);
+    kh ? go(gemm_skinny_kernel<1, 8, false, true>, dim3(gx))
+       : go(gemm_skinny_kernel<1, 8, false, false>, dim3(gx));
   else
-    hipLaunchKernelGGL((gemm_skinny_kernel<2, 8, false>), dim3(gx, (unsigned)((M + 31) / 32)),
-                       block, 0, s, x, (int)M, qw, am, ct, (int)N, (int)K, KT, (int)G, y, nullptr,
-                       0);
+    kh ? go(gemm_skinny_kernel<2, 8, false, true>, g2)
+       : go(gemm_skinny_kernel<2, 8, false, false>, g2);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, const float *am,
-                       const CodeTerms &ct, int nterm, int64_t N, int64_t K, float *y, void *,
-                       size_t, hipStream_t s) {
+                       const CodeTerms &ct, int nterm, int64_t N, int64_t K, float *y, void *ws,
+                       size_t ws_bytes, hipStream_t s) {
   const int64_t KT = tiles_k(K);
-  const uint4 *q = reinterpret_cast<const uint4 *>(qw);
-  const float2 *a = reinterpret_cast<const float2 *>(am);
-  // 32-bit byte offsets into x and the code buffer for the copies
-  const bool dma_ok = M * K * 2 < (int64_t(1) << 32) &&
-                      (N / kTileRows) * KT * kTileBytes < (int64_t(1) << 32);
-  // The skinny and tiled kernels give bit-identical rows, so the choice is
-  // about speed only: skinny up to 64 rows, and up to 256 rows when the tiled
-  // grid would occupy less than half of the CUs (narrow N).
-  if (skinny_eligible(M, N, K, nterm)) {
-    const int64_t ntile = (N + BN - 1) / BN;
-    if (M <= 64 || ntile * ((M + 127) / 128) < device_cu_count() / 2)
-      return launch_skinny(x, M, qw, am, ct, N, K, y, s);
-  }
-  if (nterm == 1 && dma_ok) {
-    // 16 row groups per workgroup (4 waves per SIMD) unless that grid would
-    // leave more than half of the CUs idle; then 8 (one workgroup per CU on
-    // twice as many CUs).
-    const int64_t G = N / kTileRows, mt = (M + tile::kBM - 1) / tile::kBM;
-    // one-dimensional grid, N tiles padded to a multiple of 8 (see the kernel)
-    auto padded = [&](int64_t nt) { return (unsigned)((nt + 7) / 8 * 8 * mt); };
-    if (((G + 15) / 16) * mt >= device_cu_count() / 2) {
-      const int64_t nt = (G + 15) / 16;
-      hipLaunchKernelGGL((gemm_tile_kernel<16, false, kTileMB>), dim3(padded(nt)),
-                         dim3(256 * 16 / kTileMB), 0, s, x, M, qw, am, ct, N, K, KT, y, (int)nt,
-                         (int)mt, nullptr, (int64_t)0);
-    } else {
-      const int64_t nt = (G + 7) / 8;
-      hipLaunchKernelGGL((gemm_tile_kernel<8, false, kTileMB8>), dim3(padded(nt)),
-                         dim3(256 * 8 / kTileMB8), 0, s, x, M, qw, am, ct, N, K, KT, y, (int)nt,
-                         (int)mt, nullptr, (int64_t)0);
-    }
+  const int cus = device_cu_count();
+  if (prefer_skinny(M, N, K, nterm, cus)) return launch_skinny(x, M, qw, am, ct, N, K, y, s);
+  if (nterm == 1 && tile_dma_ok(M, N, K)) {
+    const TilePlan p = tile_plan(M, N, K, cus);
+    if (p.kh && (!ws || ws_bytes < split_bytes(p.rg, p.nt * p.mt))) return hipErrorInvalidValue;
+    launch_tile<false>(p, x, M, qw, am, ct, N, K, y, nullptr, 0, ws, s);
     return hipGetLastError();
   }
+  const uint4 *q = reinterpret_cast<const uint4 *>(qw);
+  const float2 *a = reinterpret_cast<const float2 *>(am);
   const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM)), block(256);
-  hipLaunchKernelGGL(gemm_kernel<3>, grid, block, 0, s, x, M, q, a, ct, N, K, KT, y);
+  hipLaunchKernelGGL(gemm_kernel<3>, grid, block, 0, s, x, M, q, a, ct, N, K, KT, y,
+                     split_tiles(K));
   return hipGetLastError();
 }
 

@@ -48,6 +48,15 @@ struct Codebook {
 
 inline int64_t tiles_k(int64_t K) { return (K + kTileK - 1) / kTileK; }
 
+// Long K is summed in two parts: tiles [0, kh) and [kh, KT), each folded from
+// zero in K order, then added (one fp32 addition, which commutes).  The split
+// point depends on K alone, so every GEMM path (skinny, tiled, generic) gives
+// the same bits for a row whatever M or N.  0 = one part.
+constexpr int64_t kSplitK = 8192;
+inline int split_tiles(int64_t K) {
+  return K >= kSplitK ? (int)((tiles_k(K) + 1) / 2) : 0;
+}
+
 // The codebook 0, 1, ..., 15 as bf16 (exact): the codes of the asymmetric
 // int4 format enter the products as their integer values.
 inline CodeTerms identity_terms() {

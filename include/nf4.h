@@ -79,13 +79,16 @@ size_t nf4_qweight_bytes(int64_t N, int64_t K);
  * Returns 0 for shapes the library rejects. */
 size_t nf4_absmax_bytes(int64_t N, int64_t K);
 
-/* Bytes of scratch that nf4_gemv / nf4_gemm need for an M x N x K call on
- * the current device; the larger of the two needs.  Neither needs any on
- * this build (the GEMV sums its partials in LDS and the GEMM never splits
- * K), so this returns 0 and the workspace arguments may be NULL with 0
- * bytes; a caller that passes a workspace anyway keeps working if a later
- * build needs one (zero-filled once at allocation, calls sharing it
- * ordered). */
+/* Bytes of scratch that nf4_gemv / nf4_gemm need for an M x N x K call; the
+ * larger of the two needs.  The GEMV sums its partials in LDS and needs
+ * none.  The GEMM needs some only for K >= 8192 and M > 64, where it sums K
+ * in two halves on separate workgroups and adds them through the workspace:
+ * one 4-byte arrival counter per output tile of 128 x 128 or 128 x 256,
+ * then both halves' sums of every tile (about 8 M N bytes in all).  0
+ * otherwise, and the workspace arguments may then be NULL with 0 bytes.  A
+ * workspace must be zero-filled once at allocation; every call leaves its
+ * counters at zero again, and calls sharing one must be ordered (one
+ * stream). */
 size_t nf4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Quantize fp32 W[N][K] (row-major) into the device layout.  Per block of
@@ -168,9 +171,14 @@ nf4_status nf4_gemv_argmax(const uint16_t *x, int64_t M, const uint8_t *qweight,
 
 /* Prefill GEMM, any M >= 1: same result definition as nf4_gemv, computed on
  * bf16 matrix cores with the codes as exact bf16 operands and the fp32
- * scales applied outside the matrix product once per 64-block.  workspace:
- * at least nf4_workspace_bytes(M, N, K) bytes (may be NULL when that is 0).
- * Results are bitwise reproducible run to run. */
+ * scales applied outside the matrix product once per 64-block.  For
+ * K >= 8192 the sum runs over two halves of K (device tiles [0, kh) and
+ * [kh, ceil(K/128)), kh = ceil(ceil(K/128) / 2)), each from zero in K order,
+ * then one fp32 addition; the halves depend on K alone.  workspace: at
+ * least nf4_workspace_bytes(M, N, K) bytes, zero-filled once (may be NULL
+ * when that is 0), else NF4_ERR_NULL or NF4_ERR_WORKSPACE.  Results are
+ * bitwise reproducible run to run, and a row of y does not depend on the
+ * other rows of x. */
 nf4_status nf4_gemm(const uint16_t *x, int64_t M, const uint8_t *qweight, const float *absmax,
                     const float codebook[16], int64_t N, int64_t K, float *y, void *workspace,
                     size_t ws_bytes, hipStream_t stream);
@@ -199,8 +207,11 @@ size_t nf4_awq_params_bytes(int64_t N, int64_t K);
 
 /* Bytes of workspace nf4_awq_gemm (and nf4_awq_gemv when x does not fit its
  * on-chip path) needs: K/128 x (M rounded up to 128) floats, the sums of x
- * over every 128-k group.  0 for shapes these calls reject.  The workspace
- * is overwritten by every call; calls sharing one must be ordered. */
+ * over every 128-k group; for K >= 8192 and M > 64 also the arrival
+ * counters and half sums of nf4_gemm's two halves of K (same layout).  0
+ * for shapes these calls reject.  Every call sets what it reads (the
+ * counters included) itself, so the workspace needs no initial contents;
+ * calls sharing one must be ordered. */
 size_t nf4_awq_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Quantize fp32 W[N][K] (row-major, finite) into the device layout.  Per row
@@ -275,7 +286,8 @@ nf4_status nf4_awq_gemv_prefetch(const uint16_t *x, int64_t M, const uint8_t *qw
 /* Prefill GEMM of the int4 format, any M >= 1: the result definition of
  * nf4_awq_gemv on the tiled matrix-core kernel, after a pre-pass that writes
  * the group sums of x into the workspace (nf4_awq_workspace_bytes(M, N, K)
- * bytes, required).  Rows of y do not depend on the other rows of x.  Shapes
+ * bytes, required).  K >= 8192 is summed in the two halves nf4_gemm
+ * uses.  Rows of y do not depend on the other rows of x.  Shapes
  * whose byte offsets into x, qweight or the workspace reach 2^32 give
  * NF4_ERR_SHAPE.  Bitwise reproducible run to run. */
 nf4_status nf4_awq_gemm(const uint16_t *x, int64_t M, const uint8_t *qweight,

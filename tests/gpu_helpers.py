@@ -84,13 +84,18 @@ class Side:
     def x_dev(self, x_bits: np.ndarray):
         return self.to_dev(x_bits.astype(np.uint16).view(np.int16))
 
-    def linear(self, kind: str, xd, M: int, pw, cb, y=None):
+    def linear(self, kind: str, xd, M: int, pw, cb, y=None, ws=None):
+        """ws: a workspace to reuse (zero-filled once by the caller), else a
+        fresh zero-filled one of nf4_workspace_bytes."""
         t = self.torch
         if y is None:
             y = t.empty((M, pw.N), dtype=t.float32, device="cuda")
         fn = self.nf4.nf4_gemv if kind == "gemv" else self.nf4.nf4_gemm
         ws_bytes = self.nf4.nf4_workspace_bytes(M, pw.N, pw.K)
-        ws = t.zeros(max(ws_bytes, 16), dtype=t.uint8, device="cuda") if ws_bytes else None
+        if ws is not None:
+            assert ws.numel() >= ws_bytes
+        elif ws_bytes:
+            ws = t.zeros(max(ws_bytes, 16), dtype=t.uint8, device="cuda")
         self.stream.wait_stream(t.cuda.current_stream())  # the zero fill ran on torch's stream
         fn(xd, M, pw.qweight, pw.absmax, cb, pw.N, pw.K, y, ws, ws_bytes, stream=self.stream)
         self.sync()
@@ -143,13 +148,16 @@ class Side:
         self.sync()
         return out.cpu().numpy()
 
-    def awq_linear(self, kind: str, xd, M: int, aw, y=None):
+    def awq_linear(self, kind: str, xd, M: int, aw, y=None, ws=None):
+        """ws: a workspace to reuse (any contents), else a fresh one."""
         t = self.torch
         if y is None:
             y = t.empty((M, aw.N), dtype=t.float32, device="cuda")
         fn = self.nf4.nf4_awq_gemv if kind == "gemv" else self.nf4.nf4_awq_gemm
         ws_bytes = self.nf4.nf4_awq_workspace_bytes(M, aw.N, aw.K)
-        ws = t.empty(max(ws_bytes, 16), dtype=t.uint8, device="cuda")
+        if ws is None:
+            ws = t.empty(max(ws_bytes, 16), dtype=t.uint8, device="cuda")
+        assert ws.numel() >= ws_bytes
         self.stream.wait_stream(t.cuda.current_stream())
         fn(xd, M, aw.qweight, aw.params, aw.N, aw.K, y, ws, ws_bytes, stream=self.stream)
         self.sync()

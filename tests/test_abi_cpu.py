@@ -95,6 +95,40 @@ def test_linear_validation():
     assert g(A, 9, A, A, cbarr(), 16, 64, A, None, 0, None) == nf4.NF4_ERR_SHAPE
 
 
+def split_bytes(M, N, K):
+    """Workspace of the tiled GEMM with K in two halves (K >= 8192): per
+    output tile of 128 rows x 16 RG columns one 4-byte counter (the counters
+    padded to 256 bytes) and the two halves' fp32 sums; the larger of the
+    two workgroup widths RG = 16 and 8."""
+    if K < 8192:
+        return 0
+    G, mt = N // 16, -(-M // 128)
+
+    def width(rg):
+        tiles = -(-G // rg) * mt
+        return -(-tiles * 4 // 256) * 256 + tiles * 2 * 128 * 16 * rg * 4
+    return max(width(16), width(8))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 3584, 18944), (64, 3584, 18944), (65, 3584, 18944),
+                                   (1024, 3584, 18944), (1024, 3072, 9216), (300, 256, 8128),
+                                   (300, 256, 8192), (1024, 37888, 3584), (14449, 152064, 3584)])
+def test_gemm_workspace_bytes(M, N, K):
+    """Only nf4_gemm past 64 rows with K >= 8192 needs a workspace."""
+    assert nf4.nf4_workspace_bytes(M, N, K) == (0 if M <= 64 else split_bytes(M, N, K))
+    if M > 64 and K >= 8192:
+        assert nf4.nf4_workspace_bytes(M, N, K) >= 8 * M * N
+
+
+def test_gemm_workspace_validation():
+    m = lambda *a: call("nf4_gemm", *a)
+    M, N, K = 1024, 3584, 18944
+    need = nf4.nf4_workspace_bytes(M, N, K)
+    assert m(A, M, A, A, cbarr(), N, K, A, None, 0, None) == nf4.NF4_ERR_NULL
+    assert m(A, M, A, A, cbarr(), N, K, A, A, need - 1, None) == nf4.NF4_ERR_WORKSPACE
+    assert m(A, M, A, A, cbarr(), N, K, A, A + 8, need, None) == nf4.NF4_ERR_ALIGN
+
+
 def test_pack_validation():
     p = lambda *a: call("nf4_pack", *a)
     assert p(None, 16, 64, cbarr(), A, A, None) == nf4.NF4_ERR_NULL
@@ -189,9 +223,10 @@ def test_binding_raises_named_errors():
 @pytest.mark.parametrize("N,K", [(16, 128), (48, 256), (4608, 3584), (3584, 18944)])
 def test_awq_size_queries(N, K):
     assert nf4.nf4_awq_params_bytes(N, K) == (N // 16) * (K // 128) * 64 == 4 * N * K // 128
-    for M in (1, 8, 127, 128, 129, 14449):
+    for M in (1, 8, 64, 65, 127, 128, 129, 14449):
         Mp = -(-M // 128) * 128
-        assert nf4.nf4_awq_workspace_bytes(M, N, K) == (K // 128) * Mp * 4
+        extra = 0 if M <= 64 else split_bytes(M, N, K)
+        assert nf4.nf4_awq_workspace_bytes(M, N, K) == (K // 128) * Mp * 4 + extra
 
 
 @pytest.mark.parametrize("N,K", [(16, 64), (16, 192), (24, 128), (0, 128), (16, 0)])

@@ -128,7 +128,8 @@ def test_awq_gemv_edges(side, M, N, K):
 
 
 GEMM_EDGES = [(1, 48, 128), (9, 272, 256), (100, 16, 384), (128, 512, 3584), (129, 160, 1024),
-              (300, 272, 640), (257, 2048, 256), (64, 64, 18944)]
+              (300, 272, 640), (257, 2048, 256), (64, 64, 18944), (300, 272, 8320),
+              (129, 512, 8192)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_EDGES)
@@ -177,8 +178,11 @@ def test_awq_zero_point_cancellation(side, kind):
     say(f"  rel-L2 {rel:.2e}, worst element {worst:.3f} x bar")
 
 
-def test_awq_gemm_deterministic_and_batch_independent(side):
-    N, K = 272, 1024
+@pytest.mark.parametrize("N,K", [(272, 1024), (272, 8320)])
+def test_awq_gemm_deterministic_and_batch_independent(side, N, K):
+    """Rows do not depend on the batch (K = 8320: summed in two halves on
+    the tiled and the skinny path alike), and a reused workspace full of
+    stale bytes gives the same bits (every call sets what it reads)."""
     packed, scales, zeros, aw = awq_case(side, N, K, mid=34)
     x = synth.activations(0, 300, K, stream=12)
     y1 = side.awq_run("gemm", x, aw)
@@ -186,6 +190,12 @@ def test_awq_gemm_deterministic_and_batch_independent(side):
     np.testing.assert_array_equal(y1, y2)
     for lo, hi in ((0, 1), (5, 13), (128, 300), (290, 300)):
         np.testing.assert_array_equal(side.awq_run("gemm", x[lo:hi], aw), y1[lo:hi])
+    t = side.torch
+    ws = t.full((side.nf4.nf4_awq_workspace_bytes(300, N, K),), 0xFF, dtype=t.uint8,
+                device="cuda")
+    for _ in range(2):
+        y3 = side.awq_linear("gemm", side.x_dev(x), 300, aw, ws=ws).cpu().numpy()
+        np.testing.assert_array_equal(y3, y1)
 
 
 def test_awq_gemv_deterministic_and_agrees_with_gemm(side):
@@ -269,6 +279,9 @@ def test_awq_qwen_prefill_full_size(side, name):
     yr, b = oracle.awq_linear(x[toks], packed, scales, zeros)
     assert_linear_ok(y[toks][:, rows], yr, b, f"awq prefill {name}")
     assert np.all(np.isfinite(y))
+    np.testing.assert_array_equal(side.awq_run("gemm", x, aw), y)
+    for m in (0, 1023):
+        np.testing.assert_array_equal(side.awq_run("gemm", x[m:m + 1], aw), y[m:m + 1])
 
 
 def test_awq_long_prefill_one_call(side):

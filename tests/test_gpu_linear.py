@@ -148,12 +148,15 @@ def test_deterministic_and_batch_independent(side, cb, kind):
         np.testing.assert_array_equal(side.run(kind, x[m:m + 1], pw, cb), y1[m:m + 1])
 
 
-@pytest.mark.parametrize("N,K", [(512, 3584), (256, 18944), (272, 704)])
+@pytest.mark.parametrize("N,K", [(512, 3584), (256, 18944), (272, 704), (272, 8256),
+                                 (512, 8192)])
 def test_gemm_skinny_and_tiled_rows_identical(side, cb, N, K):
     """nf4_gemm runs rows of a narrow batch on the skinny path (one wave per
     row group streaming all of K) and a wide batch on the tiled path; both
     perform the same operations per output, so rows agree bit for bit
-    whichever path the batch size selects (K = 704 ends in a half tile)."""
+    whichever path the batch size selects (K = 704 and 8256 end in a half
+    tile; from K = 8192 on, K is summed in two halves, on two workgroups of
+    the tiled path and one after the other in a skinny wave)."""
     packed, absmax, pw = case(side, cb, N, K, mid=27)
     x = synth.activations(0, 300, K, stream=3)
     yt = side.run("gemm", x, pw, cb)            # 300 rows: tiled
@@ -162,6 +165,29 @@ def test_gemm_skinny_and_tiled_rows_identical(side, cb, N, K):
                                       err_msg=f"M={M} rows {m0}..")
     yr, b = oracle.linear(x[[0, 17, 299]], packed, absmax, cb)
     assert_linear_ok(yt[[0, 17, 299]], yr, b, f"tiled N={N} K={K}")
+
+
+def test_gemm_k_halves_repeat(side, cb):
+    """K = 8320 (65 device tiles) is summed in halves of 33 and 32 tiles that
+    meet through the workspace: calls with other inputs in between leave
+    nothing behind (the arrival counters return to zero), and sampled rows
+    match the oracle."""
+    N, K, M = 1024, 8320, 520
+    packed, absmax, pw = case(side, cb, N, K, mid=28)
+    x1 = synth.activations(0, M, K, stream=5)
+    x2 = synth.activations(0, M, K, stream=6)
+    t = side.torch
+    ws = t.zeros(side.nf4.nf4_workspace_bytes(M, N, K), dtype=t.uint8, device="cuda")
+    assert ws.numel() > 0
+    run = lambda x: side.linear("gemm", side.x_dev(x), M, pw, cb, ws=ws).cpu().numpy()
+    y1 = run(x1)
+    y2 = run(x2)
+    np.testing.assert_array_equal(run(x1), y1)
+    np.testing.assert_array_equal(side.run("gemm", x2, pw, cb), y2)  # a fresh workspace
+    picks = np.array([0, 127, 128, 300, 519])
+    for x, y in ((x1, y1), (x2, y2)):
+        yr, b = oracle.linear(x[picks], packed, absmax, cb)
+        assert_linear_ok(y[picks], yr, b, "K halves")
 
 
 def test_gemv_and_gemm_agree(side, cb):
@@ -284,6 +310,11 @@ def test_qwen_prefill_full_size(side, cb, name):
     yr, b = oracle.linear(x[toks], packed, absmax, cb)
     assert_linear_ok(y[toks][:, rows], yr, b, f"prefill {name}")
     assert np.all(np.isfinite(y))
+    # the same bits again (down: the halves' counters are back at zero), and
+    # single rows on the skinny path equal the rows of the tiled launch
+    np.testing.assert_array_equal(side.run("gemm", x, pw, cb), y)
+    for m in (0, 1023):
+        np.testing.assert_array_equal(side.run("gemm", x[m:m + 1], pw, cb), y[m:m + 1])
 
 
 def test_long_audio_prefill_chunks_and_tail(side, cb):
