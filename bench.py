@@ -62,6 +62,14 @@ LINEARS = [("qkv", HIDDEN + 2 * KV, HIDDEN), ("o", HIDDEN, HIDDEN),
 PREFILL_M = 1024
 TAIL_M = 113  # last chunk of the 14449-row long-audio prompt
 DOMINANT = ("gate_up", 2 * MLP, HIDDEN)
+# the unfused 7-linear sequence: (linear, fused matrix, first row, end row)
+UNFUSED = [("q", "qkv", 0, HIDDEN), ("k", "qkv", HIDDEN, HIDDEN + KV),
+           ("v", "qkv", HIDDEN + KV, HIDDEN + 2 * KV), ("o", "o", 0, HIDDEN),
+           ("gate", "gate_up", 0, MLP), ("up", "gate_up", MLP, 2 * MLP), ("down", "down", 0, HIDDEN)]
+# Voxtral/Mistral-shaped decoder (hidden 3072, q 4096, k and v 1024 each, FFN 9216)
+VOXTRAL_LAYERS = 26
+VOXTRAL = [("qkv", 6144, 3072), ("wo", 3072, 4096), ("w13", 18432, 3072), ("w2", 3072, 9216)]
+LONG_M, LONG_CHUNKS = 14449, 14  # the long-audio prompt: 14 x 1024 rows + the 113-row tail
 
 # HBM traffic per launch of the dominant kernels, from rocprofv3 --pmc runs of
 # `python bench.py --pmc-pass` (profiles/hbm_traffic_gate_up.md): counter KiB
@@ -69,12 +77,12 @@ DOMINANT = ("gate_up", 2 * MLP, HIDDEN)
 TRAFFIC = {
     "gemv": {"source": "gemv.hip", "fetch_kib": 42729, "write_kib": 148,
              "sha256": "5f77a7ec2181f4cf3a6616c5591104233b07a441586fca9cda18542272ac5a99"},
-    "gemm": {"source": "gemm.hip", "fetch_kib": 180754, "write_kib": 151931,
-             "sha256": "e9f716650e6cef0f4dd051301ff858a2d6bb98bed3d73b1ec43b204852f90039"},
+    "gemm": {"source": "gemm.hip", "fetch_kib": 180757, "write_kib": 151901,
+             "sha256": "16e68f398875e035410e4cb825c10b861c6f6c54bfe293cb32957c3956194c70"},
     "awq_gemv": {"source": "gemv.hip", "fetch_kib": 40366, "write_kib": 148,
                  "sha256": "5f77a7ec2181f4cf3a6616c5591104233b07a441586fca9cda18542272ac5a99"},
-    "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180912, "write_kib": 151918,
-                 "sha256": "e9f716650e6cef0f4dd051301ff858a2d6bb98bed3d73b1ec43b204852f90039"},
+    "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180912, "write_kib": 151892,
+                 "sha256": "16e68f398875e035410e4cb825c10b861c6f6c54bfe293cb32957c3956194c70"},
 }
 COPY_CALIBRATION = {"fetch_kib_per_gib": 524308, "write_kib_per_gib": 1048576}
 
@@ -478,6 +486,88 @@ def main():
     dec_ms, pre_ms = float(np.mean(dec_all)), float(np.mean(pre_all))
     log(f"[bench] {args.steps} timed steps: decode {dec_ms:.3f} ms, prefill {pre_ms:.3f} ms")
 
+    # ---- the unfused 7-linear sequence, on row views of the fused weights
+    # (the parts of a fused matrix are weights in the device layout)
+    views = [{u: mdl.weights[l][f].rows(n0, n1) for u, f, n0, n1 in UNFUSED}
+             for l in range(LAYERS)]
+    yu1 = {u: torch.empty((1, n1 - n0), dtype=torch.float32, device="cuda")
+           for u, _, n0, n1 in UNFUSED}
+    yup = {u: torch.empty((PREFILL_M, n1 - n0), dtype=torch.float32, device="cuda")
+           for u, _, n0, n1 in UNFUSED}
+    uorder = [(u, l) for l in range(LAYERS) for u, _, _, _ in UNFUSED]
+    ulabels = ["u:" + u for u, _ in uorder]
+
+    def decode_unfused():
+        for i, (u, l) in enumerate(uorder):
+            pw = views[l][u]
+            nx = views[uorder[i + 1][1]][uorder[i + 1][0]] if i + 1 < len(uorder) else mdl.lm_head
+            nf4.nf4_gemv_prefetch(mdl.x1[pw.K], 1, pw.qweight, pw.absmax, cb, pw.N, pw.K, yu1[u],
+                                  mdl.ws, mdl.ws_bytes, nx.qweight, nx.absmax, nx.N, nx.K)
+        mdl.gemv("lm_head", 0)
+
+    def prefill_unfused():
+        for u, l in uorder:
+            pw = views[l][u]
+            nf4.nf4_gemm(mdl.xp[pw.K], PREFILL_M, pw.qweight, pw.absmax, cb, pw.N, pw.K, yup[u],
+                         mdl.ws, mdl.ws_bytes)
+
+    decu_ms = graph_ms(torch, s, decode_unfused, reps)
+    launches += [("gemv", n) for _ in range(reps + 1) for n in ulabels + ["lm_head"]]
+    preu_ms = graph_ms(torch, s, prefill_unfused, reps)
+    launches += [("gemm", n) for _ in range(reps + 1) for n in ulabels]
+    log(f"[bench] unfused: decode {decu_ms:.3f} ms, prefill {preu_ms:.3f} ms")
+
+    # ---- Voxtral-shaped decode: 26 layers x 4 fused linears at M = 1
+    t1 = time.perf_counter()
+    vgen = torch.Generator(device="cuda")
+    vw = []
+    with torch.cuda.stream(s):
+        for l in range(VOXTRAL_LAYERS):
+            lw = {}
+            for i, (vn, N_, K_) in enumerate(VOXTRAL):
+                vgen.manual_seed(args.seed + 0x10000 + 16 * l + i)
+                W = torch.randn((N_, K_), generator=vgen, device="cuda") * 0.02
+                lw[vn] = nf4.pack_weight(W, cb, stream=s)
+                del W
+            vw.append(lw)
+    s.synchronize()
+    torch.cuda.empty_cache()
+    vx = {}
+    for K_ in sorted({K_ for _, _, K_ in VOXTRAL}):
+        vgen.manual_seed(args.seed + 0x20000 + K_)
+        vx[K_] = torch.randn((1, K_), generator=vgen, device="cuda").to(torch.bfloat16).view(
+            torch.int16)
+    vy = {vn: torch.empty((1, N_), dtype=torch.float32, device="cuda") for vn, N_, _ in VOXTRAL}
+    torch.cuda.synchronize()
+    log(f"[bench] Voxtral: packed {VOXTRAL_LAYERS} layers in {time.perf_counter() - t1:.1f} s")
+    vorder = [(vn, l) for l in range(VOXTRAL_LAYERS) for vn, _, _ in VOXTRAL]
+    vbytes = sum(packed_bytes(N_, K_) for _, N_, K_ in VOXTRAL) * VOXTRAL_LAYERS
+
+    def voxtral_decode():
+        for i, (vn, l) in enumerate(vorder):
+            pw = vw[l][vn]
+            if i + 1 < len(vorder):
+                nx = vw[vorder[i + 1][1]][vorder[i + 1][0]]
+                nf4.nf4_gemv_prefetch(vx[pw.K], 1, pw.qweight, pw.absmax, cb, pw.N, pw.K,
+                                      vy[vn], mdl.ws, mdl.ws_bytes, nx.qweight, nx.absmax, nx.N,
+                                      nx.K)
+            else:
+                nf4.nf4_gemv(vx[pw.K], 1, pw.qweight, pw.absmax, cb, pw.N, pw.K, vy[vn], mdl.ws,
+                             mdl.ws_bytes)
+
+    vdec_ms = graph_ms(torch, s, voxtral_decode, max(args.steps, 5))
+    launches += [("gemv", "vx:" + vn) for _ in range(max(args.steps, 5) + 1) for vn, _ in vorder]
+    log(f"[bench] Voxtral decode: {vdec_ms:.3f} ms per step")
+    del vw
+    torch.cuda.empty_cache()
+
+    # ---- the floor of one launch inside a replayed graph: a graph of as many
+    # one-element kernels as the decode step has launches
+    one = torch.zeros(1, device="cuda")
+    nlaunch = len(decode_order)
+    floor_us = graph_ms(torch, s, lambda: [one.add_(1.0) for _ in range(nlaunch)], reps) \
+        * 1e3 / nlaunch
+
     if args.launch_log:
         with open(args.launch_log, "w") as f:
             json.dump(launches, f)
@@ -516,6 +606,26 @@ def main():
         "prefill_tail": {"M": TAIL_M, "ms": round(tail_ms, 3),
                          "value": round(tail_flop / (tail_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
                          "note": "28 layers x 4 fused linears at M=113 (skinny path for narrow N)"},
+        "decode_unfused": {"value": round(decode_bytes / (decu_ms * 1e-3) / 1e9, 1),
+                           "unit": "GB/s", "ms": round(decu_ms, 4),
+                           "note": "28 x {q, k, v, o, gate, up, down} + lm_head = 197 launches "
+                                   "on row views of the fused weights, read-ahead hints"},
+        "prefill_unfused": {"value": round(prefill_flop / (preu_ms * 1e-3) / 1e12, 2),
+                            "unit": "TFLOP/s", "ms": round(preu_ms, 3),
+                            "note": "28 x 7 nf4_gemm calls at M=1024"},
+        "voxtral_decode": {"value": round(vbytes / (vdec_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                           "ms": round(vdec_ms, 4), "packed_bytes": vbytes,
+                           "note": f"{VOXTRAL_LAYERS} layers x {{q|k|v 6144x3072, wo 3072x4096, "
+                                   "w1|w3 18432x3072, w2 3072x9216}, M=1, read-ahead hints"},
+        "long_audio": {"M": LONG_M,
+                       "value": round(2 * LONG_M * sum(N_ * K_ for _, N_, K_ in LINEARS) * LAYERS
+                                      / ((LONG_CHUNKS * pre_ms + tail_ms) * 1e-3) / 1e12, 2),
+                       "unit": "TFLOP/s", "ms": round(LONG_CHUNKS * pre_ms + tail_ms, 2),
+                       "note": "14 prefill steps at M=1024 and the 113-row tail step, as timed "
+                               "above (1680 nf4_gemm calls)"},
+        "launch_floor_us": {"value": round(floor_us, 2),
+                            "note": f"a replayed graph of {nlaunch} one-element torch kernels, "
+                                    "per launch"},
         "lm_head_argmax": {"gemv_us": round(head_us, 2), "gemv_argmax_us": round(head_amx_us, 2),
                            "host_copy_bytes": {"logits": 4 * VOCAB, "index": 4},
                            "kernel": f"nf4_gemv_argmax N={VOCAB} K={HIDDEN} M=1"},

@@ -22,11 +22,11 @@
 // whatever the tile shape or M: the K order, the MFMA k-split and the
 // per-block fold never depend on the launch, so a row of y does not depend on
 // the other rows in the batch, and a column slice of a fused matrix equals
-// the separate matrix's output.  The one split of K is fixed by K alone
-// (split_tiles: two halves for K >= 8192, each folded from zero, then added
-// once): the tiled kernel runs the halves on two workgroups that meet
-// through the workspace, the skinny and generic kernels one after the other
-// in a wave.
+// the separate matrix's output when both have the same parts of K.  The
+// parts are fixed by (N, K) alone (k_parts: two halves for K >= 8192, more
+// for narrow N), each folded from zero, then added in part order: the tiled
+// kernel runs the parts on separate workgroups that meet through the
+// workspace, the skinny and generic kernels one after the other in a wave.
 #include <type_traits>
 
 #include "nf4_internal.h"
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
                                                    const uint4 *__restrict__ qw,
                                                    const float2 *__restrict__ am, CodeTerms ct,
                                                    int64_t N, int64_t K, int64_t KT,
-                                                   float *__restrict__ y, int kh) {
+                                                   float *__restrict__ y, int np) {
   __shared__ uint32_t table[NTERM * kPairWords];
   __shared__ __attribute__((aligned(16))) uint16_t xs[BM * XS];
 
@@ -63,22 +63,26 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
   const int64_t G = N / kTileRows;
   const uint32_t *tab = table + (lane & (kPairCopies - 1));
 
-  // acc1: the sums of the first part of K when K is in two parts (kh > 0)
-  f32x4 acc[4][4], acc1[4][4];
+  // K in np parts: tot adds the sums of the finished parts in part order;
+  // the next part starts at tile `cut`
+  f32x4 acc[4][4], tot[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = acc1[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < 4; ++b) acc[a][b] = tot[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int jn = 1, cut = np > 1 ? part_begin(1, KT, np) : -1;
 
   for (int64_t t = 0; t < KT; ++t) {
-    if (kh > 0 && t == kh) {  // the second part of K starts from zero
+    if (t == cut) {  // the next part of K starts from zero
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          acc1[a][b] = acc[a][b];
+          tot[a][b] = jn == 1 ? acc[a][b] : tot[a][b] + acc[a][b];
           acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+      ++jn;
+      cut = jn < np ? part_begin(jn, KT, np) : -1;
     }
     __syncthreads();  // previous x tile fully consumed (and table built)
 #pragma unroll
@@ -156,7 +160,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t row = m0 + wm * 64 + mm * 16 + 4 * h + i;
-        const float v = kh ? acc1[mm][nn][i] + acc[mm][nn][i] : acc[mm][nn][i];
+        const float v = np > 1 ? tot[mm][nn][i] + acc[mm][nn][i] : acc[mm][nn][i];
         if (row < M) y[row * N + col] = v;
       }
     }
@@ -236,11 +240,11 @@ __device__ inline void wait_copies_and_barrier() {
 // zero (two steps; P = sum x (1 + q/16)), g = fmaf(-(16 + z)/16, X, P),
 // acc = fmaf(16 s, g, acc).
 //
-// K in two parts (SPLIT, K >= 8192): the grid holds two workgroups per
-// output tile, one per half of K, each summing its half from zero; they meet
-// through the workspace (sums stored, arrival counted, the second adds the
-// first's sums to its own and stores y), which costs one extra write and read
-// of the tile but fills the CUs with wide tiles where N alone would not.
+// K in np parts (SPLIT: long K, or narrow N): the grid holds np workgroups
+// per output tile, one per part of K, each summing its part from zero; they
+// meet through the workspace (sums stored, arrival counted, the last adds
+// all parts in part order and stores y), which costs an extra write and read
+// of the tile per part but fills the CUs where N alone would not.
 namespace tile {
 constexpr int kBM = 128;
 constexpr int kTable = 256 * 64 * 4;            // one copy per lane
@@ -274,10 +278,10 @@ __global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
     const uint16_t *__restrict__ x, int64_t M, const uint8_t *__restrict__ qw,
     const float *__restrict__ am, CodeTerms ct, int64_t N, int64_t K, int64_t KT,
     float *__restrict__ y, int ntn, int ntm, const float *__restrict__ xsum, int64_t Mp,
-    int kh_arg, uint32_t *__restrict__ cnt, uint64_t *__restrict__ part) {
+    int np_arg, uint32_t *__restrict__ cnt, uint64_t *__restrict__ part) {
   using L = tile::Map<RG, AFF, MB>;
-  // K in two parts (SPLIT, kh > 0 device tiles in the first) or in one
-  const int kh = SPLIT ? kh_arg : 0;
+  // K in np parts (SPLIT) or in one
+  const int np = SPLIT ? np_arg : 1;
   // the only static LDS array, so the table sits at LDS address 0
   __shared__ __attribute__((aligned(16))) char lds[L::kBytes];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -285,25 +289,26 @@ __global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
   const int r = lane & 15, h = lane >> 4;
   const int wm = wave / L::kWN, wn = wave % L::kWN;
   // Tile order for the 8 XCDs, each with its own L2: consecutive workgroups
-  // go to consecutive XCDs, so workgroup b runs on XCD b % 8.  XCD k takes
-  // the N tiles k, k+8, ... and, for each, all M tiles one after the other,
-  // so the workgroups that expand one weight tile share an L2.  Workgroups
-  // past the last N tile (the grid is padded to a multiple of 8 N tiles)
-  // leave before any barrier.  With K in two parts (kh > 0) the two
-  // workgroups of an output tile are neighbours in that order, part kc.
-  const int ns = kh ? 2 : 1;
-  const int xcd = (int)(blockIdx.x & 7), sl = (int)(blockIdx.x >> 3);
-  const int kc = sl % ns, slot = sl / ns;
-  const int nt = (slot / ntm) * 8 + xcd, mt = slot % ntm;
-  if (nt >= ntn) return;
+  // go to consecutive XCDs, so workgroup b runs on XCD b % 8.  A unit is an
+  // N tile and a part of K (u = nt np + kc, the weight tile one workgroup
+  // expands); XCD k takes the units k, k+8, ... and, for each, all M tiles
+  // one after the other, so the workgroups that expand one weight tile share
+  // an L2.  Workgroups past the last unit (the grid is padded to a multiple
+  // of 8 units) leave before any barrier.
+  const int xcd = (int)(blockIdx.x & 7), slot = (int)(blockIdx.x >> 3);
+  const int u = (slot / ntm) * 8 + xcd, mt = slot % ntm;
+  if (u >= ntn * np) return;
+  const int nt = u / np, kc = u - nt * np;
   const int64_t m0 = (int64_t)mt * tile::kBM;
   const int64_t gblk = (int64_t)nt * RG;
   const int64_t G = N / kTileRows;
-  // this workgroup's part of K: device tiles [t0, t0 + KTp), S 64-k steps;
-  // every source is addressed from the part's first tile
-  const int t0 = kc ? kh : 0;
-  const int64_t KTp = kh ? (kc ? KT - kh : kh) : KT;
-  const int S = kh ? (kc ? (int)(K / kBK) - 2 * kh : 2 * kh) : (int)(K / kBK);
+  // this workgroup's part of K: device tiles [t0, t1), S 64-k steps (the
+  // last part may end in a half tile); every source is addressed from the
+  // part's first tile
+  const int t0 = SPLIT ? part_begin(kc, KT, np) : 0;
+  const int t1 = SPLIT ? part_begin(kc + 1, KT, np) : (int)KT;
+  const int64_t KTp = t1 - t0;
+  const int S = (int)(2 * (int64_t)t1 < K / kBK ? 2 * (int64_t)t1 : K / kBK) - 2 * t0;
   x += (int64_t)t0 * kTileK;
   qw += (int64_t)t0 * kTileBytes;
   am += (int64_t)t0 * (L::kScaleBytes / 4);
@@ -523,15 +528,14 @@ __global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   if (SPLIT) {
-    // K in two parts: each workgroup of the output tile stores its sums
+    // K in np parts: each workgroup of the output tile stores its sums
     // (thread-major, 8 bytes per lane and store) device-wide, then counts its
-    // arrival; the second to arrive adds the other part to its own and
-    // stores y, then sets the counter back to zero.  Both orders give the
-    // same bits: one fp32 addition commutes.
+    // arrival; the last to arrive adds the parts' sums in part order (its
+    // own from registers), stores y and sets the counter back to zero.
     constexpr int NV = MB * 4;  // 8-byte pairs of sums per thread
     const int64_t tile_id = (int64_t)nt * ntm + mt;
-    uint64_t *mine = part + (tile_id * 2 + kc) * (int64_t)(L::kThreads * NV) + tid;
-    const uint64_t *other = part + (tile_id * 2 + (kc ^ 1)) * (int64_t)(L::kThreads * NV) + tid;
+    const int64_t slot_u64 = (int64_t)L::kThreads * NV;
+    uint64_t *mine = part + (tile_id * np + kc) * slot_u64 + tid;
 #pragma unroll
     for (int mm = 0; mm < MB; ++mm)
 #pragma unroll
@@ -551,18 +555,38 @@ __global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
       *flag = (int)__hip_atomic_fetch_add(cnt + tile_id, 1u, __ATOMIC_RELAXED,
                                           __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    if (*flag == 0) return;
+    if (*flag != np - 1) return;
+    f32x4 tot[MB][2], pj[MB][2];
+    for (int j = 0; j < np; ++j) {
+      if (j == kc) {
+#pragma unroll
+        for (int mm = 0; mm < MB; ++mm)
+#pragma unroll
+          for (int nn = 0; nn < 2; ++nn) pj[mm][nn] = acc[mm][nn];
+      } else {
+        // one batch of loads per part
+        const uint64_t *src = part + (tile_id * np + j) * slot_u64 + tid;
+#pragma unroll
+        for (int mm = 0; mm < MB; ++mm)
+#pragma unroll
+          for (int nn = 0; nn < 2; ++nn)
+#pragma unroll
+            for (int i2 = 0; i2 < 2; ++i2) {
+              const uint64_t v = __hip_atomic_load(src + ((mm * 2 + nn) * 2 + i2) * L::kThreads,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              pj[mm][nn][2 * i2] = __uint_as_float((uint32_t)v);
+              pj[mm][nn][2 * i2 + 1] = __uint_as_float((uint32_t)(v >> 32));
+            }
+      }
+#pragma unroll
+      for (int mm = 0; mm < MB; ++mm)
+#pragma unroll
+        for (int nn = 0; nn < 2; ++nn) tot[mm][nn] = j ? tot[mm][nn] + pj[mm][nn] : pj[mm][nn];
+    }
 #pragma unroll
     for (int mm = 0; mm < MB; ++mm)
 #pragma unroll
-      for (int nn = 0; nn < 2; ++nn)
-#pragma unroll
-        for (int i2 = 0; i2 < 2; ++i2) {
-          const uint64_t v = __hip_atomic_load(other + ((mm * 2 + nn) * 2 + i2) * L::kThreads,
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          acc[mm][nn][2 * i2] += __uint_as_float((uint32_t)v);
-          acc[mm][nn][2 * i2 + 1] += __uint_as_float((uint32_t)(v >> 32));
-        }
+      for (int nn = 0; nn < 2; ++nn) acc[mm][nn] = tot[mm][nn];
     if (tid == 0) __hip_atomic_store(cnt + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
@@ -610,9 +634,9 @@ template <int MB, int D, bool AFF, bool SPLIT>
 __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ qw,
     const float *__restrict__ am, CodeTerms ct, int N, int K, int KT, int G,
-    float *__restrict__ y, const float *__restrict__ xsum, int Mp, int kh_arg) {
-  // K in two parts (SPLIT, kh > 0 device tiles in the first) or in one
-  const int kh = SPLIT ? kh_arg : 0;
+    float *__restrict__ y, const float *__restrict__ xsum, int Mp, int np_arg) {
+  // K in np parts (SPLIT) or in one
+  const int np = SPLIT ? np_arg : 1;
   constexpr int XR = 16 * MB;                  // x rows held (m-blocks of 16)
   constexpr int KX = skinny::kXBuf / (XR * 2); // k per chunk: 1024, 512, 256
   constexpr int TC = KX / kTileK;              // tiles per chunk: 8, 4, 2
@@ -706,10 +730,12 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
   __syncthreads();
 
   const uint32_t tcopy = (uint32_t)(lane & (pipe::kCopies - 1)) * 4;
-  // acc1: the sums of the first part of K when K is in two parts (kh > 0)
-  f32x4 acc[MB], acc1[MB];
+  // K in parts: tot adds the sums of the finished parts in part order; the
+  // next part starts at tile `cut`
+  f32x4 acc[MB], tot[MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = acc1[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = tot[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int jn = 1, cut = SPLIT ? part_begin(1, KT, np) : -1;
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   // A fragment of row mb*16 + r, logical chunk `cl` of the chunk's row
   const uint32_t arow = (uint32_t)(r * (KX * 2));
@@ -745,12 +771,14 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
       // Tiles past K run on clamped data and are not folded; neither is the
       // empty second block of a half tile (selects, not branches).
       const bool live0 = i < KT, live1 = live0 && !(half_tail && i == KT - 1);
-      if (SPLIT && i == kh) {  // the second part of K starts from zero
+      if (SPLIT && i == cut) {  // the next part of K starts from zero
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          acc1[mb] = acc[mb];
+          tot[mb] = jn == 1 ? acc[mb] : tot[mb] + acc[mb];
           acc[mb] = zero;
         }
+        ++jn;
+        cut = jn < np ? part_begin(jn, KT, np) : -1;
       }
       lookups(wb[(d + 1) % D], Bs[(d + 1) & 1]);
       const bf16x8 (&B)[4] = Bs[d & 1];
@@ -817,7 +845,7 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int m = m0 + mb * 16 + 4 * h + e;
-      const float v = SPLIT ? acc1[mb][e] + acc[mb][e] : acc[mb][e];
+      const float v = SPLIT ? tot[mb][e] + acc[mb][e] : acc[mb][e];
       if (g < G && m < M) y[(int64_t)m * N + (int64_t)g * 16 + r] = v;
     }
 }
@@ -865,32 +893,34 @@ bool prefer_skinny(int64_t M, int64_t N, int64_t K, int nterm, int cus) {
 
 // Tiled launch: 16 row groups per workgroup unless that grid would leave
 // more than half of the CUs idle, then 8 (one workgroup per CU on twice as
-// many CUs); kh > 0 doubles the grid (two parts of K per output tile).
+// many CUs); np parts of K multiply the grid by np.
 struct TilePlan {
   int rg;
   int64_t nt, mt;
-  int kh;
+  int np;
 };
 TilePlan tile_plan(int64_t M, int64_t N, int64_t K, int cus) {
   const int64_t G = N / kTileRows, mt = (M + tile::kBM - 1) / tile::kBM;
-  const int kh = split_tiles(K);
-  if (((G + 15) / 16) * mt * (kh ? 2 : 1) >= cus / 2) return {16, (G + 15) / 16, mt, kh};
-  return {8, (G + 7) / 8, mt, kh};
+  const int np = k_parts(N, K);
+  if (((G + 15) / 16) * mt * np >= cus / 2) return {16, (G + 15) / 16, mt, np};
+  return {8, (G + 7) / 8, mt, np};
 }
 
-// Workspace of a tiled launch with K in two parts: one 4-byte arrival counter
-// per output tile (a 256-byte aligned block), then per output tile the sums
-// of both parts (128 x 16 RG floats each).
+// Workspace of a tiled launch with K in np > 1 parts: one 4-byte arrival
+// counter per output tile (a 256-byte aligned block), then per output tile
+// the sums of every part (128 x 16 RG floats each).
 size_t split_counter_bytes(int64_t ntiles) { return (size_t)((ntiles * 4 + 255) / 256 * 256); }
-size_t split_bytes(int rg, int64_t ntiles) {
+size_t split_bytes(int rg, int64_t ntiles, int np) {
   return split_counter_bytes(ntiles) +
-         (size_t)ntiles * 2 * (size_t)(tile::kBM * kTileRows * rg) * sizeof(float);
+         (size_t)ntiles * np * (size_t)(tile::kBM * kTileRows * rg) * sizeof(float);
 }
 // the larger of the two widths (the choice between them depends on the CU count)
 size_t split_bytes_max(int64_t M, int64_t N, int64_t K) {
-  if (!split_tiles(K)) return 0;
+  const int np = k_parts(N, K);
+  if (np == 1) return 0;
   const int64_t G = N / kTileRows, mt = (M + tile::kBM - 1) / tile::kBM;
-  const size_t a = split_bytes(16, ((G + 15) / 16) * mt), b = split_bytes(8, ((G + 7) / 8) * mt);
+  const size_t a = split_bytes(16, ((G + 15) / 16) * mt, np),
+               b = split_bytes(8, ((G + 7) / 8) * mt, np);
   return a > b ? a : b;
 }
 
@@ -899,30 +929,48 @@ void launch_tile(const TilePlan &p, const uint16_t *x, int64_t M, const uint8_t 
                  const float *am, const CodeTerms &ct, int64_t N, int64_t K, float *y,
                  const float *xsum, int64_t Mp, void *split_ws, hipStream_t s) {
   const int64_t KT = tiles_k(K);
-  // one-dimensional grid, N tiles padded to a multiple of 8 (see the kernel)
-  const unsigned grid = (unsigned)((p.nt + 7) / 8 * 8 * p.mt * (p.kh ? 2 : 1));
-  uint32_t *cnt = p.kh ? reinterpret_cast<uint32_t *>(split_ws) : nullptr;
-  uint64_t *part = p.kh ? reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(split_ws) +
-                                                       split_counter_bytes(p.nt * p.mt))
-                        : nullptr;
+  // one-dimensional grid, units (N tile, part of K) padded to a multiple of 8
+  // (see the kernel)
+  const bool split = p.np > 1;
+  const unsigned grid = (unsigned)((p.nt * p.np + 7) / 8 * 8 * p.mt);
+  uint32_t *cnt = split ? reinterpret_cast<uint32_t *>(split_ws) : nullptr;
+  uint64_t *part = split ? reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(split_ws) +
+                                                        split_counter_bytes(p.nt * p.mt))
+                         : nullptr;
   auto go = [&](auto kern, int threads) {
     hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, x, M, qw, am, ct, N, K, KT, y,
-                       (int)p.nt, (int)p.mt, xsum, Mp, p.kh, cnt, part);
+                       (int)p.nt, (int)p.mt, xsum, Mp, p.np, cnt, part);
   };
   if (p.rg == 16)
-    p.kh ? go(gemm_tile_kernel<16, AFF, kTileMB, true>, 256 * 16 / kTileMB)
-         : go(gemm_tile_kernel<16, AFF, kTileMB, false>, 256 * 16 / kTileMB);
+    split ? go(gemm_tile_kernel<16, AFF, kTileMB, true>, 256 * 16 / kTileMB)
+          : go(gemm_tile_kernel<16, AFF, kTileMB, false>, 256 * 16 / kTileMB);
   else
-    p.kh ? go(gemm_tile_kernel<8, AFF, kTileMB8, true>, 256 * 8 / kTileMB8)
-         : go(gemm_tile_kernel<8, AFF, kTileMB8, false>, 256 * 8 / kTileMB8);
+    split ? go(gemm_tile_kernel<8, AFF, kTileMB8, true>, 256 * 8 / kTileMB8)
+          : go(gemm_tile_kernel<8, AFF, kTileMB8, false>, 256 * 8 / kTileMB8);
 }
 
 }  // namespace
 
+int k_parts(int64_t N, int64_t K) {
+  const int64_t KT = tiles_k(K);
+  // two halves for long K
+  int64_t P = K >= kSplitK ? 2 : 1;
+  // narrow N: the 128 x 128 output tiles of a 1024-row batch would cover
+  // less than half of a 256-CU device; then as many parts as fill it once,
+  // of at least four device tiles each
+  const int64_t tiles = (N / kTileRows + 7) / 8 * 8;
+  if (tiles * P < 128) {
+    const int64_t want = 256 / tiles, cap = KT / 4;
+    const int64_t q = want < cap ? want : cap;
+    if (q > P) P = q;
+  }
+  return (int)P;
+}
+
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  // only the tiled kernel with K in two parts needs one; the skinny kernel
-  // (up to 64 rows) and the generic kernel do not
-  if (!split_tiles(K) || !tile_dma_ok(M, N, K)) return 0;
+  // only the tiled kernel with K in parts needs one; the skinny kernel (up
+  // to 64 rows) and the generic kernel do not
+  if (k_parts(N, K) == 1 || !tile_dma_ok(M, N, K)) return 0;
   if (M <= 64 && skinny_eligible(M, N, K, 1)) return 0;
   return split_bytes_max(M, N, K);
 }
@@ -958,25 +1006,25 @@ hipError_t launch_awq_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, cons
   const int64_t ngroups = KT * Mp;
   hipLaunchKernelGGL(xsum_kernel, dim3((unsigned)((ngroups * 16 + 255) / 256)), dim3(256), 0, s,
                      x, M, K, Mp, ngroups, X, reinterpret_cast<uint32_t *>(split_ws),
-                     (!skinny && p.kh) ? p.nt * p.mt : (int64_t)0);
+                     (!skinny && p.np > 1) ? p.nt * p.mt : (int64_t)0);
   const CodeTerms ct = identity_terms();
   const int64_t G = N / kTileRows;
   const float *prf = reinterpret_cast<const float *>(pr);
   if (skinny) {
     const unsigned gx = (unsigned)((G + skinny::kWaves - 1) / skinny::kWaves);
     const dim3 block(64 * skinny::kWaves);
-    const int kh = split_tiles(K);
+    const int np = k_parts(N, K);
     auto go = [&](auto kern, dim3 grid) {
       hipLaunchKernelGGL(kern, grid, block, 0, s, x, (int)M, qw, prf, ct, (int)N, (int)K, (int)KT,
-                         (int)G, y, X, (int)Mp, kh);
+                         (int)G, y, X, (int)Mp, np);
     };
     const dim3 g2(gx, (unsigned)((M + 31) / 32));
     if (M <= 16)
-      kh ? go(gemm_skinny_kernel<1, 8, true, true>, dim3(gx))
-         : go(gemm_skinny_kernel<1, 8, true, false>, dim3(gx));
+      np > 1 ? go(gemm_skinny_kernel<1, 8, true, true>, dim3(gx))
+             : go(gemm_skinny_kernel<1, 8, true, false>, dim3(gx));
     else
-      kh ? go(gemm_skinny_kernel<2, 8, true, true>, g2)
-         : go(gemm_skinny_kernel<2, 8, true, false>, g2);
+      np > 1 ? go(gemm_skinny_kernel<2, 8, true, true>, g2)
+             : go(gemm_skinny_kernel<2, 8, true, false>, g2);
     return hipGetLastError();
   }
   launch_tile<true>(p, x, M, qw, prf, ct, N, K, y, X, Mp, split_ws, s);
@@ -995,21 +1043,21 @@ hipError_t launch_skinny(const uint16_t *x, int64_t M, const uint8_t *qw, const 
   const unsigned gx = (unsigned)((G + skinny::kWaves - 1) / skinny::kWaves);
   const dim3 block(64 * skinny::kWaves);
   const int KT = (int)tiles_k(K);
-  const int kh = split_tiles(K);
+  const int np = k_parts(N, K);
   // up to 16 rows: one m-block per wave; otherwise 32-row groups of x along
   // the grid's y (workgroups of one row-group block run side by side and
   // share the weights through the caches)
   auto go = [&](auto kern, dim3 grid) {
     hipLaunchKernelGGL(kern, grid, block, 0, s, x, (int)M, qw, am, ct, (int)N, (int)K, KT, (int)G, y,
-                       nullptr, 0, kh);
+                       nullptr, 0, np);
   };
   const dim3 g2(gx, (unsigned)((M + 31) / 32));
   if (M <= 16)
-    kh ? go(gemm_skinny_kernel<1, 8, false, true>, dim3(gx))
-       : go(gemm_skinny_kernel<1, 8, false, false>, dim3(gx));
+    np > 1 ? go(gemm_skinny_kernel<1, 8, false, true>, dim3(gx))
+           : go(gemm_skinny_kernel<1, 8, false, false>, dim3(gx));
   else
-    kh ? go(gemm_skinny_kernel<2, 8, false, true>, g2)
-       : go(gemm_skinny_kernel<2, 8, false, false>, g2);
+    np > 1 ? go(gemm_skinny_kernel<2, 8, false, true>, g2)
+           : go(gemm_skinny_kernel<2, 8, false, false>, g2);
   return hipGetLastError();
 }
 
@@ -1021,7 +1069,8 @@ hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, const fl
   if (prefer_skinny(M, N, K, nterm, cus)) return launch_skinny(x, M, qw, am, ct, N, K, y, s);
   if (nterm == 1 && tile_dma_ok(M, N, K)) {
     const TilePlan p = tile_plan(M, N, K, cus);
-    if (p.kh && (!ws || ws_bytes < split_bytes(p.rg, p.nt * p.mt))) return hipErrorInvalidValue;
+    if (p.np > 1 && (!ws || ws_bytes < split_bytes(p.rg, p.nt * p.mt, p.np)))
+      return hipErrorInvalidValue;
     launch_tile<false>(p, x, M, qw, am, ct, N, K, y, nullptr, 0, ws, s);
     return hipGetLastError();
   }
@@ -1029,7 +1078,7 @@ hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, const fl
   const float2 *a = reinterpret_cast<const float2 *>(am);
   const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM)), block(256);
   hipLaunchKernelGGL(gemm_kernel<3>, grid, block, 0, s, x, M, q, a, ct, N, K, KT, y,
-                     split_tiles(K));
+                     k_parts(N, K));
   return hipGetLastError();
 }
 

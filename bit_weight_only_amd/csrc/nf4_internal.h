@@ -48,13 +48,15 @@ struct Codebook {
 
 inline int64_t tiles_k(int64_t K) { return (K + kTileK - 1) / kTileK; }
 
-// Long K is summed in two parts: tiles [0, kh) and [kh, KT), each folded from
-// zero in K order, then added (one fp32 addition, which commutes).  The split
-// point depends on K alone, so every GEMM path (skinny, tiled, generic) gives
-// the same bits for a row whatever M or N.  0 = one part.
+// K is summed in P parts fixed by (N, K) alone (k_parts): device tiles
+// [part_begin(j), part_begin(j + 1)) for j = 0 .. P-1, each part folded from
+// zero in K order, then the parts' sums added in part order.  Every GEMM path
+// (skinny, tiled, generic) uses the same parts, so a row of y never depends
+// on M.  P = 1: one part.
 constexpr int64_t kSplitK = 8192;
-inline int split_tiles(int64_t K) {
-  return K >= kSplitK ? (int)((tiles_k(K) + 1) / 2) : 0;
+int k_parts(int64_t N, int64_t K);
+__host__ __device__ inline int part_begin(int j, int64_t KT, int P) {
+  return (int)((j * KT + P - 1) / P);
 }
 
 // The codebook 0, 1, ..., 15 as bf16 (exact): the codes of the asymmetric

@@ -257,6 +257,21 @@ class PackedWeight:
         """Algorithmic bytes a full read moves: 4-bit codes plus fp32 scales."""
         return self.N * self.K // 2 + 4 * self.N * (self.K // 64)
 
+    def rows(self, n0: int, n1: int) -> "PackedWeight":
+        """Rows [n0, n1) as a view of this weight's buffers (one part of a
+        matrix fused along N; n0, n1 multiples of 16).  The device layout keeps
+        each group of 16 rows contiguous, so the part is itself a weight in
+        the device layout."""
+        if n0 % 16 or n1 % 16 or not 0 <= n0 < n1 <= self.N:
+            raise NF4Error(NF4_ERR_SHAPE, "PackedWeight.rows")
+        v = PackedWeight.__new__(PackedWeight)
+        v.N, v.K = n1 - n0, self.K
+        per_q = self.qweight.numel() // (self.N // 16)
+        per_a = self.absmax.numel() // (self.N // 16)
+        v.qweight = self.qweight[n0 // 16 * per_q:n1 // 16 * per_q]
+        v.absmax = self.absmax[n0 // 16 * per_a:n1 // 16 * per_a]
+        return v
+
 
 def pack_weight(W, codebook, stream=None) -> PackedWeight:
     """Quantize a device fp32 [N, K] tensor into a new PackedWeight."""

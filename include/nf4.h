@@ -81,14 +81,14 @@ size_t nf4_absmax_bytes(int64_t N, int64_t K);
 
 /* Bytes of scratch that nf4_gemv / nf4_gemm need for an M x N x K call; the
  * larger of the two needs.  The GEMV sums its partials in LDS and needs
- * none.  The GEMM needs some only for K >= 8192 and M > 64, where it sums K
- * in two halves on separate workgroups and adds them through the workspace:
- * one 4-byte arrival counter per output tile of 128 x 128 or 128 x 256,
- * then both halves' sums of every tile (about 8 M N bytes in all).  0
- * otherwise, and the workspace arguments may then be NULL with 0 bytes.  A
- * workspace must be zero-filled once at allocation; every call leaves its
- * counters at zero again, and calls sharing one must be ordered (one
- * stream). */
+ * none.  The GEMM needs some only past 64 rows when it sums K in P > 1
+ * parts (see nf4_gemm), which it runs on separate workgroups that meet
+ * through the workspace: one 4-byte arrival counter per output tile of
+ * 128 x 128 or 128 x 256, then every part's sums of every tile (about
+ * 4 P M N bytes in all).  0 otherwise, and the workspace arguments may then
+ * be NULL with 0 bytes.  A workspace must be zero-filled once at
+ * allocation; every call leaves its counters at zero again, and calls
+ * sharing one must be ordered (one stream). */
 size_t nf4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Quantize fp32 W[N][K] (row-major) into the device layout.  Per block of
@@ -171,14 +171,18 @@ nf4_status nf4_gemv_argmax(const uint16_t *x, int64_t M, const uint8_t *qweight,
 
 /* Prefill GEMM, any M >= 1: same result definition as nf4_gemv, computed on
  * bf16 matrix cores with the codes as exact bf16 operands and the fp32
- * scales applied outside the matrix product once per 64-block.  For
- * K >= 8192 the sum runs over two halves of K (device tiles [0, kh) and
- * [kh, ceil(K/128)), kh = ceil(ceil(K/128) / 2)), each from zero in K order,
- * then one fp32 addition; the halves depend on K alone.  workspace: at
+ * scales applied outside the matrix product once per 64-block.  The sum
+ * over K runs in P parts, device tiles [b_j, b_j+1) with
+ * b_j = ceil(j KT / P), KT = ceil(K/128): each part from zero in K order,
+ * then the parts' sums added in part order.  P depends on N and K only:
+ * P = 2 from K = 8192 on, else 1; then, when T P < 128 for
+ * T = 8 ceil(N/128) (the 128 x 128 output tiles of a 1024-row batch),
+ * P = max(P, min(256 / T, KT / 4)) (integer divisions).  workspace: at
  * least nf4_workspace_bytes(M, N, K) bytes, zero-filled once (may be NULL
  * when that is 0), else NF4_ERR_NULL or NF4_ERR_WORKSPACE.  Results are
  * bitwise reproducible run to run, and a row of y does not depend on the
- * other rows of x. */
+ * other rows of x; column slices of a matrix fused along N equal the
+ * separate matrices' outputs bit for bit when both have the same P. */
 nf4_status nf4_gemm(const uint16_t *x, int64_t M, const uint8_t *qweight, const float *absmax,
                     const float codebook[16], int64_t N, int64_t K, float *y, void *workspace,
                     size_t ws_bytes, hipStream_t stream);
@@ -207,9 +211,9 @@ size_t nf4_awq_params_bytes(int64_t N, int64_t K);
 
 /* Bytes of workspace nf4_awq_gemm (and nf4_awq_gemv when x does not fit its
  * on-chip path) needs: K/128 x (M rounded up to 128) floats, the sums of x
- * over every 128-k group; for K >= 8192 and M > 64 also the arrival
- * counters and half sums of nf4_gemm's two halves of K (same layout).  0
- * for shapes these calls reject.  Every call sets what it reads (the
+ * over every 128-k group; past 64 rows with K in P > 1 parts (nf4_gemm's
+ * rule) also the arrival counters and part sums (nf4_workspace_bytes'
+ * layout).  0 for shapes these calls reject.  Every call sets what it reads (the
  * counters included) itself, so the workspace needs no initial contents;
  * calls sharing one must be ordered. */
 size_t nf4_awq_workspace_bytes(int64_t M, int64_t N, int64_t K);
@@ -286,8 +290,7 @@ nf4_status nf4_awq_gemv_prefetch(const uint16_t *x, int64_t M, const uint8_t *qw
 /* Prefill GEMM of the int4 format, any M >= 1: the result definition of
  * nf4_awq_gemv on the tiled matrix-core kernel, after a pre-pass that writes
  * the group sums of x into the workspace (nf4_awq_workspace_bytes(M, N, K)
- * bytes, required).  K >= 8192 is summed in the two halves nf4_gemm
- * uses.  Rows of y do not depend on the other rows of x.  Shapes
+ * bytes, required).  K is summed in the parts nf4_gemm uses.  Rows of y do not depend on the other rows of x.  Shapes
  * whose byte offsets into x, qweight or the workspace reach 2^32 give
  * NF4_ERR_SHAPE.  Bitwise reproducible run to run. */
 nf4_status nf4_awq_gemm(const uint16_t *x, int64_t M, const uint8_t *qweight,

@@ -20,6 +20,19 @@ VOXTRAL_FUSED = {"qkv": (6144, 3072), "wo": (3072, 4096), "w13": (18432, 3072),
                  "w2": (3072, 9216)}
 
 
+def k_parts(N, K):
+    """Parts of K as nf4.h documents them: 2 from K = 8192 on; for narrow N
+    (fewer than 128 output tiles of 128 x 128 at 1024 rows, counted after
+    the first rule) as many as fill 256 CUs once, of at least 4 device tiles
+    each."""
+    KT = -(-K // 128)
+    P = 2 if K >= 8192 else 1
+    tiles = -(-(N // 16) // 8) * 8
+    if tiles * P < 128:
+        P = max(P, min(256 // tiles, KT // 4))
+    return P
+
+
 def torch_cuda():
     import torch
     if not torch.cuda.is_available():

@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 from bit_weight_only_amd import nf4
+from gpu_helpers import k_parts
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "nf4.h")
@@ -96,28 +97,42 @@ def test_linear_validation():
 
 
 def split_bytes(M, N, K):
-    """Workspace of the tiled GEMM with K in two halves (K >= 8192): per
-    output tile of 128 rows x 16 RG columns one 4-byte counter (the counters
-    padded to 256 bytes) and the two halves' fp32 sums; the larger of the
-    two workgroup widths RG = 16 and 8."""
-    if K < 8192:
+    """Workspace of the tiled GEMM with K in P > 1 parts: per output tile of
+    128 rows x 16 RG columns one 4-byte counter (the counters padded to 256
+    bytes) and every part's fp32 sums; the larger of the two workgroup
+    widths RG = 16 and 8."""
+    P = k_parts(N, K)
+    if P == 1:
         return 0
     G, mt = N // 16, -(-M // 128)
 
     def width(rg):
         tiles = -(-G // rg) * mt
-        return -(-tiles * 4 // 256) * 256 + tiles * 2 * 128 * 16 * rg * 4
+        return -(-tiles * 4 // 256) * 256 + tiles * P * 128 * 16 * rg * 4
     return max(width(16), width(8))
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 3584, 18944), (64, 3584, 18944), (65, 3584, 18944),
                                    (1024, 3584, 18944), (1024, 3072, 9216), (300, 256, 8128),
-                                   (300, 256, 8192), (1024, 37888, 3584), (14449, 152064, 3584)])
+                                   (300, 256, 8192), (1024, 37888, 3584), (14449, 152064, 3584),
+                                   (1024, 512, 3584), (1024, 1024, 3072), (1024, 3584, 3584),
+                                   (1024, 4608, 3584), (300, 272, 704), (1024, 256, 256)])
 def test_gemm_workspace_bytes(M, N, K):
-    """Only nf4_gemm past 64 rows with K >= 8192 needs a workspace."""
+    """Only nf4_gemm past 64 rows with K in more than one part needs a
+    workspace (K >= 8192, or narrow N with enough K)."""
     assert nf4.nf4_workspace_bytes(M, N, K) == (0 if M <= 64 else split_bytes(M, N, K))
-    if M > 64 and K >= 8192:
-        assert nf4.nf4_workspace_bytes(M, N, K) >= 8 * M * N
+    if M > 64 and k_parts(N, K) > 1:
+        assert nf4.nf4_workspace_bytes(M, N, K) >= 4 * k_parts(N, K) * M * N
+
+
+def test_k_parts_at_the_model_shapes():
+    """The parts the rule gives the Qwen2-7B and Voxtral linears: one for the
+    wide fused ones, two for long K, more only for narrow N."""
+    assert [k_parts(N, K) for N, K in [(4608, 3584), (3584, 3584), (37888, 3584),
+                                       (3584, 18944), (152064, 3584)]] == [1, 1, 1, 2, 1]
+    assert [k_parts(N, K) for N, K in [(6144, 3072), (3072, 4096), (18432, 3072),
+                                       (3072, 9216)]] == [1, 1, 1, 2]
+    assert [k_parts(N, K) for N, K in [(512, 3584), (1024, 3072), (256, 256)]] == [7, 4, 1]
 
 
 def test_gemm_workspace_validation():
@@ -217,6 +232,28 @@ def test_binding_raises_named_errors():
     with pytest.raises(nf4.NF4Error) as e:
         nf4.nf4_gemv(A, 9, A, A, CB, 16, 64, A, stream=0)
     assert e.value.status == nf4.NF4_ERR_SHAPE and "NF4_ERR_SHAPE" in str(e.value)
+
+
+@pytest.mark.parametrize("K", [64, 192, 3584])
+def test_packed_weight_rows_view(K):
+    """A row range of a packed weight is the contiguous run of its 16-row
+    groups in both buffers, shared with the whole (no copy)."""
+    import torch
+    N = 96
+    pw = nf4.PackedWeight(N, K, device="cpu")
+    pw.qweight.copy_(torch.arange(pw.qweight.numel(), dtype=torch.int64).to(torch.uint8))
+    pw.absmax.copy_(torch.arange(pw.absmax.numel(), dtype=torch.float32))
+    KT = -(-K // 128)
+    v = pw.rows(32, 80)
+    assert (v.N, v.K) == (48, K)
+    assert v.qweight.numel() == nf4.nf4_qweight_bytes(48, K)
+    assert v.absmax.numel() * 4 == nf4.nf4_absmax_bytes(48, K)
+    assert v.qweight.data_ptr() == pw.qweight.data_ptr() + 2 * KT * 1024
+    assert v.absmax.data_ptr() == pw.absmax.data_ptr() + 2 * KT * 128
+    assert torch.equal(v.absmax, pw.absmax[2 * KT * 32:5 * KT * 32])
+    for n0, n1 in ((0, 8), (8, 32), (32, 32), (0, 112), (-16, 16)):
+        with pytest.raises(nf4.NF4Error):
+            pw.rows(n0, n1)
 
 
 # ----------------------------------------------- asymmetric int4, group 128
