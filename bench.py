@@ -78,11 +78,11 @@ TRAFFIC = {
     "gemv": {"source": "gemv.hip", "fetch_kib": 42729, "write_kib": 148,
              "sha256": "5f77a7ec2181f4cf3a6616c5591104233b07a441586fca9cda18542272ac5a99"},
     "gemm": {"source": "gemm.hip", "fetch_kib": 180757, "write_kib": 151901,
-             "sha256": "16e68f398875e035410e4cb825c10b861c6f6c54bfe293cb32957c3956194c70"},
+             "sha256": "0cade2a0da7fcd5f52c9ad5a087bf95dde976a32f217c6ccf94450adefd2f796"},
     "awq_gemv": {"source": "gemv.hip", "fetch_kib": 40366, "write_kib": 148,
                  "sha256": "5f77a7ec2181f4cf3a6616c5591104233b07a441586fca9cda18542272ac5a99"},
     "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180912, "write_kib": 151892,
-                 "sha256": "16e68f398875e035410e4cb825c10b861c6f6c54bfe293cb32957c3956194c70"},
+                 "sha256": "0cade2a0da7fcd5f52c9ad5a087bf95dde976a32f217c6ccf94450adefd2f796"},
 }
 COPY_CALIBRATION = {"fetch_kib_per_gib": 524308, "write_kib_per_gib": 1048576}
 

@@ -856,7 +856,7 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
 // its 8 values in k order, then row16_sum; the GEMV sums the same way.
 // Consecutive 16-lane groups take consecutive m, so a wave writes 16
 // consecutive bytes of X.  Also sets the ncnt arrival counters of a tiled
-// launch with K in two parts to zero.
+// launch with K in parts to zero.
 __global__ __launch_bounds__(256) void xsum_kernel(const uint16_t *__restrict__ x, int64_t M,
                                                    int64_t K, int64_t Mp, int64_t ngroups,
                                                    float *__restrict__ X, uint32_t *__restrict__ cnt,
@@ -989,7 +989,7 @@ bool awq_gemm_supported(int64_t M, int64_t N, int64_t K) {
 }
 
 size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  // the x sums, then what a tiled launch with K in two parts needs
+  // the x sums, then what a tiled launch with K in parts needs
   const bool skinny_only = M <= 64 && skinny_eligible(M, N, K, 1);
   return awq_xsum_bytes(M, K) + (skinny_only ? 0 : split_bytes_max(M, N, K));
 }

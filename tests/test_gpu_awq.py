@@ -180,9 +180,9 @@ def test_awq_zero_point_cancellation(side, kind):
 
 @pytest.mark.parametrize("N,K", [(272, 1024), (272, 8320)])
 def test_awq_gemm_deterministic_and_batch_independent(side, N, K):
-    """Rows do not depend on the batch (K = 8320: summed in two halves on
-    the tiled and the skinny path alike), and a reused workspace full of
-    stale bytes gives the same bits (every call sets what it reads)."""
+    """Rows do not depend on the batch (K = 8320, N = 272: summed in 10
+    parts on the tiled and the skinny path alike), and a reused workspace
+    full of stale bytes gives the same bits (every call sets what it reads)."""
     packed, scales, zeros, aw = awq_case(side, N, K, mid=34)
     x = synth.activations(0, 300, K, stream=12)
     y1 = side.awq_run("gemm", x, aw)
