@@ -169,11 +169,12 @@ def test_gemm_skinny_and_tiled_rows_identical(side, cb, N, K):
 
 
 def test_gemm_k_halves_repeat(side, cb):
-    """K = 8320 (65 device tiles) is summed in halves of 33 and 32 tiles that
-    meet through the workspace: calls with other inputs in between leave
-    nothing behind (the arrival counters return to zero), and sampled rows
-    match the oracle."""
+    """K = 8320 (65 device tiles) at N = 1024 is summed in halves of 33 and 32
+    tiles that meet through the workspace: calls with other inputs in
+    between leave nothing behind (the arrival counters return to zero), and
+    sampled rows match the oracle."""
     N, K, M = 1024, 8320, 520
+    assert k_parts(N, K) == 2
     packed, absmax, pw = case(side, cb, N, K, mid=28)
     x1 = synth.activations(0, M, K, stream=5)
     x2 = synth.activations(0, M, K, stream=6)
@@ -223,11 +224,12 @@ def test_fused_projection_slices_equal_separate_calls(side, cb):
     """q|k|v concatenated along N at pack time: each column slice of one call
     matches the separate projection (vibevoice.c README, decode GEMV bullet:
     same-input projections share one launch).  The GEMM computes each output
-    from the same operations when both matrices sum K in the same parts
-    (q|k|v and q: one part), so those slices are bit-identical; k and v
-    alone are narrow enough to take more parts of K, and the GEMV splits the
-    fused matrix's tiles over waves differently from the separate ones: those
-    slices agree to the oracle's bar."""
+    from the same operations when both matrices sum K in the same parts, so
+    those slices are bit-identical (q and q|k|v; two 4096-row halves of an
+    8192-row matrix: one part each); k and v alone are narrow enough to take
+    more parts of K, and the GEMV splits the fused matrix's tiles over waves
+    differently from the separate ones: those slices agree to the oracle's
+    bar."""
     K = 3584
     parts = [oracle_layer(2, 0, mid, n, K, cb) for mid, n in
              [(synth.Q, 3584), (synth.K_, 512), (synth.V, 512)]]
@@ -250,6 +252,14 @@ def test_fused_projection_slices_equal_separate_calls(side, cb):
             assert_linear_ok(ys, yr, b, "separate gemm")
         col += n
     assert [k_parts(p[1].shape[0], K) for p in parts] == [1, 7, 7]
+    # two halves with the fused matrix's parts: bit-identical GEMM slices
+    halves = [oracle_layer(2, 1, mid, 4096, K, cb) for mid in (synth.Q, synth.O)]
+    assert k_parts(8192, K) == k_parts(4096, K) == 1
+    fused = side.repack(np.vstack([p[1] for p in halves]), np.vstack([p[2] for p in halves]))
+    yg = side.run("gemm", x, fused, cb)
+    for i, (W, packed, absmax) in enumerate(halves):
+        np.testing.assert_array_equal(yg[:, 4096 * i:4096 * (i + 1)],
+                                      side.run("gemm", x, side.repack(packed, absmax), cb))
 
 
 # --------------------------------------------------------------- full sizes
