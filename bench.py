@@ -561,6 +561,26 @@ def main():
     del vw
     torch.cuda.empty_cache()
 
+    # ---- what one launch moving the same bytes reaches on this machine: device
+    # copies (torch's copy kernel) of a gate|up GEMV's bytes (half read, half
+    # written) rotated over 8 buffer pairs (beyond the memory-side cache), and
+    # of 1 GiB
+    def copy_rate(total, pairs):
+        n = total // 8  # floats per side: total/2 bytes read, total/2 written
+        bufs = [(torch.empty(n, device="cuda"), torch.empty(n, device="cuda"))
+                for _ in range(pairs)]
+        for a, b in bufs:
+            a.fill_(1.0)
+        torch.cuda.synchronize()
+        ms = graph_ms(torch, s, lambda: [b.copy_(a) for a, b in bufs], reps) / pairs
+        del bufs
+        torch.cuda.empty_cache()
+        return 8 * n / (ms * 1e-3) / 1e9, ms * 1e3
+    ref_small = copy_rate(packed_bytes(N, K), 8)
+    ref_big = copy_rate(1 << 30, 2)
+    log(f"[bench] copies: {ref_small[0]:.0f} GB/s at {packed_bytes(N, K) / 1e6:.1f} MB, "
+        f"{ref_big[0]:.0f} GB/s at 1 GiB")
+
     # ---- the floor of one launch inside a replayed graph: a graph of as many
     # one-element kernels as the decode step has launches
     one = torch.zeros(1, device="cuda")
@@ -623,6 +643,12 @@ def main():
                        "unit": "TFLOP/s", "ms": round(LONG_CHUNKS * pre_ms + tail_ms, 2),
                        "note": "14 prefill steps at M=1024 and the 113-row tail step, as timed "
                                "above (1680 nf4_gemm calls)"},
+        "hbm_reference": {"copy_gbps_gate_up_bytes": round(ref_small[0], 1),
+                          "copy_us_gate_up_bytes": round(ref_small[1], 2),
+                          "copy_gbps_1gib": round(ref_big[0], 1), "unit": "GB/s",
+                          "note": "torch device copies moving the bytes of one gate|up GEMV "
+                                  "launch (half read, half written; 8 buffer pairs rotated) "
+                                  "and 1 GiB, one copy per launch, in a replayed graph"},
         "launch_floor_us": {"value": round(floor_us, 2),
                             "note": f"a replayed graph of {nlaunch} one-element torch kernels, "
                                     "per launch"},
