@@ -202,13 +202,14 @@ def test_gemv_and_gemm_agree(side, cb):
     assert_linear_ok(ym, yr, b, "gemm")
 
 
-@pytest.mark.parametrize("kind", ["gemv", "gemm"])
-def test_codebook_needing_three_bf16_terms(side, kind):
+@pytest.mark.parametrize("kind,N,K", [("gemv", 256, 256), ("gemm", 256, 256),
+                                      ("gemm", 64, 3584), ("gemm", 32, 8256)])
+def test_codebook_needing_three_bf16_terms(side, kind, N, K):
     """A codebook that is not bf16-exact (the unrounded quantiles as fp32)
-    runs as three exact bf16 terms."""
+    runs as three exact bf16 terms (the generic kernels; the GEMM with K in
+    1, 7 and 16 parts here)."""
     _, unr = oracle.codebook()
     cb32 = unr.astype(np.float32)
-    N, K = 256, 256
     W = synth.weights(0, 0, 30, N, K)
     codes, absmax = oracle.quantize(W, cb32)
     packed = oracle.pack(codes)
@@ -218,6 +219,8 @@ def test_codebook_needing_three_bf16_terms(side, kind):
     x = synth.activations(0, 4, K)
     yr, b = oracle.linear(x, packed, absmax, cb32)
     assert_linear_ok(side.run(kind, x, pw, cb32), yr, b, f"{kind} 3-term codebook")
+    if kind == "gemm":
+        assert k_parts(N, K) == {256: 1, 3584: 7, 8256: 16}[K]
 
 
 def test_fused_projection_slices_equal_separate_calls(side, cb):
