@@ -392,3 +392,31 @@ def test_awq_prefetch_hint_keeps_results_bitwise(side, M):
         packed, scales, zeros = refs[n]
         yr, bd = oracle.awq_linear(x, packed, scales, zeros)
         assert_linear_ok(b[:, rows[n]], yr, bd, f"awq prefetch {n} M={M}")
+
+
+def test_awq_gemm_k_parts_in_a_replayed_graph(side):
+    """The int4 GEMM with K in parts (pre-pass, which zeroes the counters
+    with ordinary stores, then the tiled kernel) captured in a HIP graph:
+    every replay equals the eager call bit for bit, with an eager call on
+    the same workspace between replays."""
+    t = side.torch
+    N, K, M = 512, 8192, 300
+    packed, scales, zeros, aw = awq_case(side, N, K, mid=36)
+    xd = side.x_dev(synth.activations(0, M, K, stream=13))
+    wsb = side.nf4.nf4_awq_workspace_bytes(M, N, K)
+    ws = t.full((wsb,), 0x5A, dtype=t.uint8, device="cuda")
+    y0 = side.awq_linear("gemm", xd, M, aw, ws=ws).clone()
+    y = t.empty((M, N), dtype=t.float32, device="cuda")
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g, stream=side.stream):
+        side.nf4.nf4_awq_gemm(xd, M, aw.qweight, aw.params, N, K, y, ws, wsb, stream=side.stream)
+    side.sync()
+    for rep in range(3):
+        with t.cuda.stream(side.stream):
+            y.fill_(float("nan"))
+            g.replay()
+        side.sync()
+        assert t.equal(y.view(t.int32), y0.view(t.int32)), f"replay {rep}"
+        assert t.equal(side.awq_linear("gemm", xd, M, aw, ws=ws).view(t.int32), y0.view(t.int32))
+    yr, b = oracle.awq_linear(synth.activations(0, M, K, stream=13)[[0, 299]], packed, scales, zeros)
+    assert_linear_ok(y0.cpu().numpy()[[0, 299]], yr, b, "awq gemm K in parts")

@@ -364,3 +364,41 @@ def test_long_audio_prefill_chunks_and_tail(side, cb):
     xin = side.x_dev(x[M - 1024:])
     yin = side.linear("gemm", xin, 1024, pw, cb).cpu().numpy()
     np.testing.assert_array_equal(yin[1024 - 113:], y[tail])
+
+
+def test_gemm_k_parts_in_a_replayed_graph(side, cb):
+    """The parts of K meet through counters that each call sets back to zero
+    itself (no memset anywhere): a HIP graph holding two GEMMs with K in parts
+    (N = 512, K = 3584: 7 parts; N = 256, K = 18944: 16 parts) replays with
+    the eager results bit for bit, with eager calls on the same workspace and
+    fills of y between the replays."""
+    t = side.torch
+    M = 300
+    shapes = [(512, 3584, 41), (256, 18944, 42)]
+    assert [k_parts(N, K) for N, K, _ in shapes] == [7, 16]
+    wsb = max(side.nf4.nf4_workspace_bytes(M, N, K) for N, K, _ in shapes)
+    ws = t.zeros(wsb, dtype=t.uint8, device="cuda")
+    cases, eager = [], []
+    for N, K, mid in shapes:
+        packed, absmax, pw = case(side, cb, N, K, mid=mid)
+        xd = side.x_dev(synth.activations(0, M, K, stream=mid))
+        eager.append(side.linear("gemm", xd, M, pw, cb, ws=ws).clone())
+        cases.append((pw, xd, t.empty((M, N), dtype=t.float32, device="cuda")))
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g, stream=side.stream):
+        for pw, xd, y in cases:
+            side.nf4.nf4_gemm(xd, M, pw.qweight, pw.absmax, cb, pw.N, pw.K, y, ws, wsb,
+                              stream=side.stream)
+    side.sync()
+    for rep in range(3):
+        with t.cuda.stream(side.stream):
+            for _, _, y in cases:
+                y.fill_(float("nan"))
+            g.replay()
+        side.sync()
+        for (pw, xd, y), y0 in zip(cases, eager):
+            assert t.equal(y.view(t.int32), y0.view(t.int32)), f"replay {rep} N={pw.N} K={pw.K}"
+        # an eager call on the shared workspace between replays
+        pw, xd, _ = cases[rep % 2]
+        assert t.equal(side.linear("gemm", xd, M, pw, cb, ws=ws).view(t.int32),
+                       eager[rep % 2].view(t.int32))
