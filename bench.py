@@ -75,13 +75,13 @@ LONG_M, LONG_CHUNKS = 14449, 14  # the long-audio prompt: 14 x 1024 rows + the 1
 # `python bench.py --pmc-pass` (profiles/hbm_traffic_gate_up.md): counter KiB
 # per dispatch and the calibration of each counter on a plain 1 GiB copy.
 TRAFFIC = {
-    "gemv": {"source": "gemv.hip", "fetch_kib": 42729, "write_kib": 148,
-             "sha256": "5f77a7ec2181f4cf3a6616c5591104233b07a441586fca9cda18542272ac5a99"},
-    "gemm": {"source": "gemm.hip", "fetch_kib": 180757, "write_kib": 151901,
+    "gemv": {"source": "gemv.hip", "fetch_kib": 42725, "write_kib": 148,
+             "sha256": "6657fdb10136fe069cf4f9d6a0ab2e196900198d4eba9f417e46a365a0664ffd"},
+    "gemm": {"source": "gemm.hip", "fetch_kib": 180757, "write_kib": 151828,
              "sha256": "0cade2a0da7fcd5f52c9ad5a087bf95dde976a32f217c6ccf94450adefd2f796"},
-    "awq_gemv": {"source": "gemv.hip", "fetch_kib": 40366, "write_kib": 148,
-                 "sha256": "5f77a7ec2181f4cf3a6616c5591104233b07a441586fca9cda18542272ac5a99"},
-    "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180912, "write_kib": 151892,
+    "awq_gemv": {"source": "gemv.hip", "fetch_kib": 40367, "write_kib": 148,
+                 "sha256": "6657fdb10136fe069cf4f9d6a0ab2e196900198d4eba9f417e46a365a0664ffd"},
+    "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180912, "write_kib": 151873,
                  "sha256": "0cade2a0da7fcd5f52c9ad5a087bf95dde976a32f217c6ccf94450adefd2f796"},
 }
 COPY_CALIBRATION = {"fetch_kib_per_gib": 524308, "write_kib_per_gib": 1048576}

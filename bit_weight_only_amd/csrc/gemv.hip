@@ -298,9 +298,11 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float *__restrict__ y
 // lane % 16 the weight row.  The cost per tile is four matrix instructions
 // whatever M (up to 8), and the vector ALU is left with the lookups.
 //
-// LDS (dynamic, sized per launch): the pair table in 64 copies with a
-// 256-byte entry stride, so the address (code byte << 8) | (lane << 2) is one
-// v_perm_b32 and the 64 lanes of a wave hit 64 different banks; x for all M
+// LDS: the pair table (static) in 32 copies at a 256-byte entry stride
+// (entry e in bytes 256 e .. 256 e + 127), so the address (code byte << 8) |
+// ((lane % 32) << 2) is one v_perm_b32 and each half of a wave hits 32
+// different banks; writing half of a 64-copy table shortens the set-up of
+// every launch.  Dynamic, sized per launch: x for all M
 // rows, each padded with zeros to a whole number of 128-k tiles and stored
 // with a 16-byte skew per row (so the M rows of one operand-A read fall in
 // different banks); and the partial sums [row group][wave][16 rows][M].
@@ -318,8 +320,8 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float *__restrict__ y
 // acc = fmaf(16 s, g, acc) (both constants exact).
 // ---------------------------------------------------------------------------
 constexpr int kFastWaves = 8;
-constexpr int kFastCopies = 64;
-constexpr int kFastTableWords = 256 * kFastCopies;  // 64 KB
+constexpr int kFastCopies = 64;                     // copy slots per 256-byte entry line
+constexpr int kFastTableWords = 256 * kFastCopies;  // 64 KB of LDS, copies 0 .. 31 written
 constexpr int kFastDepth = 4;                        // tiles in flight per wave
 constexpr int kFastSkew = 8;                         // x row skew in LDS, elements
 constexpr int kLdsBytes = 160 * 1024;                // LDS per workgroup on gfx950
@@ -420,12 +422,12 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
     if (c < chunks && k < K) xv0[u] = *reinterpret_cast<const uint4 *>(x + (int64_t)m * K + k);
   }
   __syncthreads();
-  // Pair table: consecutive lanes fill consecutive 16-byte chunks (four
-  // copies of one entry each), so the stores are free of bank conflicts.
-  for (int c = threadIdx.x; c < (AFF ? 0 : kFastTableWords / 4); c += blockDim.x) {
-    const int e = c / (kFastCopies / 4);
+  // Pair table, copies 0 .. 31 of every entry: consecutive lanes fill
+  // consecutive 16-byte chunks (four copies each), eight chunks per entry.
+  for (int c = threadIdx.x; c < (AFF ? 0 : kFastTableWords / 8); c += blockDim.x) {
+    const int e = c >> 3;
     const uint32_t v = (uint32_t)codes_lds[e & 15] | ((uint32_t)codes_lds[e >> 4] << 16);
-    reinterpret_cast<uint4 *>(table)[c] = make_uint4(v, v, v, v);
+    reinterpret_cast<uint4 *>(table)[e * 16 + (c & 7)] = make_uint4(v, v, v, v);
   }
 #pragma unroll
   for (int u = 0; u < kStage; ++u) {
@@ -464,7 +466,7 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
   }
   __syncthreads();
 
-  const uint32_t lane4 = (uint32_t)lane << 2;
+  const uint32_t lane4 = ((uint32_t)lane & 31u) << 2;  // copy lane % 32
   const char *tabc = reinterpret_cast<const char *>(table);
   const uint32_t magic = 0x3F803F80u;  // bf16 pair (1.0, 1.0), affine B operands
   // D rows 4h + i (i < NA) of the lane that can be real output rows
