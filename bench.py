@@ -75,14 +75,14 @@ LONG_M, LONG_CHUNKS = 14449, 14  # the long-audio prompt: 14 x 1024 rows + the 1
 # `python bench.py --pmc-pass` (profiles/hbm_traffic_gate_up.md): counter KiB
 # per dispatch and the calibration of each counter on a plain 1 GiB copy.
 TRAFFIC = {
-    "gemv": {"source": "gemv.hip", "fetch_kib": 42725, "write_kib": 148,
-             "sha256": "6657fdb10136fe069cf4f9d6a0ab2e196900198d4eba9f417e46a365a0664ffd"},
-    "gemm": {"source": "gemm.hip", "fetch_kib": 180757, "write_kib": 151828,
-             "sha256": "0cade2a0da7fcd5f52c9ad5a087bf95dde976a32f217c6ccf94450adefd2f796"},
-    "awq_gemv": {"source": "gemv.hip", "fetch_kib": 40367, "write_kib": 148,
-                 "sha256": "6657fdb10136fe069cf4f9d6a0ab2e196900198d4eba9f417e46a365a0664ffd"},
-    "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180912, "write_kib": 151873,
-                 "sha256": "0cade2a0da7fcd5f52c9ad5a087bf95dde976a32f217c6ccf94450adefd2f796"},
+    "gemv": {"source": "gemv.hip", "fetch_kib": 42713, "write_kib": 148,
+             "sha256": "06d88eadf44e341f16f0ed60b6f9b9a215b0837c03260c23416ab488040e22aa"},
+    "gemm": {"source": "gemm.hip", "fetch_kib": 180757, "write_kib": 151802,
+             "sha256": "9dbb7c43b1cb85b57adcb3eb4d2e46a0d795fa55ad341191097ad7138a1938b8"},
+    "awq_gemv": {"source": "gemv.hip", "fetch_kib": 40356, "write_kib": 148,
+                 "sha256": "06d88eadf44e341f16f0ed60b6f9b9a215b0837c03260c23416ab488040e22aa"},
+    "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180912, "write_kib": 151944,
+                 "sha256": "9dbb7c43b1cb85b57adcb3eb4d2e46a0d795fa55ad341191097ad7138a1938b8"},
 }
 COPY_CALIBRATION = {"fetch_kib_per_gib": 524308, "write_kib_per_gib": 1048576}
 

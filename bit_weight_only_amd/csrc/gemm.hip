@@ -182,23 +182,6 @@ constexpr int kHalfRow = 64;                    // bytes of one row in one 32-k 
 constexpr int kCopies = 32;                     // pair-table copies (lane % 32)
 constexpr int kTableBytes = 256 * kCopies * 4;
 
-typedef __attribute__((address_space(3))) void lds_void;
-__device__ inline uint32_t lds_addr(const void *p) {
-  return (uint32_t)(uintptr_t)(const lds_void *)p;
-}
-// One copy from global memory (uniform base + per-lane 32-bit byte offset)
-// straight into LDS: 16 bytes per lane land at m0 + 16 * lane (copy16), or 4
-// bytes at m0 + 4 * lane (copy4).  Issued from inline assembly, so the
-// compiler neither waits for them nor knows what they write: every use is
-// ordered by an explicit vmcnt wait and a barrier.
-__device__ inline void copy16(uint32_t m0, const void *base, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(base)
-               : "memory");
-}
-__device__ inline void copy4(uint32_t m0, const void *base, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0), "v"(voff), "s"(base)
-               : "memory");
-}
 // Wait until at most N of this wave's copies are in flight and its LDS
 // operations are done, then meet the other waves.
 template <int N>
@@ -313,7 +296,7 @@ __global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
   qw += (int64_t)t0 * kTileBytes;
   am += (int64_t)t0 * (L::kScaleBytes / 4);
   if (AFF) xsum += (int64_t)t0 * Mp;
-  const uint32_t base = pipe::lds_addr(lds);
+  const uint32_t base = lds_addr(lds);
   const char *ldsA = lds + L::kOffA, *ldsC = lds + L::kOffC, *ldsS = lds + L::kOffS;
 
   // Copy assignment (W waves).  x: copy i (16 per step, 1 KB each) fills
@@ -350,7 +333,7 @@ __global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
     const uint32_t sc = (uint32_t)(step < S ? step : S - 1) * (kBK * 2);
 #pragma unroll
     for (int v = 0; v < L::kACopies; ++v)
-      pipe::copy16(mA[v] + (step & 1) * 2 * tile::kAHalf, x, aoff[v] + sc);
+      copy16_to_lds(mA[v] + (step & 1) * 2 * tile::kAHalf, x, aoff[v] + sc);
   };
   // device tile T (steps 2T, 2T+1) of the wave's row group: 1 KB of code
   // words and 128 bytes of scales, into ring slot T & 1
@@ -358,9 +341,9 @@ __global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
     const uint32_t tc = (uint32_t)(T < KTp ? T : KTp - 1);
 #pragma unroll
     for (int u = 0; u < L::kRGW; ++u) {
-      pipe::copy16(mC[u] + (T & 1) * kTileBytes, qw, coff[u] + tc * kTileBytes);
+      copy16_to_lds(mC[u] + (T & 1) * kTileBytes, qw, coff[u] + tc * kTileBytes);
       if (lane < L::kScaleBytes / 16)
-        pipe::copy16(mS[u] + (T & 1) * kTileScales * 4, am, soff[u] + tc * L::kScaleBytes);
+        copy16_to_lds(mS[u] + (T & 1) * kTileScales * 4, am, soff[u] + tc * L::kScaleBytes);
     }
   };
   // x sums of device tile T (affine) into ring slot T & 1
@@ -368,7 +351,7 @@ __global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
     if constexpr (AFF) {
       const uint32_t tc = (uint32_t)(T < KTp ? T : KTp - 1);
       if (lane < L::kXLanes)
-        pipe::copy16(mX + (T & 1) * tile::kXSum, xsum, xoff + tc * (uint32_t)(Mp * 4));
+        copy16_to_lds(mX + (T & 1) * tile::kXSum, xsum, xoff + tc * (uint32_t)(Mp * 4));
     }
   };
 
@@ -425,7 +408,7 @@ __global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
       const uint32_t xo = min((uint32_t)(t + 1) * (kBK * 2), xlast);
 #pragma unroll
       for (int v = 0; v < L::kACopies; ++v)
-        pipe::copy16(mA[v] + ((PH + 1) & 1) * 2 * tile::kAHalf, x, aoff[v] + xo);
+        copy16_to_lds(mA[v] + ((PH + 1) & 1) * 2 * tile::kAHalf, x, aoff[v] + xo);
       if (PH == 1) copy_tile((t >> 1) + 2);
       if (PH == 0) copy_xsum((t >> 1) + 1);
     }

@@ -394,12 +394,13 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
   }
 
   // Setup.  The 16 codes go through LDS (indexing the kernel-argument block
-  // with a per-thread index would be one memory round trip per use); the x
-  // loads are issued before the first barrier and stored after the table is
-  // built, so their latency hides behind it.  Affine: a row has a whole
-  // number of 128-k tiles, so the 16 lanes of a DPP row hold the 16 chunks
-  // of one tile row of x, and their sum goes to X as x is stored (the
-  // chunk sums in k order, then row16_sum).
+  // with a per-thread index would be one memory round trip per use).  x is
+  // copied straight from global memory into LDS (one 1 KB copy per row
+  // segment, no pass through registers), issued before the table is built
+  // and waited for before the second barrier.  Affine: x goes through
+  // registers, since a row has a whole number of 128-k tiles and the 16
+  // lanes of a DPP row hold the 16 chunks of one tile row of x, whose sum
+  // goes to X as x is stored (the chunk sums in k order, then row16_sum).
   if (!AFF && threadIdx.x < 16) codes_lds[threadIdx.x] = ct.t[0][threadIdx.x];
   const int chunks = M * KP / 8, cpr = KP / 8;
   constexpr int kStage = 4;
@@ -414,12 +415,26 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
     }
   };
   uint4 xv0[kStage];
+  if constexpr (!AFF) {
+    // x rows straight into LDS: one copy is 64 lanes x 16 bytes of one row
+    // (1 KB); lanes at or past K copy nothing, their chunks are zeroed below
+    const int segs = (cpr + 63) / 64;
+    const uint32_t xs_base = lds_addr(xs);
+    for (int q = wave; q < M * segs; q += kFastWaves) {
+      const int m = q / segs, seg = q - m * segs;
+      const int c = seg * 64 + lane, k = c * 8;
+      if (c < cpr && k < K)
+        copy16_to_lds(xs_base + (uint32_t)(m * XS + seg * 512) * 2u, x,
+                  (uint32_t)(((int64_t)m * K + k) * 2));
+    }
+  } else {
 #pragma unroll
   for (int u = 0; u < kStage; ++u) {
     const int c = (int)threadIdx.x + u * (int)blockDim.x;
     const int m = c / cpr, k = (c - m * cpr) * 8;
     xv0[u] = make_uint4(0u, 0u, 0u, 0u);
     if (c < chunks && k < K) xv0[u] = *reinterpret_cast<const uint4 *>(x + (int64_t)m * K + k);
+  }
   }
   __syncthreads();
   // Pair table, copies 0 .. 31 of every entry: consecutive lanes fill
@@ -429,6 +444,16 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
     const uint32_t v = (uint32_t)codes_lds[e & 15] | ((uint32_t)codes_lds[e >> 4] << 16);
     reinterpret_cast<uint4 *>(table)[e * 16 + (c & 7)] = make_uint4(v, v, v, v);
   }
+  if constexpr (!AFF) {
+    // the zero padding k in [K, KP) of every row
+    const int padc = (KP - K) / 8, kc0 = K / 8;
+    for (int c = threadIdx.x; c < M * padc; c += blockDim.x) {
+      const int m = c / (padc ? padc : 1), k = (kc0 + c - m * padc) * 8;
+      *reinterpret_cast<uint4 *>(&xs[m * XS + k]) = make_uint4(0u, 0u, 0u, 0u);
+    }
+    // the copies of x have landed before the barrier below
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
 #pragma unroll
   for (int u = 0; u < kStage; ++u) {
     const int c = (int)threadIdx.x + u * (int)blockDim.x;
@@ -436,7 +461,8 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
     if (c < chunks) *reinterpret_cast<uint4 *>(&xs[m * XS + k]) = xv0[u];
     store_xsum(c, xv0[u]);
   }
-  for (int c0 = (int)threadIdx.x + kStage * (int)blockDim.x; c0 < chunks;
+  }
+  for (int c0 = (int)threadIdx.x + kStage * (int)blockDim.x; c0 < (AFF ? chunks : 0);
        c0 += kStage * (int)blockDim.x) {
     uint4 v[kStage];
 #pragma unroll

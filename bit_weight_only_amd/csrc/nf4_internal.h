@@ -121,6 +121,19 @@ hipError_t launch_skinny(const uint16_t *x, int64_t M, const uint8_t *qw, const 
                          const CodeTerms &ct, int64_t N, int64_t K, float *y, hipStream_t s);
 
 
+// LDS byte address of a pointer into LDS.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ inline uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)(const lds_void *)p; }
+// One copy from global memory (uniform base + per-lane 32-bit byte offset)
+// straight into LDS: 16 bytes per active lane land at m0 + 16 * lane.
+// Issued from inline assembly, so the compiler neither waits for it nor
+// knows what it writes: every use is ordered by an explicit vmcnt wait and a
+// barrier.
+__device__ inline void copy16_to_lds(uint32_t m0, const void *base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(base)
+               : "memory");
+}
+
 // Sum of the 8 bf16 values of a 16-byte chunk, in k order.
 __device__ inline float chunk_sum8(uint4 c) {
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
