@@ -77,12 +77,12 @@ LONG_M, LONG_CHUNKS = 14449, 14  # the long-audio prompt: 14 x 1024 rows + the 1
 TRAFFIC = {
     "gemv": {"source": "gemv.hip", "fetch_kib": 42713, "write_kib": 148,
              "sha256": "06d88eadf44e341f16f0ed60b6f9b9a215b0837c03260c23416ab488040e22aa"},
-    "gemm": {"source": "gemm.hip", "fetch_kib": 180757, "write_kib": 151802,
-             "sha256": "9dbb7c43b1cb85b57adcb3eb4d2e46a0d795fa55ad341191097ad7138a1938b8"},
-    "awq_gemv": {"source": "gemv.hip", "fetch_kib": 40356, "write_kib": 148,
+    "gemm": {"source": "gemm.hip", "fetch_kib": 180758, "write_kib": 151927,
+             "sha256": "6f3c721d2d40b424f86ffb1bddfd4f77df49186a794a5037d06508a0d2dd76a7"},
+    "awq_gemv": {"source": "gemv.hip", "fetch_kib": 40355, "write_kib": 148,
                  "sha256": "06d88eadf44e341f16f0ed60b6f9b9a215b0837c03260c23416ab488040e22aa"},
-    "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180912, "write_kib": 151944,
-                 "sha256": "9dbb7c43b1cb85b57adcb3eb4d2e46a0d795fa55ad341191097ad7138a1938b8"},
+    "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180910, "write_kib": 152018,
+                 "sha256": "6f3c721d2d40b424f86ffb1bddfd4f77df49186a794a5037d06508a0d2dd76a7"},
 }
 COPY_CALIBRATION = {"fetch_kib_per_gib": 524308, "write_kib_per_gib": 1048576}
 

@@ -15,6 +15,8 @@
 //     per workgroup, waves of 16 MB x 32, copies straight from global memory
 //     into LDS rings, each wave expanding the code words of its own columns;
 //   gemm_skinny_kernel<MB, D, AFF, SPLIT>  few rows (below);
+//   gemm_narrow_kernel<SPLIT>  codebook format, up to 32 rows on a matrix of
+//     few row groups: the waves of a workgroup share one row group (below);
 //   xsum_kernel           the int4 format's per-group sums of x (pre-pass);
 //   gemm_kernel<3>        any finite codebook (each value split into three
 //     bf16 terms), and shapes whose byte offsets exceed 32 bits.
@@ -26,7 +28,8 @@
 // parts are fixed by (N, K) alone (k_parts: two halves for K >= 8192, more
 // for narrow N), each folded from zero, then added in part order: the tiled
 // kernel runs the parts on separate workgroups that meet through the
-// workspace, the skinny and generic kernels one after the other in a wave.
+// workspace, the skinny, narrow and generic kernels one after the other in
+// the K order of each output.
 #include <type_traits>
 
 #include "nf4_internal.h"
@@ -594,7 +597,7 @@ __global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
 // memory rate, which a K loop synchronised at every step cannot do with few
 // tiles across N.  Instead each wave owns one row group and streams all of
 // its K on its own, like the decode GEMV, keeping kSkD weight tiles in
-// flight in registers; only x is shared, staged in LDS in 32 KB chunks
+// flight in registers; only x is shared, staged in LDS in 16 KB chunks
 // (double buffered, one barrier per chunk).  Per tile the lane's 16 code
 // bytes become the B fragments of four 32-k MFMA steps through the pair
 // table, and the MB m-blocks of x supply the A fragments.
@@ -610,7 +613,7 @@ __global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
 // ---------------------------------------------------------------------------
 namespace skinny {
 constexpr int kWaves = 4;        // row groups per workgroup
-constexpr int kXBuf = 32 * 1024; // bytes of one x chunk buffer
+constexpr int kXBuf = 16 * 1024; // bytes of one x chunk buffer (2 workgroups per CU fit)
 }  // namespace skinny
 
 template <int MB, int D, bool AFF, bool SPLIT>
@@ -621,8 +624,8 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
   // K in np parts (SPLIT) or in one
   const int np = SPLIT ? np_arg : 1;
   constexpr int XR = 16 * MB;                  // x rows held (m-blocks of 16)
-  constexpr int KX = skinny::kXBuf / (XR * 2); // k per chunk: 1024, 512, 256
-  constexpr int TC = KX / kTileK;              // tiles per chunk: 8, 4, 2
+  constexpr int KX = skinny::kXBuf / (XR * 2); // k per chunk: 512 (MB 1), 256 (MB 2)
+  constexpr int TC = KX / kTileK;              // tiles per chunk: 4, 2
   constexpr int CPR = KX / 8;                  // 16-byte chunks per x row
   constexpr int XV = skinny::kXBuf / 16 / (64 * skinny::kWaves);  // loads per thread per chunk
   static_assert(D % TC == 0, "the prefetch ring is a whole number of chunks");
@@ -834,6 +837,190 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Narrow kernel (codebook format, short M, few row groups).  The skinny kernel
+// gives each row group one wave, so q|k|v, o and down (224 to 288 row groups)
+// run on that many waves, each bound by its own chain of lookups, products
+// and folds: with every weight load hitting the caches it is no faster.
+// Here the kWaves waves of a workgroup share one row group and one 16-row
+// block of x and take its tiles in turn: window j is tiles kWaves j .. +
+// kWaves - 1, wave w computing tile w of each window.  Per tile a wave forms
+// the block products of its two 64-blocks as the other kernels do
+// (P = MFMA(kk=0, zero), MFMA(kk=1, P)) and parks them in LDS with the
+// tile's block scales; one window later, past the next barrier, wave e folds
+// outputs 16 e .. 16 e + 15 of the lane order (lane l: output lane
+// 16 e + l / 4, element l % 4) through the window's tiles in K order,
+// acc = fmaf(s, P, acc).  Every output gets the other kernels' operations
+// in their order, so its rows are bit-identical to theirs.
+// x (16 rows x 512 k per window), code words and scales all arrive by copies
+// into LDS rings kLead windows ahead; there are no register loads in the
+// loop, so one explicit count waits for exactly the window about to be used.
+// x row R is copied with its 16-byte chunk c stored at c ^ R, so the 16 rows
+// of an A fragment read fall in 16 bank groups.
+// LDS (bytes): pair table 32 K (32 copies), x ring (kLead + 1) x 16 K, code
+// ring (kLead + 1) x kWaves x 1 K, scale ring (kLead + 1) x kWaves x 128,
+// block products 2 x kWaves x 2 K and their scales 2 x kWaves x 512.
+// ---------------------------------------------------------------------------
+namespace narrow {
+constexpr int kWaves = 4;                            // waves per row group = tiles per window
+constexpr int kLead = 3;                             // windows copied ahead
+constexpr int kSlots = kLead + 1;                    // ring slots
+constexpr int kKW = kWaves * kTileK;                 // k per window: 512
+constexpr int kXSlot = 16 * kKW * 2;                 // 16 K
+constexpr int kCSlot = kWaves * kTileBytes;          // 4 K
+constexpr int kSSlot = kWaves * kTileScales * 4;     // 512
+constexpr int kPBuf = kWaves * 2 * 1024;             // 8 K
+constexpr int kSBuf = kWaves * 64 * 8;               // 2 K
+constexpr int kOffX = pipe::kTableBytes;
+constexpr int kOffC = kOffX + kSlots * kXSlot;
+constexpr int kOffS = kOffC + kSlots * kCSlot;
+constexpr int kOffP = kOffS + kSlots * kSSlot;
+constexpr int kOffSB = kOffP + 2 * kPBuf;
+constexpr int kBytes = kOffSB + 2 * kSBuf;
+constexpr int kCopiesPerWindow = 16 / kWaves + 2;    // per wave: x rows, code words, scales
+static_assert(16 % kWaves == 0, "x rows split evenly over the waves");
+static_assert(kBytes <= 160 * 1024, "LDS of one workgroup");
+static_assert((kLead - 1) * kCopiesPerWindow <= 63, "vmcnt range");
+}  // namespace narrow
+
+template <bool SPLIT>
+__global__ __launch_bounds__(64 * narrow::kWaves) void gemm_narrow_kernel(
+    const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ qw,
+    const float *__restrict__ am, CodeTerms ct, int N, int K, int KT, int G,
+    float *__restrict__ y, int np_arg) {
+  using namespace narrow;
+  const int np = SPLIT ? np_arg : 1;
+  // the only static LDS array: the pair table sits at LDS address 0
+  __shared__ __attribute__((aligned(16))) char lds[kBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, h = lane >> 4;
+  const int g = blockIdx.x;           // row group
+  const int m0 = blockIdx.y * 16;     // first x row
+  const int NW = (KT + kWaves - 1) / kWaves;
+  const bool half_tail = (K & (kTileK - 1)) != 0;  // last tile holds one 64-block
+  const uint32_t base = lds_addr(lds);
+
+  // copy sources: x rows 16-row block rows kRows w .. (rows past M re-read
+  // row M - 1, k past K re-reads the row's last chunk: such values only
+  // reach products that are never folded)
+  constexpr int kRows = 16 / kWaves;
+  uint32_t xrow[kRows];
+  int xc[kRows];
+#pragma unroll
+  for (int v = 0; v < kRows; ++v) {
+    const int R = wave * kRows + v;
+    const int m = m0 + R < M ? m0 + R : M - 1;
+    xrow[v] = (uint32_t)m * (uint32_t)K * 2u;
+    xc[v] = lane ^ R;  // logical chunk copied into chunk slot `lane`
+  }
+  const uint32_t gtile = (uint32_t)g * (uint32_t)KT;
+  auto copy_window = [&](int jw) {
+    const int sl = jw % kSlots;
+#pragma unroll
+    for (int v = 0; v < kRows; ++v) {
+      const int k = jw * kKW + xc[v] * 8;
+      const uint32_t kk = (uint32_t)(k < K ? k : K - 8);
+      copy16_to_lds(base + kOffX + sl * kXSlot + (wave * kRows + v) * (kKW * 2), x,
+                    xrow[v] + kk * 2u);
+    }
+    const int i = jw * kWaves + wave;
+    const uint32_t ti = gtile + (uint32_t)(i < KT ? i : KT - 1);
+    copy16_to_lds(base + kOffC + sl * kCSlot + wave * kTileBytes, qw,
+                  ti * (uint32_t)kTileBytes + (uint32_t)lane * 16u);
+    if (lane < kTileScales * 4 / 16)
+      copy16_to_lds(base + kOffS + sl * kSSlot + wave * (kTileScales * 4), am,
+                    ti * (uint32_t)(kTileScales * 4) + (uint32_t)lane * 16u);
+  };
+#pragma unroll
+  for (int jw = 0; jw < kLead; ++jw) copy_window(jw);
+
+  // pair table, from the codebook staged in the (not yet used) product buffers
+  uint16_t *codes16 = reinterpret_cast<uint16_t *>(lds + kOffP);
+  if (tid < 16) codes16[tid] = ct.t[0][tid];
+  __syncthreads();
+  for (int c = tid; c < pipe::kTableBytes / 16; c += 64 * kWaves) {
+    const int e = c / (pipe::kCopies / 4);
+    const uint32_t v = (uint32_t)codes16[e & 15] | ((uint32_t)codes16[e >> 4] << 16);
+    reinterpret_cast<uint4 *>(lds)[c] = make_uint4(v, v, v, v);
+  }
+
+  const uint32_t tcopy = (uint32_t)(lane & (pipe::kCopies - 1)) * 4;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  // products of this wave's tile of window j into buffer j & 1
+  auto compute = [&](int j) {
+    const int sl = j % kSlots;
+    const uint4 w = *reinterpret_cast<const uint4 *>(lds + kOffC + sl * kCSlot + wave * kTileBytes +
+                                                     lane * 16);
+    const float2 sv = *reinterpret_cast<const float2 *>(lds + kOffS + sl * kSSlot +
+                                                        wave * (kTileScales * 4) + r * 8);
+    bf16x8 A[4], B[4];
+    const char *xr = lds + kOffX + sl * kXSlot + r * (kKW * 2);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      A[jj] = *reinterpret_cast<const bf16x8 *>(xr + (((wave * 16 + jj * 4 + h) ^ r) * 16));
+      const uint32_t wd = jj == 0 ? w.x : jj == 1 ? w.y : jj == 2 ? w.z : w.w;
+      uint32_t bb[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t e = (wd >> (8 * q)) & 0xFFu;
+        bb[q] = *reinterpret_cast<const uint32_t *>(lds + e * (pipe::kCopies * 4) + tcopy);
+      }
+      B[jj] = __builtin_bit_cast(bf16x8, make_uint4(bb[0], bb[1], bb[2], bb[3]));
+    }
+    f32x4 p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0], B[0], zero, 0, 0, 0);
+    p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1], B[1], p, 0, 0, 0);
+    f32x4 q2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[2], B[2], zero, 0, 0, 0);
+    q2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[3], B[3], q2, 0, 0, 0);
+    char *pb = lds + kOffP + (j & 1) * kPBuf + wave * 2048 + lane * 16;
+    *reinterpret_cast<f32x4 *>(pb) = p;
+    *reinterpret_cast<f32x4 *>(pb + 1024) = q2;
+    *reinterpret_cast<float2 *>(lds + kOffSB + (j & 1) * kSBuf + wave * 512 + lane * 8) = sv;
+  };
+  // fold window jf: this lane's output is element lane % 4 of output lane
+  // 16 wave + lane / 4
+  float acc = 0.0f, tot = 0.0f;
+  int jn = 1, cut = SPLIT ? part_begin(1, KT, np) : -1;
+  auto fold = [&](int jf) {
+    const char *pb = lds + kOffP + (jf & 1) * kPBuf + wave * 256 + lane * 4;
+    const char *sb = lds + kOffSB + (jf & 1) * kSBuf + (16 * wave + (lane >> 2)) * 8;
+#pragma unroll
+    for (int tw = 0; tw < kWaves; ++tw) {
+      const int i = jf * kWaves + tw;
+      if (SPLIT && i == cut) {  // the next part of K starts from zero
+        tot = jn == 1 ? acc : tot + acc;
+        acc = 0.0f;
+        ++jn;
+        cut = jn < np ? part_begin(jn, KT, np) : -1;
+      }
+      const bool live0 = i < KT, live1 = live0 && !(half_tail && i == KT - 1);
+      const float2 s = *reinterpret_cast<const float2 *>(sb + tw * 512);
+      const float p0 = *reinterpret_cast<const float *>(pb + tw * 2048);
+      const float p1 = *reinterpret_cast<const float *>(pb + tw * 2048 + 1024);
+      const float f0 = fmaf(s.x, p0, acc);
+      const float a0 = live0 ? f0 : acc;
+      const float f1 = fmaf(s.y, p1, a0);
+      acc = live1 ? f1 : a0;
+    }
+  };
+
+  for (int j = 0; j < NW; ++j) {
+    // window j's copies have landed for every wave, and the products of
+    // window j - 1 are in LDS
+    pipe::wait_copies_and_barrier<(kLead - 1) * kCopiesPerWindow>();
+    copy_window(j + kLead);  // into the slot window j - 1 used
+    compute(j);
+    if (j > 0) fold(j - 1);
+  }
+  // every copy has landed (the clamped ones past the end too) before the
+  // workgroup can end, and the last window's products are in LDS
+  pipe::wait_copies_and_barrier<0>();
+  fold(NW - 1);
+
+  const int m = m0 + 4 * wave + (lane & 3);
+  if (m < M) y[(int64_t)m * N + (int64_t)g * 16 + (lane >> 2)] = SPLIT ? tot + acc : acc;
+}
+
+// ---------------------------------------------------------------------------
 // Pre-pass of the affine GEMM: X[t][m] = sum of x[m][128 t .. 128 t + 127]
 // for m < Mp (zero past M), 16 lanes (a DPP row) per (t, m): each lane adds
 // its 8 values in k order, then row16_sum; the GEMV sums the same way.
@@ -1020,9 +1207,28 @@ bool skinny_eligible(int64_t M, int64_t N, int64_t K, int nterm) {
          (N / kTileRows) * tiles_k(K) < (int64_t(1) << 31);
 }
 
+// The narrow kernel rather than the skinny one (bit-identical rows): short M
+// on a matrix of few row groups, where one wave per row group leaves most
+// SIMDs idle.
+constexpr int64_t kNarrowMaxG = 1024;
+constexpr int64_t kNarrowMaxM = 32;
+bool prefer_narrow(int64_t M, int64_t N, int64_t K) {
+  return M <= kNarrowMaxM && N / kTileRows <= kNarrowMaxG && tile_dma_ok(M, N, K);
+}
+
 hipError_t launch_skinny(const uint16_t *x, int64_t M, const uint8_t *qw, const float *am,
                          const CodeTerms &ct, int64_t N, int64_t K, float *y, hipStream_t s) {
   const int64_t G = N / kTileRows;
+  if (prefer_narrow(M, N, K)) {
+    const int np = k_parts(N, K);
+    const dim3 grid((unsigned)G, (unsigned)((M + 15) / 16)), block(64 * narrow::kWaves);
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, block, 0, s, x, (int)M, qw, am, ct, (int)N, (int)K,
+                         (int)tiles_k(K), (int)G, y, np);
+    };
+    np > 1 ? go(gemm_narrow_kernel<true>) : go(gemm_narrow_kernel<false>);
+    return hipGetLastError();
+  }
   const unsigned gx = (unsigned)((G + skinny::kWaves - 1) / skinny::kWaves);
   const dim3 block(64 * skinny::kWaves);
   const int KT = (int)tiles_k(K);

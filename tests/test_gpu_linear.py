@@ -72,7 +72,7 @@ def test_gemv_edges(side, cb, M, N, K):
 GEMM_EDGES = [(1, 48, 192), (2, 16, 64), (3, 512, 256), (5, 48, 128), (8, 4608, 256),
               (9, 16, 3584), (16, 256, 192), (113, 512, 3584), (127, 144, 256),
               (128, 128, 128), (129, 400, 320), (256, 64, 18944), (1024, 48, 64),
-              (300, 1024, 1024)]
+              (300, 1024, 1024), (17, 512, 18944), (32, 272, 704)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_EDGES)
@@ -151,17 +151,20 @@ def test_deterministic_and_batch_independent(side, cb, kind):
 @pytest.mark.parametrize("N,K", [(512, 3584), (256, 18944), (272, 704), (272, 8256),
                                  (512, 8192), (4608, 3584), (16, 18944)])
 def test_gemm_skinny_and_tiled_rows_identical(side, cb, N, K):
-    """nf4_gemm runs rows of a narrow batch on the skinny path (one wave per
-    row group streaming all of K) and a wide batch on the tiled path; both
-    perform the same operations per output, so rows agree bit for bit
-    whichever path the batch size selects (K = 704 and 8256 end in a half
-    tile).  K is summed in the same parts on both paths (k_parts: 1 to 32
-    here), on separate workgroups of the tiled path and one after the other
-    in a skinny wave."""
+    """nf4_gemm runs a batch of up to 32 rows on the narrow path (these
+    matrices have at most 1024 row groups: the four waves of a workgroup
+    take turns over one row group's tiles and fold in K order), up to 64
+    rows on the skinny path (one wave per row group streaming all of K) and
+    a wide batch on the tiled path; all perform the same operations per
+    output, so rows agree bit for bit whichever path the batch size selects
+    (K = 704 and 8256 end in a half tile).  K is summed in the same parts on
+    every path (k_parts: 1 to 32 here), on separate workgroups of the tiled
+    path and one after the other in the other two."""
     packed, absmax, pw = case(side, cb, N, K, mid=27)
     x = synth.activations(0, 300, K, stream=3)
     yt = side.run("gemm", x, pw, cb)            # 300 rows: tiled
-    for M, m0 in ((1, 0), (1, 299), (29, 17), (64, 200), (256, 40)):
+    for M, m0 in ((1, 0), (1, 299), (16, 3), (29, 17), (32, 100), (33, 150), (64, 200),
+                  (256, 40)):
         np.testing.assert_array_equal(side.run("gemm", x[m0:m0 + M], pw, cb), yt[m0:m0 + M],
                                       err_msg=f"M={M} rows {m0}..")
     yr, b = oracle.linear(x[[0, 17, 299]], packed, absmax, cb)
