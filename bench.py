@@ -61,6 +61,7 @@ LINEARS = [("qkv", HIDDEN + 2 * KV, HIDDEN), ("o", HIDDEN, HIDDEN),
            ("gate_up", 2 * MLP, HIDDEN), ("down", HIDDEN, MLP)]
 PREFILL_M = 1024
 TAIL_M = 113  # last chunk of the 14449-row long-audio prompt
+CHUNK_M = 29  # rows of one chunk of streamed input
 DOMINANT = ("gate_up", 2 * MLP, HIDDEN)
 # the unfused 7-linear sequence: (linear, fused matrix, first row, end row)
 UNFUSED = [("q", "qkv", 0, HIDDEN), ("k", "qkv", HIDDEN, HIDDEN + KV),
@@ -77,11 +78,11 @@ LONG_M, LONG_CHUNKS = 14449, 14  # the long-audio prompt: 14 x 1024 rows + the 1
 TRAFFIC = {
     "gemv": {"source": "gemv.hip", "fetch_kib": 42713, "write_kib": 148,
              "sha256": "06d88eadf44e341f16f0ed60b6f9b9a215b0837c03260c23416ab488040e22aa"},
-    "gemm": {"source": "gemm.hip", "fetch_kib": 180758, "write_kib": 151927,
+    "gemm": {"source": "gemm.hip", "fetch_kib": 180758, "write_kib": 151839,
              "sha256": "6f3c721d2d40b424f86ffb1bddfd4f77df49186a794a5037d06508a0d2dd76a7"},
     "awq_gemv": {"source": "gemv.hip", "fetch_kib": 40355, "write_kib": 148,
                  "sha256": "06d88eadf44e341f16f0ed60b6f9b9a215b0837c03260c23416ab488040e22aa"},
-    "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180910, "write_kib": 152018,
+    "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180919, "write_kib": 151964,
                  "sha256": "6f3c721d2d40b424f86ffb1bddfd4f77df49186a794a5037d06508a0d2dd76a7"},
 }
 COPY_CALIBRATION = {"fetch_kib_per_gib": 524308, "write_kib_per_gib": 1048576}
@@ -209,7 +210,7 @@ class Model:
         self.y1["lm_head"] = torch.empty((1, VOCAB), dtype=torch.float32, device=dev)
         self.yp = {name: torch.empty((PREFILL_M, N), dtype=torch.float32, device=dev)
                    for name, N, _ in LINEARS}
-        self.ws_bytes = max([nf4.nf4_workspace_bytes(M, N, K) for M in (1, PREFILL_M)
+        self.ws_bytes = max([nf4.nf4_workspace_bytes(M, N, K) for M in (1, CHUNK_M, TAIL_M, PREFILL_M)
                              for _, N, K in LINEARS] + [nf4.nf4_workspace_bytes(1, VOCAB, HIDDEN)])
         self.ws = torch.zeros(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()  # inputs and the zeroed workspace are ready before stream s runs
@@ -268,7 +269,7 @@ class AwqModel:
         stream.synchronize()
         torch.cuda.empty_cache()
         self.ws_bytes = max(nf4.nf4_awq_workspace_bytes(M, N, K)
-                            for M in (1, TAIL_M, PREFILL_M) for _, N, K in LINEARS)
+                            for M in (1, CHUNK_M, TAIL_M, PREFILL_M) for _, N, K in LINEARS)
         self.ws = torch.zeros(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 
@@ -465,6 +466,18 @@ def main():
     launches += [("gemm", n) for _ in range(reps + 1) for n in prefill_labels()]
     tail_flop = 2 * TAIL_M * sum(N_ * K_ for _, N_, K_ in LINEARS) * LAYERS
     log(f"[bench] prefill tail M={TAIL_M}: {tail_ms:.3f} ms")
+    # ---- one 29-row chunk of streamed input through the same linears
+    def chunk_step():
+        for layer in range(LAYERS):
+            for lname, _, _ in LINEARS:
+                pw = mdl.weights[layer][lname]
+                nf4.nf4_gemm(mdl.xp[pw.K], CHUNK_M, pw.qweight, pw.absmax, cb, pw.N, pw.K,
+                             mdl.yp[lname], mdl.ws, mdl.ws_bytes)
+    chunk_ms = graph_ms(torch, s, chunk_step, reps)
+    launches += [("gemm", n) for _ in range(reps + 1) for n in prefill_labels()]
+    chunk_flop = 2 * CHUNK_M * sum(N_ * K_ for _, N_, K_ in LINEARS) * LAYERS
+    chunk_bytes = sum(packed_bytes(N_, K_) for _, N_, K_ in LINEARS) * LAYERS
+    log(f"[bench] prefill chunk M={CHUNK_M}: {chunk_ms:.3f} ms")
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -626,6 +639,11 @@ def main():
         "prefill_tail": {"M": TAIL_M, "ms": round(tail_ms, 3),
                          "value": round(tail_flop / (tail_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
                          "note": "28 layers x 4 fused linears at M=113 (skinny path for narrow N)"},
+        "prefill_chunk": {"M": CHUNK_M, "ms": round(chunk_ms, 3),
+                          "value": round(chunk_flop / (chunk_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                          "weight_gbps": round(chunk_bytes / (chunk_ms * 1e-3) / 1e9, 1),
+                          "note": "28 layers x 4 fused linears at M=29 (narrow kernel on q|k|v, o "
+                                  "and down, skinny kernel on gate|up)"},
         "decode_unfused": {"value": round(decode_bytes / (decu_ms * 1e-3) / 1e9, 1),
                            "unit": "GB/s", "ms": round(decu_ms, 4),
                            "note": "28 x {q, k, v, o, gate, up, down} + lm_head = 197 launches "
