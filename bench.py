@@ -78,12 +78,12 @@ LONG_M, LONG_CHUNKS = 14449, 14  # the long-audio prompt: 14 x 1024 rows + the 1
 TRAFFIC = {
     "gemv": {"source": "gemv.hip", "fetch_kib": 42713, "write_kib": 148,
              "sha256": "06d88eadf44e341f16f0ed60b6f9b9a215b0837c03260c23416ab488040e22aa"},
-    "gemm": {"source": "gemm.hip", "fetch_kib": 180758, "write_kib": 151839,
-             "sha256": "6f3c721d2d40b424f86ffb1bddfd4f77df49186a794a5037d06508a0d2dd76a7"},
+    "gemm": {"source": "gemm.hip", "fetch_kib": 180752, "write_kib": 151916,
+             "sha256": "84c04b2bb605e915d46badd56c33c616cd60541f253563b1e935aad2b9098509"},
     "awq_gemv": {"source": "gemv.hip", "fetch_kib": 40355, "write_kib": 148,
                  "sha256": "06d88eadf44e341f16f0ed60b6f9b9a215b0837c03260c23416ab488040e22aa"},
-    "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180919, "write_kib": 151964,
-                 "sha256": "6f3c721d2d40b424f86ffb1bddfd4f77df49186a794a5037d06508a0d2dd76a7"},
+    "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180912, "write_kib": 151943,
+                 "sha256": "84c04b2bb605e915d46badd56c33c616cd60541f253563b1e935aad2b9098509"},
 }
 COPY_CALIBRATION = {"fetch_kib_per_gib": 524308, "write_kib_per_gib": 1048576}
 

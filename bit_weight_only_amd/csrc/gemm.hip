@@ -15,8 +15,8 @@
 //     per workgroup, waves of 16 MB x 32, copies straight from global memory
 //     into LDS rings, each wave expanding the code words of its own columns;
 //   gemm_skinny_kernel<MB, D, AFF, SPLIT>  few rows (below);
-//   gemm_narrow_kernel<SPLIT>  codebook format, up to 32 rows on a matrix of
-//     few row groups: the waves of a workgroup share one row group (below);
+//   gemm_narrow_kernel<AFF, SPLIT>  up to 32 rows on a matrix of few row
+//     groups, both formats: the waves of a workgroup share one row group;
 //   xsum_kernel           the int4 format's per-group sums of x (pre-pass);
 //   gemm_kernel<3>        any finite codebook (each value split into three
 //     bf16 terms), and shapes whose byte offsets exceed 32 bits.
@@ -837,7 +837,7 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Narrow kernel (codebook format, short M, few row groups).  The skinny kernel
+// Narrow kernel (short M, few row groups, both formats).  The skinny kernel
 // gives each row group one wave, so q|k|v, o and down (224 to 288 row groups)
 // run on that many waves, each bound by its own chain of lookups, products
 // and folds: with every weight load hitting the caches it is no faster.
@@ -859,6 +859,13 @@ __global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
 // LDS (bytes): pair table 32 K (32 copies), x ring (kLead + 1) x 16 K, code
 // ring (kLead + 1) x kWaves x 1 K, scale ring (kLead + 1) x kWaves x 128,
 // block products 2 x kWaves x 2 K and their scales 2 x kWaves x 512.
+// Affine variant (AFF, int4 in groups of 128): no pair table (B pairs from
+// the interleaved code words by shift and mask), one product per tile (four
+// MFMAs from zero), 64 bytes of params per tile, and the x sums X[t][m0 ..
+// m0 + 15] of the pre-pass copied with each window; the computing wave moves
+// its tile's 16 sums next to the product, and the fold takes
+// g = fmaf(-(16 + z)/16, X, P), acc = fmaf(16 s, g, acc), as the tiled and
+// skinny kernels' affine variants do.
 // ---------------------------------------------------------------------------
 namespace narrow {
 constexpr int kWaves = 4;                            // waves per row group = tiles per window
@@ -867,30 +874,43 @@ constexpr int kSlots = kLead + 1;                    // ring slots
 constexpr int kKW = kWaves * kTileK;                 // k per window: 512
 constexpr int kXSlot = 16 * kKW * 2;                 // 16 K
 constexpr int kCSlot = kWaves * kTileBytes;          // 4 K
-constexpr int kSSlot = kWaves * kTileScales * 4;     // 512
-constexpr int kPBuf = kWaves * 2 * 1024;             // 8 K
-constexpr int kSBuf = kWaves * 64 * 8;               // 2 K
-constexpr int kOffX = pipe::kTableBytes;
-constexpr int kOffC = kOffX + kSlots * kXSlot;
-constexpr int kOffS = kOffC + kSlots * kCSlot;
-constexpr int kOffP = kOffS + kSlots * kSSlot;
-constexpr int kOffSB = kOffP + 2 * kPBuf;
-constexpr int kBytes = kOffSB + 2 * kSBuf;
-constexpr int kCopiesPerWindow = 16 / kWaves + 2;    // per wave: x rows, code words, scales
 static_assert(16 % kWaves == 0, "x rows split evenly over the waves");
-static_assert(kBytes <= 160 * 1024, "LDS of one workgroup");
-static_assert((kLead - 1) * kCopiesPerWindow <= 63, "vmcnt range");
+// LDS layout; the affine variant has no pair table, one block product per
+// tile, 64 bytes of params per tile and a ring of the x sums (16 rows per tile)
+template <bool AFF>
+struct Lay {
+  static constexpr int kSBytes = AFF ? kTileRows * 4 : kTileScales * 4;  // scales of a tile
+  static constexpr int kSSlot = kWaves * kSBytes;
+  static constexpr int kXSSlot = AFF ? kWaves * 16 * 4 : 0;
+  static constexpr int kBlocks = AFF ? 1 : 2;         // block products per tile
+  static constexpr int kPBuf = kWaves * kBlocks * 1024;
+  static constexpr int kSBuf = kWaves * 64 * 8;
+  static constexpr int kXBuf = AFF ? kWaves * 16 * 4 : 0;
+  static constexpr int kOffX = AFF ? 0 : pipe::kTableBytes;
+  static constexpr int kOffC = kOffX + kSlots * kXSlot;
+  static constexpr int kOffS = kOffC + kSlots * kCSlot;
+  static constexpr int kOffXS = kOffS + kSlots * kSSlot;
+  static constexpr int kOffP = kOffXS + kSlots * kXSSlot;
+  static constexpr int kOffSB = kOffP + 2 * kPBuf;
+  static constexpr int kOffXB = kOffSB + 2 * kSBuf;
+  static constexpr int kBytes = kOffXB + 2 * kXBuf;
+  // per wave and window: x rows, code words, scales (and x sums)
+  static constexpr int kCopies = 16 / kWaves + 2 + (AFF ? 1 : 0);
+  static_assert(kBytes <= 160 * 1024, "LDS of one workgroup");
+  static_assert((kLead - 1) * kCopies <= 63, "vmcnt range");
+};
 }  // namespace narrow
 
-template <bool SPLIT>
+template <bool AFF, bool SPLIT>
 __global__ __launch_bounds__(64 * narrow::kWaves) void gemm_narrow_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ qw,
     const float *__restrict__ am, CodeTerms ct, int N, int K, int KT, int G,
-    float *__restrict__ y, int np_arg) {
+    float *__restrict__ y, const float *__restrict__ xsum, int Mp, int np_arg) {
   using namespace narrow;
+  using L = Lay<AFF>;
   const int np = SPLIT ? np_arg : 1;
   // the only static LDS array: the pair table sits at LDS address 0
-  __shared__ __attribute__((aligned(16))) char lds[kBytes];
+  __shared__ __attribute__((aligned(16))) char lds[L::kBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, h = lane >> 4;
@@ -900,7 +920,7 @@ __global__ __launch_bounds__(64 * narrow::kWaves) void gemm_narrow_kernel(
   const bool half_tail = (K & (kTileK - 1)) != 0;  // last tile holds one 64-block
   const uint32_t base = lds_addr(lds);
 
-  // copy sources: x rows 16-row block rows kRows w .. (rows past M re-read
+  // copy sources: x rows kRows w .. of the 16-row block (rows past M re-read
   // row M - 1, k past K re-reads the row's last chunk: such values only
   // reach products that are never folded)
   constexpr int kRows = 16 / kWaves;
@@ -920,41 +940,57 @@ __global__ __launch_bounds__(64 * narrow::kWaves) void gemm_narrow_kernel(
     for (int v = 0; v < kRows; ++v) {
       const int k = jw * kKW + xc[v] * 8;
       const uint32_t kk = (uint32_t)(k < K ? k : K - 8);
-      copy16_to_lds(base + kOffX + sl * kXSlot + (wave * kRows + v) * (kKW * 2), x,
+      copy16_to_lds(base + L::kOffX + sl * kXSlot + (wave * kRows + v) * (kKW * 2), x,
                     xrow[v] + kk * 2u);
     }
     const int i = jw * kWaves + wave;
-    const uint32_t ti = gtile + (uint32_t)(i < KT ? i : KT - 1);
-    copy16_to_lds(base + kOffC + sl * kCSlot + wave * kTileBytes, qw,
+    const int tl = i < KT ? i : KT - 1;
+    const uint32_t ti = gtile + (uint32_t)tl;
+    copy16_to_lds(base + L::kOffC + sl * kCSlot + wave * kTileBytes, qw,
                   ti * (uint32_t)kTileBytes + (uint32_t)lane * 16u);
-    if (lane < kTileScales * 4 / 16)
-      copy16_to_lds(base + kOffS + sl * kSSlot + wave * (kTileScales * 4), am,
-                    ti * (uint32_t)(kTileScales * 4) + (uint32_t)lane * 16u);
+    if (lane < L::kSBytes / 16)
+      copy16_to_lds(base + L::kOffS + sl * L::kSSlot + wave * L::kSBytes, am,
+                    ti * (uint32_t)L::kSBytes + (uint32_t)lane * 16u);
+    if constexpr (AFF) {
+      // x sums X[tile][m0 .. m0 + 15] (rows up to Mp, a multiple of 128)
+      if (lane < 4)
+        copy16_to_lds(base + L::kOffXS + sl * L::kXSSlot + wave * 64, xsum,
+                      ((uint32_t)tl * (uint32_t)Mp + (uint32_t)m0) * 4u + (uint32_t)lane * 16u);
+    }
   };
 #pragma unroll
   for (int jw = 0; jw < kLead; ++jw) copy_window(jw);
 
   // pair table, from the codebook staged in the (not yet used) product buffers
-  uint16_t *codes16 = reinterpret_cast<uint16_t *>(lds + kOffP);
-  if (tid < 16) codes16[tid] = ct.t[0][tid];
-  __syncthreads();
-  for (int c = tid; c < pipe::kTableBytes / 16; c += 64 * kWaves) {
-    const int e = c / (pipe::kCopies / 4);
-    const uint32_t v = (uint32_t)codes16[e & 15] | ((uint32_t)codes16[e >> 4] << 16);
-    reinterpret_cast<uint4 *>(lds)[c] = make_uint4(v, v, v, v);
+  if constexpr (!AFF) {
+    uint16_t *codes16 = reinterpret_cast<uint16_t *>(lds + L::kOffP);
+    if (tid < 16) codes16[tid] = ct.t[0][tid];
+    __syncthreads();
+    for (int c = tid; c < pipe::kTableBytes / 16; c += 64 * kWaves) {
+      const int e = c / (pipe::kCopies / 4);
+      const uint32_t v = (uint32_t)codes16[e & 15] | ((uint32_t)codes16[e >> 4] << 16);
+      reinterpret_cast<uint4 *>(lds)[c] = make_uint4(v, v, v, v);
+    }
   }
 
   const uint32_t tcopy = (uint32_t)(lane & (pipe::kCopies - 1)) * 4;
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  // products of this wave's tile of window j into buffer j & 1
+  // products of this wave's tile of window j into buffer j & 1, with the
+  // tile's scales (and, affine, its x sums)
   auto compute = [&](int j) {
     const int sl = j % kSlots;
-    const uint4 w = *reinterpret_cast<const uint4 *>(lds + kOffC + sl * kCSlot + wave * kTileBytes +
+    const uint4 w = *reinterpret_cast<const uint4 *>(lds + L::kOffC + sl * kCSlot + wave * kTileBytes +
                                                      lane * 16);
-    const float2 sv = *reinterpret_cast<const float2 *>(lds + kOffS + sl * kSSlot +
-                                                        wave * (kTileScales * 4) + r * 8);
+    float2 sv;
+    if constexpr (AFF)
+      sv = make_float2(*reinterpret_cast<const float *>(lds + L::kOffS + sl * L::kSSlot +
+                                                        wave * L::kSBytes + r * 4),
+                       0.0f);
+    else
+      sv = *reinterpret_cast<const float2 *>(lds + L::kOffS + sl * L::kSSlot + wave * L::kSBytes +
+                                             r * 8);
     bf16x8 A[4], B[4];
-    const char *xr = lds + kOffX + sl * kXSlot + r * (kKW * 2);
+    const char *xr = lds + L::kOffX + sl * kXSlot + r * (kKW * 2);
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       A[jj] = *reinterpret_cast<const bf16x8 *>(xr + (((wave * 16 + jj * 4 + h) ^ r) * 16));
@@ -962,27 +998,44 @@ __global__ __launch_bounds__(64 * narrow::kWaves) void gemm_narrow_kernel(
       uint32_t bb[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint32_t e = (wd >> (8 * q)) & 0xFFu;
-        bb[q] = *reinterpret_cast<const uint32_t *>(lds + e * (pipe::kCopies * 4) + tcopy);
+        if constexpr (AFF) {
+          // bf16 (1 + c/16) of codes 2q, 2q + 1 (interleaved nibbles)
+          bb[q] = awq_pair(wd, q, 0x3F803F80u);
+        } else {
+          const uint32_t e = (wd >> (8 * q)) & 0xFFu;
+          bb[q] = *reinterpret_cast<const uint32_t *>(lds + e * (pipe::kCopies * 4) + tcopy);
+        }
       }
       B[jj] = __builtin_bit_cast(bf16x8, make_uint4(bb[0], bb[1], bb[2], bb[3]));
     }
-    f32x4 p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0], B[0], zero, 0, 0, 0);
-    p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1], B[1], p, 0, 0, 0);
-    f32x4 q2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[2], B[2], zero, 0, 0, 0);
-    q2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[3], B[3], q2, 0, 0, 0);
-    char *pb = lds + kOffP + (j & 1) * kPBuf + wave * 2048 + lane * 16;
-    *reinterpret_cast<f32x4 *>(pb) = p;
-    *reinterpret_cast<f32x4 *>(pb + 1024) = q2;
-    *reinterpret_cast<float2 *>(lds + kOffSB + (j & 1) * kSBuf + wave * 512 + lane * 8) = sv;
+    char *pb = lds + L::kOffP + (j & 1) * L::kPBuf + wave * (L::kBlocks * 1024) + lane * 16;
+    if constexpr (AFF) {
+      // one group of 128: four MFMAs from zero
+      f32x4 p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0], B[0], zero, 0, 0, 0);
+#pragma unroll
+      for (int jj = 1; jj < 4; ++jj) p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[jj], B[jj], p, 0, 0, 0);
+      *reinterpret_cast<f32x4 *>(pb) = p;
+      if (lane < 16)
+        *reinterpret_cast<float *>(lds + L::kOffXB + (j & 1) * L::kXBuf + wave * 64 + lane * 4) =
+            *reinterpret_cast<const float *>(lds + L::kOffXS + sl * L::kXSSlot + wave * 64 + lane * 4);
+    } else {
+      f32x4 p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0], B[0], zero, 0, 0, 0);
+      p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1], B[1], p, 0, 0, 0);
+      f32x4 q2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[2], B[2], zero, 0, 0, 0);
+      q2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[3], B[3], q2, 0, 0, 0);
+      *reinterpret_cast<f32x4 *>(pb) = p;
+      *reinterpret_cast<f32x4 *>(pb + 1024) = q2;
+    }
+    *reinterpret_cast<float2 *>(lds + L::kOffSB + (j & 1) * L::kSBuf + wave * 512 + lane * 8) = sv;
   };
   // fold window jf: this lane's output is element lane % 4 of output lane
-  // 16 wave + lane / 4
+  // 16 wave + lane / 4 (x row m0 + 4 wave + lane % 4, weight row lane / 4)
   float acc = 0.0f, tot = 0.0f;
   int jn = 1, cut = SPLIT ? part_begin(1, KT, np) : -1;
   auto fold = [&](int jf) {
-    const char *pb = lds + kOffP + (jf & 1) * kPBuf + wave * 256 + lane * 4;
-    const char *sb = lds + kOffSB + (jf & 1) * kSBuf + (16 * wave + (lane >> 2)) * 8;
+    const char *pb = lds + L::kOffP + (jf & 1) * L::kPBuf + wave * 256 + lane * 4;
+    const char *sb = lds + L::kOffSB + (jf & 1) * L::kSBuf + (16 * wave + (lane >> 2)) * 8;
+    const char *xb = lds + L::kOffXB + (jf & 1) * L::kXBuf + (4 * wave + (lane & 3)) * 4;
 #pragma unroll
     for (int tw = 0; tw < kWaves; ++tw) {
       const int i = jf * kWaves + tw;
@@ -994,19 +1047,30 @@ __global__ __launch_bounds__(64 * narrow::kWaves) void gemm_narrow_kernel(
       }
       const bool live0 = i < KT, live1 = live0 && !(half_tail && i == KT - 1);
       const float2 s = *reinterpret_cast<const float2 *>(sb + tw * 512);
-      const float p0 = *reinterpret_cast<const float *>(pb + tw * 2048);
-      const float p1 = *reinterpret_cast<const float *>(pb + tw * 2048 + 1024);
-      const float f0 = fmaf(s.x, p0, acc);
-      const float a0 = live0 ? f0 : acc;
-      const float f1 = fmaf(s.y, p1, a0);
-      acc = live1 ? f1 : a0;
+      if constexpr (AFF) {
+        // 16 s and -(16 + z)/16 from the params dword (binary16 s | z << 16)
+        const uint32_t pv = __float_as_uint(s.x);
+        const float sc = 16.0f * (float)__builtin_bit_cast(_Float16, (uint16_t)(pv & 0xFFFFu));
+        const float nz = -(float)(16u + (pv >> 16)) * 0.0625f;
+        const float P = *reinterpret_cast<const float *>(pb + tw * 1024);
+        const float xz = *reinterpret_cast<const float *>(xb + tw * 64);
+        const float f = fmaf(sc, fmaf(nz, xz, P), acc);
+        acc = live0 ? f : acc;
+      } else {
+        const float p0 = *reinterpret_cast<const float *>(pb + tw * 2048);
+        const float p1 = *reinterpret_cast<const float *>(pb + tw * 2048 + 1024);
+        const float f0 = fmaf(s.x, p0, acc);
+        const float a0 = live0 ? f0 : acc;
+        const float f1 = fmaf(s.y, p1, a0);
+        acc = live1 ? f1 : a0;
+      }
     }
   };
 
   for (int j = 0; j < NW; ++j) {
     // window j's copies have landed for every wave, and the products of
     // window j - 1 are in LDS
-    pipe::wait_copies_and_barrier<(kLead - 1) * kCopiesPerWindow>();
+    pipe::wait_copies_and_barrier<(kLead - 1) * L::kCopies>();
     copy_window(j + kLead);  // into the slot window j - 1 used
     compute(j);
     if (j > 0) fold(j - 1);
@@ -1051,6 +1115,15 @@ __global__ __launch_bounds__(256) void xsum_kernel(const uint16_t *__restrict__ 
 bool tile_dma_ok(int64_t M, int64_t N, int64_t K) {
   return M * K * 2 < (int64_t(1) << 32) &&
          (N / kTileRows) * tiles_k(K) * kTileBytes < (int64_t(1) << 32);
+}
+
+// The narrow kernel rather than the skinny one (bit-identical rows): short M
+// on a matrix of few row groups, where one wave per row group leaves most
+// SIMDs idle.
+constexpr int64_t kNarrowMaxG = 1024;
+constexpr int64_t kNarrowMaxM = 32;
+bool prefer_narrow(int64_t M, int64_t N, int64_t K) {
+  return M <= kNarrowMaxM && N / kTileRows <= kNarrowMaxG && tile_dma_ok(M, N, K);
 }
 
 // The skinny kernel rather than the tiled one (bit-identical rows, so the
@@ -1181,9 +1254,18 @@ hipError_t launch_awq_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, cons
   const int64_t G = N / kTileRows;
   const float *prf = reinterpret_cast<const float *>(pr);
   if (skinny) {
+    const int np = k_parts(N, K);
+    if (prefer_narrow(M, N, K)) {
+      const dim3 grid((unsigned)G, (unsigned)((M + 15) / 16)), block(64 * narrow::kWaves);
+      auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, block, 0, s, x, (int)M, qw, prf, ct, (int)N, (int)K,
+                           (int)KT, (int)G, y, X, (int)Mp, np);
+      };
+      np > 1 ? go(gemm_narrow_kernel<true, true>) : go(gemm_narrow_kernel<true, false>);
+      return hipGetLastError();
+    }
     const unsigned gx = (unsigned)((G + skinny::kWaves - 1) / skinny::kWaves);
     const dim3 block(64 * skinny::kWaves);
-    const int np = k_parts(N, K);
     auto go = [&](auto kern, dim3 grid) {
       hipLaunchKernelGGL(kern, grid, block, 0, s, x, (int)M, qw, prf, ct, (int)N, (int)K, (int)KT,
                          (int)G, y, X, (int)Mp, np);
@@ -1207,15 +1289,6 @@ bool skinny_eligible(int64_t M, int64_t N, int64_t K, int nterm) {
          (N / kTileRows) * tiles_k(K) < (int64_t(1) << 31);
 }
 
-// The narrow kernel rather than the skinny one (bit-identical rows): short M
-// on a matrix of few row groups, where one wave per row group leaves most
-// SIMDs idle.
-constexpr int64_t kNarrowMaxG = 1024;
-constexpr int64_t kNarrowMaxM = 32;
-bool prefer_narrow(int64_t M, int64_t N, int64_t K) {
-  return M <= kNarrowMaxM && N / kTileRows <= kNarrowMaxG && tile_dma_ok(M, N, K);
-}
-
 hipError_t launch_skinny(const uint16_t *x, int64_t M, const uint8_t *qw, const float *am,
                          const CodeTerms &ct, int64_t N, int64_t K, float *y, hipStream_t s) {
   const int64_t G = N / kTileRows;
@@ -1224,9 +1297,9 @@ hipError_t launch_skinny(const uint16_t *x, int64_t M, const uint8_t *qw, const 
     const dim3 grid((unsigned)G, (unsigned)((M + 15) / 16)), block(64 * narrow::kWaves);
     auto go = [&](auto kern) {
       hipLaunchKernelGGL(kern, grid, block, 0, s, x, (int)M, qw, am, ct, (int)N, (int)K,
-                         (int)tiles_k(K), (int)G, y, np);
+                         (int)tiles_k(K), (int)G, y, nullptr, 0, np);
     };
-    np > 1 ? go(gemm_narrow_kernel<true>) : go(gemm_narrow_kernel<false>);
+    np > 1 ? go(gemm_narrow_kernel<false, true>) : go(gemm_narrow_kernel<false, false>);
     return hipGetLastError();
   }
   const unsigned gx = (unsigned)((G + skinny::kWaves - 1) / skinny::kWaves);

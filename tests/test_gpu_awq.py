@@ -129,7 +129,7 @@ def test_awq_gemv_edges(side, M, N, K):
 
 GEMM_EDGES = [(1, 48, 128), (9, 272, 256), (100, 16, 384), (128, 512, 3584), (129, 160, 1024),
               (300, 272, 640), (257, 2048, 256), (64, 64, 18944), (300, 272, 8320),
-              (129, 512, 8192)]
+              (129, 512, 8192), (29, 512, 3584), (32, 64, 18944)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_EDGES)
@@ -180,15 +180,16 @@ def test_awq_zero_point_cancellation(side, kind):
 
 @pytest.mark.parametrize("N,K", [(272, 1024), (272, 8320)])
 def test_awq_gemm_deterministic_and_batch_independent(side, N, K):
-    """Rows do not depend on the batch (K = 8320, N = 272: summed in 10
-    parts on the tiled and the skinny path alike), and a reused workspace
-    full of stale bytes gives the same bits (every call sets what it reads)."""
+    """Rows do not depend on the batch: 300 rows take the tiled path, up to
+    32 rows the narrow path, 33 the skinny path (K = 8320, N = 272: summed
+    in 10 parts on every path), and a reused workspace full of stale bytes
+    gives the same bits (every call sets what it reads)."""
     packed, scales, zeros, aw = awq_case(side, N, K, mid=34)
     x = synth.activations(0, 300, K, stream=12)
     y1 = side.awq_run("gemm", x, aw)
     y2 = side.awq_run("gemm", x, aw)
     np.testing.assert_array_equal(y1, y2)
-    for lo, hi in ((0, 1), (5, 13), (128, 300), (290, 300)):
+    for lo, hi in ((0, 1), (5, 13), (17, 46), (40, 73), (128, 300), (290, 300)):
         np.testing.assert_array_equal(side.awq_run("gemm", x[lo:hi], aw), y1[lo:hi])
     t = side.torch
     ws = t.full((side.nf4.nf4_awq_workspace_bytes(300, N, K),), 0xFF, dtype=t.uint8,
