@@ -78,11 +78,11 @@ LONG_M, LONG_CHUNKS = 14449, 14  # the long-audio prompt: 14 x 1024 rows + the 1
 TRAFFIC = {
     "gemv": {"source": "gemv.hip", "fetch_kib": 42713, "write_kib": 148,
              "sha256": "06d88eadf44e341f16f0ed60b6f9b9a215b0837c03260c23416ab488040e22aa"},
-    "gemm": {"source": "gemm.hip", "fetch_kib": 180752, "write_kib": 151916,
+    "gemm": {"source": "gemm.hip", "fetch_kib": 180752, "write_kib": 151822,
              "sha256": "84c04b2bb605e915d46badd56c33c616cd60541f253563b1e935aad2b9098509"},
     "awq_gemv": {"source": "gemv.hip", "fetch_kib": 40355, "write_kib": 148,
                  "sha256": "06d88eadf44e341f16f0ed60b6f9b9a215b0837c03260c23416ab488040e22aa"},
-    "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180912, "write_kib": 151943,
+    "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180912, "write_kib": 151845,
                  "sha256": "84c04b2bb605e915d46badd56c33c616cd60541f253563b1e935aad2b9098509"},
 }
 COPY_CALIBRATION = {"fetch_kib_per_gib": 524308, "write_kib_per_gib": 1048576}
@@ -340,7 +340,8 @@ def main():
     ap.add_argument("--launch-log", default=None,
                     help="write the label of every nf4_gemv/nf4_gemm launch, in order, to FILE")
     ap.add_argument("--pmc-pass", action="store_true",
-                    help="run only the counter workload: a 1 GiB copy, 3 gate|up GEMVs, 1 GEMM")
+                    help="run only the counter workload: a 1 GiB copy, 3 gate|up GEMVs, 1 GEMM "
+                         "(both formats), and down at M=29")
     ap.add_argument("--summarize", default=None, metavar="DIR",
                     help="print a markdown summary of rocprofv3 CSV output under DIR")
     ap.add_argument("--title", default="")
@@ -790,7 +791,7 @@ def int4_leg(torch, nf4, args, s, mdl, launches):
 def pmc_pass(torch, nf4, cb, seed, s):
     """Counter workload, each step synchronized: a plain copy of 1 GiB
     (counter calibration), then three gate|up GEMVs on distinct weights and
-    one gate|up GEMM."""
+    one gate|up GEMM, and down at M=29 (the narrow kernel, K in two parts)."""
     src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -805,6 +806,14 @@ def pmc_pass(torch, nf4, cb, seed, s):
             s.synchronize()
         mdl.gemm("gate_up", 0)
         s.synchronize()
+    dmdl = Model(torch, nf4, cb, seed, s, layers=1, with_head=False, only=("down",))
+    pw = dmdl.weights[0]["down"]
+    with torch.cuda.stream(s):
+        nf4.nf4_gemm(dmdl.xp[pw.K], CHUNK_M, pw.qweight, pw.absmax, cb, pw.N, pw.K,
+                     dmdl.yp["down"], dmdl.ws, dmdl.ws_bytes)
+        s.synchronize()
+    del dmdl
+    torch.cuda.empty_cache()
     amdl = AwqModel(torch, nf4, seed, s, mdl, layers=3, with_head=False, only=("gate_up",))
     with torch.cuda.stream(s):
         for layer in range(3):
@@ -812,7 +821,8 @@ def pmc_pass(torch, nf4, cb, seed, s):
             s.synchronize()
         amdl.gemm("gate_up", 0)
         s.synchronize()
-    log("[bench] pmc pass: copy 1 GiB, 3 x gate|up gemv, 1 x gate|up gemm, both formats")
+    log("[bench] pmc pass: copy 1 GiB, 3 x gate|up gemv, 1 x gate|up gemm, both formats; "
+        "down at M=29")
 
 
 def _kernel_short(name):
