@@ -78,12 +78,12 @@ LONG_M, LONG_CHUNKS = 14449, 14  # the long-audio prompt: 14 x 1024 rows + the 1
 TRAFFIC = {
     "gemv": {"source": "gemv.hip", "fetch_kib": 42713, "write_kib": 148,
              "sha256": "06d88eadf44e341f16f0ed60b6f9b9a215b0837c03260c23416ab488040e22aa"},
-    "gemm": {"source": "gemm.hip", "fetch_kib": 180752, "write_kib": 151822,
-             "sha256": "84c04b2bb605e915d46badd56c33c616cd60541f253563b1e935aad2b9098509"},
+    "gemm": {"source": "gemm.hip", "fetch_kib": 180759, "write_kib": 151961,
+             "sha256": "48ca7077af481c8e09889f6509177380f245e767fa71cb5cbf878ecfb837e4f2"},
     "awq_gemv": {"source": "gemv.hip", "fetch_kib": 40355, "write_kib": 148,
                  "sha256": "06d88eadf44e341f16f0ed60b6f9b9a215b0837c03260c23416ab488040e22aa"},
-    "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180912, "write_kib": 151845,
-                 "sha256": "84c04b2bb605e915d46badd56c33c616cd60541f253563b1e935aad2b9098509"},
+    "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180913, "write_kib": 151929,
+                 "sha256": "48ca7077af481c8e09889f6509177380f245e767fa71cb5cbf878ecfb837e4f2"},
 }
 COPY_CALIBRATION = {"fetch_kib_per_gib": 524308, "write_kib_per_gib": 1048576}
 

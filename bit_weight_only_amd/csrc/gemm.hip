@@ -936,12 +936,22 @@ __global__ __launch_bounds__(64 * narrow::kWaves) void gemm_narrow_kernel(
   const uint32_t gtile = (uint32_t)g * (uint32_t)KT;
   auto copy_window = [&](int jw) {
     const int sl = jw % kSlots;
+    if (!AFF && (jw + 1) * kKW <= K) {
+      // whole window inside K: the window's k goes into the scalar base
+      // (codebook format; the affine instances measured no faster)
+      const char *xw = reinterpret_cast<const char *>(x) + (size_t)jw * (kKW * 2);
 #pragma unroll
-    for (int v = 0; v < kRows; ++v) {
-      const int k = jw * kKW + xc[v] * 8;
-      const uint32_t kk = (uint32_t)(k < K ? k : K - 8);
-      copy16_to_lds(base + L::kOffX + sl * kXSlot + (wave * kRows + v) * (kKW * 2), x,
-                    xrow[v] + kk * 2u);
+      for (int v = 0; v < kRows; ++v)
+        copy16_to_lds(base + L::kOffX + sl * kXSlot + (wave * kRows + v) * (kKW * 2), xw,
+                      xrow[v] + (uint32_t)xc[v] * 16u);
+    } else {
+#pragma unroll
+      for (int v = 0; v < kRows; ++v) {
+        const int k = jw * kKW + xc[v] * 8;
+        const uint32_t kk = (uint32_t)(k < K ? k : K - 8);
+        copy16_to_lds(base + L::kOffX + sl * kXSlot + (wave * kRows + v) * (kKW * 2), x,
+                      xrow[v] + kk * 2u);
+      }
     }
     const int i = jw * kWaves + wave;
     const int tl = i < KT ? i : KT - 1;
@@ -1036,35 +1046,44 @@ __global__ __launch_bounds__(64 * narrow::kWaves) void gemm_narrow_kernel(
     const char *pb = lds + L::kOffP + (jf & 1) * L::kPBuf + wave * 256 + lane * 4;
     const char *sb = lds + L::kOffSB + (jf & 1) * L::kSBuf + (16 * wave + (lane >> 2)) * 8;
     const char *xb = lds + L::kOffXB + (jf & 1) * L::kXBuf + (4 * wave + (lane & 3)) * 4;
+    // WHOLE: four whole tiles inside K, folded without selects (codebook
+    // format; the affine instances measured no faster)
+    auto body = [&](auto wc) {
+      constexpr bool WHOLE = decltype(wc)::value;
 #pragma unroll
-    for (int tw = 0; tw < kWaves; ++tw) {
-      const int i = jf * kWaves + tw;
-      if (SPLIT && i == cut) {  // the next part of K starts from zero
-        tot = jn == 1 ? acc : tot + acc;
-        acc = 0.0f;
-        ++jn;
-        cut = jn < np ? part_begin(jn, KT, np) : -1;
+      for (int tw = 0; tw < kWaves; ++tw) {
+        const int i = jf * kWaves + tw;
+        if (SPLIT && i == cut) {  // the next part of K starts from zero
+          tot = jn == 1 ? acc : tot + acc;
+          acc = 0.0f;
+          ++jn;
+          cut = jn < np ? part_begin(jn, KT, np) : -1;
+        }
+        const bool live0 = i < KT, live1 = live0 && !(half_tail && i == KT - 1);
+        const float2 s = *reinterpret_cast<const float2 *>(sb + tw * 512);
+        if constexpr (AFF) {
+          // 16 s and -(16 + z)/16 from the params dword (binary16 s | z << 16)
+          const uint32_t pv = __float_as_uint(s.x);
+          const float sc = 16.0f * (float)__builtin_bit_cast(_Float16, (uint16_t)(pv & 0xFFFFu));
+          const float nz = -(float)(16u + (pv >> 16)) * 0.0625f;
+          const float P = *reinterpret_cast<const float *>(pb + tw * 1024);
+          const float xz = *reinterpret_cast<const float *>(xb + tw * 64);
+          const float f = fmaf(sc, fmaf(nz, xz, P), acc);
+          acc = WHOLE || live0 ? f : acc;
+        } else {
+          const float p0 = *reinterpret_cast<const float *>(pb + tw * 2048);
+          const float p1 = *reinterpret_cast<const float *>(pb + tw * 2048 + 1024);
+          const float f0 = fmaf(s.x, p0, acc);
+          const float a0 = WHOLE || live0 ? f0 : acc;
+          const float f1 = fmaf(s.y, p1, a0);
+          acc = WHOLE || live1 ? f1 : a0;
+        }
       }
-      const bool live0 = i < KT, live1 = live0 && !(half_tail && i == KT - 1);
-      const float2 s = *reinterpret_cast<const float2 *>(sb + tw * 512);
-      if constexpr (AFF) {
-        // 16 s and -(16 + z)/16 from the params dword (binary16 s | z << 16)
-        const uint32_t pv = __float_as_uint(s.x);
-        const float sc = 16.0f * (float)__builtin_bit_cast(_Float16, (uint16_t)(pv & 0xFFFFu));
-        const float nz = -(float)(16u + (pv >> 16)) * 0.0625f;
-        const float P = *reinterpret_cast<const float *>(pb + tw * 1024);
-        const float xz = *reinterpret_cast<const float *>(xb + tw * 64);
-        const float f = fmaf(sc, fmaf(nz, xz, P), acc);
-        acc = live0 ? f : acc;
-      } else {
-        const float p0 = *reinterpret_cast<const float *>(pb + tw * 2048);
-        const float p1 = *reinterpret_cast<const float *>(pb + tw * 2048 + 1024);
-        const float f0 = fmaf(s.x, p0, acc);
-        const float a0 = live0 ? f0 : acc;
-        const float f1 = fmaf(s.y, p1, a0);
-        acc = live1 ? f1 : a0;
-      }
-    }
+    };
+    if (!AFF && (jf + 1) * kWaves <= KT - (half_tail ? 1 : 0))
+      body(std::true_type{});
+    else
+      body(std::false_type{});
   };
 
   for (int j = 0; j < NW; ++j) {
