@@ -358,13 +358,12 @@ def main():
     import numpy as np
     import torch
 
-    import oracle
     from bit_weight_only_amd import nf4
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     nf4.lib()
-    cb, _ = oracle.codebook()
+    cb = nf4.nf4_codebook()  # the library's default table (host computation)
     s = torch.cuda.Stream()
     if args.pmc_pass:
         pmc_pass(torch, nf4, cb, args.seed, s)

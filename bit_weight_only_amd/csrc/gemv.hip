@@ -207,13 +207,17 @@ __device__ void finish(float (&bv)[M], int (&bn)[M], int b, int P, uint32_t *cou
   if (threadIdx.x < M) {
     __hip_atomic_store(cand + (size_t)b * M + threadIdx.x, pack(v, n), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-    // the candidate is stored device-wide before the arrival is counted
+    // the candidate's store has completed before the arrival is counted
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
+  // Release/acquire through the arrival counter: the barrier orders the
+  // candidates' agent-scope stores before the counting read-modify-write,
+  // which is acquire-release at agent scope, and the barrier after it orders
+  // that acquire before the last workgroup's loads of the candidates.
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t old =
-        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     *flag = old == (uint32_t)(P - 1);
   }
   __syncthreads();

@@ -75,6 +75,10 @@ int split_codebook(const float *cb, nf4::CodeTerms &ct) {
   return nterm;
 }
 
+// bfloat16 activations as their bit patterns (hip_bfloat16 is a 2-byte
+// standard-layout wrapper of them).
+const uint16_t *bf16_bits(const hip_bfloat16 *x) { return reinterpret_cast<const uint16_t *>(x); }
+
 nf4_status from_hip(hipError_t e) { return e == hipSuccess ? NF4_OK : NF4_ERR_HIP; }
 
 // Shapes of the asymmetric int4 format: one group of 128 k per tile row.
@@ -122,6 +126,52 @@ const char *nf4_status_string(nf4_status status) {
     case NF4_ERR_HIP: return "NF4_ERR_HIP: the HIP runtime rejected a launch";
   }
   return "NF4 unknown status";
+}
+
+namespace {
+// Standard normal CDF through the complementary error function of libm.
+double phi_cdf(double z) { return 0.5 * erfc(-z / sqrt(2.0)); }
+
+// Inverse standard normal CDF for p in (1/2, 1): Newton's method on
+// Phi(z) - p from z = 0.  Phi is increasing and concave on z > 0, so every
+// tangent step lands at or below the root and the iterates rise to it
+// monotonically (quadratically near it); stop when a step no longer moves z.
+double phi_inv_upper(double p) {
+  const double inv_sqrt_2pi = 0.39894228040143267794;
+  double z = 0.0;
+  for (int it = 0; it < 200; ++it) {
+    const double step = (p - phi_cdf(z)) / (inv_sqrt_2pi * exp(-0.5 * z * z));
+    const double zn = z + step;
+    if (!(zn > z)) break;
+    z = zn;
+  }
+  return z;
+}
+
+// Nearest bfloat16 (8 significant bits, ties to even) of a finite double in
+// the normal range, as a float: v = q * 2^(e - 8) rounded to an integer q.
+float round_to_bf16(double v) {
+  if (v == 0.0) return 0.0f;
+  int e = 0;
+  frexp(v, &e);  // |v| = f 2^e, f in [1/2, 1)
+  const double scaled = ldexp(v, 8 - e);
+  return (float)ldexp(nearbyint(scaled), e - 8);
+}
+}  // namespace
+
+nf4_status nf4_codebook(double delta, float codebook[16]) {
+  if (!codebook) return NF4_ERR_NULL;
+  if (!(delta > 0.75 && delta <= 0.9999)) return NF4_ERR_CODEBOOK;
+  const double d = phi_inv_upper(delta);
+  double v[16];
+  v[7] = 0.0;
+  for (int j = 1; j <= 7; ++j) v[7 - j] = -phi_inv_upper(0.5 + (delta - 0.5) * j / 7.0) / d;
+  for (int j = 1; j <= 8; ++j) v[7 + j] = phi_inv_upper(0.5 + (delta - 0.5) * j / 8.0) / d;
+  // the end points are exactly -1 and +1 (each level j = 7 or 8 is Phi^-1(delta) / d)
+  v[0] = -1.0;
+  v[15] = 1.0;
+  for (int i = 0; i < 16; ++i) codebook[i] = round_to_bf16(v[i]);
+  return NF4_OK;
 }
 
 size_t nf4_qweight_bytes(int64_t N, int64_t K) {
@@ -192,9 +242,10 @@ nf4_status nf4_unpack(const uint8_t *qweight, const float *absmax, int64_t N, in
   return from_hip(nf4::launch_unpack(qweight, absmax, N, K, codes, scales, stream));
 }
 
-nf4_status nf4_gemv(const uint16_t *x, int64_t M, const uint8_t *qweight, const float *absmax,
+nf4_status nf4_gemv(const hip_bfloat16 *xb, int64_t M, const uint8_t *qweight, const float *absmax,
                     const float codebook[16], int64_t N, int64_t K, float *y, void *workspace,
                     size_t ws_bytes, hipStream_t stream) {
+  const uint16_t *x = bf16_bits(xb);
   nf4_status st = check_linear_args(x, M, qweight, absmax, codebook, N, K, y, kMaxGemvM);
   if (st != NF4_OK) return st;
   const size_t need = nf4::gemv_workspace_bytes(M, N, K);
@@ -208,11 +259,12 @@ nf4_status nf4_gemv(const uint16_t *x, int64_t M, const uint8_t *qweight, const 
       nf4::launch_gemv(x, (int)M, qweight, absmax, ct, nterm, N, K, y, workspace, stream));
 }
 
-nf4_status nf4_gemv_prefetch(const uint16_t *x, int64_t M, const uint8_t *qweight,
+nf4_status nf4_gemv_prefetch(const hip_bfloat16 *xb, int64_t M, const uint8_t *qweight,
                              const float *absmax, const float codebook[16], int64_t N, int64_t K,
                              float *y, void *workspace, size_t ws_bytes,
                              const uint8_t *next_qweight, const float *next_absmax,
                              int64_t next_N, int64_t next_K, hipStream_t stream) {
+  const uint16_t *x = bf16_bits(xb);
   nf4_status st = check_linear_args(x, M, qweight, absmax, codebook, N, K, y, kMaxGemvM);
   if (st != NF4_OK) return st;
   nf4::NextMatrix next;
@@ -241,10 +293,11 @@ size_t nf4_gemv_argmax_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return nf4::gemv_argmax_workspace_bytes(M, N, K);
 }
 
-nf4_status nf4_gemv_argmax(const uint16_t *x, int64_t M, const uint8_t *qweight,
+nf4_status nf4_gemv_argmax(const hip_bfloat16 *xb, int64_t M, const uint8_t *qweight,
                            const float *absmax, const float codebook[16], int64_t N, int64_t K,
                            float *y, int32_t *index, void *workspace, size_t ws_bytes,
                            hipStream_t stream) {
+  const uint16_t *x = bf16_bits(xb);
   nf4_status st = check_linear_args(x, M, qweight, absmax, codebook, N, K, y, kMaxGemvM);
   if (st != NF4_OK) return st;
   if (!index || !workspace) return NF4_ERR_NULL;
@@ -257,9 +310,10 @@ nf4_status nf4_gemv_argmax(const uint16_t *x, int64_t M, const uint8_t *qweight,
                                           workspace, stream));
 }
 
-nf4_status nf4_gemm(const uint16_t *x, int64_t M, const uint8_t *qweight, const float *absmax,
+nf4_status nf4_gemm(const hip_bfloat16 *xb, int64_t M, const uint8_t *qweight, const float *absmax,
                     const float codebook[16], int64_t N, int64_t K, float *y, void *workspace,
                     size_t ws_bytes, hipStream_t stream) {
+  const uint16_t *x = bf16_bits(xb);
   nf4_status st = check_linear_args(x, M, qweight, absmax, codebook, N, K, y, kMaxGemmM);
   if (st != NF4_OK) return st;
   const size_t need = nf4::gemm_workspace_bytes(M, N, K);
@@ -324,8 +378,10 @@ nf4_status nf4_awq_dequant(const uint8_t *qweight, const uint32_t *params, int64
   return from_hip(nf4::launch_awq_dequant(qweight, params, N, K, W_out, stream));
 }
 
-nf4_status nf4_gather_columns(const uint16_t *x, int64_t M, int64_t K, const int32_t *perm,
-                              uint16_t *x_out, hipStream_t stream) {
+nf4_status nf4_gather_columns(const hip_bfloat16 *xb, int64_t M, int64_t K, const int32_t *perm,
+                              hip_bfloat16 *x_out_bf16, hipStream_t stream) {
+  const uint16_t *x = bf16_bits(xb);
+  uint16_t *x_out = reinterpret_cast<uint16_t *>(x_out_bf16);
   if (!x || !perm || !x_out) return NF4_ERR_NULL;
   if (M < 1 || M > kMaxGemmM || K < 8 || K % 8 != 0 || K > kMaxDim || M * K > kMaxElems)
     return NF4_ERR_SHAPE;
@@ -354,9 +410,10 @@ nf4_status check_awq_workspace(int64_t M, int64_t N, int64_t K, const void *ws, 
 
 extern "C" {
 
-nf4_status nf4_awq_gemv(const uint16_t *x, int64_t M, const uint8_t *qweight,
+nf4_status nf4_awq_gemv(const hip_bfloat16 *xb, int64_t M, const uint8_t *qweight,
                         const uint32_t *params, int64_t N, int64_t K, float *y, void *workspace,
                         size_t ws_bytes, hipStream_t stream) {
+  const uint16_t *x = bf16_bits(xb);
   nf4_status st = check_awq_linear(x, M, qweight, params, N, K, y, kMaxGemvM);
   if (st != NF4_OK) return st;
   if (nf4::awq_gemv_fast_eligible(M, N, K))
@@ -367,11 +424,12 @@ nf4_status nf4_awq_gemv(const uint16_t *x, int64_t M, const uint8_t *qweight,
   return from_hip(nf4::launch_awq_gemm(x, M, qweight, params, N, K, y, workspace, stream));
 }
 
-nf4_status nf4_awq_gemv_prefetch(const uint16_t *x, int64_t M, const uint8_t *qweight,
+nf4_status nf4_awq_gemv_prefetch(const hip_bfloat16 *xb, int64_t M, const uint8_t *qweight,
                                  const uint32_t *params, int64_t N, int64_t K, float *y,
                                  void *workspace, size_t ws_bytes, const uint8_t *next_qweight,
                                  const uint32_t *next_params, int64_t next_N, int64_t next_K,
                                  hipStream_t stream) {
+  const uint16_t *x = bf16_bits(xb);
   nf4_status st = check_awq_linear(x, M, qweight, params, N, K, y, kMaxGemvM);
   if (st != NF4_OK) return st;
   nf4::NextMatrix next;
@@ -392,9 +450,10 @@ nf4_status nf4_awq_gemv_prefetch(const uint16_t *x, int64_t M, const uint8_t *qw
   return from_hip(nf4::launch_awq_gemm(x, M, qweight, params, N, K, y, workspace, stream));
 }
 
-nf4_status nf4_awq_gemm(const uint16_t *x, int64_t M, const uint8_t *qweight,
+nf4_status nf4_awq_gemm(const hip_bfloat16 *xb, int64_t M, const uint8_t *qweight,
                         const uint32_t *params, int64_t N, int64_t K, float *y, void *workspace,
                         size_t ws_bytes, hipStream_t stream) {
+  const uint16_t *x = bf16_bits(xb);
   nf4_status st = check_awq_linear(x, M, qweight, params, N, K, y, kMaxGemmM);
   if (st != NF4_OK) return st;
   st = check_awq_workspace(M, N, K, workspace, ws_bytes);

@@ -128,10 +128,11 @@ __device__ inline uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t
 // straight into LDS: 16 bytes per active lane land at m0 + 16 * lane.
 // Issued from inline assembly, so the compiler neither waits for it nor
 // knows what it writes: every use is ordered by an explicit vmcnt wait and a
-// barrier.
+// barrier.  m0 is an input operand of the statement ("{m0}"): the compiler
+// sets it and knows that it holds the destination, so no value of its own
+// is kept in m0 across the copy.
 __device__ inline void copy16_to_lds(uint32_t m0, const void *base, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(base)
-               : "memory");
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(m0) : "memory");
 }
 
 // Sum of the 8 bf16 values of a 16-byte chunk, in k order.

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libnf4.so")
 NF4_OK, NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_CODEBOOK, NF4_ERR_WORKSPACE, \
     NF4_ERR_HIP = range(7)
 
-EXPORTS = ("nf4_status_string", "nf4_qweight_bytes", "nf4_absmax_bytes", "nf4_workspace_bytes",
+EXPORTS = ("nf4_status_string", "nf4_codebook", "nf4_qweight_bytes", "nf4_absmax_bytes", "nf4_workspace_bytes",
            "nf4_pack", "nf4_dequant", "nf4_repack", "nf4_unpack", "nf4_gemv", "nf4_gemm",
            "nf4_gemv_argmax_workspace_bytes", "nf4_gemv_argmax", "nf4_gemv_prefetch",
            "nf4_awq_params_bytes", "nf4_awq_workspace_bytes", "nf4_awq_pack", "nf4_awq_repack",
@@ -43,6 +43,8 @@ def lib() -> ctypes.CDLL:
         fp = ctypes.POINTER(ctypes.c_float)
         L.nf4_status_string.restype = ctypes.c_char_p
         L.nf4_status_string.argtypes = [st]
+        L.nf4_codebook.restype = st
+        L.nf4_codebook.argtypes = [ctypes.c_double, fp]
         for f in (L.nf4_qweight_bytes, L.nf4_absmax_bytes):
             f.restype = sz
             f.argtypes = [i64, i64]
@@ -119,6 +121,17 @@ def _check(status: int, where: str) -> None:
 
 def nf4_status_string(status: int) -> str:
     return lib().nf4_status_string(int(status)).decode()
+
+
+DEFAULT_DELTA = 0.9677083  # tail probability of the default codebook
+
+
+def nf4_codebook(delta: float = DEFAULT_DELTA) -> np.ndarray:
+    """The library's default 16-entry codebook (host computation): normal
+    quantiles normalised to [-1, 1] with an exact zero, each a bfloat16 value."""
+    out = (ctypes.c_float * 16)()
+    _check(lib().nf4_codebook(float(delta), out), "nf4_codebook")
+    return np.array(out[:], dtype=np.float32)
 
 
 def nf4_qweight_bytes(N: int, K: int) -> int:

@@ -30,7 +30,7 @@
  *  - Shapes: N % 16 == 0, N >= 16; K % 64 == 0, K >= 64; 1 <= M <= 2^23.
  *    N, K <= 2^30 and N*K <= 2^40.
  *  - Device pointers must be 16-byte aligned (else NF4_ERR_ALIGN).
- *  - x is bfloat16 bit patterns, [M][K] row-major.  y is fp32 [M][N]
+ *  - x is bfloat16 (hip_bfloat16: the 2-byte bit pattern), [M][K] row-major.  y is fp32 [M][N]
  *    row-major, overwritten (never accumulated), no bias.
  *
  * Device weight layout (what nf4_pack writes and the GEMV/GEMM read)
@@ -52,6 +52,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <hip/hip_bfloat16.h>
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
@@ -86,12 +87,31 @@ size_t nf4_absmax_bytes(int64_t N, int64_t K);
  * through the workspace: one 4-byte arrival counter per output tile of
  * 128 x 128 or 128 x 256, then every part's sums of every tile (about
  * 4 P M N bytes in all).  0 otherwise, and the workspace arguments may then
- * be NULL with 0 bytes.  A workspace must be zero-filled once at
- * allocation; every call leaves its counters at zero again, and calls
- * sharing one must be ordered (one stream). */
+ * be NULL with 0 bytes.  The workspace needs no initial contents: each call
+ * that uses it first clears its counters with a small kernel on its stream.
+ * Calls sharing one workspace must be ordered (one stream). */
 size_t nf4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
-/* Quantize fp32 W[N][K] (row-major) into the device layout.  Per block of
+/* The default 16-entry codebook, computed on the host (no device work):
+ * normal quantiles normalised to [-1, 1] with an exact zero (vibevoice.c
+ * README, "Int8 activations: W8A8 and W4A8": NF4's codes index a
+ * non-uniform table; "Quantization" > "Weights": NF4 blocks of 64 with
+ * absmax scales).  With Phi the standard normal CDF and d = Phi^-1(delta):
+ * 8 positive levels Phi^-1(1/2 + (delta - 1/2) j / 8) / d, j = 1..8, 7
+ * negative levels -Phi^-1(1/2 + (delta - 1/2) j / 7) / d, j = 1..7, and +0.0,
+ * sorted; each value rounded to the nearest bfloat16 (ties to even) and
+ * stored as fp32, so c[0] = -1, c[7] = +0.0, c[15] = +1 and every product of
+ * a bf16 activation with a code is exact in fp32.  delta = 0.9677083 gives
+ * the table the rest of the library is measured with; any delta in
+ * (0.75, 0.9999] is accepted (else NF4_ERR_CODEBOOK, nothing written).
+ * codebook: host array of 16 floats, written. */
+nf4_status nf4_codebook(double delta, float codebook[16]);
+
+/* Quantize fp32 W[N][K] (row-major) into the device layout (vibevoice.c
+ * README, "Quantization" > "Weights": blocks of 64 with an absmax scale
+ * each, quantized deterministically once per projection at load, before
+ * placement; the nearest-code rule and its tie-break are this library's
+ * reading, which the page leaves open).  Per block of
  * 64: s = max |w| (exact); s == 0 gives every weight the index of the +0.0
  * code; otherwise idx = #{ i < 15 : (double)w > m_i * (double)s } with
  * m_i = ((double)c_i + (double)c_{i+1}) / 2, i.e. the nearest code with an
@@ -102,28 +122,39 @@ size_t nf4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 nf4_status nf4_pack(const float *W, int64_t N, int64_t K, const float codebook[16],
                     uint8_t *qweight, float *absmax, hipStream_t stream);
 
-/* Debug path: W_out[n][k] = fl32(c[idx] * s), one binary32 multiply per
- * weight, fp32 [N][K] row-major.  Any finite codebook. */
+/* Debug path (vibevoice.c README, "Quantization" > "Weights": a weight reads
+ * back as its code's table value times its block's absmax):
+ * W_out[n][k] = fl32(c[idx] * s), one binary32 multiply per weight, fp32
+ * [N][K] row-major.  Any finite codebook. */
 nf4_status nf4_dequant(const uint8_t *qweight, const float *absmax, const float codebook[16],
                        int64_t N, int64_t K, float *W_out, hipStream_t stream);
 
 /* Layout conversion from the canonical format (codes[N][K/2] bytes, byte j
  * = idx[2j] | idx[2j+1] << 4; scales[N][K/64] fp32 row-major) into the
- * device layout; for weights quantized elsewhere. */
+ * device layout; for weights quantized elsewhere (vibevoice.c README,
+ * "Quantization" > "Weights": checkpoints are repacked once at load into
+ * one row-major layout whose 16-byte runs are permuted for the kernels). */
 nf4_status nf4_repack(const uint8_t *codes, const float *scales, int64_t N, int64_t K,
                       uint8_t *qweight, float *absmax, hipStream_t stream);
 
-/* Inverse of nf4_repack: device layout back to the canonical format. */
+/* Inverse of nf4_repack (same passage): device layout back to the
+ * canonical format. */
 nf4_status nf4_unpack(const uint8_t *qweight, const float *absmax, int64_t N, int64_t K,
                       uint8_t *codes, float *scales, hipStream_t stream);
 
-/* Decode GEMV, 1 <= M <= 8: y[m][n] = sum_b s[n][b] * sum_{k in b} x[m][k] *
- * c[idx[n][k]], fp32 accumulation.  Codebook: any finite values whose fp32
+/* Decode GEMV, 1 <= M <= 8 (vibevoice.c README, "The kernels that matter":
+ * single-token decode reads every weight once and is bound by memory
+ * bandwidth, with the dequantization fused into the multiply;
+ * "Quantization" > "Weights", decode-GEMV bullet: 128-bit loads, same-input
+ * projections in one launch):
+ * y[m][n] = sum_b s[n][b] * sum_{k in b} x[m][k] * c[idx[n][k]], fp32
+ * accumulation.  x: bfloat16 [M][K] row-major (hip_bfloat16 is the 2-byte
+ * bit pattern).  y: fp32 [M][N] row-major, overwritten.  Codebook: any finite values whose fp32
  * entries are sums of at most three bfloat16 values (every normal fp32 is);
  * else NF4_ERR_CODEBOOK.  workspace: at least nf4_workspace_bytes(M, N, K)
- * bytes, zero-filled once at allocation.  Results are bitwise reproducible
- * run to run for a given shape and device. */
-nf4_status nf4_gemv(const uint16_t *x, int64_t M, const uint8_t *qweight, const float *absmax,
+ * bytes (any contents).  Results are bitwise reproducible run to run for a
+ * given shape and device. */
+nf4_status nf4_gemv(const hip_bfloat16 *x, int64_t M, const uint8_t *qweight, const float *absmax,
                     const float codebook[16], int64_t N, int64_t K, float *y, void *workspace,
                     size_t ws_bytes, hipStream_t stream);
 
@@ -142,7 +173,7 @@ nf4_status nf4_gemv(const uint16_t *x, int64_t M, const uint8_t *qweight, const 
  * 16-byte aligned device buffers of an existing packed matrix whose shape
  * nf4_gemv accepts (else NF4_ERR_NULL, NF4_ERR_ALIGN, NF4_ERR_SHAPE); the
  * next matrix is only read.  Other arguments and errors as nf4_gemv. */
-nf4_status nf4_gemv_prefetch(const uint16_t *x, int64_t M, const uint8_t *qweight,
+nf4_status nf4_gemv_prefetch(const hip_bfloat16 *x, int64_t M, const uint8_t *qweight,
                              const float *absmax, const float codebook[16], int64_t N, int64_t K,
                              float *y, void *workspace, size_t ws_bytes,
                              const uint8_t *next_qweight, const float *next_absmax,
@@ -164,12 +195,16 @@ size_t nf4_gemv_argmax_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * allocation; every call leaves its counter at zero, and calls sharing one
  * workspace must be ordered.  Errors as nf4_gemv, plus NF4_ERR_NULL for a
  * NULL index or workspace. */
-nf4_status nf4_gemv_argmax(const uint16_t *x, int64_t M, const uint8_t *qweight,
+nf4_status nf4_gemv_argmax(const hip_bfloat16 *x, int64_t M, const uint8_t *qweight,
                            const float *absmax, const float codebook[16], int64_t N, int64_t K,
                            float *y, int32_t *index, void *workspace, size_t ws_bytes,
                            hipStream_t stream);
 
-/* Prefill GEMM, any M >= 1: same result definition as nf4_gemv, computed on
+/* Prefill GEMM, any M >= 1 (vibevoice.c README, "Quantization" > "Weights",
+ * M > 1 bullet: a matrix-core GEMM that keeps the weights 4-bit into on-chip
+ * memory, expands them next to the matrix instruction, and splits K when the
+ * grid would not cover the device, its partials in the caller's scratch):
+ * same result definition as nf4_gemv, computed on
  * bf16 matrix cores with the codes as exact bf16 operands and the fp32
  * scales applied outside the matrix product once per 64-block.  The sum
  * over K runs in P parts, device tiles [b_j, b_j+1) with
@@ -178,12 +213,12 @@ nf4_status nf4_gemv_argmax(const uint16_t *x, int64_t M, const uint8_t *qweight,
  * P = 2 from K = 8192 on, else 1; then, when T P < 128 for
  * T = 8 ceil(N/128) (the 128 x 128 output tiles of a 1024-row batch),
  * P = max(P, min(256 / T, KT / 4)) (integer divisions).  workspace: at
- * least nf4_workspace_bytes(M, N, K) bytes, zero-filled once (may be NULL
- * when that is 0), else NF4_ERR_NULL or NF4_ERR_WORKSPACE.  Results are
+ * least nf4_workspace_bytes(M, N, K) bytes, any contents (may be NULL when
+ * that is 0), else NF4_ERR_NULL or NF4_ERR_WORKSPACE.  Results are
  * bitwise reproducible run to run, and a row of y does not depend on the
  * other rows of x; column slices of a matrix fused along N equal the
  * separate matrices' outputs bit for bit when both have the same P. */
-nf4_status nf4_gemm(const uint16_t *x, int64_t M, const uint8_t *qweight, const float *absmax,
+nf4_status nf4_gemm(const hip_bfloat16 *x, int64_t M, const uint8_t *qweight, const float *absmax,
                     const float codebook[16], int64_t N, int64_t K, float *y, void *workspace,
                     size_t ws_bytes, hipStream_t stream);
 
@@ -257,8 +292,8 @@ nf4_status nf4_awq_dequant(const uint8_t *qweight, const uint32_t *params, int64
  * row-major).  perm: device int32[K]; values outside [0, K) are clamped into
  * it.  1 <= M <= 2^23, K % 8 == 0 (else NF4_ERR_SHAPE); x, perm and x_out
  * 16-byte aligned device buffers; x_out must not overlap x. */
-nf4_status nf4_gather_columns(const uint16_t *x, int64_t M, int64_t K, const int32_t *perm,
-                              uint16_t *x_out, hipStream_t stream);
+nf4_status nf4_gather_columns(const hip_bfloat16 *x, int64_t M, int64_t K, const int32_t *perm,
+                              hip_bfloat16 *x_out, hipStream_t stream);
 
 /* Decode GEMV of the int4 format, 1 <= M <= 8:
  * y[m][n] = sum_t s[n][t] * sum_{k in group t} x[m][k] * (q[n][k] - z[n][t]),
@@ -269,7 +304,7 @@ nf4_status nf4_gather_columns(const uint16_t *x, int64_t M, int64_t K, const int
  * 160 KB of LDS, about M * K <= 78000); otherwise the call runs the GEMM of
  * nf4_awq_gemm and needs nf4_awq_workspace_bytes(M, N, K) bytes (else
  * NF4_ERR_NULL or NF4_ERR_WORKSPACE).  Bitwise reproducible run to run. */
-nf4_status nf4_awq_gemv(const uint16_t *x, int64_t M, const uint8_t *qweight,
+nf4_status nf4_awq_gemv(const hip_bfloat16 *x, int64_t M, const uint8_t *qweight,
                         const uint32_t *params, int64_t N, int64_t K, float *y, void *workspace,
                         size_t ws_bytes, hipStream_t stream);
 
@@ -281,7 +316,7 @@ nf4_status nf4_awq_gemv(const uint16_t *x, int64_t M, const uint8_t *qweight,
  * both 16-byte aligned, and the next shape one that nf4_awq_gemv accepts
  * (else NF4_ERR_NULL, NF4_ERR_ALIGN, NF4_ERR_SHAPE).  The hint is ignored
  * when this call runs the GEMM path. */
-nf4_status nf4_awq_gemv_prefetch(const uint16_t *x, int64_t M, const uint8_t *qweight,
+nf4_status nf4_awq_gemv_prefetch(const hip_bfloat16 *x, int64_t M, const uint8_t *qweight,
                                  const uint32_t *params, int64_t N, int64_t K, float *y,
                                  void *workspace, size_t ws_bytes, const uint8_t *next_qweight,
                                  const uint32_t *next_params, int64_t next_N, int64_t next_K,
@@ -293,7 +328,7 @@ nf4_status nf4_awq_gemv_prefetch(const uint16_t *x, int64_t M, const uint8_t *qw
  * bytes, required).  K is summed in the parts nf4_gemm uses.  Rows of y do not depend on the other rows of x.  Shapes
  * whose byte offsets into x, qweight or the workspace reach 2^32 give
  * NF4_ERR_SHAPE.  Bitwise reproducible run to run. */
-nf4_status nf4_awq_gemm(const uint16_t *x, int64_t M, const uint8_t *qweight,
+nf4_status nf4_awq_gemm(const hip_bfloat16 *x, int64_t M, const uint8_t *qweight,
                         const uint32_t *params, int64_t N, int64_t K, float *y, void *workspace,
                         size_t ws_bytes, hipStream_t stream);
 

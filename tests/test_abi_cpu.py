@@ -366,3 +366,42 @@ def test_awq_prefetch_validation():
         bad = list(ok)
         bad[11], bad[12] = nN, nK
         assert f(*bad) == nf4.NF4_ERR_SHAPE, (nN, nK)
+
+
+# ------------------------------------------------------- the default codebook
+def golden_codebook():
+    """The 16 hex floats of tests/golden/nf4_codebook.txt (written from the oracle)."""
+    path = os.path.join(ROOT, "tests", "golden", "nf4_codebook.txt")
+    vals = [float.fromhex(ln.split("#")[0].strip()) for ln in open(path)
+            if ln.strip() and not ln.startswith("#")]
+    return np.array(vals, np.float32)
+
+
+def test_library_codebook_equals_the_golden_table():
+    """nf4_codebook (host code of the library: Newton's method on erfc, its own
+    bf16 rounding) gives the fixture's table bit for bit, and the oracle's."""
+    import oracle
+    cb = nf4.nf4_codebook()
+    gold = golden_codebook()
+    assert np.array_equal(cb.view(np.uint32), gold.view(np.uint32))
+    assert np.array_equal(cb.view(np.uint32), oracle.codebook()[0].view(np.uint32))
+
+
+@pytest.mark.parametrize("delta", [0.8, 0.9, 0.95, 0.99, 0.9999])
+def test_library_codebook_invariants_and_oracle_agreement(delta):
+    """Other tail probabilities: 16 strictly increasing bf16 values, -1, +0.0
+    and +1 at indices 0, 7 and 15, equal to the oracle's construction."""
+    import oracle
+    cb = nf4.nf4_codebook(delta)
+    assert np.all(np.diff(cb) > 0)
+    assert cb[0] == -1.0 and cb[15] == 1.0
+    assert cb[7] == 0.0 and not np.signbit(cb[7])
+    assert np.all((cb.view(np.uint32) & 0xFFFF) == 0)  # bf16-exact
+    assert np.array_equal(cb.view(np.uint32), oracle.codebook(delta)[0].view(np.uint32))
+
+
+@pytest.mark.parametrize("delta", [0.5, 0.75, 1.0, float("nan"), -1.0])
+def test_library_codebook_rejects_bad_delta(delta):
+    with pytest.raises(nf4.NF4Error) as e:
+        nf4.nf4_codebook(delta)
+    assert e.value.status == nf4.NF4_ERR_CODEBOOK
