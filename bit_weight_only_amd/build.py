@@ -24,6 +24,10 @@ ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-instruction results in VGPRs: the compiler otherwise picks the
+    # AGPR form for kernels that may use more than 256 registers, and every
+    # product read by a vector instruction then costs v_accvgpr_read moves
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"),
 ]
 

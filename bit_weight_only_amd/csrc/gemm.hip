@@ -34,6 +34,7 @@
 
 #include "nf4_internal.h"
 
+
 namespace nf4 {
 namespace {
 
@@ -533,12 +534,16 @@ __global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
           __hip_atomic_store(mine + ((mm * 2 + nn) * 2 + i2) * L::kThreads, v, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
         }
-    // the sums are stored device-wide before the arrival is counted
+    // Release/acquire through the arrival counter: every wave's stores of
+    // its sums have completed (agent-scope atomic stores, waited for), the
+    // barrier orders them before the counting read-modify-write, which is
+    // acquire-release at agent scope, and the barrier after it orders that
+    // acquire before every wave's loads of the other parts.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // also: no wave reads LDS any more
     int *flag = reinterpret_cast<int *>(lds);
     if (tid == 0)
-      *flag = (int)__hip_atomic_fetch_add(cnt + tile_id, 1u, __ATOMIC_RELAXED,
+      *flag = (int)__hip_atomic_fetch_add(cnt + tile_id, 1u, __ATOMIC_ACQ_REL,
                                           __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (*flag != np - 1) return;
@@ -587,6 +592,341 @@ __global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
       for (int i = 0; i < 4; ++i) {
         const int64_t row = m0 + wm * 16 * MB + mm * 16 + 4 * h + i;
         if (row < M) y[row * N + col] = acc[mm][nn][i];
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined tiled kernel (codebook format, 128 x 256 outputs per
+// workgroup): WAVES waves, each owning all 128 rows and 16 / WAVES row
+// groups (8 waves: 128 x 32 each, two per SIMD in one workgroup per CU;
+// 4 waves: 128 x 64 each, one per SIMD, two workgroups per CU).
+//
+// What shaped it (measured on MI355X, LDS read rates per CU):
+//  - A fragments: a 16-byte read per lane is conflict free when the four
+//    16-byte chunks of row r sit at chunk ^ ((r >> 1) & 3); the swizzle
+//    (r >> 2) & 3 halves the rate.
+//  - Lookups of code bytes: 4-byte reads of random entries cost about eight
+//    cycles per wave whatever the table's replication (the LDS serves a
+//    limited number of distinct 16-byte lines per cycle), so the pair table
+//    is one copy of 256 entries (1 KB) at byte << 2, which leaves LDS for
+//    two workgroups per CU.
+//  - Two workgroups per CU (4 waves each) are not held in step by each
+//    other's barriers; on matrices with enough output tiles this is 8-10 %
+//    faster than one workgroup of 8 waves, on few tiles slower.
+//
+// Pipeline.  x sits in two LDS stages of one 64-k step (16 KB, the two
+// 32-k halves each laid out [row][32 bf16] in 16-row blocks of 1 KB).  Step
+// t opens with the workgroup's barrier: every wave has landed its copies of
+// x(t) (waited for with vmcnt) and no wave reads stage (t - 1) % 2 any
+// more, so right after it each wave copies its share of x(t + 1) into that
+// stage.  Code words and scales are wave-private: each wave copies the
+// device tiles of its own row groups into a two-slot ring (tile T + 1 at
+// step 2T - 1) and only waits for its own copies.  A fragments are read
+// PD blocks ahead within the step; the B fragments (table lookups) and
+// block scales of step t + 1 are formed during step t.  Items (16-row
+// block, row group) run in order, each its two products and then the fold
+// of the item two before it, whose products have finished: the fold's
+// vector FMAs run beside the matrix instructions and only three products
+// are live.
+// Every output gets the operations of the other kernels: per 64-block
+// P = MFMA(kk=0, zero), MFMA(kk=1, P), acc = fmaf(s, P, acc), in K order.
+// K in np parts (SPLIT) as gemm_tile_kernel.
+namespace wide {
+constexpr int kBM = 128, kMB = 8, kRG = 16;
+constexpr int kXStage = 2 * tile::kAHalf;       // 16 KB: both halves of a step
+constexpr int kStages = 2;
+constexpr int kTable = 256 * 4;                 // pairs of bf16 codes by code byte
+constexpr int kOffX = kTable;
+constexpr int kOffC = kOffX + kStages * kXStage;
+constexpr int kOffS = kOffC + kRG * 2 * kTileBytes;
+constexpr int kBytes = kOffS + kRG * 2 * kTileScales * 4;  // 69 KB
+constexpr int kPrefetch = 3;                    // A blocks read ahead
+template <int WAVES>
+struct Geo {
+  static constexpr int kThreads = 64 * WAVES;
+  static constexpr int kRGW = kRG / WAVES;               // row groups per wave
+  static constexpr int kXCopies = 16 / WAVES;            // 1 KB copies of x per wave and step
+  static constexpr int kTileCopies = 2 * kRGW;           // code + scale copies per wave and tile
+  static constexpr int kItems = kMB * kRGW;              // items per step
+  static constexpr int kWordItem = 2 * kRGW;             // code words of step t + 1
+  static constexpr int kLookItem = 3 * kRGW + 4;         // first B lookup of step t + 1
+  static_assert(kMB % (kPrefetch + 1) == 0, "A ring slots repeat per step");
+  static_assert(kLookItem + 2 * kRGW <= kItems, "lookups within the step");
+};
+}  // namespace wide
+
+template <int WAVES, bool SPLIT>
+__global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void gemm_wide_kernel(
+    const uint16_t *__restrict__ x, int64_t M, const uint8_t *__restrict__ qw,
+    const float *__restrict__ am, CodeTerms ct, int64_t N, int64_t K, int64_t KT,
+    float *__restrict__ y, int ntn, int ntm, int np_arg, uint32_t *__restrict__ cnt,
+    uint64_t *__restrict__ part) {
+  namespace W = wide;
+  using Gm = W::Geo<WAVES>;
+  constexpr int RGW = Gm::kRGW, PD = W::kPrefetch;
+  const int np = SPLIT ? np_arg : 1;
+  // the only static LDS array, so the table sits at LDS address 0
+  __shared__ __attribute__((aligned(16))) char lds[W::kBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, h = lane >> 4;
+  // tile order for the 8 XCDs as in gemm_tile_kernel
+  const int xcd = (int)(blockIdx.x & 7), slot = (int)(blockIdx.x >> 3);
+  const int u = (slot / ntm) * 8 + xcd, mt = slot % ntm;
+  if (u >= ntn * np) return;
+  const int nt = u / np, kc = u - nt * np;
+  const int64_t m0 = (int64_t)mt * W::kBM;
+  const int64_t gblk = (int64_t)nt * W::kRG;
+  const int64_t G = N / kTileRows;
+  const int t0 = SPLIT ? part_begin(kc, KT, np) : 0;
+  const int t1 = SPLIT ? part_begin(kc + 1, KT, np) : (int)KT;
+  const int KTp = t1 - t0;
+  const int S = (int)(2 * (int64_t)t1 < K / kBK ? 2 * (int64_t)t1 : K / kBK) - 2 * t0;
+  x += (int64_t)t0 * kTileK;
+  qw += (int64_t)t0 * kTileBytes;
+  am += (int64_t)t0 * kTileScales;
+  const uint32_t base = lds_addr(lds);
+
+  // x copies: copy i (16 per step, 1 KB each) fills rows 16 (i % 8) .. + 15
+  // of half i / 8; wave w issues i = w, w + WAVES, ...  Lane l fills chunk
+  // slot l % 4 of row 16 (i % 8) + l / 4, i.e. logical chunk
+  // (l % 4) ^ ((l >> 3) & 3).  The row block and half go into the scalar
+  // base, the lane's row and chunk into one offset shared by the copies; in
+  // the last, ragged row tile rows past M re-read row M - 1 (never stored),
+  // with offsets from x formed per copy (M K 2 < 2^32).
+  const int cx = (lane & 3) ^ ((lane >> 3) & 3);
+  const uint32_t xl = (uint32_t)(((lane >> 2) * K + cx * 8) * 2);
+  const bool ragged = m0 + W::kBM > M;
+  const uint32_t lane16 = (uint32_t)lane * 16;
+  auto copy_x = [&](int step, int stage) {
+    const int64_t sc = (int64_t)(step < S ? step : S - 1) * kBK;
+#pragma unroll
+    for (int v = 0; v < Gm::kXCopies; ++v) {
+      const int i = wave + v * WAVES, blk = i % 8, half = i / 8;
+      const int64_t r0 = m0 + 16 * blk;
+      const uint32_t dst = base + W::kOffX + stage * W::kXStage + half * tile::kAHalf + blk * 1024;
+      if (!ragged) {
+        copy16_to_lds(dst, x + r0 * K + half * 32 + sc, xl);
+      } else {
+        // offsets from x itself (a block may lie wholly past M)
+        const int64_t R = r0 + (lane >> 2);
+        const uint32_t off = (uint32_t)(((R < M ? R : M - 1) * K + cx * 8) * 2);
+        copy16_to_lds(dst, x + half * 32 + sc, off);
+      }
+    }
+  };
+  // code words and scales of this wave's row groups (past N: the last row
+  // group, never stored), one scalar base per row group
+  auto copy_tile = [&](int T) {
+    const int64_t tc = T < KTp ? T : KTp - 1;
+#pragma unroll
+    for (int q = 0; q < RGW; ++q) {
+      const int64_t rg = gblk + wave * RGW + q;
+      const int64_t g = rg < G ? rg : G - 1;
+      const int dst = (q * 2 + (T & 1));
+      copy16_to_lds(base + W::kOffC + (wave * RGW * 2 + dst) * kTileBytes,
+                    qw + (g * KT + tc) * kTileBytes, lane16);
+      if (lane < kTileScales * 4 / 16)
+        copy16_to_lds(base + W::kOffS + (wave * RGW * 2 + dst) * kTileScales * 4,
+                      am + (g * KT + tc) * kTileScales, lane16);
+    }
+  };
+
+  // table entry e: the bf16 pair of codes e & 15 (low half) and e >> 4
+  for (int e = tid; e < 256; e += Gm::kThreads)
+    reinterpret_cast<uint32_t *>(lds)[e] =
+        (uint32_t)ct.t[0][e & 15] | ((uint32_t)ct.t[0][e >> 4] << 16);
+  copy_x(0, 0);
+  copy_tile(0);
+  copy_tile(1);
+  pipe::wait_copies_and_barrier<0>();
+
+  // A fragment: lane (r, h) holds row r of a 16-row block, bf16 8h .. 8h+7
+  // of the half
+  const char *pa0 = lds + W::kOffX + r * pipe::kHalfRow + ((h ^ ((r >> 1) & 3)) * 16);
+  const char *pc0 = lds + W::kOffC + wave * RGW * 2 * kTileBytes + lane * 16;
+  const char *ps0 = lds + W::kOffS + wave * RGW * 2 * kTileScales * 4 + r * 8;
+
+  // B fragments (both 32-k halves of the wave's column blocks) and block
+  // scales of step t: tile t / 2 in ring slot (t / 2) & 1, quarter 2 (t % 2)
+  // + hf.  Two sets, by the parity of the step they serve.
+  bf16x8 B[2][2][RGW];
+  float sc[2][RGW];
+  uint2 cw[RGW];  // code words of the coming step
+  auto read_words = [&](int t) {
+    const int slt = (t >> 1) & 1, par = t & 1;
+#pragma unroll
+    for (int q = 0; q < RGW; ++q)
+      cw[q] = *reinterpret_cast<const uint2 *>(pc0 + (q * 2 + slt) * kTileBytes + par * 8);
+  };
+  auto read_scales = [&](int t, float (&so)[RGW]) {
+    const int slt = (t >> 1) & 1, par = t & 1;
+#pragma unroll
+    for (int q = 0; q < RGW; ++q)
+      so[q] = *reinterpret_cast<const float *>(ps0 + (q * 2 + slt) * kTileScales * 4 + par * 4);
+  };
+  // fragment f = hf * RGW + q from the code words: byte qq of the code word
+  // (codes 2qq, 2qq + 1) is the table entry of B dword qq
+  auto look = [&](int f, bf16x8 (&Bo)[2][RGW]) {
+    const int hf = f / RGW, q = f % RGW;
+    const uint32_t w = hf ? cw[q].y : cw[q].x;
+    uint32_t bb[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+      bb[qq] = *reinterpret_cast<const uint32_t *>(lds + 4 * ((w >> (8 * qq)) & 0xFFu));
+    Bo[hf][q] = __builtin_bit_cast(bf16x8, make_uint4(bb[0], bb[1], bb[2], bb[3]));
+  };
+  auto read_a = [&](int stage, int mm, bf16x8 &a0, bf16x8 &a1) {
+    const char *p = pa0 + stage * W::kXStage + mm * 1024;
+    a0 = *reinterpret_cast<const bf16x8 *>(p);
+    a1 = *reinterpret_cast<const bf16x8 *>(p + tile::kAHalf);
+  };
+
+  f32x4 acc[W::kMB][RGW];
+#pragma unroll
+  for (int a2 = 0; a2 < W::kMB; ++a2)
+#pragma unroll
+    for (int b2 = 0; b2 < RGW; ++b2) acc[a2][b2] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  // A fragments in flight: block mm is read PD blocks before its products,
+  // into ring slot mm % (PD + 1)
+  bf16x8 A0[PD + 1], A1[PD + 1];
+  read_words(0);
+  read_scales(0, sc[0]);
+#pragma unroll
+  for (int f = 0; f < 2 * RGW; ++f) look(f, B[0]);
+
+  // step t, x in stage st = t % 2; PH = t % 2 fixes the copy wait: the
+  // copies of x(t) that the barrier waits for were followed, when t - 1 was
+  // odd, by the copies of a device tile, which may stay in flight
+  auto step = [&](auto phc, int t) {
+    constexpr int PH = decltype(phc)::value;
+    constexpr int st = PH;
+    constexpr int kLag = 2;
+    f32x4 pr[kLag + 1];
+    auto fold = [&](int item) {
+      const int fm = item / RGW, fq = item % RGW;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[fm][fq][i] = fmaf(sc[PH][fq], pr[item % (kLag + 1)][i], acc[fm][fq][i]);
+      // keeps the fold here: the compiler would otherwise sink it towards the
+      // next use of acc, a step later, with every product of the step live
+      asm volatile("" : "+v"(acc[fm][fq]));
+    };
+#pragma unroll
+    for (int item = 0; item < Gm::kItems; ++item) {
+      const int mm = item / RGW, q = item % RGW;
+      if (item == 0) {
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(PH == 0 ? Gm::kTileCopies : 0)
+                     : "memory");
+        copy_x(t + 1, st ^ 1);
+        if (PH == 1) copy_tile((t >> 1) + 2);
+#pragma unroll
+        for (int i = 0; i < PD; ++i) read_a(st, i, A0[i], A1[i]);
+      }
+      if (item == Gm::kWordItem) {
+        read_words(t + 1);
+        read_scales(t + 1, sc[PH ^ 1]);
+      }
+      if (q == 0 && mm + PD < W::kMB) read_a(st, mm + PD, A0[(mm + PD) % (PD + 1)],
+                                             A1[(mm + PD) % (PD + 1)]);
+      if (item >= Gm::kLookItem && item < Gm::kLookItem + 2 * RGW)
+        look(item - Gm::kLookItem, B[PH ^ 1]);
+      f32x4 &p = pr[item % (kLag + 1)];
+      const int sa = mm % (PD + 1);
+      p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0[sa], B[PH][0][q], zero, 0, 0, 0);
+      p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[sa], B[PH][1][q], p, 0, 0, 0);
+      if (item >= kLag) fold(item - kLag);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int item = Gm::kItems - kLag; item < Gm::kItems; ++item) fold(item);
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  if constexpr (SPLIT) asm volatile("" ::"s"(cnt), "s"(part));
+  int t = 0;
+  for (; t + 1 < S; t += 2) {
+    step(P0{}, t);
+    step(P1{}, t + 1);
+  }
+  if (t < S) step(P0{}, t);
+  // the clamped copies of the last steps must land before the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  if (SPLIT) {
+    // as gemm_tile_kernel: sums stored, arrival counted, the last workgroup
+    // of the output tile adds the parts in part order
+    constexpr int NV = W::kMB * RGW * 2;  // 8-byte pairs of sums per thread
+    const int64_t tile_id = (int64_t)nt * ntm + mt;
+    const int64_t slot_u64 = (int64_t)Gm::kThreads * NV;
+    uint64_t *mine = part + (tile_id * np + kc) * slot_u64 + tid;
+#pragma unroll
+    for (int mm = 0; mm < W::kMB; ++mm)
+#pragma unroll
+      for (int q = 0; q < RGW; ++q)
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2) {
+          const uint64_t v = (uint64_t)__float_as_uint(acc[mm][q][2 * i2]) |
+                             ((uint64_t)__float_as_uint(acc[mm][q][2 * i2 + 1]) << 32);
+          __hip_atomic_store(mine + ((mm * RGW + q) * 2 + i2) * Gm::kThreads, v,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    // Release/acquire through the arrival counter (see gemm_tile_kernel)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // also: no wave reads LDS any more
+    int *flag = reinterpret_cast<int *>(lds);
+    if (tid == 0)
+      *flag = (int)__hip_atomic_fetch_add(cnt + tile_id, 1u, __ATOMIC_ACQ_REL,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (*flag != np - 1) return;
+    f32x4 tot[W::kMB][RGW];
+    for (int j = 0; j < np; ++j) {
+      f32x4 pj[W::kMB][RGW];
+      if (j == kc) {
+#pragma unroll
+        for (int mm = 0; mm < W::kMB; ++mm)
+#pragma unroll
+          for (int q = 0; q < RGW; ++q) pj[mm][q] = acc[mm][q];
+      } else {
+        const uint64_t *src = part + (tile_id * np + j) * slot_u64 + tid;
+#pragma unroll
+        for (int mm = 0; mm < W::kMB; ++mm)
+#pragma unroll
+          for (int q = 0; q < RGW; ++q)
+#pragma unroll
+            for (int i2 = 0; i2 < 2; ++i2) {
+              const uint64_t v = __hip_atomic_load(src + ((mm * RGW + q) * 2 + i2) * Gm::kThreads,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              pj[mm][q][2 * i2] = __uint_as_float((uint32_t)v);
+              pj[mm][q][2 * i2 + 1] = __uint_as_float((uint32_t)(v >> 32));
+            }
+      }
+#pragma unroll
+      for (int mm = 0; mm < W::kMB; ++mm)
+#pragma unroll
+        for (int q = 0; q < RGW; ++q) tot[mm][q] = j ? tot[mm][q] + pj[mm][q] : pj[mm][q];
+    }
+#pragma unroll
+    for (int mm = 0; mm < W::kMB; ++mm)
+#pragma unroll
+      for (int q = 0; q < RGW; ++q) acc[mm][q] = tot[mm][q];
+    if (tid == 0) __hip_atomic_store(cnt + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+#pragma unroll
+  for (int mm = 0; mm < W::kMB; ++mm)
+#pragma unroll
+    for (int q = 0; q < RGW; ++q) {
+      const int64_t g = gblk + wave * RGW + q;
+      if (g >= G) continue;
+      const int64_t col = g * kTileRows + r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t row = m0 + mm * 16 + 4 * h + i;
+        if (row < M) y[row * N + col] = acc[mm][q][i];
       }
     }
 }
@@ -1127,6 +1467,15 @@ __global__ __launch_bounds__(256) void xsum_kernel(const uint16_t *__restrict__ 
   if (ok && q == 0) X[g] = m < M ? v : 0.0f;
 }
 
+// Arrival counters of a tiled launch with K in parts set to zero before the
+// launch (the int4 format's pre-pass does the same): a workspace shared by
+// calls of other shapes holds part sums where this call keeps counters.
+__global__ __launch_bounds__(256) void zero_counters_kernel(uint32_t *__restrict__ cnt,
+                                                            int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    cnt[i] = 0u;
+}
+
 // ---------------------------------------------------------------------------
 // Launch choices, shared by both formats.
 
@@ -1203,7 +1552,19 @@ void launch_tile(const TilePlan &p, const uint16_t *x, int64_t M, const uint8_t 
     hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, x, M, qw, am, ct, N, K, KT, y,
                        (int)p.nt, (int)p.mt, xsum, Mp, p.np, cnt, part);
   };
-  if (p.rg == 16)
+  if (p.rg == 16 && !AFF) {
+    // two 4-wave workgroups per CU when the grid fills two rounds of CUs,
+    // else one workgroup of 8 waves
+    const bool two = (int64_t)grid >= 2 * (int64_t)device_cu_count();
+    auto gw = [&](auto kern, int threads) {
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, x, M, qw, am, ct, N, K,
+                         KT, y, (int)p.nt, (int)p.mt, p.np, cnt, part);
+    };
+    if (two)
+      split ? gw(gemm_wide_kernel<4, true>, 256) : gw(gemm_wide_kernel<4, false>, 256);
+    else
+      split ? gw(gemm_wide_kernel<8, true>, 512) : gw(gemm_wide_kernel<8, false>, 512);
+  } else if (p.rg == 16)
     split ? go(gemm_tile_kernel<16, AFF, kTileMB, true>, 256 * 16 / kTileMB)
           : go(gemm_tile_kernel<16, AFF, kTileMB, false>, 256 * 16 / kTileMB);
   else
@@ -1352,6 +1713,11 @@ hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, const fl
     const TilePlan p = tile_plan(M, N, K, cus);
     if (p.np > 1 && (!ws || ws_bytes < split_bytes(p.rg, p.nt * p.mt, p.np)))
       return hipErrorInvalidValue;
+    if (p.np > 1) {
+      const int64_t n = p.nt * p.mt;
+      hipLaunchKernelGGL(zero_counters_kernel, dim3((unsigned)((n + 255) / 256 < 64 ? (n + 255) / 256 : 64)),
+                         dim3(256), 0, s, reinterpret_cast<uint32_t *>(ws), n);
+    }
     launch_tile<false>(p, x, M, qw, am, ct, N, K, y, nullptr, 0, ws, s);
     return hipGetLastError();
   }

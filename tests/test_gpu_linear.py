@@ -195,6 +195,29 @@ def test_gemm_k_halves_repeat(side, cb):
         assert_linear_ok(y[picks], yr, b, "K halves")
 
 
+def test_gemm_workspace_shared_by_shapes_and_garbage(side, cb):
+    """One workspace serves GEMMs with K in parts of different shapes: the
+    arrival counters of a call with more output tiles lie where a call with
+    fewer kept part sums, so every call clears its counters first.  Calls on
+    a workspace full of 0xFF bytes, and alternating between M = 520 and
+    M = 1040 (twice the tiles), give the bits of a fresh workspace."""
+    N, K = 1024, 8320
+    assert k_parts(N, K) == 2
+    packed, absmax, pw = case(side, cb, N, K, mid=29)
+    t = side.torch
+    xs = {M: side.x_dev(synth.activations(0, M, K, stream=M)) for M in (520, 1040)}
+    fresh = {M: side.linear("gemm", xs[M], M, pw, cb).cpu().numpy() for M in xs}
+    wsb = max(side.nf4.nf4_workspace_bytes(M, N, K) for M in xs)
+    ws = t.full((wsb,), 255, dtype=t.uint8, device="cuda")
+    for M in (1040, 520, 1040, 520, 520, 1040):
+        y = side.linear("gemm", xs[M], M, pw, cb, ws=ws).cpu().numpy()
+        np.testing.assert_array_equal(y, fresh[M])
+    picks = np.array([0, 519, 1039])
+    x = synth.activations(0, 1040, K, stream=1040)
+    yr, b = oracle.linear(x[picks], packed, absmax, cb)
+    assert_linear_ok(fresh[1040][picks], yr, b, "shared workspace")
+
+
 def test_gemv_and_gemm_agree(side, cb):
     N, K = 1024, 3584
     packed, absmax, pw = case(side, cb, N, K, mid=26)
