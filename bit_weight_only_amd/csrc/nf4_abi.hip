@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/nf4.h"
 #include "nf4_internal.h"
@@ -124,6 +125,8 @@ const char *nf4_status_string(nf4_status status) {
     case NF4_ERR_CODEBOOK: return "NF4_ERR_CODEBOOK: codebook not usable by this entry point";
     case NF4_ERR_WORKSPACE: return "NF4_ERR_WORKSPACE: workspace smaller than nf4_workspace_bytes()";
     case NF4_ERR_HIP: return "NF4_ERR_HIP: the HIP runtime rejected a launch";
+    case NF4_ERR_SCRATCH:
+      return "NF4_ERR_SCRATCH: the call needs more than the library's static scratch (64 KiB)";
   }
   return "NF4 unknown status";
 }
@@ -308,6 +311,75 @@ nf4_status nf4_gemv_argmax(const hip_bfloat16 *xb, int64_t M, const uint8_t *qwe
   if (nterm == 0) return NF4_ERR_CODEBOOK;
   return from_hip(nf4::launch_gemv_argmax(x, (int)M, qweight, absmax, ct, nterm, N, K, y, index,
                                           workspace, stream));
+}
+
+}  // extern "C"
+
+// Scratch of nf4_gemv_argmax_noalloc: the arrival counter (first 256 bytes)
+// and the per-workgroup candidates of the argmax that nf4_gemv_argmax keeps
+// in the caller's workspace.  Each device the library runs on holds its own
+// copy until the process ends; every call on a device shares it.
+static constexpr size_t kStaticScratchBytes = 64 * 1024;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+// Device address of `scratch` on the current device, taken once per device
+// with that device current (the array's name is not a device address in
+// host code).
+hipError_t scratch_address(void **out) {
+  static std::atomic<void *> addr[64];
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  void *p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+// Zero the first `words` dwords of p (a kernel, not a memset, so that a
+// captured graph clears it on every replay).
+__global__ void zero_words_kernel(uint32_t *p, int words) {
+  for (int i = threadIdx.x; i < words; i += blockDim.x) p[i] = 0u;
+}
+}  // namespace
+
+extern "C" {
+
+nf4_status nf4_gemv_argmax_noalloc(const hip_bfloat16 *xb, int64_t M, const uint8_t *qweight,
+                                   const float *absmax, const float codebook[16], int64_t N,
+                                   int64_t K, float *y, int32_t *index, hipStream_t stream) {
+  const uint16_t *x = bf16_bits(xb);
+  nf4_status st = check_linear_args(x, M, qweight, absmax, codebook, N, K, y, kMaxGemvM);
+  if (st != NF4_OK) return st;
+  if (!index) return NF4_ERR_NULL;
+  if (!aligned16(index)) return NF4_ERR_ALIGN;
+  if (nf4::gemv_argmax_workspace_bytes(M, N, K) > kStaticScratchBytes) return NF4_ERR_SCRATCH;
+  nf4::CodeTerms ct;
+  const int nterm = split_codebook(codebook, ct);
+  if (nterm == 0) return NF4_ERR_CODEBOOK;
+  void *ws = nullptr;
+  hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return NF4_ERR_HIP;
+  // the arrival counter starts at zero whatever an earlier call left
+  hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, stream,
+                     reinterpret_cast<uint32_t *>(ws), 64);
+  e = hipGetLastError();
+  if (e != hipSuccess) return NF4_ERR_HIP;
+  return from_hip(nf4::launch_gemv_argmax(x, (int)M, qweight, absmax, ct, nterm, N, K, y, index,
+                                          ws, stream));
 }
 
 nf4_status nf4_gemm(const hip_bfloat16 *xb, int64_t M, const uint8_t *qweight, const float *absmax,

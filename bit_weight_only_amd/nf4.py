@@ -15,11 +15,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnf4.so")
 
 NF4_OK, NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_CODEBOOK, NF4_ERR_WORKSPACE, \
-    NF4_ERR_HIP = range(7)
+    NF4_ERR_HIP, NF4_ERR_SCRATCH = range(8)
 
 EXPORTS = ("nf4_status_string", "nf4_codebook", "nf4_qweight_bytes", "nf4_absmax_bytes", "nf4_workspace_bytes",
            "nf4_pack", "nf4_dequant", "nf4_repack", "nf4_unpack", "nf4_gemv", "nf4_gemm",
-           "nf4_gemv_argmax_workspace_bytes", "nf4_gemv_argmax", "nf4_gemv_prefetch",
+           "nf4_gemv_argmax_workspace_bytes", "nf4_gemv_argmax", "nf4_gemv_argmax_noalloc",
+           "nf4_gemv_prefetch",
            "nf4_awq_params_bytes", "nf4_awq_workspace_bytes", "nf4_awq_pack", "nf4_awq_repack",
            "nf4_awq_unpack", "nf4_awq_dequant", "nf4_gather_columns", "nf4_awq_gemv_prefetch", "nf4_awq_gemv", "nf4_awq_gemm")
 
@@ -65,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.nf4_gemv_argmax_workspace_bytes.argtypes = [i64, i64, i64]
         L.nf4_gemv_argmax.restype = st
         L.nf4_gemv_argmax.argtypes = [vp, i64, vp, vp, fp, i64, i64, vp, vp, vp, sz, vp]
+        L.nf4_gemv_argmax_noalloc.restype = st
+        L.nf4_gemv_argmax_noalloc.argtypes = [vp, i64, vp, vp, fp, i64, i64, vp, vp, vp]
         L.nf4_gemv_prefetch.restype = st
         L.nf4_gemv_prefetch.argtypes = [vp, i64, vp, vp, fp, i64, i64, vp, vp, sz, vp, vp, i64,
                                         i64, vp]
@@ -196,6 +199,13 @@ def nf4_gemv_argmax(x, M: int, qweight, absmax, codebook, N: int, K: int, y, ind
     _check(lib().nf4_gemv_argmax(_ptr(x), M, _ptr(qweight), _ptr(absmax), _codebook(codebook),
                                  N, K, _ptr(y), _ptr(index), _ptr(workspace), ws_bytes,
                                  _stream(stream)), "nf4_gemv_argmax")
+
+
+def nf4_gemv_argmax_noalloc(x, M: int, qweight, absmax, codebook, N: int, K: int, y, index,
+                            stream=None) -> None:
+    _check(lib().nf4_gemv_argmax_noalloc(_ptr(x), M, _ptr(qweight), _ptr(absmax),
+                                         _codebook(codebook), N, K, _ptr(y), _ptr(index),
+                                         _stream(stream)), "nf4_gemv_argmax_noalloc")
 
 
 def nf4_awq_params_bytes(N: int, K: int) -> int:

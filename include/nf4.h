@@ -66,7 +66,8 @@ typedef enum nf4_status {
   NF4_ERR_ALIGN = 3,     /* a device pointer is not 16-byte aligned */
   NF4_ERR_CODEBOOK = 4,  /* codebook not usable by this entry point */
   NF4_ERR_WORKSPACE = 5, /* workspace smaller than nf4_workspace_bytes() */
-  NF4_ERR_HIP = 6        /* the HIP runtime rejected a launch */
+  NF4_ERR_HIP = 6,       /* the HIP runtime rejected a launch */
+  NF4_ERR_SCRATCH = 7    /* more scratch than nf4_gemv_argmax_noalloc holds */
 } nf4_status;
 
 /* Static string naming a status; never NULL. */
@@ -199,6 +200,26 @@ nf4_status nf4_gemv_argmax(const hip_bfloat16 *x, int64_t M, const uint8_t *qwei
                            const float *absmax, const float codebook[16], int64_t N, int64_t K,
                            float *y, int32_t *index, void *workspace, size_t ws_bytes,
                            hipStream_t stream);
+
+/* nf4_gemv_argmax for callers that cannot allocate or pass a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same kernels and results (y and index bit for bit those
+ * of nf4_gemv_argmax with the same arguments), with the arrival counter and
+ * candidates in a static device array of the library, 64 KiB per device,
+ * held from the first call on a device until the process ends.  Each call
+ * first clears the counter with a small kernel on `stream`, then runs the
+ * GEMV + argmax; it calls no allocation routine.  Calls needing more than
+ * 64 KiB (nf4_gemv_argmax_workspace_bytes(M, N, K) > 65536, i.e. more than
+ * about 1000 workgroups' candidates; a 152064-row head at M = 8 on 256 CUs
+ * needs 16.6 KB) return NF4_ERR_SCRATCH and enqueue nothing.  All calls of
+ * a process on one device share the array: calls that overlap in time on
+ * one device (two streams or two threads) race and must be ordered by the
+ * caller.  The first call on a device looks up the array's
+ * device address (NF4_ERR_HIP if that fails).  Other arguments and errors
+ * as nf4_gemv_argmax. */
+nf4_status nf4_gemv_argmax_noalloc(const hip_bfloat16 *x, int64_t M, const uint8_t *qweight,
+                                   const float *absmax, const float codebook[16], int64_t N,
+                                   int64_t K, float *y, int32_t *index, hipStream_t stream);
 
 /* Prefill GEMM, any M >= 1 (vibevoice.c README, "Quantization" > "Weights",
  * M > 1 bullet: a matrix-core GEMM that keeps the weights 4-bit into on-chip

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert nf4.nf4_status_string(s).startswith("NF4_")
     assert "unknown" in nf4.nf4_status_string(99)
 
@@ -405,3 +405,18 @@ def test_library_codebook_rejects_bad_delta(delta):
     with pytest.raises(nf4.NF4Error) as e:
         nf4.nf4_codebook(delta)
     assert e.value.status == nf4.NF4_ERR_CODEBOOK
+
+
+# ------------------------------------------- GEMV + argmax without allocation
+def test_noalloc_rejects_bad_arguments_on_the_host():
+    """nf4_gemv_argmax_noalloc validates like nf4_gemv_argmax before any HIP
+    call (no compute call is made here)."""
+    L, cb = nf4.lib(), (ctypes.c_float * 16)(*nf4.nf4_codebook().tolist())
+    f = L.nf4_gemv_argmax_noalloc
+    assert f(None, 1, A, A, cb, 256, 256, A, A, None) == nf4.NF4_ERR_NULL
+    assert f(A, 1, A, A, cb, 256, 256, A, None, None) == nf4.NF4_ERR_NULL
+    assert f(A, 9, A, A, cb, 256, 256, A, A, None) == nf4.NF4_ERR_SHAPE
+    assert f(A, 0, A, A, cb, 256, 256, A, A, None) == nf4.NF4_ERR_SHAPE
+    assert f(A, 1, A, A, cb, 24, 256, A, A, None) == nf4.NF4_ERR_SHAPE
+    assert f(A + 4, 1, A, A, cb, 256, 256, A, A, None) == nf4.NF4_ERR_ALIGN
+    assert f(A, 1, A, A, cb, 256, 256, A, A + 4, None) == nf4.NF4_ERR_ALIGN
