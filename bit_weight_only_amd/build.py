@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import subprocess
 import sys
 
@@ -32,17 +33,40 @@ FLAGS = [
 ]
 
 
+# the compiler's per-kernel resource report, read to refuse register spills
+REPORT = "-Rpass-analysis=kernel-resource-usage"
+
+
+def scratch_kernels(report: str) -> list[tuple[str, int]]:
+    """(kernel, bytes per lane) for every kernel of a resource report whose
+    private segment is nonzero, i.e. that spills registers to scratch."""
+    out, name = [], None
+    for ln in report.splitlines():
+        m = re.search(r"Function Name: (\S+)", ln)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", ln)
+        if m and int(m.group(1)) > 0:
+            out.append((name, int(m.group(1))))
+    return out
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, REPORT, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+    spills = scratch_kernels(r.stderr)
+    if spills:
+        raise RuntimeError(f"{src}: kernels spill registers to scratch (bytes per lane):\n" +
+                           "\n".join(f"  {b:5d}  {k}" for k, b in spills))
     # hipcc's host pass does not know the packed-fp32 feature; that warning is harmless
-    noise = [ln for ln in r.stderr.splitlines() if ln.strip() and "packed-fp32-ops" not in ln
-             and "not a recognized feature" not in ln]
+    noise = [ln for ln in r.stderr.splitlines() if ("warning" in ln or "error" in ln)
+             and "packed-fp32-ops" not in ln and "not a recognized feature" not in ln]
     if verbose and noise:
         print("\n".join(noise), file=sys.stderr)
     return obj

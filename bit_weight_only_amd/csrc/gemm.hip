@@ -882,37 +882,29 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void gemm_wide_kern
                                           __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (*flag != np - 1) return;
-    f32x4 tot[W::kMB][RGW];
-    for (int j = 0; j < np; ++j) {
-      f32x4 pj[W::kMB][RGW];
-      if (j == kc) {
+    // one 16-row block at a time, every part (this one's too) read back from
+    // its slot: the registers hold one block's sums, not all parts' at once
 #pragma unroll
-        for (int mm = 0; mm < W::kMB; ++mm)
-#pragma unroll
-          for (int q = 0; q < RGW; ++q) pj[mm][q] = acc[mm][q];
-      } else {
+    for (int mm = 0; mm < W::kMB; ++mm) {
+      f32x4 tot[RGW];
+      for (int j = 0; j < np; ++j) {
         const uint64_t *src = part + (tile_id * np + j) * slot_u64 + tid;
+        f32x4 pj[RGW];
 #pragma unroll
-        for (int mm = 0; mm < W::kMB; ++mm)
+        for (int q = 0; q < RGW; ++q)
 #pragma unroll
-          for (int q = 0; q < RGW; ++q)
+          for (int i2 = 0; i2 < 2; ++i2) {
+            const uint64_t v = __hip_atomic_load(src + ((mm * RGW + q) * 2 + i2) * Gm::kThreads,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            pj[q][2 * i2] = __uint_as_float((uint32_t)v);
+            pj[q][2 * i2 + 1] = __uint_as_float((uint32_t)(v >> 32));
+          }
 #pragma unroll
-            for (int i2 = 0; i2 < 2; ++i2) {
-              const uint64_t v = __hip_atomic_load(src + ((mm * RGW + q) * 2 + i2) * Gm::kThreads,
-                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              pj[mm][q][2 * i2] = __uint_as_float((uint32_t)v);
-              pj[mm][q][2 * i2 + 1] = __uint_as_float((uint32_t)(v >> 32));
-            }
+        for (int q = 0; q < RGW; ++q) tot[q] = j ? tot[q] + pj[q] : pj[q];
       }
 #pragma unroll
-      for (int mm = 0; mm < W::kMB; ++mm)
-#pragma unroll
-        for (int q = 0; q < RGW; ++q) tot[mm][q] = j ? tot[mm][q] + pj[mm][q] : pj[mm][q];
+      for (int q = 0; q < RGW; ++q) acc[mm][q] = tot[q];
     }
-#pragma unroll
-    for (int mm = 0; mm < W::kMB; ++mm)
-#pragma unroll
-      for (int q = 0; q < RGW; ++q) acc[mm][q] = tot[mm][q];
     if (tid == 0) __hip_atomic_store(cnt + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 

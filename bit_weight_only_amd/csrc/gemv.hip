@@ -37,15 +37,24 @@ __device__ inline float dot2(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2, b), c, false);
 }
 
-constexpr int kMaxWaves = 16;
+// Waves per workgroup and the largest tile batch TT that stay in registers
+// (no scratch) at that wave count: 16 waves leave 128 VGPRs per lane, 8
+// waves 256; the batch's loads and the M rows' sums grow with M and NTERM.
+template <int M>
+constexpr int generic_waves() { return M <= 4 ? 16 : 8; }
+template <int M, int NTERM>
+constexpr int generic_tt_max() {
+  return M <= 1 ? 8 : M == 2 ? (NTERM == 1 ? 8 : 4) : M == 3 ? (NTERM == 1 ? 4 : 2)
+       : M == 4 ? (NTERM == 1 ? 4 : 1) : 8;
+}
 
-template <int M, int NTERM, int TT>
-__global__ __launch_bounds__(kMaxWaves * 64) void gemv_generic_kernel(
+template <int M, int NTERM, int TT, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void gemv_generic_kernel(
     const uint16_t *__restrict__ x, const uint4 *__restrict__ qw,
     const float2 *__restrict__ am, CodeTerms ct, int64_t N, int64_t K, int64_t KT, int T,
     float *__restrict__ y) {
   __shared__ uint32_t table[NTERM * kPairWords];
-  __shared__ float red[kMaxWaves][16][M];
+  __shared__ float red[WAVES][16][M];
 
   for (int e = threadIdx.x; e < NTERM * kPairWords; e += blockDim.x) {
     const int term = e / kPairWords;
@@ -714,19 +723,25 @@ hipError_t launch_fast(const uint16_t *x, const uint4 *qw, const float2 *am, con
 template <int M, int NTERM>
 hipError_t launch_m(const uint16_t *x, const uint4 *qw, const float2 *am, const CodeTerms &ct,
                     int64_t N, int64_t K, float *y, hipStream_t s) {
+  constexpr int W = generic_waves<M>(), TTM = generic_tt_max<M, NTERM>();
   const int64_t KT = tiles_k(K);
-  int nw = KT < kMaxWaves ? (int)KT : kMaxWaves;
+  int nw = KT < W ? (int)KT : W;
   const int T = (int)((KT + nw - 1) / nw);
   nw = (int)((KT + T - 1) / T);
   const dim3 grid((unsigned)(N / kTileRows)), block(nw * 64);
-  if (T >= 8)
-    hipLaunchKernelGGL((gemv_generic_kernel<M, NTERM, 8>), grid, block, 0, s, x, qw, am, ct, N, K, KT, T, y);
-  else if (T >= 4)
-    hipLaunchKernelGGL((gemv_generic_kernel<M, NTERM, 4>), grid, block, 0, s, x, qw, am, ct, N, K, KT, T, y);
-  else if (T >= 2)
-    hipLaunchKernelGGL((gemv_generic_kernel<M, NTERM, 2>), grid, block, 0, s, x, qw, am, ct, N, K, KT, T, y);
+  const int tt = T < TTM ? T : TTM;
+  if (tt >= 8)
+    hipLaunchKernelGGL((gemv_generic_kernel<M, NTERM, (TTM < 8 ? TTM : 8), W>), grid, block, 0, s,
+                       x, qw, am, ct, N, K, KT, T, y);
+  else if (tt >= 4)
+    hipLaunchKernelGGL((gemv_generic_kernel<M, NTERM, (TTM < 4 ? TTM : 4), W>), grid, block, 0, s,
+                       x, qw, am, ct, N, K, KT, T, y);
+  else if (tt >= 2)
+    hipLaunchKernelGGL((gemv_generic_kernel<M, NTERM, (TTM < 2 ? TTM : 2), W>), grid, block, 0, s,
+                       x, qw, am, ct, N, K, KT, T, y);
   else
-    hipLaunchKernelGGL((gemv_generic_kernel<M, NTERM, 1>), grid, block, 0, s, x, qw, am, ct, N, K, KT, T, y);
+    hipLaunchKernelGGL((gemv_generic_kernel<M, NTERM, 1, W>), grid, block, 0, s, x, qw, am, ct,
+                       N, K, KT, T, y);
   return hipGetLastError();
 }
 
