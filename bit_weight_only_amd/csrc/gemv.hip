@@ -333,6 +333,25 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float *__restrict__ y
 // acc = fmaf(16 s, g, acc) (both constants exact).
 // ---------------------------------------------------------------------------
 constexpr int kFastWaves = 8;
+constexpr int kFastThreads = kFastWaves * 64;  // the launch's block size
+
+// Code i (as its bf16 bit pattern) of the first term, i in 0..15 per lane
+// or per wave: each code is read from the kernel argument at a fixed index
+// (readfirstlane keeps it a scalar value, so the selects cannot be folded
+// back into one read at an index that varies by lane).  The 16 codes are
+// contiguous halfwords, code 2 j in the low half of dword j.
+__device__ __forceinline__ uint32_t pick_code(const CodeTerms &ct, int i) {
+  // whole dwords (two codes each): the argument block is read with scalar
+  // loads only in units of dwords
+  const uint32_t *w = reinterpret_cast<const uint32_t *>(&ct.t[0][0]);
+  uint32_t v = 0;
+#pragma unroll
+  for (int j = 0; j < 16; j += 2) {
+    const uint32_t pj = __builtin_amdgcn_readfirstlane(w[j >> 1]);
+    v = i == j ? (pj & 0xFFFFu) : i == j + 1 ? (pj >> 16) : v;
+  }
+  return v;
+}
 constexpr int kFastCopies = 64;                     // copy slots per 256-byte entry line
 constexpr int kFastTableWords = 256 * kFastCopies;  // 64 KB of LDS, copies 0 .. 31 written
 constexpr int kFastDepth = 4;                        // tiles in flight per wave
@@ -354,19 +373,34 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
   // dynamic LDS.
   __shared__ __attribute__((aligned(16))) uint32_t table[AFF ? 4 : kFastTableWords];
   extern __shared__ __attribute__((aligned(16))) uint32_t lds_dyn[];
+  // Every argument is read here, in one batch of scalar loads with one wait:
+  // left to itself the compiler reads each argument in the block that first
+  // uses it, and each such block waits for the argument memory again before
+  // the first weight load can be issued.  The empty asm statements need the
+  // values in registers at this point.
+  {
+    const uint32_t *cw = reinterpret_cast<const uint32_t *>(&ct.t[0][0]);
+    asm volatile("" ::"s"(x), "s"(qw), "s"(am), "s"(y), "s"(nq), "s"(nsb), "s"(N), "s"(K),
+                 "s"(KT), "s"(G), "s"(P), "s"(nG), "s"(nKT), "s"(nP), "s"(cw[0]), "s"(cw[1]),
+                 "s"(cw[2]), "s"(cw[3]), "s"(cw[4]), "s"(cw[5]), "s"(cw[6]), "s"(cw[7]));
+  }
   const int KP = KT * kTileK;                 // padded x row length
   const int XS = KP + kFastSkew;              // x row stride in LDS
   uint16_t *xs = reinterpret_cast<uint16_t *>(lds_dyn);
   float *red = reinterpret_cast<float *>(lds_dyn + M * XS / 2);
-  uint16_t *codes_lds = reinterpret_cast<uint16_t *>(red);  // until the table is built
 
   // the wave index as a scalar: every per-wave quantity below (tile cursor,
   // share end, read-ahead cursor, trip count) stays in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, h = lane >> 4;
-  const int g0 = (int)((int64_t)G * blockIdx.x / P), g1 = (int)((int64_t)G * (blockIdx.x + 1) / P);
-  const int Gw = g1 - g0, T0 = g0 * KT, Twg = Gw * KT;
+  // G row groups over P workgroups: the first G % P take one more.  32-bit
+  // arithmetic throughout (a 64-bit division is a long branching sequence,
+  // and the argument loads after each branch wait again).
+  const uint32_t wg = blockIdx.x;
+  const uint32_t gbase = (uint32_t)G / (uint32_t)P, grem = (uint32_t)G % (uint32_t)P;
+  const int g0 = (int)(wg * gbase + (wg < grem ? wg : grem));
+  const int Gw = (int)(gbase + (wg < grem ? 1u : 0u)), T0 = g0 * KT, Twg = Gw * KT;
   const int n = Twg > wave ? (Twg - wave + kFastWaves - 1) / kFastWaves : 0;
   const char *qbase = reinterpret_cast<const char *>(qw);
   const char *sbase = reinterpret_cast<const char *>(am);
@@ -378,8 +412,9 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
   // workgroup's first tile.  Their data is never used.
   uint32_t pn = 0, ntile_end = 0;
   if (nq != nullptr && (int)blockIdx.x < nP) {
-    const int ng0 = (int)((int64_t)nG * blockIdx.x / nP);
-    const int ng1 = (int)((int64_t)nG * (blockIdx.x + 1) / nP);
+    const uint32_t nbase = (uint32_t)nG / (uint32_t)nP, nrem = (uint32_t)nG % (uint32_t)nP;
+    const int ng0 = (int)(wg * nbase + (wg < nrem ? wg : nrem));
+    const int ng1 = ng0 + (int)(nbase + (wg < nrem ? 1u : 0u));
     pn = (uint32_t)(ng0 * nKT + wave);
     ntile_end = (uint32_t)(ng1 * nKT);
   }
@@ -393,6 +428,22 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
     else
       return *reinterpret_cast<const float2 *>(src + (lt * 128u + r * 8u));
   };
+  // x rows straight into LDS, issued before the weight loads below so that
+  // they can be waited for without waiting for those: one copy is 64 lanes
+  // x 16 bytes of one row (1 KB); lanes at or past K copy nothing, their
+  // chunks are zeroed below.
+  const int chunks = M * KP / 8, cpr = KP / 8;
+  if constexpr (!AFF) {
+    const int segs = (cpr + 63) / 64;
+    const uint32_t xs_base = lds_addr(xs);
+    for (int q = wave; q < M * segs; q += kFastWaves) {
+      const int m = q / segs, seg = q - m * segs;
+      const int c = seg * 64 + lane, k = c * 8;
+      if (c < cpr && k < K)
+        copy16_to_lds(xs_base + (uint32_t)(m * XS + seg * 512) * 2u, x,
+                      (uint32_t)(((int64_t)m * K + k) * 2));
+    }
+  }
   // Prefetch cursor; steps past the wave's share re-read the workgroup's
   // first tile so that every step issues the same loads.
   uint32_t ptau = (uint32_t)(T0 + wave);
@@ -405,17 +456,20 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
     sb[d] = load_scales(sbase, lt);
     ptau += kFastWaves;
   }
+  // every load above is issued before the set-up below starts (the
+  // scheduler would otherwise pull the table's selects, which wait for the
+  // codebook argument, in between the loads)
+  __builtin_amdgcn_sched_barrier(0);
 
-  // Setup.  The 16 codes go through LDS (indexing the kernel-argument block
-  // with a per-thread index would be one memory round trip per use).  x is
-  // copied straight from global memory into LDS (one 1 KB copy per row
-  // segment, no pass through registers), issued before the table is built
-  // and waited for before the second barrier.  Affine: x goes through
-  // registers, since a row has a whole number of 128-k tiles and the 16
-  // lanes of a DPP row hold the 16 chunks of one tile row of x, whose sum
+  // Setup, one barrier in all, everything in it overlapping the first
+  // tiles' flight.  The x copies are waited for just before the barrier.
+  // The table entries take the 16 codes from the
+  // kernel argument by compile-time index (scalar reads) and pick with
+  // selects: an index varying by lane into the argument block would be a
+  // vector memory read, waited for behind the tiles above.  Affine: x goes
+  // through registers, since a row has a whole number of 128-k tiles and the
+  // 16 lanes of a DPP row hold the 16 chunks of one tile row of x, whose sum
   // goes to X as x is stored (the chunk sums in k order, then row16_sum).
-  if (!AFF && threadIdx.x < 16) codes_lds[threadIdx.x] = ct.t[0][threadIdx.x];
-  const int chunks = M * KP / 8, cpr = KP / 8;
   constexpr int kStage = 4;
   float *Xl = red + Gw * kFastWaves * 16 * M;  // affine: X[t][m], 8 floats per tile
   auto store_xsum = [&](int c, uint4 v) {
@@ -428,81 +482,75 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
     }
   };
   uint4 xv0[kStage];
-  if constexpr (!AFF) {
-    // x rows straight into LDS: one copy is 64 lanes x 16 bytes of one row
-    // (1 KB); lanes at or past K copy nothing, their chunks are zeroed below
-    const int segs = (cpr + 63) / 64;
-    const uint32_t xs_base = lds_addr(xs);
-    for (int q = wave; q < M * segs; q += kFastWaves) {
-      const int m = q / segs, seg = q - m * segs;
-      const int c = seg * 64 + lane, k = c * 8;
-      if (c < cpr && k < K)
-        copy16_to_lds(xs_base + (uint32_t)(m * XS + seg * 512) * 2u, x,
-                  (uint32_t)(((int64_t)m * K + k) * 2));
-    }
-  } else {
+  if constexpr (AFF) {
 #pragma unroll
   for (int u = 0; u < kStage; ++u) {
-    const int c = (int)threadIdx.x + u * (int)blockDim.x;
+    const int c = (int)threadIdx.x + u * kFastThreads;
     const int m = c / cpr, k = (c - m * cpr) * 8;
     xv0[u] = make_uint4(0u, 0u, 0u, 0u);
     if (c < chunks && k < K) xv0[u] = *reinterpret_cast<const uint4 *>(x + (int64_t)m * K + k);
   }
   }
-  __syncthreads();
-  // Pair table, copies 0 .. 31 of every entry: consecutive lanes fill
-  // consecutive 16-byte chunks (four copies each), eight chunks per entry.
-  for (int c = threadIdx.x; c < (AFF ? 0 : kFastTableWords / 8); c += blockDim.x) {
-    const int e = c >> 3;
-    const uint32_t v = (uint32_t)codes_lds[e & 15] | ((uint32_t)codes_lds[e >> 4] << 16);
-    reinterpret_cast<uint4 *>(table)[e * 16 + (c & 7)] = make_uint4(v, v, v, v);
-  }
   if constexpr (!AFF) {
+    // Pair table, copies 0 .. 31 of every entry: 16-byte chunk c (four
+    // copies) of entry c / 8, for c = threadIdx.x + 512 i.  Its low code
+    // index (c / 8) % 16 = (threadIdx.x / 8) % 16 is fixed per lane, its
+    // high one c / 128 = threadIdx.x / 128 + 4 i fixed per wave and step.
+    static_assert(kFastTableWords / 8 == 4 * kFastWaves * 64, "four chunks per thread");
+    const uint32_t lo = pick_code(ct, ((int)threadIdx.x >> 3) & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t v = lo | pick_code(ct, (wave >> 1) + 4 * i) << 16;
+      const int c = (int)threadIdx.x + i * kFastWaves * 64;
+      reinterpret_cast<uint4 *>(table)[(c >> 3) * 16 + (c & 7)] = make_uint4(v, v, v, v);
+    }
     // the zero padding k in [K, KP) of every row
     const int padc = (KP - K) / 8, kc0 = K / 8;
-    for (int c = threadIdx.x; c < M * padc; c += blockDim.x) {
+    for (int c = threadIdx.x; c < M * padc; c += kFastThreads) {
       const int m = c / (padc ? padc : 1), k = (kc0 + c - m * padc) * 8;
       *reinterpret_cast<uint4 *>(&xs[m * XS + k]) = make_uint4(0u, 0u, 0u, 0u);
     }
-    // the copies of x have landed before the barrier below
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   } else {
 #pragma unroll
   for (int u = 0; u < kStage; ++u) {
-    const int c = (int)threadIdx.x + u * (int)blockDim.x;
+    const int c = (int)threadIdx.x + u * kFastThreads;
     const int m = c / cpr, k = (c - m * cpr) * 8;
     if (c < chunks) *reinterpret_cast<uint4 *>(&xs[m * XS + k]) = xv0[u];
     store_xsum(c, xv0[u]);
   }
   }
-  for (int c0 = (int)threadIdx.x + kStage * (int)blockDim.x; c0 < (AFF ? chunks : 0);
-       c0 += kStage * (int)blockDim.x) {
+  for (int c0 = (int)threadIdx.x + kStage * kFastThreads; c0 < (AFF ? chunks : 0);
+       c0 += kStage * kFastThreads) {
     uint4 v[kStage];
 #pragma unroll
     for (int u = 0; u < kStage; ++u) {
-      const int c = c0 + u * (int)blockDim.x;
+      const int c = c0 + u * kFastThreads;
       const int m = c / cpr, k = (c - m * cpr) * 8;
       v[u] = make_uint4(0u, 0u, 0u, 0u);
       if (c < chunks && k < K) v[u] = *reinterpret_cast<const uint4 *>(x + (int64_t)m * K + k);
     }
 #pragma unroll
     for (int u = 0; u < kStage; ++u) {
-      const int c = c0 + u * (int)blockDim.x;
+      const int c = c0 + u * kFastThreads;
       const int m = c / cpr, k = (c - m * cpr) * 8;
       if (c < chunks) *reinterpret_cast<uint4 *>(&xs[m * XS + k]) = v[u];
       store_xsum(c, v[u]);
     }
   }
-  __syncthreads();
   // Partial slots start at zero (a wave may touch no tile of a row group
-  // when a row group has fewer than 8 tiles).  The codes' words are reused
-  // here, after the barrier above.
-  for (int c = threadIdx.x; c < Gw * kFastWaves * 16 * M; c += blockDim.x) red[c] = 0.0f;
-  // the x sums of rows M .. 7 (read by lanes whose output rows are dropped)
+  // when a row group has fewer than 8 tiles).
+  for (int c = threadIdx.x; c < Gw * kFastWaves * 16 * M; c += kFastThreads) red[c] = 0.0f;
+  // the x sums of rows M .. 7 (read by lanes whose output rows are dropped;
+  // store_xsum writes rows below M only)
   if constexpr (AFF && M < 8) {
-    for (int c = threadIdx.x; c < KT * 8; c += blockDim.x)
+    for (int c = threadIdx.x; c < KT * 8; c += kFastThreads)
       if ((c & 7) >= M) Xl[c] = 0.0f;
   }
+  // The copies of x have landed before the barrier: at least 2 D vector
+  // memory instructions (the D tiles' code and scale loads) were issued after
+  // the last copy, and they complete in order, so at most D outstanding
+  // means every copy is done (the tiles may still be in flight).
+  if constexpr (!AFF) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D) : "memory");
   __syncthreads();
 
   const uint32_t lane4 = ((uint32_t)lane & 31u) << 2;  // copy lane % 32
@@ -636,7 +684,7 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
     bv[m] = -INFINITY;
     bn[m] = INT_MAX;
   }
-  for (int c = threadIdx.x; c < Gw * 16; c += blockDim.x) {
+  for (int c = threadIdx.x; c < Gw * 16; c += kFastThreads) {
     const int jj = c >> 4, rr = c & 15;
     const int n = (g0 + jj) * 16 + rr;
 #pragma unroll

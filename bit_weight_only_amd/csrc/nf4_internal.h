@@ -30,8 +30,10 @@ constexpr int kPairWords = 256 * kPairCopies;
 
 // Codebook split into bf16 terms c = t0 + t1 + t2 (exact for binary32 when
 // the host check passes); the GEMV/GEMM products with each term are exact in
-// fp32.
-struct CodeTerms {
+// fp32.  Passed by value as a kernel argument; the 16-byte alignment lets a
+// kernel read it with scalar loads (a 2-byte aligned block is read with
+// vector loads, which wait in line behind the kernel's other vector loads).
+struct alignas(16) CodeTerms {
   uint16_t t[3][16];
 };
 
