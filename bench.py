@@ -21,17 +21,24 @@ nf4_awq_gemm; algorithmic bytes N K / 2 + 4 N K / 128: codes and one 4-byte
 (s, z) per group).
 
 `roofline` covers the dominant decode kernel (the gate|up GEMV, 28 launches
-per step): its 28 launches on distinct weights are replayed back to back in
-one graph, each naming the next as its hint as in the step, each replay
-timed with events on the launch stream; the median
-replay / 28 is the launch duration.  `roofline_prefill`
-does the same for the gate|up GEMM.  `traffic` is the HBM bytes per launch
-from rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, each scaled by what the
-counter reads for a plain 1 GiB copy), recorded below together with a hash of
-the kernel source they were taken on; it is null when the source differs.
+per step) and `roofline_prefill` the gate|up GEMM: 28 launches on the 28
+layers' distinct matrices, replayed back to back in one graph (each GEMV
+naming the next as its hint, as in the step).  Before this process touches
+the GPU it runs rocprofv3 on child runs of itself: a kernel trace of
+`--kernel-pass` (the same replays), whose mean dispatch duration is the
+launch duration `achieved` is computed from (`rocprof_mean_us`; the event
+time per launch of this run's own replays is `event_us`), and two counter
+runs of `--pmc-pass` (FETCH_SIZE, then WRITE_SIZE) whose readings, each
+scaled by what the counter reads for a plain 1 GiB copy, give `traffic`, the
+HBM bytes per launch.  Without rocprofv3 (or with --no-rocprof) `achieved`
+falls back to the event time and `traffic` is null; `timed_on` says which.
+
+`cpu_baseline` times the CPU oracle on this host (see cpu_baseline()).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu] [--no-int4]
-    python bench.py --pmc-pass          # workload for rocprofv3 --pmc runs
+                    [--no-rocprof] [--profile-out DIR]
+    python bench.py --kernel-pass --launch-log FILE   # rocprofv3 kernel-trace workload
+    python bench.py --pmc-pass --launch-log FILE      # rocprofv3 --pmc workload
     python bench.py --summarize DIR --launch-log FILE --title T --command C
 """
 from __future__ import annotations
@@ -40,7 +47,9 @@ import argparse
 import collections
 import csv
 import glob
-import hashlib
+import shutil
+import subprocess
+import tempfile
 import json
 import os
 import sys
@@ -72,22 +81,6 @@ VOXTRAL_LAYERS = 26
 VOXTRAL = [("qkv", 6144, 3072), ("wo", 3072, 4096), ("w13", 18432, 3072), ("w2", 3072, 9216)]
 LONG_M, LONG_CHUNKS = 14449, 14  # the long-audio prompt: 14 x 1024 rows + the 113-row tail
 
-# HBM traffic per launch of the dominant kernels, from rocprofv3 --pmc runs of
-# `python bench.py --pmc-pass` (profiles/hbm_traffic_gate_up.md): counter KiB
-# per dispatch and the calibration of each counter on a plain 1 GiB copy.
-TRAFFIC = {
-    "gemv": {"source": "gemv.hip", "fetch_kib": 42713, "write_kib": 148,
-             "sha256": "06d88eadf44e341f16f0ed60b6f9b9a215b0837c03260c23416ab488040e22aa"},
-    "gemm": {"source": "gemm.hip", "fetch_kib": 180759, "write_kib": 151961,
-             "sha256": "48ca7077af481c8e09889f6509177380f245e767fa71cb5cbf878ecfb837e4f2"},
-    "awq_gemv": {"source": "gemv.hip", "fetch_kib": 40355, "write_kib": 148,
-                 "sha256": "06d88eadf44e341f16f0ed60b6f9b9a215b0837c03260c23416ab488040e22aa"},
-    "awq_gemm": {"source": "gemm.hip", "fetch_kib": 180913, "write_kib": 151929,
-                 "sha256": "48ca7077af481c8e09889f6509177380f245e767fa71cb5cbf878ecfb837e4f2"},
-}
-COPY_CALIBRATION = {"fetch_kib_per_gib": 524308, "write_kib_per_gib": 1048576}
-
-
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -109,58 +102,133 @@ def cpu_threads():
     return n
 
 
-def source_sha256(name):
-    with open(os.path.join(CSRC, name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def pin_cpus(n):
+    """Restrict this process (and the oracle threads it starts) to the first
+    n CPUs of its allowed set, one oracle thread per CPU; returns them."""
+    use = sorted(os.sched_getaffinity(0))[:n]
+    os.sched_setaffinity(0, use)
+    return use
 
 
-def traffic_bytes(kind):
-    """HBM bytes per launch from the recorded counters, or None when they
-    were not taken or the kernel source changed since."""
-    t, cal = TRAFFIC[kind], COPY_CALIBRATION
-    if t is None:
-        return None
-    if None in (t["sha256"], t["fetch_kib"], t["write_kib"], cal["fetch_kib_per_gib"],
-                cal["write_kib_per_gib"]):
-        return None
-    if source_sha256(t["source"]) != t["sha256"]:
-        return None
-    gib = float(1 << 30)
-    return int(t["fetch_kib"] / cal["fetch_kib_per_gib"] * gib +
-               t["write_kib"] / cal["write_kib_per_gib"] * gib)
+# The unfused linears of the two decoder shapes, (N, K) = (out, in)
+VOXTRAL_UNFUSED = [(4096, 3072), (1024, 3072), (1024, 3072), (3072, 4096), (9216, 3072),
+                   (9216, 3072), (3072, 9216)]
+QWEN_UNFUSED = [(HIDDEN, HIDDEN), (KV, HIDDEN), (KV, HIDDEN), (HIDDEN, HIDDEN), (MLP, HIDDEN),
+                (MLP, HIDDEN), (HIDDEN, MLP)]
 
 
-def cpu_baseline(target_s: float):
-    """The oracle (scalar dequant + fp64 dot, threads over rows) on a bounded
-    sample of the decode workload: 2048 output rows of each fused linear of
-    layer 0 at M = 1, repeated until about `target_s` seconds elapse."""
+def cpu_baseline():
+    """The CPU oracle (scalar dequant + fp64 dot, its own threads over output
+    rows) timed on this host, pinned one thread per CPU:
+      C0  the tiny layer (N = K = 256) at M = 1 and 4, repeated for 0.3 s;
+      C1  the full Voxtral decode at M = 1: 26 layers x 7 linears;
+      C2  the full Qwen2-7B decode at M = 1 and M = 2: 28 layers x 7 linears
+          + lm_head;
+      C3  one 1024-row prefill chunk, sampled: rows {0, 1023} and 6 seeded
+          random rows through layer 0's 7 linears;
+      C4  the 14449-row prompt, sampled: C3's rows plus the 113 tail rows
+          through layer 0's 7 linears.
+    C3 and C4 are extrapolated (labelled so) from the two samples: per
+    layer a + b M seconds for M rows (every layer has the same shapes), a and
+    b fitted to the 8-row and 113-row samples.  Each layer of C1 and C2 is
+    a distinct copy in memory of one generated layer (the oracle's time does
+    not depend on the values; distinct copies keep a layer from being served
+    by the caches the previous one filled); inputs are the seeded synthetic
+    ones (SplitMix64 + Box-Muller), quantized by the oracle's quantizer."""
     import numpy as np
 
     import oracle
     from bit_weight_only_amd import synth
 
-    cb, _ = oracle.codebook()
     threads = cpu_threads()
-    rows = 2048
-    mats = []
-    for i, (name, N, K) in enumerate(LINEARS):
-        sel = np.arange(rows) * (N // rows)
-        W = synth.weights(2, 0, 50 + i, N, K, rows=sel)
-        codes, absmax = oracle.quantize(W, cb, threads=threads)
-        mats.append((oracle.pack(codes), absmax, synth.activations(2, 1, K), K))
-    per_pass = sum(packed_bytes(rows, K) for _, _, _, K in mats)
-    done, t0 = 0, time.perf_counter()
-    while True:
-        for packed, absmax, x, K in mats:
-            oracle.linear(x, packed, absmax, cb, threads=threads)
-        done += 1
+    cpus = pin_cpus(threads)
+    cb, _ = oracle.codebook()
+    t_start = time.perf_counter()
+
+    def make(cfg, shapes, base_id):
+        mats = []
+        for i, (N, K) in enumerate(shapes):
+            W = synth.weights(cfg, 0, base_id + i, N, K)
+            codes, absmax = oracle.quantize(W, cb, threads=threads)
+            del W
+            mats.append((oracle.pack(codes), absmax))
+        return mats
+
+    def copies(mats, n):
+        return [[(p.copy(), a.copy()) for p, a in mats] for _ in range(n)]
+
+    def run(layers, xs):
+        t0 = time.perf_counter()
+        for mats in layers:
+            for p, a in mats:
+                oracle.linear(xs[p.shape[1] * 2], p, a, cb, threads=threads)
+        return time.perf_counter() - t0
+
+    def nbytes(mats):
+        return sum(packed_bytes(p.shape[0], p.shape[1] * 2) for p, _ in mats)
+
+    out = {}
+    # C0
+    c0 = make(0, [(256, 256)], 0)
+    for M in (1, 4):
+        xs = {256: synth.activations(0, M, 256)}
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 0.3:
+            run([c0], xs)
+            n += 1
         el = time.perf_counter() - t0
-        if el >= target_s:
-            break
-    return {"value": round(done * per_pass / el / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{rows} output rows of each of the 4 fused layer linears (layer 0), M=1, "
-                      f"{done} passes of {per_pass / 1e6:.1f} MB packed weight in {el:.1f} s"}
+        out[f"C0_m{M}"] = {"ms": round(el / n * 1e3, 4),
+                           "gbps": round(nbytes(c0) * n / el / 1e9, 3)}
+    # C1: Voxtral decode, M = 1
+    layer = make(1, VOXTRAL_UNFUSED, 0)
+    layers = copies(layer, VOXTRAL_LAYERS)
+    xs = {K: synth.activations(1, 1, K) for K in (3072, 4096, 9216)}
+    el = run(layers, xs)
+    b1 = nbytes(layer) * VOXTRAL_LAYERS
+    out["C1_m1"] = {"ms": round(el * 1e3, 1), "gbps": round(b1 / el / 1e9, 3),
+                    "packed_bytes": b1}
+    del layers, layer
+    # C2: Qwen2-7B decode, M = 1 and 2 (lm_head: 8 distinct copies of a
+    # generated 1/8 of its rows)
+    layer = make(2, QWEN_UNFUSED, 0)
+    layers = copies(layer, LAYERS)
+    hp, ha = make(2, [(VOCAB // 8, HIDDEN)], 100)[0]
+    head = [(np.concatenate([hp] * 8), np.concatenate([ha] * 8))]
+    b2 = nbytes(layer) * LAYERS + nbytes(head)
+    for M in (1, 2):
+        xs = {K: synth.activations(2, M, K, stream=M) for K in (HIDDEN, MLP)}
+        el = run(layers + [head], xs)
+        out[f"C2_m{M}"] = {"ms": round(el * 1e3, 1), "gbps": round(b2 / el / 1e9, 3),
+                           "packed_bytes": b2}
+    del layers, head
+    # C3 / C4 samples through layer 0
+    rng = np.random.default_rng(0xC3)
+    rows8 = np.concatenate([[0, 1023], np.sort(rng.choice(np.arange(1, 1023), 6, replace=False))])
+    x8 = {K: synth.activations(3, PREFILL_M, K, rows=rows8) for K in (HIDDEN, MLP)}
+    t8 = run([layer], x8)
+    x113 = {K: synth.activations(4, LONG_M, K, rows=np.arange(LONG_CHUNKS * PREFILL_M, LONG_M))
+            for K in (HIDDEN, MLP)}
+    t113 = run([layer], x113)
+    b = max((t113 - t8) / (TAIL_M - 8), 0.0)
+    a = max(t8 - 8 * b, 0.0)
+    layer_flop = 2 * sum(N * K for N, K in QWEN_UNFUSED)
+    c3_s = LAYERS * (a + b * PREFILL_M)
+    c4_s = LAYERS * (LONG_CHUNKS * (a + b * PREFILL_M) + a + b * TAIL_M)
+    out["C3_m1024"] = {"extrapolated_s": round(c3_s, 1),
+                       "gflops": round(LAYERS * PREFILL_M * layer_flop / c3_s / 1e9, 2),
+                       "sample": "rows 0, 1023 and 6 seeded random rows of the chunk through "
+                                 f"layer 0's 7 linears: {t8:.2f} s"}
+    out["C4_m14449"] = {"extrapolated_s": round(c4_s, 1),
+                        "gflops": round(LAYERS * LONG_M * layer_flop / c4_s / 1e9, 2),
+                        "sample": f"the 113 tail rows through layer 0's 7 linears: {t113:.2f} s, "
+                                  "with the 8-row sample above"}
+    total = time.perf_counter() - t_start
+    return {"value": out["C2_m1"]["gbps"], "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "value: the full Qwen2-7B decode step at M=1 (28 layers x 7 linears + "
+                      "lm_head, 3.977 GB packed) through the oracle; C0-C2 full runs, C3/C4 "
+                      "extrapolated from row samples (per layer a + b M, fitted to 8 and 113 "
+                      f"rows); {total:.0f} s in all including input generation",
+            "pinned_cpus": cpus, "configs": out}
 
 
 class Model:
@@ -334,14 +402,19 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-int4", action="store_true",
                     help="skip the int4 group-128 format's decode and prefill measurements")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--seed", type=int, default=0x4E4634)
     ap.add_argument("--dominant-replays", type=int, default=9)
     ap.add_argument("--launch-log", default=None,
                     help="write the label of every nf4_gemv/nf4_gemm launch, in order, to FILE")
     ap.add_argument("--pmc-pass", action="store_true",
-                    help="run only the counter workload: a 1 GiB copy, 3 gate|up GEMVs, 1 GEMM "
-                         "(both formats), and down at M=29")
+                    help="run only the counter workload: a 1 GiB copy, 3 gate|up GEMVs and "
+                         "1 GEMM in both formats (labels to --launch-log)")
+    ap.add_argument("--kernel-pass", action="store_true",
+                    help="run only the dominant kernels' timing workload (labels to --launch-log)")
+    ap.add_argument("--no-rocprof", action="store_true",
+                    help="do not run the live rocprofv3 passes (rooflines from events only)")
+    ap.add_argument("--profile-out", default=None, metavar="DIR",
+                    help="write markdown summaries of the live rocprofv3 passes to DIR")
     ap.add_argument("--summarize", default=None, metavar="DIR",
                     help="print a markdown summary of rocprofv3 CSV output under DIR")
     ap.add_argument("--title", default="")
@@ -355,6 +428,20 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
+    child = args.pmc_pass or args.kernel_pass
+    if child:
+        prof = {}
+    elif args.no_rocprof:
+        prof = {"error": "not run (--no-rocprof)"}
+    else:
+        # before this process touches the GPU: the children are profiled
+        # processes of their own
+        prof = run_profiler(args)
+        if "error" in prof:
+            log(f"[bench] rocprofv3 passes: {prof['error']}")
+        elif args.profile_out:
+            write_profiles(prof, args.profile_out)
+
     import numpy as np
     import torch
 
@@ -366,7 +453,10 @@ def main():
     cb = nf4.nf4_codebook()  # the library's default table (host computation)
     s = torch.cuda.Stream()
     if args.pmc_pass:
-        pmc_pass(torch, nf4, cb, args.seed, s)
+        pmc_pass(torch, nf4, cb, args, s)
+        return
+    if args.kernel_pass:
+        kernel_pass(torch, nf4, cb, args, s)
         return
 
     t0 = time.perf_counter()
@@ -416,20 +506,14 @@ def main():
         launches += [("gemv", n) for n in decode_labels()] + \
                     [("gemm", n) for n in prefill_labels()]
 
-    # ---- dominant kernels, timed alone before the steps: the 28 gate|up
-    # launches back to back
+    # ---- dominant kernels, timed alone before the steps (the same
+    # sequence the live rocprofv3 kernel trace times)
     name, N, K = DOMINANT
     reps = args.dominant_replays
-    # (each launch hints the next layer's gate|up, as the launch before a
-    # gate|up in a decode step hints it)
-    gemv_ms = graph_ms(torch, s, lambda: [mdl.gemv(name, l, (name, (l + 1) % LAYERS))
-                                          for l in range(LAYERS)], reps)
-    gemv_us = gemv_ms * 1e3 / LAYERS
-    launches += [("gemv", name)] * (LAYERS * (reps + 1))
-    gemm_ms = graph_ms(torch, s, lambda: [mdl.gemm(name, l) for l in range(LAYERS)], reps)
-    gemm_us = gemm_ms * 1e3 / LAYERS
-    launches += [("gemm", name)] * (LAYERS * (reps + 1))
-    log(f"[bench] dominant {name}: gemv {gemv_us:.2f} us, gemm {gemm_us:.2f} us per launch")
+    dom = dominant(torch, s, mdl, None, reps, launches)
+    gemv_us, gemm_us = dom["nf4_gemv_us"], dom["nf4_gemm_us"]
+    log(f"[bench] dominant {name}: gemv {gemv_us:.2f} us, gemm {gemm_us:.2f} us per launch "
+        "(events)")
     # ---- the decode step with two slots (M = 2), same read-ahead hints
     def decode_step_m2():
         for i, (nm, layer) in enumerate(decode_order):
@@ -463,7 +547,7 @@ def main():
                 nf4.nf4_gemm(mdl.xp[pw.K], TAIL_M, pw.qweight, pw.absmax, cb, pw.N, pw.K,
                              mdl.yp[lname], mdl.ws, mdl.ws_bytes)
     tail_ms = graph_ms(torch, s, tail_step, reps)
-    launches += [("gemm", n) for _ in range(reps + 1) for n in prefill_labels()]
+    launches += [("gemm", "t113:" + n) for _ in range(reps + 1) for n in prefill_labels()]
     tail_flop = 2 * TAIL_M * sum(N_ * K_ for _, N_, K_ in LINEARS) * LAYERS
     log(f"[bench] prefill tail M={TAIL_M}: {tail_ms:.3f} ms")
     # ---- one 29-row chunk of streamed input through the same linears
@@ -474,7 +558,7 @@ def main():
                 nf4.nf4_gemm(mdl.xp[pw.K], CHUNK_M, pw.qweight, pw.absmax, cb, pw.N, pw.K,
                              mdl.yp[lname], mdl.ws, mdl.ws_bytes)
     chunk_ms = graph_ms(torch, s, chunk_step, reps)
-    launches += [("gemm", n) for _ in range(reps + 1) for n in prefill_labels()]
+    launches += [("gemm", "c29:" + n) for _ in range(reps + 1) for n in prefill_labels()]
     chunk_flop = 2 * CHUNK_M * sum(N_ * K_ for _, N_, K_ in LINEARS) * LAYERS
     chunk_bytes = sum(packed_bytes(N_, K_) for _, N_, K_ in LINEARS) * LAYERS
     log(f"[bench] prefill chunk M={CHUNK_M}: {chunk_ms:.3f} ms")
@@ -608,9 +692,7 @@ def main():
     dec_gbps = decode_bytes / (dec_ms * 1e-3) / 1e9
     pre_tflops = prefill_flop / (pre_ms * 1e-3) / 1e12
     gv_bytes = packed_bytes(N, K)
-    gv_gbps = gv_bytes / (gemv_us * 1e-6) / 1e9
     gm_flop = 2 * PREFILL_M * N * K
-    gm_tflops = gm_flop / (gemm_us * 1e-6) / 1e12
     out = {
         "metric": METRIC, "value": round(dec_gbps, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 3),
@@ -631,11 +713,9 @@ def main():
         "prefill": {"value": round(pre_tflops, 2), "unit": "TFLOP/s", "ms": round(pre_ms, 3),
                     "ms_median": round(float(np.median(pre_all)), 3),
                     "ms_min": round(float(np.min(pre_all)), 3)},
-        "roofline": {"bound": "hbm", "achieved": round(gv_gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(gv_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic_bytes("gemv"),
-                     "kernel": f"nf4_gemv gate|up N={N} K={K} M=1",
-                     "algorithmic_bytes": gv_bytes, "launch_us": round(gemv_us, 2)},
+        "roofline": roofline_entry(prof, "dom:" + name, gemv_us, gv_bytes, HBM_PEAK_GBPS, "GB/s",
+                                   "hbm", f"nf4_gemv gate|up N={N} K={K} M=1",
+                                   "algorithmic_bytes"),
         "prefill_tail": {"M": TAIL_M, "ms": round(tail_ms, 3),
                          "value": round(tail_flop / (tail_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
                          "note": "28 layers x 4 fused linears at M=113 (skinny path for narrow N)"},
@@ -673,26 +753,24 @@ def main():
         "lm_head_argmax": {"gemv_us": round(head_us, 2), "gemv_argmax_us": round(head_amx_us, 2),
                            "host_copy_bytes": {"logits": 4 * VOCAB, "index": 4},
                            "kernel": f"nf4_gemv_argmax N={VOCAB} K={HIDDEN} M=1"},
-        "roofline_prefill": {"bound": "mfma", "achieved": round(gm_tflops, 2),
-                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                             "frac": round(gm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                             "traffic": traffic_bytes("gemm"),
-                             "kernel": f"nf4_gemm gate|up N={N} K={K} M={PREFILL_M}",
-                             "algorithmic_flop": gm_flop, "launch_us": round(gemm_us, 2)},
+        "roofline_prefill": roofline_entry(prof, "dom:" + name, gemm_us, gm_flop,
+                                           MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", "mfma",
+                                           f"nf4_gemm gate|up N={N} K={K} M={PREFILL_M}",
+                                           "algorithmic_flop"),
     }
     if not args.no_int4:
         del g_dec, g_pre
-        out["int4_group128"] = int4_leg(torch, nf4, args, s, mdl, launches)
+        out["int4_group128"] = int4_leg(torch, nf4, args, s, mdl, launches, prof)
         if args.launch_log:
             with open(args.launch_log, "w") as f:
                 json.dump(launches, f)
     if not args.no_cpu:
         log("[bench] timing the CPU oracle baseline")
-        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
 
 
-def int4_leg(torch, nf4, args, s, mdl, launches):
+def int4_leg(torch, nf4, args, s, mdl, launches, prof):
     """Decode (M=1) and prefill (M=1024) steps and the gate|up rooflines for
     the int4 group-128 format; launch labels go to `launches` as int4:<linear>."""
     import numpy as np
@@ -736,14 +814,10 @@ def int4_leg(torch, nf4, args, s, mdl, launches):
     launches += ([("gemv", n) for n in dec_labels] + [("gemm", n) for n in pre_labels]) \
         * args.warmup
     name, N, K = DOMINANT
-    reps = args.dominant_replays
-    gemv_us = graph_ms(torch, s, lambda: [amdl.gemv(name, l, (name, (l + 1) % LAYERS))
-                                          for l in range(LAYERS)], reps) * 1e3 / LAYERS
-    launches += [("gemv", "int4:" + name)] * (LAYERS * (reps + 1))
-    gemm_us = graph_ms(torch, s, lambda: [amdl.gemm(name, l) for l in range(LAYERS)],
-                       reps) * 1e3 / LAYERS
-    launches += [("gemm", "int4:" + name)] * (LAYERS * (reps + 1))
-    log(f"[bench] int4 dominant {name}: gemv {gemv_us:.2f} us, gemm {gemm_us:.2f} us per launch")
+    dom = dominant(torch, s, None, amdl, args.dominant_replays, launches)
+    gemv_us, gemm_us = dom["int4_gemv_us"], dom["int4_gemm_us"]
+    log(f"[bench] int4 dominant {name}: gemv {gemv_us:.2f} us, gemm {gemm_us:.2f} us per launch "
+        "(events)")
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -761,9 +835,7 @@ def int4_leg(torch, nf4, args, s, mdl, launches):
     pre_ms = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in ev]))
     log(f"[bench] int4 {args.steps} timed steps: decode {dec_ms:.3f} ms, prefill {pre_ms:.3f} ms")
     gv_bytes = awq_packed_bytes(N, K)
-    gv_gbps = gv_bytes / (gemv_us * 1e-6) / 1e9
     gm_flop = 2 * PREFILL_M * N * K
-    gm_tflops = gm_flop / (gemm_us * 1e-6) / 1e12
     del g_dec, g_pre, amdl
     torch.cuda.empty_cache()
     return {
@@ -773,24 +845,58 @@ def int4_leg(torch, nf4, args, s, mdl, launches):
         "prefill": {"value": round(prefill_flop / (pre_ms * 1e-3) / 1e12, 2),
                     "unit": "TFLOP/s", "ms": round(pre_ms, 3),
                     "note": "each nf4_awq_gemm = x-sum pre-pass + GEMM kernel"},
-        "roofline": {"bound": "hbm", "achieved": round(gv_gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(gv_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic_bytes("awq_gemv"),
-                     "kernel": f"nf4_awq_gemv gate|up N={N} K={K} M=1",
-                     "algorithmic_bytes": gv_bytes, "launch_us": round(gemv_us, 2)},
-        "roofline_prefill": {"bound": "mfma", "achieved": round(gm_tflops, 2),
-                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                             "frac": round(gm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                             "traffic": traffic_bytes("awq_gemm"),
-                             "kernel": f"nf4_awq_gemm gate|up N={N} K={K} M={PREFILL_M}",
-                             "algorithmic_flop": gm_flop, "launch_us": round(gemm_us, 2)},
+        "roofline": roofline_entry(prof, "dom:int4:" + name, gemv_us, gv_bytes, HBM_PEAK_GBPS,
+                                   "GB/s", "hbm", f"nf4_awq_gemv gate|up N={N} K={K} M=1",
+                                   "algorithmic_bytes"),
+        "roofline_prefill": roofline_entry(prof, "dom:int4:" + name, gemm_us, gm_flop,
+                                           MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", "mfma",
+                                           f"nf4_awq_gemm gate|up N={N} K={K} M={PREFILL_M}",
+                                           "algorithmic_flop"),
     }
 
 
-def pmc_pass(torch, nf4, cb, seed, s):
-    """Counter workload, each step synchronized: a plain copy of 1 GiB
-    (counter calibration), then three gate|up GEMVs on distinct weights and
-    one gate|up GEMM, and down at M=29 (the narrow kernel, K in two parts)."""
+def dominant(torch, s, mdl, amdl, reps, launches):
+    """The dominant kernels timed alone, at a fixed point of a run (after the
+    weights are packed and one warm-up replay): 28 gate|up GEMV launches on
+    the 28 layers' distinct matrices replayed back to back in one graph, each
+    naming the next as its read-ahead hint as in a decode step, then the 28
+    gate|up GEMMs (M = 1024) the same way; `reps` timed replays each, events
+    on the launch stream around each replay, the median replay / 28 per
+    launch.  amdl: the same for the int4 group-128 format (or None)."""
+    name = DOMINANT[0]
+    res = {}
+    for fmt, m in (("nf4", mdl), ("int4", amdl)):
+        if m is None:
+            continue
+        tag = "dom:" if fmt == "nf4" else "dom:int4:"
+        res[fmt + "_gemv_us"] = graph_ms(
+            torch, s, lambda: [m.gemv(name, l, (name, (l + 1) % LAYERS)) for l in range(LAYERS)],
+            reps) * 1e3 / LAYERS
+        launches += [("gemv", tag + name)] * (LAYERS * (reps + 1))
+        res[fmt + "_gemm_us"] = graph_ms(torch, s, lambda: [m.gemm(name, l) for l in range(LAYERS)],
+                                         reps) * 1e3 / LAYERS
+        launches += [("gemm", tag + name)] * (LAYERS * (reps + 1))
+    return res
+
+
+def kernel_pass(torch, nf4, cb, args, s):
+    """Workload of the live rocprofv3 kernel-trace run: the dominant kernels
+    of both formats exactly as the main run times them (dominant())."""
+    mdl = Model(torch, nf4, cb, args.seed, s, with_head=False, only=("gate_up",))
+    amdl = AwqModel(torch, nf4, args.seed, s, mdl, with_head=False, only=("gate_up",))
+    launches = []
+    res = dominant(torch, s, mdl, amdl, args.dominant_replays, launches)
+    with open(args.launch_log, "w") as f:
+        json.dump(launches, f)
+    log(f"[bench] kernel pass: {res}")
+
+
+def pmc_pass(torch, nf4, cb, args, s):
+    """Counter workload, each step synchronized: a plain device copy of 1 GiB
+    (counter calibration), then three gate|up GEMVs on distinct weights, each
+    naming the next as its hint, and one gate|up GEMM, in both formats; then
+    down at M = 29."""
+    launches = []
     src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -798,28 +904,27 @@ def pmc_pass(torch, nf4, cb, seed, s):
     torch.cuda.synchronize()
     del src, dst
     torch.cuda.empty_cache()
-    mdl = Model(torch, nf4, cb, seed, s, layers=3, with_head=False, only=("gate_up",))
-    with torch.cuda.stream(s):
-        for layer in range(3):
-            mdl.gemv("gate_up", layer, ("gate_up", (layer + 1) % 3))
+    mdl = Model(torch, nf4, cb, args.seed, s, layers=3, with_head=False, only=("gate_up",))
+    amdl = AwqModel(torch, nf4, args.seed, s, mdl, layers=3, with_head=False, only=("gate_up",))
+    for tag, m in (("pmc:", mdl), ("pmc:int4:", amdl)):
+        with torch.cuda.stream(s):
+            for layer in range(3):
+                m.gemv("gate_up", layer, ("gate_up", (layer + 1) % 3))
+                s.synchronize()
+                launches.append(("gemv", tag + "gate_up"))
+            m.gemm("gate_up", 0)
             s.synchronize()
-        mdl.gemm("gate_up", 0)
-        s.synchronize()
-    dmdl = Model(torch, nf4, cb, seed, s, layers=1, with_head=False, only=("down",))
+            launches.append(("gemm", tag + "gate_up"))
+    # the 29-row chunk through down (the narrow kernel, K in two parts)
+    dmdl = Model(torch, nf4, cb, args.seed, s, layers=1, with_head=False, only=("down",))
     pw = dmdl.weights[0]["down"]
     with torch.cuda.stream(s):
         nf4.nf4_gemm(dmdl.xp[pw.K], CHUNK_M, pw.qweight, pw.absmax, cb, pw.N, pw.K,
                      dmdl.yp["down"], dmdl.ws, dmdl.ws_bytes)
         s.synchronize()
-    del dmdl
-    torch.cuda.empty_cache()
-    amdl = AwqModel(torch, nf4, seed, s, mdl, layers=3, with_head=False, only=("gate_up",))
-    with torch.cuda.stream(s):
-        for layer in range(3):
-            amdl.gemv("gate_up", layer, ("gate_up", (layer + 1) % 3))
-            s.synchronize()
-        amdl.gemm("gate_up", 0)
-        s.synchronize()
+    launches.append(("gemm", "pmc:c29:down"))
+    with open(args.launch_log, "w") as f:
+        json.dump(launches, f)
     log("[bench] pmc pass: copy 1 GiB, 3 x gate|up gemv, 1 x gate|up gemm, both formats; "
         "down at M=29")
 
@@ -829,64 +934,321 @@ def _kernel_short(name):
     return name.split("(")[0]
 
 
+_K_OF = {n: K for n, _, K in LINEARS}
+SHAPES = {**{n: (N, K) for n, N, K in LINEARS}, "lm_head": (VOCAB, HIDDEN),
+          **{"vx:" + n: (N, K) for n, N, K in VOXTRAL},
+          **{"u:" + u: (n1 - n0, _K_OF[f]) for u, f, n0, n1 in UNFUSED}}
+GEMM_ROWS = {"": PREFILL_M, "t113:": TAIL_M, "c29:": CHUNK_M}
+
+
+def label_work(kind, label):
+    """(work per launch, unit, peak) of a launch-log label: packed bytes for a
+    GEMV (GB/s against HBM), flop for a GEMM (TFLOP/s against bf16 MFMA)."""
+    lab = label
+    for p in ("dom:", "pmc:"):
+        lab = lab[len(p):] if lab.startswith(p) else lab
+    awq = lab.startswith("int4:")
+    lab = lab[5:] if awq else lab
+    rows = 1
+    if kind == "gemv" and lab.startswith("m2:"):
+        lab = lab[3:]
+    if kind == "gemm":
+        rows = PREFILL_M
+        for p, m in GEMM_ROWS.items():
+            if p and lab.startswith(p):
+                lab, rows = lab[len(p):], m
+    if lab == "lm_head_argmax":
+        lab = "lm_head"
+    if lab not in SHAPES:
+        return None
+    N, K = SHAPES[lab]
+    if kind == "gemv":
+        return (awq_packed_bytes(N, K) if awq else packed_bytes(N, K)), "GB/s", HBM_PEAK_GBPS
+    return 2 * rows * N * K, "TFLOP/s", MFMA_BF16_PEAK_TFLOPS
+
+
 def summarize(args):
-    """Markdown summary of rocprofv3 CSV output: kernel trace (per kernel and
-    linear, using the launch log to label nf4 launches in dispatch order) and
-    counter collection (per kernel, KiB per dispatch)."""
+    """Markdown summary of rocprofv3 CSV output under args.summarize: the
+    per-kernel statistics, the nf4 dispatches per launch-log label (mean
+    duration and the rate it gives against the peak), and counter values."""
     print(f"# {args.title}\n\nCommand (from the repository root, on one MI355X):\n\n```\n"
           f"{args.command}\n```\n")
-    stats = glob.glob(os.path.join(args.summarize, "**", "*kernel_stats.csv"), recursive=True)
-    for st in stats:
+    for r0 in [_csvs(args.summarize, "kernel_stats.csv")]:
+        if not r0:
+            continue
         print("rocprofv3 --stats, per kernel:\n")
         print("| kernel | calls | total ms | mean us | min us | max us | % of GPU time |")
         print("|---|---|---|---|---|---|---|")
-        for r in csv.DictReader(open(st)):
+        for r in r0:
             print(f"| `{_kernel_short(r['Name'])[:60]}` | {r['Calls']} | "
                   f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['AverageNs']) / 1e3:.2f} | "
                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                   f"{float(r['Percentage']):.2f} |")
         print()
-    traces = glob.glob(os.path.join(args.summarize, "**", "*kernel_trace.csv"), recursive=True)
-    if traces:
-        rows = []
-        for t in traces:
-            rows += list(csv.DictReader(open(t)))
-        rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-        labels = json.load(open(args.launch_log)) if args.launch_log else None
-        nf4_rows = [r for r in rows if "nf4::" in r["Kernel_Name"] and
-                    ("gemv" in r["Kernel_Name"] or "gemm" in r["Kernel_Name"])]
-        if labels is not None:
-            assert len(labels) == len(nf4_rows), (len(labels), len(nf4_rows))
-        d = collections.defaultdict(list)
-        for i, r in enumerate(nf4_rows):
-            lab = labels[i][1] if labels else ""
-            d[(_kernel_short(r["Kernel_Name"]), lab)].append(
-                int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-        print("Per kernel and linear (nf4 launches labelled in dispatch order from the "
-              "launch log):\n")
-        print("| kernel | linear | calls | mean us | median us | min us | total ms |")
-        print("|---|---|---|---|---|---|---|")
-        for (k, lab), v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
-            v.sort()
-            print(f"| `{k}` | {lab} | {len(v)} | {sum(v) / len(v) / 1e3:.2f} | "
-                  f"{v[len(v) // 2] / 1e3:.2f} | {v[0] / 1e3:.2f} | {sum(v) / 1e6:.3f} |")
+    if args.launch_log and _csvs(args.summarize, "kernel_trace.csv"):
+        d = labelled_durations(args.summarize, args.launch_log)
+        print("nf4 launches per label (dispatch order matched to the launch log); rate = "
+              "algorithmic work per launch / mean duration:\n")
+        print("| entry | label | kernel | calls | mean us | median us | min us | rate | of peak |")
+        print("|---|---|---|---|---|---|---|---|---|")
+        for (kind, lab), (names, v) in sorted(d.items(), key=lambda kv: -sum(kv[1][1])):
+            v = sorted(v)
+            mean = sum(v) / len(v) / 1e3
+            w = label_work(kind, lab)
+            rate = frac = ""
+            if w:
+                scale = 1e9 if w[1] == "GB/s" else 1e12
+                r = w[0] / (mean * 1e-6) / scale
+                rate, frac = f"{r:.1f} {w[1]}", f"{r / w[2]:.3f}"
+            print(f"| {kind} | {lab} | `{', '.join(sorted(names))[:48]}` | {len(v)} | {mean:.2f} | "
+                  f"{v[len(v) // 2] / 1e3:.2f} | {v[0] / 1e3:.2f} | {rate} | {frac} |")
         print()
-    counters = glob.glob(os.path.join(args.summarize, "**", "*counter_collection.csv"),
-                         recursive=True)
+    counters = _csvs(args.summarize, "counter_collection.csv")
     if counters:
         d = collections.defaultdict(list)
-        for c in counters:
-            for r in csv.DictReader(open(c)):
-                kn = r["Kernel_Name"]
-                if not ("copy" in kn.lower() or ("nf4::" in kn and ("gemv" in kn or "gemm" in kn))):
-                    continue
-                d[(_kernel_short(kn)[:60], r["Counter_Name"])].append(
-                    float(r["Counter_Value"]))
-        print("| kernel | counter | dispatches | values per dispatch |")
+        for r in counters:
+            kn = r["Kernel_Name"]
+            if COPY_KERNEL in kn or _nf4_launch(kn):
+                d[(_kernel_short(kn)[:60], r["Counter_Name"])].append(float(r["Counter_Value"]))
+        print("| kernel | counter | dispatches | values per dispatch (KiB for FETCH_SIZE and "
+              "WRITE_SIZE) |")
         print("|---|---|---|---|")
         for (k, cn), v in d.items():
             print(f"| `{k}` | {cn} | {len(v)} | {', '.join(f'{x:.0f}' for x in v)} |")
         print()
+        mfma_summary(d)
+
+
+def mfma_summary(d):
+    """Derived matrix-core figures per kernel from the SQ counters, when the
+    run took them: MFMA work (MOPS_BF16 x 512 flop), busy cycles per MFMA,
+    MFMA busy (busy cycles over 1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs: the
+    GRBM count is summed over the XCDs), VALU and LDS instructions per MFMA
+    (VALU counts include the MFMAs) and the share of wave cycles in
+    s_waitcnt."""
+    need = ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+            "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_INSTS_LDS",
+            "SQ_INSTS_VALU", "GRBM_GUI_ACTIVE")
+    kernels = sorted({k for k, _ in d})
+    rows = []
+    for k in kernels:
+        if not all((k, c) in d for c in need):
+            continue
+        m = {c: sum(d[(k, c)]) / len(d[(k, c)]) for c in need}
+        if not m["SQ_INSTS_MFMA"]:
+            continue
+        rows.append(
+            f"| `{k}` | {len(d[(k, need[0])])} | {m['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / 1e9:.1f} "
+            f"GFLOP | {m['SQ_VALU_MFMA_BUSY_CYCLES'] / m['SQ_INSTS_MFMA']:.1f} | "
+            f"{100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * m['GRBM_GUI_ACTIVE'] / 8):.1f} % | "
+            f"{m['SQ_INSTS_VALU'] / m['SQ_INSTS_MFMA']:.2f} | "
+            f"{m['SQ_INSTS_LDS'] / m['SQ_INSTS_MFMA']:.2f} | "
+            f"{100 * m['SQ_WAIT_INST_ANY'] / m['SQ_WAVE_CYCLES']:.0f} % "
+            f"({100 * m['SQ_WAIT_INST_LDS'] / m['SQ_WAVE_CYCLES']:.0f} % on LDS) |")
+    if rows:
+        print("Derived, mean per dispatch:\n")
+        print("| kernel | dispatches | MFMA work | busy cycles per MFMA | MFMA busy | "
+              "VALU instr. per MFMA | LDS instr. per MFMA | wave cycles in s_waitcnt |")
+        print("|---|---|---|---|---|---|---|---|")
+        print("\n".join(rows))
+        print()
+
+
+# ---------------------------------------------------------------- rocprofv3
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 1 << 30
+
+
+def _nf4_launch(kernel_name):
+    """Is this dispatch an nf4_gemv / nf4_gemm main kernel (the ones the
+    launch logs label)?"""
+    return "nf4::" in kernel_name and ("gemv" in kernel_name or "gemm" in kernel_name)
+
+
+def _csvs(d, suffix):
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def labelled_durations(d, launch_log):
+    """{(kind, label): (kernel names, [ns per dispatch])} from a kernel trace
+    under d, its nf4 dispatches labelled in dispatch order by the launch log
+    (kind: gemv or gemm, the entry point the label belongs to)."""
+    rows = sorted(_csvs(d, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
+    rows = [r for r in rows if _nf4_launch(r["Kernel_Name"])]
+    labels = json.load(open(launch_log))
+    if len(labels) != len(rows):
+        raise RuntimeError(f"{len(rows)} nf4 dispatches in the trace, {len(labels)} in the log")
+    out = collections.defaultdict(lambda: (set(), []))
+    for (kind, lab), r in zip(labels, rows):
+        out[(kind, lab)][0].add(_kernel_short(r["Kernel_Name"]))
+        out[(kind, lab)][1].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return dict(out)
+
+
+def labelled_counters(d, launch_log, counter):
+    """({(kind, label): [KiB per dispatch]}, copy kernel KiB) from a counter
+    run."""
+    rows = [r for r in _csvs(d, "counter_collection.csv") if r["Counter_Name"] == counter]
+    key = "Dispatch_Id" if rows and "Dispatch_Id" in rows[0] else "Correlation_Id"
+    rows.sort(key=lambda r: int(r[key]))
+    copy = [float(r["Counter_Value"]) for r in rows if COPY_KERNEL in r["Kernel_Name"]]
+    rows = [r for r in rows if _nf4_launch(r["Kernel_Name"])]
+    labels = json.load(open(launch_log))
+    if len(labels) != len(rows):
+        raise RuntimeError(f"{len(rows)} nf4 dispatches counted, {len(labels)} in the log")
+    out = collections.defaultdict(list)
+    for (kind, lab), r in zip(labels, rows):
+        out[(kind, lab)].append(float(r["Counter_Value"]))
+    return dict(out), (copy[0] if copy else None)
+
+
+def run_profiler(args):
+    """rocprofv3 on child runs of this script, started before this process
+    touches the GPU: a kernel trace of --kernel-pass (the dominant kernels'
+    mean durations) and two counter runs of --pmc-pass (FETCH_SIZE, then
+    WRITE_SIZE, each calibrated on a plain 1 GiB copy: counter KiB per byte
+    read or written).  Returns the parsed results, or {"error": ...}."""
+    exe = shutil.which("rocprofv3") or "/opt/rocm/bin/rocprofv3"
+    if not os.path.exists(exe):
+        return {"error": "rocprofv3 not found"}
+    base = tempfile.mkdtemp(prefix="nf4_bench_rocprof_", dir="/tmp")
+    env = dict(os.environ, TMPDIR="/tmp")
+    me = os.path.abspath(__file__)
+    runs = {
+        "trace": (["--kernel-trace", "--stats"], "--kernel-pass", 900),
+        "fetch": (["--pmc", "FETCH_SIZE"], "--pmc-pass", 600),
+        "write": (["--pmc", "WRITE_SIZE"], "--pmc-pass", 600),
+    }
+    res = {"dir": base, "commands": {}}
+    for key, (opts, mode, limit) in runs.items():
+        d = os.path.join(base, key)
+        lg = os.path.join(base, key + "_launches.json")
+        cmd = [exe, *opts, "--output-format", "csv", "-d", d, "-o", "run", "--", sys.executable,
+               me, mode, "--launch-log", lg, "--seed", str(args.seed),
+               "--dominant-replays", str(args.dominant_replays)]
+        res["commands"][key] = "cd /tmp && " + " ".join(cmd)
+        log(f"[bench] rocprofv3 {key}: {' '.join(opts)} on {mode}")
+        t0 = time.perf_counter()
+        try:
+            p = subprocess.run(cmd, cwd="/tmp", env=env, timeout=limit, capture_output=True,
+                               text=True)
+            rc = p.returncode
+        except subprocess.TimeoutExpired:
+            return {"error": f"rocprofv3 {key} run timed out after {limit} s"}
+        log(f"[bench] rocprofv3 {key}: exit {rc} in {time.perf_counter() - t0:.0f} s")
+        # rocprofv3 may end with a fault of its own after the program's last
+        # line; the results are used whenever the program's log is complete
+        if not os.path.exists(lg):
+            tail = (p.stderr or "")[-800:]
+            return {"error": f"rocprofv3 {key} run failed (exit {rc}): {tail}"}
+        try:
+            if key == "trace":
+                res["trace"] = labelled_durations(d, lg)
+            else:
+                res[key] = labelled_counters(d, lg, "FETCH_SIZE" if key == "fetch" else
+                                             "WRITE_SIZE")
+        except (RuntimeError, KeyError, ValueError) as e:
+            return {"error": f"rocprofv3 {key}: {e}"}
+    return res
+
+
+def write_profiles(prof, outdir):
+    """Markdown summary of the live rocprofv3 passes (kernel trace and the two
+    counter runs, with the traffic derived from them) into outdir."""
+    import contextlib
+    import io
+    import types
+    os.makedirs(outdir, exist_ok=True)
+    buf = io.StringIO()
+    with contextlib.redirect_stdout(buf):
+        for key, title in (("trace", "kernel trace of the dominant kernels (--kernel-pass)"),
+                           ("fetch", "FETCH_SIZE per dispatch (--pmc-pass)"),
+                           ("write", "WRITE_SIZE per dispatch (--pmc-pass)")):
+            ns = types.SimpleNamespace(
+                summarize=os.path.join(prof["dir"], key),
+                launch_log=os.path.join(prof["dir"], key + "_launches.json") if key == "trace"
+                else None,
+                title=title, command=prof["commands"][key])
+            summarize(ns)
+        (fd, fcopy), (wd, wcopy) = prof["fetch"], prof["write"]
+        print("# HBM traffic per launch\n")
+        print(f"Calibration on the plain 1 GiB device copy ({COPY_KERNEL}, reads and writes "
+              f"1 GiB): FETCH_SIZE {fcopy:.0f} KiB, WRITE_SIZE {wcopy:.0f} KiB; each counter is "
+              "scaled by 1 GiB over its reading.\n")
+        print("| entry | label | FETCH_SIZE KiB (mean) | WRITE_SIZE KiB (mean) | traffic MB | "
+              "algorithmic | traffic / algorithmic |")
+        print("|---|---|---|---|---|---|---|")
+        for key in sorted(fd):
+            f, w = fd[key], wd.get(key, [0.0])
+            t = traffic_bytes(prof, key)
+            work = label_work(*key)
+            alg = ""
+            ratio = ""
+            if work and work[1] == "GB/s":
+                alg, ratio = f"{work[0] / 1e6:.2f} MB packed weight", f"{t / work[0]:.3f}"
+            elif work:
+                # weight + x + y bytes of an M = 1024 (or labelled M) GEMM
+                rows = work[0] // (2 * SHAPES[key[1].split(":")[-1]][0] *
+                                   SHAPES[key[1].split(":")[-1]][1])
+                N, K = SHAPES[key[1].split(":")[-1]]
+                bts = (awq_packed_bytes(N, K) if "int4:" in key[1] else packed_bytes(N, K)) \
+                    + rows * K * 2 + rows * N * 4
+                alg, ratio = f"{bts / 1e6:.2f} MB (weight + x + y)", f"{t / bts:.3f}"
+            print(f"| {key[0]} | {key[1]} | {sum(f) / len(f):.0f} | {sum(w) / len(w):.0f} | "
+                  f"{t / 1e6:.2f} | {alg} | {ratio} |")
+        print()
+    text = buf.getvalue().replace(prof["dir"], "<tmp>").replace(ROOT, "<repo>").replace(
+        sys.executable, "python3")
+    path = os.path.join(outdir, "dominant_kernels_gate_up.md")
+    with open(path, "w") as fh:
+        fh.write(f"Made by `python bench.py --profile-out {outdir}` on one MI355X, which runs "
+                 "the three rocprofv3 commands below as child processes before it touches the "
+                 "GPU itself (<tmp>: a fresh temporary directory).\n\n" + text)
+    log(f"[bench] wrote {path}")
+
+
+def rocprof_mean_us(prof, key):
+    """(mean us, kernel names) of the dispatches of key = (kind, label), or
+    (None, None)."""
+    if "trace" not in prof or key not in prof["trace"]:
+        return None, None
+    names, v = prof["trace"][key]
+    return sum(v) / len(v) / 1e3, sorted(names)
+
+
+def traffic_bytes(prof, key):
+    """HBM bytes per launch of the labelled pmc dispatches: mean FETCH_SIZE
+    and WRITE_SIZE, each scaled by the counter's reading on the 1 GiB copy
+    (which reads 1 GiB and writes 1 GiB)."""
+    try:
+        (fd, fcopy), (wd, wcopy) = prof["fetch"], prof["write"]
+        f, w = fd[key], wd[key]
+    except (KeyError, TypeError):
+        return None
+    if not fcopy or not wcopy:
+        return None
+    return int(sum(f) / len(f) * COPY_BYTES / fcopy + sum(w) / len(w) * COPY_BYTES / wcopy)
+
+
+def roofline_entry(prof, label, event_us, work, peak, unit, bound, kernel, work_key):
+    """The roofline object: `achieved` is the algorithmic work per launch over
+    the rocprofv3 mean duration of the labelled dispatches (events beside)."""
+    kind = "gemv" if unit == "GB/s" else "gemm"
+    mean_us, names = rocprof_mean_us(prof, (kind, label))
+    t_us = mean_us if mean_us else event_us
+    scale = 1e9 if unit == "GB/s" else 1e12
+    ach = work / (t_us * 1e-6) / scale
+    return {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+            "frac": round(ach / peak, 4),
+            "traffic": traffic_bytes(prof, (kind, label.replace("dom:", "pmc:"))), "kernel": kernel,
+            work_key: work, "rocprof_mean_us": round(mean_us, 3) if mean_us else None,
+            "rocprof_kernels": names, "event_us": round(event_us, 3),
+            "timed_on": ("rocprofv3 kernel trace of `bench.py --kernel-pass` (the same 28-launch "
+                         "graph replays as the event timing)") if mean_us else
+                        "events only (" + prof.get("error", "no rocprofv3 run") + ")"}
 
 
 if __name__ == "__main__":
