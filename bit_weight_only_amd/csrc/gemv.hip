@@ -340,14 +340,14 @@ constexpr int kFastThreads = kFastWaves * 64;  // the launch's block size
 // (readfirstlane keeps it a scalar value, so the selects cannot be folded
 // back into one read at an index that varies by lane).  The 16 codes are
 // contiguous halfwords, code 2 j in the low half of dword j.
-__device__ __forceinline__ uint32_t pick_code(const CodeTerms &ct, int i) {
-  // whole dwords (two codes each): the argument block is read with scalar
-  // loads only in units of dwords
-  const uint32_t *w = reinterpret_cast<const uint32_t *>(&ct.t[0][0]);
+__device__ __forceinline__ uint32_t pick_code(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
+                                              int i) {
+  const uint32_t w[8] = {(uint32_t)c0, (uint32_t)(c0 >> 32), (uint32_t)c1, (uint32_t)(c1 >> 32),
+                         (uint32_t)c2, (uint32_t)(c2 >> 32), (uint32_t)c3, (uint32_t)(c3 >> 32)};
   uint32_t v = 0;
 #pragma unroll
   for (int j = 0; j < 16; j += 2) {
-    const uint32_t pj = __builtin_amdgcn_readfirstlane(w[j >> 1]);
+    const uint32_t pj = w[j >> 1];
     v = i == j ? (pj & 0xFFFFu) : i == j + 1 ? (pj >> 16) : v;
   }
   return v;
@@ -363,8 +363,9 @@ constexpr int kSchedAllButGlobalLoads = 0x1 | 0x2 | 0x4 | 0x8 | 0x80 | 0x100 | 0
 
 template <int M, bool ARGMAX, bool AFF>
 __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
-    const uint16_t *__restrict__ x, const uint4 *__restrict__ qw,
-    const float2 *__restrict__ am, CodeTerms ct, int N, int K, int KT, int G, int P,
+    uint64_t cw0, uint64_t cw1, uint64_t cw2, uint64_t cw3, const uint16_t *__restrict__ x,
+    const uint4 *__restrict__ qw,
+    const float2 *__restrict__ am, int N, int K, int KT, int G, int P,
     float *__restrict__ y, uint32_t *counter, uint64_t *cand, int32_t *index,
     const char *__restrict__ nq, const char *__restrict__ nsb, int nG, int nKT, int nP) {
   constexpr int D = kFastDepth;
@@ -378,12 +379,8 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
   // uses it, and each such block waits for the argument memory again before
   // the first weight load can be issued.  The empty asm statements need the
   // values in registers at this point.
-  {
-    const uint32_t *cw = reinterpret_cast<const uint32_t *>(&ct.t[0][0]);
-    asm volatile("" ::"s"(x), "s"(qw), "s"(am), "s"(y), "s"(nq), "s"(nsb), "s"(N), "s"(K),
-                 "s"(KT), "s"(G), "s"(P), "s"(nG), "s"(nKT), "s"(nP), "s"(cw[0]), "s"(cw[1]),
-                 "s"(cw[2]), "s"(cw[3]), "s"(cw[4]), "s"(cw[5]), "s"(cw[6]), "s"(cw[7]));
-  }
+  asm volatile("" ::"s"(x), "s"(qw), "s"(am), "s"(y), "s"(nq), "s"(nsb), "s"(N), "s"(K),
+               "s"(KT), "s"(G), "s"(P), "s"(nG), "s"(nKT), "s"(nP));
   const int KP = KT * kTileK;                 // padded x row length
   const int XS = KP + kFastSkew;              // x row stride in LDS
   uint16_t *xs = reinterpret_cast<uint16_t *>(lds_dyn);
@@ -497,10 +494,10 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
     // index (c / 8) % 16 = (threadIdx.x / 8) % 16 is fixed per lane, its
     // high one c / 128 = threadIdx.x / 128 + 4 i fixed per wave and step.
     static_assert(kFastTableWords / 8 == 4 * kFastWaves * 64, "four chunks per thread");
-    const uint32_t lo = pick_code(ct, ((int)threadIdx.x >> 3) & 15);
+    const uint32_t lo = pick_code(cw0, cw1, cw2, cw3, ((int)threadIdx.x >> 3) & 15);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t v = lo | pick_code(ct, (wave >> 1) + 4 * i) << 16;
+      const uint32_t v = lo | pick_code(cw0, cw1, cw2, cw3, (wave >> 1) + 4 * i) << 16;
       const int c = (int)threadIdx.x + i * kFastWaves * 64;
       reinterpret_cast<uint4 *>(table)[(c >> 3) * 16 + (c & 7)] = make_uint4(v, v, v, v);
     }
@@ -762,8 +759,16 @@ hipError_t launch_fast(const uint16_t *x, const uint4 *qw, const float2 *am, con
     nKT = (int)tiles_k(next->K);
     nP = fast_plan(M, next->N, next->K, AFF).P;
   }
-  hipLaunchKernelGGL((gemv_fast_kernel<M, ARGMAX, AFF>), dim3(p.P), dim3(kFastWaves * 64), p.lds, s, x,
-                     qw, am, ct, (int)N, (int)K, (int)tiles_k(K), (int)(N / kTileRows), p.P, y,
+  // the first term's 16 codes as four 8-byte arguments ahead of the rest
+  // (code 4 j + i in bits 16 i .. 16 i + 15 of argument j)
+  uint64_t cw[4];
+  for (int j = 0; j < 4; ++j) {
+    cw[j] = 0;
+    for (int i = 0; i < 4; ++i) cw[j] |= (uint64_t)ct.t[0][4 * j + i] << (16 * i);
+  }
+  hipLaunchKernelGGL((gemv_fast_kernel<M, ARGMAX, AFF>), dim3(p.P), dim3(kFastWaves * 64), p.lds, s,
+                     cw[0], cw[1], cw[2], cw[3], x,
+                     qw, am, (int)N, (int)K, (int)tiles_k(K), (int)(N / kTileRows), p.P, y,
                      counter, cand, index, nq, nsb, nG, nKT, nP);
   return hipGetLastError();
 }
