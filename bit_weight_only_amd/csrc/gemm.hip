@@ -947,9 +947,13 @@ namespace skinny {
 constexpr int kWaves = 4;        // row groups per workgroup
 constexpr int kXBuf = 16 * 1024; // bytes of one x chunk buffer (2 workgroups per CU fit)
 }  // namespace skinny
+// Two workgroups per CU (the launch bound caps a lane at 256 registers): at
+// one wave per SIMD each wave's chain of lookups, products and folds is
+// exposed.  The 32-row instance keeps 4 tiles in flight per wave (8 do not
+// fit in 256 registers).
 
 template <int MB, int D, bool AFF, bool SPLIT>
-__global__ __launch_bounds__(64 * skinny::kWaves) void gemm_skinny_kernel(
+__global__ __launch_bounds__(64 * skinny::kWaves, 2) void gemm_skinny_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ qw,
     const float *__restrict__ am, CodeTerms ct, int N, int K, int KT, int G,
     float *__restrict__ y, const float *__restrict__ xsum, int Mp, int np_arg) {
@@ -1647,8 +1651,8 @@ hipError_t launch_awq_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, cons
       np > 1 ? go(gemm_skinny_kernel<1, 8, true, true>, dim3(gx))
              : go(gemm_skinny_kernel<1, 8, true, false>, dim3(gx));
     else
-      np > 1 ? go(gemm_skinny_kernel<2, 8, true, true>, g2)
-             : go(gemm_skinny_kernel<2, 8, true, false>, g2);
+      np > 1 ? go(gemm_skinny_kernel<2, 4, true, true>, g2)
+             : go(gemm_skinny_kernel<2, 4, true, false>, g2);
     return hipGetLastError();
   }
   launch_tile<true>(p, x, M, qw, prf, ct, N, K, y, X, Mp, split_ws, s);
@@ -1690,8 +1694,8 @@ hipError_t launch_skinny(const uint16_t *x, int64_t M, const uint8_t *qw, const 
     np > 1 ? go(gemm_skinny_kernel<1, 8, false, true>, dim3(gx))
            : go(gemm_skinny_kernel<1, 8, false, false>, dim3(gx));
   else
-    np > 1 ? go(gemm_skinny_kernel<2, 8, false, true>, g2)
-           : go(gemm_skinny_kernel<2, 8, false, false>, g2);
+    np > 1 ? go(gemm_skinny_kernel<2, 4, false, true>, g2)
+           : go(gemm_skinny_kernel<2, 4, false, false>, g2);
   return hipGetLastError();
 }
 
