@@ -363,9 +363,8 @@ constexpr int kSchedAllButGlobalLoads = 0x1 | 0x2 | 0x4 | 0x8 | 0x80 | 0x100 | 0
 
 template <int M, bool ARGMAX, bool AFF>
 __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
-    uint64_t cw0, uint64_t cw1, uint64_t cw2, uint64_t cw3, const uint16_t *__restrict__ x,
-    const uint4 *__restrict__ qw,
-    const float2 *__restrict__ am, int N, int K, int KT, int G, int P,
+    const uint4 *__restrict__ qw, const float2 *__restrict__ am, const uint16_t *__restrict__ x,
+    int KT, int G, int P, int K, int N, uint64_t cw0, uint64_t cw1, uint64_t cw2, uint64_t cw3,
     float *__restrict__ y, uint32_t *counter, uint64_t *cand, int32_t *index,
     const char *__restrict__ nq, const char *__restrict__ nsb, int nG, int nKT, int nP) {
   constexpr int D = kFastDepth;
@@ -374,13 +373,14 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
   // dynamic LDS.
   __shared__ __attribute__((aligned(16))) uint32_t table[AFF ? 4 : kFastTableWords];
   extern __shared__ __attribute__((aligned(16))) uint32_t lds_dyn[];
-  // Every argument is read here, in one batch of scalar loads with one wait:
-  // left to itself the compiler reads each argument in the block that first
-  // uses it, and each such block waits for the argument memory again before
-  // the first weight load can be issued.  The empty asm statements need the
-  // values in registers at this point.
-  asm volatile("" ::"s"(x), "s"(qw), "s"(am), "s"(y), "s"(nq), "s"(nsb), "s"(N), "s"(K),
-               "s"(KT), "s"(G), "s"(P), "s"(nG), "s"(nKT), "s"(nP));
+  // The arguments the first weight loads need lead the list, and the build
+  // preloads the first eight arguments into scalar registers at dispatch, so
+  // those loads wait for no read of the argument memory (left to itself the
+  // compiler reads each argument in the block that first uses it, and each
+  // such block waits again).  The empty asm statement needs them in
+  // registers here; the read-ahead cursor, which needs later arguments, is
+  // formed after the prefetch.
+  asm volatile("" ::"s"(x), "s"(qw), "s"(am), "s"(N), "s"(K), "s"(KT), "s"(G), "s"(P));
   const int KP = KT * kTileK;                 // padded x row length
   const int XS = KP + kFastSkew;              // x row stride in LDS
   uint16_t *xs = reinterpret_cast<uint16_t *>(lds_dyn);
@@ -407,14 +407,6 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
   // workgroup index loads first in that launch, so they are in the caches
   // when it starts.  Otherwise, and past that share, they re-read the
   // workgroup's first tile.  Their data is never used.
-  uint32_t pn = 0, ntile_end = 0;
-  if (nq != nullptr && (int)blockIdx.x < nP) {
-    const uint32_t nbase = (uint32_t)nG / (uint32_t)nP, nrem = (uint32_t)nG % (uint32_t)nP;
-    const int ng0 = (int)(wg * nbase + (wg < nrem ? wg : nrem));
-    const int ng1 = ng0 + (int)(nbase + (wg < nrem ? 1u : 0u));
-    pn = (uint32_t)(ng0 * nKT + wave);
-    ntile_end = (uint32_t)(ng1 * nKT);
-  }
 
   // The lane's scales of tile lt: two block scales, or (affine) the params
   // dword in .x.
@@ -457,6 +449,14 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
   // scheduler would otherwise pull the table's selects, which wait for the
   // codebook argument, in between the loads)
   __builtin_amdgcn_sched_barrier(0);
+  uint32_t pn = 0, ntile_end = 0;
+  if (nq != nullptr && (int)blockIdx.x < nP) {
+    const uint32_t nbase = (uint32_t)nG / (uint32_t)nP, nrem = (uint32_t)nG % (uint32_t)nP;
+    const int ng0 = (int)(wg * nbase + (wg < nrem ? wg : nrem));
+    const int ng1 = ng0 + (int)(nbase + (wg < nrem ? 1u : 0u));
+    pn = (uint32_t)(ng0 * nKT + wave);
+    ntile_end = (uint32_t)(ng1 * nKT);
+  }
 
   // Setup, one barrier in all, everything in it overlapping the first
   // tiles' flight.  The x copies are waited for just before the barrier.
@@ -767,8 +767,8 @@ hipError_t launch_fast(const uint16_t *x, const uint4 *qw, const float2 *am, con
     for (int i = 0; i < 4; ++i) cw[j] |= (uint64_t)ct.t[0][4 * j + i] << (16 * i);
   }
   hipLaunchKernelGGL((gemv_fast_kernel<M, ARGMAX, AFF>), dim3(p.P), dim3(kFastWaves * 64), p.lds, s,
-                     cw[0], cw[1], cw[2], cw[3], x,
-                     qw, am, (int)N, (int)K, (int)tiles_k(K), (int)(N / kTileRows), p.P, y,
+                     qw, am, x, (int)tiles_k(K), (int)(N / kTileRows), p.P, (int)K, (int)N,
+                     cw[0], cw[1], cw[2], cw[3], y,
                      counter, cand, index, nq, nsb, nG, nKT, nP);
   return hipGetLastError();
 }
