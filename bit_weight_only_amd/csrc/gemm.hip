@@ -15,7 +15,7 @@
 //     per workgroup, waves of 16 MB x 32, copies straight from global memory
 //     into LDS rings, each wave expanding the code words of its own columns;
 //   gemm_skinny_kernel<MB, D, AFF, SPLIT>  few rows (below);
-//   gemm_narrow_kernel<AFF, SPLIT>  up to 32 rows on a matrix of few row
+//   gemm_narrow_kernel<AFF, SPLIT, LEAD>  up to 32 rows on a matrix of few row
 //     groups, both formats: the waves of a workgroup share one row group;
 //   xsum_kernel           the int4 format's per-group sums of x (pre-pass);
 //   gemm_kernel<3>        any finite codebook (each value split into three
@@ -1188,13 +1188,20 @@ __global__ __launch_bounds__(64 * skinny::kWaves, 2) void gemm_skinny_kernel(
 // acc = fmaf(s, P, acc).  Every output gets the other kernels' operations
 // in their order, so its rows are bit-identical to theirs.
 // x (16 rows x 512 k per window), code words and scales all arrive by copies
-// into LDS rings kLead windows ahead; there are no register loads in the
+// into LDS rings LEAD windows ahead; there are no register loads in the
 // loop, so one explicit count waits for exactly the window about to be used.
 // x row R is copied with its 16-byte chunk c stored at c ^ R, so the 16 rows
 // of an A fragment read fall in 16 bank groups.
-// LDS (bytes): pair table 32 K (32 copies), x ring (kLead + 1) x 16 K, code
-// ring (kLead + 1) x kWaves x 1 K, scale ring (kLead + 1) x kWaves x 128,
-// block products 2 x kWaves x 2 K and their scales 2 x kWaves x 512.
+// LDS (bytes): pair table, x ring (LEAD + 1) x 16 K, code ring (LEAD + 1) x
+// kWaves x 1 K, scale ring (LEAD + 1) x kWaves x 128, block products 2 x
+// kWaves x 2 K and their scales 2 x kWaves x 128.  LEAD 2 with a one-copy
+// table (1 K): 79.5 K, so two workgroups share a CU (8 waves), for grids of
+// more workgroups than CUs; with one per CU the waves, one per SIMD, sat
+// mostly waiting on their chain of LDS reads, products and barriers, and two
+// per CU measured 1.25-1.35 x faster on 29- and 32-row batches.  LEAD 3 with
+// 32 copies (32 K, lane % 32 reads its own) at one workgroup per CU for
+// grids that fit the CUs once: there the replicated table measured 8 %
+// faster on long K than the single copy.
 // Affine variant (AFF, int4 in groups of 128): no pair table (B pairs from
 // the interleaved code words by shift and mask), one product per tile (four
 // MFMAs from zero), 64 bytes of params per tile, and the x sums X[t][m0 ..
@@ -1205,24 +1212,27 @@ __global__ __launch_bounds__(64 * skinny::kWaves, 2) void gemm_skinny_kernel(
 // ---------------------------------------------------------------------------
 namespace narrow {
 constexpr int kWaves = 4;                            // waves per row group = tiles per window
-constexpr int kLead = 3;                             // windows copied ahead
-constexpr int kSlots = kLead + 1;                    // ring slots
 constexpr int kKW = kWaves * kTileK;                 // k per window: 512
 constexpr int kXSlot = 16 * kKW * 2;                 // 16 K
 constexpr int kCSlot = kWaves * kTileBytes;          // 4 K
+constexpr int kCuLds = 160 * 1024;                   // LDS per CU
 static_assert(16 % kWaves == 0, "x rows split evenly over the waves");
 // LDS layout; the affine variant has no pair table, one block product per
 // tile, 64 bytes of params per tile and a ring of the x sums (16 rows per tile)
-template <bool AFF>
+template <bool AFF, int LEAD>
 struct Lay {
+  static constexpr int kSlots = LEAD + 1;             // ring slots
+  // pair-table copies (lane % kCopiesT): 32 at one workgroup per CU, one at two
+  static constexpr int kCopiesT = AFF ? 0 : LEAD == 2 ? 1 : 32;
+  static constexpr int kTable = 256 * 4 * kCopiesT;
   static constexpr int kSBytes = AFF ? kTileRows * 4 : kTileScales * 4;  // scales of a tile
   static constexpr int kSSlot = kWaves * kSBytes;
   static constexpr int kXSSlot = AFF ? kWaves * 16 * 4 : 0;
   static constexpr int kBlocks = AFF ? 1 : 2;         // block products per tile
   static constexpr int kPBuf = kWaves * kBlocks * 1024;
-  static constexpr int kSBuf = kWaves * 64 * 8;
+  static constexpr int kSBuf = kWaves * 16 * 8;     // one float2 per weight row
   static constexpr int kXBuf = AFF ? kWaves * 16 * 4 : 0;
-  static constexpr int kOffX = AFF ? 0 : pipe::kTableBytes;
+  static constexpr int kOffX = kTable;
   static constexpr int kOffC = kOffX + kSlots * kXSlot;
   static constexpr int kOffS = kOffC + kSlots * kCSlot;
   static constexpr int kOffXS = kOffS + kSlots * kSSlot;
@@ -1232,18 +1242,20 @@ struct Lay {
   static constexpr int kBytes = kOffXB + 2 * kXBuf;
   // per wave and window: x rows, code words, scales (and x sums)
   static constexpr int kCopies = 16 / kWaves + 2 + (AFF ? 1 : 0);
-  static_assert(kBytes <= 160 * 1024, "LDS of one workgroup");
-  static_assert((kLead - 1) * kCopies <= 63, "vmcnt range");
+  static_assert(LEAD != 2 || 2 * kBytes <= kCuLds, "LDS of two workgroups");
+  static_assert(kBytes <= kCuLds, "LDS of one workgroup");
+  static_assert((LEAD - 1) * kCopies <= 63, "vmcnt range");
 };
 }  // namespace narrow
 
-template <bool AFF, bool SPLIT>
-__global__ __launch_bounds__(64 * narrow::kWaves) void gemm_narrow_kernel(
+template <bool AFF, bool SPLIT, int LEAD>
+__global__ __launch_bounds__(64 * narrow::kWaves, LEAD == 2 ? 2 : 1) void gemm_narrow_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ qw,
     const float *__restrict__ am, CodeTerms ct, int N, int K, int KT, int G,
     float *__restrict__ y, const float *__restrict__ xsum, int Mp, int np_arg) {
   using namespace narrow;
-  using L = Lay<AFF>;
+  using L = Lay<AFF, LEAD>;
+  constexpr int kSlots = L::kSlots;
   const int np = SPLIT ? np_arg : 1;
   // the only static LDS array: the pair table sits at LDS address 0
   __shared__ __attribute__((aligned(16))) char lds[L::kBytes];
@@ -1305,21 +1317,27 @@ __global__ __launch_bounds__(64 * narrow::kWaves) void gemm_narrow_kernel(
     }
   };
 #pragma unroll
-  for (int jw = 0; jw < kLead; ++jw) copy_window(jw);
+  for (int jw = 0; jw < LEAD; ++jw) copy_window(jw);
 
   // pair table, from the codebook staged in the (not yet used) product buffers
   if constexpr (!AFF) {
     uint16_t *codes16 = reinterpret_cast<uint16_t *>(lds + L::kOffP);
     if (tid < 16) codes16[tid] = ct.t[0][tid];
     __syncthreads();
-    for (int c = tid; c < pipe::kTableBytes / 16; c += 64 * kWaves) {
-      const int e = c / (pipe::kCopies / 4);
+    // entry e, copy c at 4 (e kCopiesT + c); with copies, four per 16-byte
+    // store (each thread's chain of codebook reads stays short)
+    constexpr int kPer = L::kCopiesT >= 4 ? 4 : 1;  // copies per store
+    for (int i = tid; i < 256 * L::kCopiesT / kPer; i += 64 * kWaves) {
+      const int e = i / (L::kCopiesT / kPer);
       const uint32_t v = (uint32_t)codes16[e & 15] | ((uint32_t)codes16[e >> 4] << 16);
-      reinterpret_cast<uint4 *>(lds)[c] = make_uint4(v, v, v, v);
+      if constexpr (kPer == 4)
+        reinterpret_cast<uint4 *>(lds)[i] = make_uint4(v, v, v, v);
+      else
+        reinterpret_cast<uint32_t *>(lds)[i] = v;
     }
   }
+  const uint32_t tcopy = (uint32_t)(lane % (L::kCopiesT > 0 ? L::kCopiesT : 1)) * 4;
 
-  const uint32_t tcopy = (uint32_t)(lane & (pipe::kCopies - 1)) * 4;
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   // products of this wave's tile of window j into buffer j & 1, with the
   // tile's scales (and, affine, its x sums)
@@ -1349,7 +1367,7 @@ __global__ __launch_bounds__(64 * narrow::kWaves) void gemm_narrow_kernel(
           bb[q] = awq_pair(wd, q, 0x3F803F80u);
         } else {
           const uint32_t e = (wd >> (8 * q)) & 0xFFu;
-          bb[q] = *reinterpret_cast<const uint32_t *>(lds + e * (pipe::kCopies * 4) + tcopy);
+          bb[q] = *reinterpret_cast<const uint32_t *>(lds + e * (L::kCopiesT * 4) + tcopy);
         }
       }
       B[jj] = __builtin_bit_cast(bf16x8, make_uint4(bb[0], bb[1], bb[2], bb[3]));
@@ -1372,7 +1390,9 @@ __global__ __launch_bounds__(64 * narrow::kWaves) void gemm_narrow_kernel(
       *reinterpret_cast<f32x4 *>(pb) = p;
       *reinterpret_cast<f32x4 *>(pb + 1024) = q2;
     }
-    *reinterpret_cast<float2 *>(lds + L::kOffSB + (j & 1) * L::kSBuf + wave * 512 + lane * 8) = sv;
+    // the scales of weight row r, once per row
+    if (lane < 16)
+      *reinterpret_cast<float2 *>(lds + L::kOffSB + (j & 1) * L::kSBuf + wave * 128 + lane * 8) = sv;
   };
   // fold window jf: this lane's output is element lane % 4 of output lane
   // 16 wave + lane / 4 (x row m0 + 4 wave + lane % 4, weight row lane / 4)
@@ -1380,7 +1400,7 @@ __global__ __launch_bounds__(64 * narrow::kWaves) void gemm_narrow_kernel(
   int jn = 1, cut = SPLIT ? part_begin(1, KT, np) : -1;
   auto fold = [&](int jf) {
     const char *pb = lds + L::kOffP + (jf & 1) * L::kPBuf + wave * 256 + lane * 4;
-    const char *sb = lds + L::kOffSB + (jf & 1) * L::kSBuf + (16 * wave + (lane >> 2)) * 8;
+    const char *sb = lds + L::kOffSB + (jf & 1) * L::kSBuf + (lane >> 2) * 8;
     const char *xb = lds + L::kOffXB + (jf & 1) * L::kXBuf + (4 * wave + (lane & 3)) * 4;
     // WHOLE: four whole tiles inside K, folded without selects (codebook
     // format; the affine instances measured no faster)
@@ -1396,7 +1416,7 @@ __global__ __launch_bounds__(64 * narrow::kWaves) void gemm_narrow_kernel(
           cut = jn < np ? part_begin(jn, KT, np) : -1;
         }
         const bool live0 = i < KT, live1 = live0 && !(half_tail && i == KT - 1);
-        const float2 s = *reinterpret_cast<const float2 *>(sb + tw * 512);
+        const float2 s = *reinterpret_cast<const float2 *>(sb + tw * 128);
         if constexpr (AFF) {
           // 16 s and -(16 + z)/16 from the params dword (binary16 s | z << 16)
           const uint32_t pv = __float_as_uint(s.x);
@@ -1425,8 +1445,8 @@ __global__ __launch_bounds__(64 * narrow::kWaves) void gemm_narrow_kernel(
   for (int j = 0; j < NW; ++j) {
     // window j's copies have landed for every wave, and the products of
     // window j - 1 are in LDS
-    pipe::wait_copies_and_barrier<(kLead - 1) * L::kCopies>();
-    copy_window(j + kLead);  // into the slot window j - 1 used
+    pipe::wait_copies_and_barrier<(LEAD - 1) * L::kCopies>();
+    copy_window(j + LEAD);  // into the slot window j - 1 used
     compute(j);
     if (j > 0) fold(j - 1);
   }
@@ -1489,6 +1509,9 @@ constexpr int64_t kNarrowMaxM = 32;
 bool prefer_narrow(int64_t M, int64_t N, int64_t K) {
   return M <= kNarrowMaxM && N / kTileRows <= kNarrowMaxG && tile_dma_ok(M, N, K);
 }
+// Narrow launches: three windows ahead at one workgroup per CU when the grid
+// fits the CUs once, else two windows ahead at two per CU.
+inline bool narrow_long_lead(int64_t blocks) { return blocks <= device_cu_count(); }
 
 // The skinny kernel rather than the tiled one (bit-identical rows, so the
 // choice is about speed only): up to 64 rows, and up to 256 rows when the
@@ -1637,7 +1660,10 @@ hipError_t launch_awq_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, cons
         hipLaunchKernelGGL(kern, grid, block, 0, s, x, (int)M, qw, prf, ct, (int)N, (int)K,
                            (int)KT, (int)G, y, X, (int)Mp, np);
       };
-      np > 1 ? go(gemm_narrow_kernel<true, true>) : go(gemm_narrow_kernel<true, false>);
+      if (narrow_long_lead((int64_t)grid.x * grid.y))
+        np > 1 ? go(gemm_narrow_kernel<true, true, 3>) : go(gemm_narrow_kernel<true, false, 3>);
+      else
+        np > 1 ? go(gemm_narrow_kernel<true, true, 2>) : go(gemm_narrow_kernel<true, false, 2>);
       return hipGetLastError();
     }
     const unsigned gx = (unsigned)((G + skinny::kWaves - 1) / skinny::kWaves);
@@ -1675,7 +1701,10 @@ hipError_t launch_skinny(const uint16_t *x, int64_t M, const uint8_t *qw, const 
       hipLaunchKernelGGL(kern, grid, block, 0, s, x, (int)M, qw, am, ct, (int)N, (int)K,
                          (int)tiles_k(K), (int)G, y, nullptr, 0, np);
     };
-    np > 1 ? go(gemm_narrow_kernel<false, true>) : go(gemm_narrow_kernel<false, false>);
+    if (narrow_long_lead((int64_t)grid.x * grid.y))
+      np > 1 ? go(gemm_narrow_kernel<false, true, 3>) : go(gemm_narrow_kernel<false, false, 3>);
+    else
+      np > 1 ? go(gemm_narrow_kernel<false, true, 2>) : go(gemm_narrow_kernel<false, false, 2>);
     return hipGetLastError();
   }
   const unsigned gx = (unsigned)((G + skinny::kWaves - 1) / skinny::kWaves);
