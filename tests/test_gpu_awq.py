@@ -178,12 +178,14 @@ def test_awq_zero_point_cancellation(side, kind):
     say(f"  rel-L2 {rel:.2e}, worst element {worst:.3f} x bar")
 
 
-@pytest.mark.parametrize("N,K", [(272, 1024), (272, 8320)])
+@pytest.mark.parametrize("N,K", [(272, 1024), (272, 8320), (4608, 3584), (4608, 8192)])
 def test_awq_gemm_deterministic_and_batch_independent(side, N, K):
     """Rows do not depend on the batch: 300 rows take the tiled path, up to
     32 rows the narrow path, 33 the skinny path (K = 8320, N = 272: summed
-    in 10 parts on every path), and a reused workspace full of stale bytes
-    gives the same bits (every call sets what it reads)."""
+    in 10 parts on every path; N = 4608: the narrow form with two
+    workgroups per CU, K in one part and, at K = 8192, in two), and a reused
+    workspace full of stale bytes gives the same bits (every call sets what
+    it reads)."""
     packed, scales, zeros, aw = awq_case(side, N, K, mid=34)
     x = synth.activations(0, 300, K, stream=12)
     y1 = side.awq_run("gemm", x, aw)

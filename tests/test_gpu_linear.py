@@ -149,7 +149,7 @@ def test_deterministic_and_batch_independent(side, cb, kind):
 
 
 @pytest.mark.parametrize("N,K", [(512, 3584), (256, 18944), (272, 704), (272, 8256),
-                                 (512, 8192), (4608, 3584), (16, 18944)])
+                                 (512, 8192), (4608, 3584), (4608, 8192), (16, 18944)])
 def test_gemm_skinny_and_tiled_rows_identical(side, cb, N, K):
     """nf4_gemm runs a batch of up to 32 rows on the narrow path (these
     matrices have at most 1024 row groups: the four waves of a workgroup
@@ -159,7 +159,10 @@ def test_gemm_skinny_and_tiled_rows_identical(side, cb, N, K):
     output, so rows agree bit for bit whichever path the batch size selects
     (K = 704 and 8256 end in a half tile).  K is summed in the same parts on
     every path (k_parts: 1 to 32 here), on separate workgroups of the tiled
-    path and one after the other in the other two."""
+    path and one after the other in the other two.  Narrow grids of more
+    workgroups than CUs (N = 4608: 288 row groups per 16-row block) take
+    the form with two workgroups per CU, K in one part (K = 3584) and in two
+    (K = 8192); smaller grids the form with one."""
     packed, absmax, pw = case(side, cb, N, K, mid=27)
     x = synth.activations(0, 300, K, stream=3)
     yt = side.run("gemm", x, pw, cb)            # 300 rows: tiled
