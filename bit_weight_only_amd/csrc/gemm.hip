@@ -14,7 +14,7 @@
 //     default one) and the asymmetric int4 format (AFF): 128 x 16 RG outputs
 //     per workgroup, waves of 16 MB x 32, copies straight from global memory
 //     into LDS rings, each wave expanding the code words of its own columns;
-//   gemm_skinny_kernel<MB, D, AFF, SPLIT>  few rows (below);
+//   gemm_skinny_kernel<MB, D, AFF, SPLIT, OCC>  few rows (below);
 //   gemm_narrow_kernel<AFF, SPLIT, LEAD>  up to 32 rows on a matrix of few row
 //     groups, both formats: the waves of a workgroup share one row group;
 //   xsum_kernel           the int4 format's per-group sums of x (pre-pass);
@@ -180,11 +180,10 @@ constexpr int kTileMB = 8, kTileMB8 = 4;
 
 // ---------------------------------------------------------------------------
 // Copies straight from global memory into LDS, shared by the tiled and the
-// skinny kernels, and the 32-copy pair table the skinny kernel uses.
+// skinny kernels, and the copies of the skinny kernel's pair table.
 namespace pipe {
 constexpr int kHalfRow = 64;                    // bytes of one row in one 32-k half
 constexpr int kCopies = 32;                     // pair-table copies (lane % 32)
-constexpr int kTableBytes = 256 * kCopies * 4;
 
 // Wait until at most N of this wave's copies are in flight and its LDS
 // operations are done, then meet the other waves.
@@ -945,15 +944,19 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void gemm_wide_kern
 // ---------------------------------------------------------------------------
 namespace skinny {
 constexpr int kWaves = 4;        // row groups per workgroup
-constexpr int kXBuf = 16 * 1024; // bytes of one x chunk buffer (2 workgroups per CU fit)
+constexpr int kXBuf = 16 * 1024; // bytes of one x chunk buffer (2 or 3 workgroups per CU fit)
 }  // namespace skinny
-// Two workgroups per CU (the launch bound caps a lane at 256 registers): at
-// one wave per SIMD each wave's chain of lookups, products and folds is
-// exposed.  The 32-row instance keeps 4 tiles in flight per wave (8 do not
-// fit in 256 registers).
+// OCC workgroups per CU.  Two (the launch bound caps a lane at 256
+// registers): at one wave per SIMD each wave's chain of lookups, products
+// and folds is exposed; the 32-row instance keeps 4 tiles in flight per wave
+// (8 do not fit in 256 registers).  Three, for grids of more than two rounds
+// of two (gate|up at up to 64 rows: 592 or 1184 workgroups on 256 CUs): 168
+// registers, so half the tiles in flight (4 and 2), and a pair table of 16
+// copies (48 KB of LDS with x); one round of three measured 5-14 % faster
+// than two rounds of two, and slower on grids of one round.
 
-template <int MB, int D, bool AFF, bool SPLIT>
-__global__ __launch_bounds__(64 * skinny::kWaves, 2) void gemm_skinny_kernel(
+template <int MB, int D, bool AFF, bool SPLIT, int OCC>
+__global__ __launch_bounds__(64 * skinny::kWaves, OCC) void gemm_skinny_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ qw,
     const float *__restrict__ am, CodeTerms ct, int N, int K, int KT, int G,
     float *__restrict__ y, const float *__restrict__ xsum, int Mp, int np_arg) {
@@ -967,7 +970,8 @@ __global__ __launch_bounds__(64 * skinny::kWaves, 2) void gemm_skinny_kernel(
   static_assert(D % TC == 0, "the prefetch ring is a whole number of chunks");
   constexpr int XSB = TC * XR * 4;             // x sums of a chunk, bytes (512)
   static_assert(XSB / 16 <= 64 * skinny::kWaves, "one 16-byte load per thread");
-  constexpr int TB = AFF ? 0 : pipe::kTableBytes;  // the affine variant has no table
+  constexpr int SKC = OCC == 3 ? 16 : pipe::kCopies;  // pair-table copies
+  constexpr int TB = AFF ? 0 : 256 * SKC * 4;  // the affine variant has no table
   __shared__ __attribute__((aligned(16))) char lds[2 * skinny::kXBuf + TB + (AFF ? 2 * XSB : 0)];
   char *ldsT = lds + 2 * skinny::kXBuf;
   char *ldsX = ldsT + TB;  // affine: x sums [buffer][tile][row]
@@ -1043,7 +1047,7 @@ __global__ __launch_bounds__(64 * skinny::kWaves, 2) void gemm_skinny_kernel(
   load_x(0, xv);
   __syncthreads();
   for (int c = tid; c < TB / 16; c += 64 * skinny::kWaves) {
-    const int e = c / (pipe::kCopies / 4);
+    const int e = c / (SKC / 4);
     const uint32_t v = (uint32_t)codes16[e & 15] | ((uint32_t)codes16[e >> 4] << 16);
     reinterpret_cast<uint4 *>(ldsT)[c] = make_uint4(v, v, v, v);
   }
@@ -1051,7 +1055,7 @@ __global__ __launch_bounds__(64 * skinny::kWaves, 2) void gemm_skinny_kernel(
   load_x(1, xv);
   __syncthreads();
 
-  const uint32_t tcopy = (uint32_t)(lane & (pipe::kCopies - 1)) * 4;
+  const uint32_t tcopy = (uint32_t)(lane & (SKC - 1)) * 4;
   // K in parts: tot adds the sums of the finished parts in part order; the
   // next part starts at tile `cut`
   f32x4 acc[MB], tot[MB];
@@ -1073,7 +1077,7 @@ __global__ __launch_bounds__(64 * skinny::kWaves, 2) void gemm_skinny_kernel(
           bb[q] = awq_pair(wd, q, 0x3F803F80u);
         } else {
           const uint32_t e = (wd >> (8 * q)) & 0xFFu;
-          bb[q] = *reinterpret_cast<const uint32_t *>(ldsT + e * (pipe::kCopies * 4) + tcopy);
+          bb[q] = *reinterpret_cast<const uint32_t *>(ldsT + e * (SKC * 4) + tcopy);
         }
       }
       B[j] = __builtin_bit_cast(bf16x8, make_uint4(bb[0], bb[1], bb[2], bb[3]));
@@ -1673,12 +1677,18 @@ hipError_t launch_awq_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, cons
                          (int)G, y, X, (int)Mp, np);
     };
     const dim3 g2(gx, (unsigned)((M + 31) / 32));
+    // three workgroups per CU for grids of more than two rounds (32-row
+    // instance; the 16-row one of this format does not fit 168 registers)
+    const bool three = M > 16 && (int64_t)gx * g2.y > 2 * (int64_t)cus;
     if (M <= 16)
-      np > 1 ? go(gemm_skinny_kernel<1, 8, true, true>, dim3(gx))
-             : go(gemm_skinny_kernel<1, 8, true, false>, dim3(gx));
+      np > 1 ? go(gemm_skinny_kernel<1, 8, true, true, 2>, dim3(gx))
+             : go(gemm_skinny_kernel<1, 8, true, false, 2>, dim3(gx));
+    else if (three)
+      np > 1 ? go(gemm_skinny_kernel<2, 2, true, true, 3>, g2)
+             : go(gemm_skinny_kernel<2, 2, true, false, 3>, g2);
     else
-      np > 1 ? go(gemm_skinny_kernel<2, 4, true, true>, g2)
-             : go(gemm_skinny_kernel<2, 4, true, false>, g2);
+      np > 1 ? go(gemm_skinny_kernel<2, 4, true, true, 2>, g2)
+             : go(gemm_skinny_kernel<2, 4, true, false, 2>, g2);
     return hipGetLastError();
   }
   launch_tile<true>(p, x, M, qw, prf, ct, N, K, y, X, Mp, split_ws, s);
@@ -1719,12 +1729,22 @@ hipError_t launch_skinny(const uint16_t *x, int64_t M, const uint8_t *qw, const 
                        nullptr, 0, np);
   };
   const dim3 g2(gx, (unsigned)((M + 31) / 32));
-  if (M <= 16)
-    np > 1 ? go(gemm_skinny_kernel<1, 8, false, true>, dim3(gx))
-           : go(gemm_skinny_kernel<1, 8, false, false>, dim3(gx));
+  // three workgroups per CU (half the tiles in flight, a 16-copy table) for
+  // grids of more than two rounds
+  const bool three = (int64_t)gx * (M <= 16 ? 1 : g2.y) > 2 * (int64_t)device_cu_count();
+  if (M <= 16) {
+    if (three)
+      np > 1 ? go(gemm_skinny_kernel<1, 4, false, true, 3>, dim3(gx))
+             : go(gemm_skinny_kernel<1, 4, false, false, 3>, dim3(gx));
+    else
+      np > 1 ? go(gemm_skinny_kernel<1, 8, false, true, 2>, dim3(gx))
+             : go(gemm_skinny_kernel<1, 8, false, false, 2>, dim3(gx));
+  } else if (three)
+    np > 1 ? go(gemm_skinny_kernel<2, 2, false, true, 3>, g2)
+           : go(gemm_skinny_kernel<2, 2, false, false, 3>, g2);
   else
-    np > 1 ? go(gemm_skinny_kernel<2, 4, false, true>, g2)
-           : go(gemm_skinny_kernel<2, 4, false, false>, g2);
+    np > 1 ? go(gemm_skinny_kernel<2, 4, false, true, 2>, g2)
+           : go(gemm_skinny_kernel<2, 4, false, false, 2>, g2);
   return hipGetLastError();
 }
 

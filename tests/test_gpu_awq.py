@@ -423,3 +423,22 @@ def test_awq_gemm_k_parts_in_a_replayed_graph(side):
         assert t.equal(side.awq_linear("gemm", xd, M, aw, ws=ws).view(t.int32), y0.view(t.int32))
     yr, b = oracle.awq_linear(synth.activations(0, M, K, stream=13)[[0, 299]], packed, scales, zeros)
     assert_linear_ok(y0.cpu().numpy()[[0, 299]], yr, b, "awq gemm K in parts")
+
+
+@pytest.mark.parametrize("N,K", [(33024, 1024), (16512, 8192)])
+def test_awq_gemm_skinny_three_per_cu_rows_identical(side, N, K):
+    """Int4 skinny grids of more than two rounds of two workgroups per CU at
+    17-64 rows (the 32-row instance) run three per CU: rows agree bit for bit
+    with the tiled path (K in one part, and in two at K = 8192), and sampled
+    outputs match the oracle."""
+    say(f"[awq gemm] skinny, three per CU: N={N} K={K}")
+    rows = sample_rows(N, 8)
+    aw, packed, scales, zeros = full_awq_case(side, 4, 72 + (K > 4096), N, K, rows)
+    x = synth.activations(4, 300, K, stream=10)
+    yt = side.awq_run("gemm", x, aw)
+    for lo, hi in ((3, 4), (10, 26), (40, 69), (100, 164)):
+        np.testing.assert_array_equal(side.awq_run("gemm", x[lo:hi], aw), yt[lo:hi],
+                                      err_msg=f"rows {lo}..{hi}")
+    picks = [3, 40, 163, 299]
+    yr, b = oracle.awq_linear(x[picks], packed, scales, zeros)
+    assert_linear_ok(yt[picks][:, rows], yr, b, f"awq three per CU N={N} K={K}")

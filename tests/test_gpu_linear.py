@@ -431,3 +431,23 @@ def test_gemm_k_parts_in_a_replayed_graph(side, cb):
         pw, xd, _ = cases[rep % 2]
         assert t.equal(side.linear("gemm", xd, M, pw, cb, ws=ws).view(t.int32),
                        eager[rep % 2].view(t.int32))
+
+
+@pytest.mark.parametrize("N,K", [(37888, 3584), (33024, 8192)])
+def test_gemm_skinny_three_per_cu_rows_identical(side, cb, N, K):
+    """Skinny grids of more than two rounds of two workgroups per CU (more
+    than 2048 row groups up to 32 rows, 1024 from 33 to 64 rows: gate|up
+    shapes) run three workgroups per CU with half the tiles in flight and a
+    16-copy pair table.  Rows agree bit for bit with the tiled path, with K
+    in one part and in two, and sampled outputs match the oracle."""
+    say(f"[gemm] skinny, three per CU: N={N} K={K}")
+    rows = sample_rows(N, 7)
+    pw, packed, absmax = full_case(side, cb, 4, 70 + (K > 4096), N, K, rows)
+    x = synth.activations(4, 300, K, stream=9)
+    yt = side.run("gemm", x, pw, cb)
+    for M, m0 in ((1, 5), (16, 20), (29, 40), (64, 100)):
+        np.testing.assert_array_equal(side.run("gemm", x[m0:m0 + M], pw, cb), yt[m0:m0 + M],
+                                      err_msg=f"M={M} rows {m0}..")
+    picks = [5, 40, 163, 299]
+    yr, b = oracle.linear(x[picks], packed, absmax, cb)
+    assert_linear_ok(yt[picks][:, rows], yr, b, f"three per CU N={N} K={K}")
