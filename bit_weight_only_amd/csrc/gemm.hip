@@ -1729,9 +1729,20 @@ hipError_t launch_skinny(const uint16_t *x, int64_t M, const uint8_t *qw, const 
                        nullptr, 0, np);
   };
   const dim3 g2(gx, (unsigned)((M + 31) / 32));
+  const int64_t cus = device_cu_count();
   // three workgroups per CU (half the tiles in flight, a 16-copy table) for
   // grids of more than two rounds
-  const bool three = (int64_t)gx * (M <= 16 ? 1 : g2.y) > 2 * (int64_t)device_cu_count();
+  const bool three = (int64_t)gx * (M <= 16 ? 1 : g2.y) > 2 * cus;
+  // 16-row blocks past 16 rows when their grid fits the CUs once, or twice
+  // on long K: twice the waves per row group, each with half the products
+  // per tile (the lookups are repeated per block)
+  const int64_t g16 = (int64_t)gx * ((M + 15) / 16);
+  if (M > 16 && (g16 <= cus || (g16 <= 2 * cus && K >= kSplitK))) {
+    const dim3 g1(gx, (unsigned)((M + 15) / 16));
+    np > 1 ? go(gemm_skinny_kernel<1, 8, false, true, 2>, g1)
+           : go(gemm_skinny_kernel<1, 8, false, false, 2>, g1);
+    return hipGetLastError();
+  }
   if (M <= 16) {
     if (three)
       np > 1 ? go(gemm_skinny_kernel<1, 4, false, true, 3>, dim3(gx))
