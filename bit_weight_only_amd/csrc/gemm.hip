@@ -596,10 +596,11 @@ __global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined tiled kernel (codebook format, 128 x 256 outputs per
-// workgroup): WAVES waves, each owning all 128 rows and 16 / WAVES row
-// groups (8 waves: 128 x 32 each, two per SIMD in one workgroup per CU;
-// 4 waves: 128 x 64 each, one per SIMD, two workgroups per CU).
+// Pipelined tiled kernel (codebook format, 128 x 16 RG outputs per
+// workgroup): WAVES waves, each owning all 128 rows and RG / WAVES row
+// groups (RG 16, 8 waves: 128 x 32 each, two per SIMD in one workgroup per
+// CU; RG 16, 4 waves: 128 x 64 each, one per SIMD, two workgroups per CU;
+// RG 14, 7 waves: 128 x 32 each, one workgroup per CU).
 //
 // What shaped it (measured on MI355X, LDS read rates per CU):
 //  - A fragments: a 16-byte read per lane is conflict free when the four
@@ -632,20 +633,25 @@ __global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
 // P = MFMA(kk=0, zero), MFMA(kk=1, P), acc = fmaf(s, P, acc), in K order.
 // K in np parts (SPLIT) as gemm_tile_kernel.
 namespace wide {
-constexpr int kBM = 128, kMB = 8, kRG = 16;
+constexpr int kBM = 128, kMB = 8;
 constexpr int kXStage = 2 * tile::kAHalf;       // 16 KB: both halves of a step
 constexpr int kStages = 2;
 constexpr int kTable = 256 * 4;                 // pairs of bf16 codes by code byte
 constexpr int kOffX = kTable;
-constexpr int kOffC = kOffX + kStages * kXStage;
-constexpr int kOffS = kOffC + kRG * 2 * kTileBytes;
-constexpr int kBytes = kOffS + kRG * 2 * kTileScales * 4;  // 69 KB
 constexpr int kPrefetch = 3;                    // A blocks read ahead
-template <int WAVES>
+// LDS of a workgroup of RG row groups (69 KB for 16)
+template <int RG>
+struct Lay {
+  static constexpr int kOffC = kOffX + kStages * kXStage;
+  static constexpr int kOffS = kOffC + RG * 2 * kTileBytes;
+  static constexpr int kBytes = kOffS + RG * 2 * kTileScales * 4;
+};
+template <int WAVES, int RG>
 struct Geo {
+  static_assert(RG % WAVES == 0, "row groups split evenly over the waves");
   static constexpr int kThreads = 64 * WAVES;
-  static constexpr int kRGW = kRG / WAVES;               // row groups per wave
-  static constexpr int kXCopies = 16 / WAVES;            // 1 KB copies of x per wave and step
+  static constexpr int kRGW = RG / WAVES;                // row groups per wave
+  static constexpr int kXCopies = (16 + WAVES - 1) / WAVES;  // 1 KB copies of x per wave and step (at most)
   static constexpr int kTileCopies = 2 * kRGW;           // code + scale copies per wave and tile
   static constexpr int kItems = kMB * kRGW;              // items per step
   static constexpr int kWordItem = 2 * kRGW;             // code words of step t + 1
@@ -655,18 +661,19 @@ struct Geo {
 };
 }  // namespace wide
 
-template <int WAVES, bool SPLIT>
+template <int WAVES, int RG, bool SPLIT>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void gemm_wide_kernel(
     const uint16_t *__restrict__ x, int64_t M, const uint8_t *__restrict__ qw,
     const float *__restrict__ am, CodeTerms ct, int64_t N, int64_t K, int64_t KT,
     float *__restrict__ y, int ntn, int ntm, int np_arg, uint32_t *__restrict__ cnt,
     uint64_t *__restrict__ part) {
   namespace W = wide;
-  using Gm = W::Geo<WAVES>;
+  using Gm = W::Geo<WAVES, RG>;
+  using L = W::Lay<RG>;
   constexpr int RGW = Gm::kRGW, PD = W::kPrefetch;
   const int np = SPLIT ? np_arg : 1;
   // the only static LDS array, so the table sits at LDS address 0
-  __shared__ __attribute__((aligned(16))) char lds[W::kBytes];
+  __shared__ __attribute__((aligned(16))) char lds[L::kBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, h = lane >> 4;
@@ -676,7 +683,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void gemm_wide_kern
   if (u >= ntn * np) return;
   const int nt = u / np, kc = u - nt * np;
   const int64_t m0 = (int64_t)mt * W::kBM;
-  const int64_t gblk = (int64_t)nt * W::kRG;
+  const int64_t gblk = (int64_t)nt * RG;
   const int64_t G = N / kTileRows;
   const int t0 = SPLIT ? part_begin(kc, KT, np) : 0;
   const int t1 = SPLIT ? part_begin(kc + 1, KT, np) : (int)KT;
@@ -703,6 +710,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void gemm_wide_kern
 #pragma unroll
     for (int v = 0; v < Gm::kXCopies; ++v) {
       const int i = wave + v * WAVES, blk = i % 8, half = i / 8;
+      if (Gm::kXCopies * WAVES != 16 && i >= 16) break;  // uneven split: scalar branch
       const int64_t r0 = m0 + 16 * blk;
       const uint32_t dst = base + W::kOffX + stage * W::kXStage + half * tile::kAHalf + blk * 1024;
       if (!ragged) {
@@ -724,10 +732,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void gemm_wide_kern
       const int64_t rg = gblk + wave * RGW + q;
       const int64_t g = rg < G ? rg : G - 1;
       const int dst = (q * 2 + (T & 1));
-      copy16_to_lds(base + W::kOffC + (wave * RGW * 2 + dst) * kTileBytes,
+      copy16_to_lds(base + L::kOffC + (wave * RGW * 2 + dst) * kTileBytes,
                     qw + (g * KT + tc) * kTileBytes, lane16);
       if (lane < kTileScales * 4 / 16)
-        copy16_to_lds(base + W::kOffS + (wave * RGW * 2 + dst) * kTileScales * 4,
+        copy16_to_lds(base + L::kOffS + (wave * RGW * 2 + dst) * kTileScales * 4,
                       am + (g * KT + tc) * kTileScales, lane16);
     }
   };
@@ -744,8 +752,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void gemm_wide_kern
   // A fragment: lane (r, h) holds row r of a 16-row block, bf16 8h .. 8h+7
   // of the half
   const char *pa0 = lds + W::kOffX + r * pipe::kHalfRow + ((h ^ ((r >> 1) & 3)) * 16);
-  const char *pc0 = lds + W::kOffC + wave * RGW * 2 * kTileBytes + lane * 16;
-  const char *ps0 = lds + W::kOffS + wave * RGW * 2 * kTileScales * 4 + r * 8;
+  const char *pc0 = lds + L::kOffC + wave * RGW * 2 * kTileBytes + lane * 16;
+  const char *ps0 = lds + L::kOffS + wave * RGW * 2 * kTileScales * 4 + r * 8;
 
   // B fragments (both 32-k halves of the wave's column blocks) and block
   // scales of step t: tile t / 2 in ring slot (t / 2) & 1, quarter 2 (t % 2)
@@ -1527,16 +1535,28 @@ bool prefer_skinny(int64_t M, int64_t N, int64_t K, int nterm, int cus) {
 
 // Tiled launch: 16 row groups per workgroup unless that grid would leave
 // more than half of the CUs idle, then 8 (one workgroup per CU on twice as
-// many CUs); np parts of K multiply the grid by np.
+// many CUs); np parts of K multiply the grid by np.  In the codebook format,
+// with K in parts, a 16-row-group grid of fewer workgroups than CUs takes 14
+// row groups per workgroup (7 waves) when that grid fits the CUs once: down
+// at 1024 rows (224 row groups, K in two parts) then runs 256 workgroups
+// instead of 224, 169 -> 163 us.  The waves of a workgroup share the CU's
+// four SIMDs (2, 2, 2 and 1 of them), so a workgroup of 7 waves takes about
+// as long as one of 8: on q|k|v (K in one part) 14 or 12 row groups gave no
+// gain, and gate|up at 113 rows was 59.3 -> 60.8 us.
 struct TilePlan {
   int rg;
   int64_t nt, mt;
   int np;
 };
-TilePlan tile_plan(int64_t M, int64_t N, int64_t K, int cus) {
+TilePlan tile_plan(int64_t M, int64_t N, int64_t K, int cus, bool wide = false) {
   const int64_t G = N / kTileRows, mt = (M + tile::kBM - 1) / tile::kBM;
   const int np = k_parts(N, K);
-  if (((G + 15) / 16) * mt * np >= cus / 2) return {16, (G + 15) / 16, mt, np};
+  const int64_t w16 = ((G + 15) / 16) * mt * np, w14 = ((G + 13) / 14) * mt * np;
+  // codebook format, K in parts, fewer wide workgroups than CUs: tiles of 14
+  // row groups (7 waves) when their grid still fits the CUs once
+  if (wide && np > 1 && w16 >= cus / 2 && w16 < cus && w14 <= cus)
+    return {14, (G + 13) / 14, mt, np};
+  if (w16 >= cus / 2) return {16, (G + 15) / 16, mt, np};
   return {8, (G + 7) / 8, mt, np};
 }
 
@@ -1553,9 +1573,12 @@ size_t split_bytes_max(int64_t M, int64_t N, int64_t K) {
   const int np = k_parts(N, K);
   if (np == 1) return 0;
   const int64_t G = N / kTileRows, mt = (M + tile::kBM - 1) / tile::kBM;
-  const size_t a = split_bytes(16, ((G + 15) / 16) * mt, np),
-               b = split_bytes(8, ((G + 7) / 8) * mt, np);
-  return a > b ? a : b;
+  size_t best = 0;
+  for (int rg : {16, 14, 8}) {
+    const size_t b = split_bytes(rg, ((G + rg - 1) / rg) * mt, np);
+    if (b > best) best = b;
+  }
+  return best;
 }
 
 template <bool AFF>
@@ -1584,9 +1607,14 @@ void launch_tile(const TilePlan &p, const uint16_t *x, int64_t M, const uint8_t 
                          KT, y, (int)p.nt, (int)p.mt, p.np, cnt, part);
     };
     if (two)
-      split ? gw(gemm_wide_kernel<4, true>, 256) : gw(gemm_wide_kernel<4, false>, 256);
+      split ? gw(gemm_wide_kernel<4, 16, true>, 256) : gw(gemm_wide_kernel<4, 16, false>, 256);
     else
-      split ? gw(gemm_wide_kernel<8, true>, 512) : gw(gemm_wide_kernel<8, false>, 512);
+      split ? gw(gemm_wide_kernel<8, 16, true>, 512) : gw(gemm_wide_kernel<8, 16, false>, 512);
+  } else if (p.rg == 14 && !AFF) {
+    // 128 x 224 tiles, 7 waves of two row groups, one workgroup per CU (the
+    // plan takes them only with K in parts)
+    hipLaunchKernelGGL(gemm_wide_kernel<7, 14, true>, dim3(grid), dim3(448), 0, s, x, M, qw, am,
+                       ct, N, K, KT, y, (int)p.nt, (int)p.mt, p.np, cnt, part);
   } else if (p.rg == 16)
     split ? go(gemm_tile_kernel<16, AFF, kTileMB, true>, 256 * 16 / kTileMB)
           : go(gemm_tile_kernel<16, AFF, kTileMB, false>, 256 * 16 / kTileMB);
@@ -1766,7 +1794,7 @@ hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *qw, const fl
   const int cus = device_cu_count();
   if (prefer_skinny(M, N, K, nterm, cus)) return launch_skinny(x, M, qw, am, ct, N, K, y, s);
   if (nterm == 1 && tile_dma_ok(M, N, K)) {
-    const TilePlan p = tile_plan(M, N, K, cus);
+    const TilePlan p = tile_plan(M, N, K, cus, true);
     if (p.np > 1 && (!ws || ws_bytes < split_bytes(p.rg, p.nt * p.mt, p.np)))
       return hipErrorInvalidValue;
     if (p.np > 1) {

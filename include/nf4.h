@@ -86,8 +86,9 @@ size_t nf4_absmax_bytes(int64_t N, int64_t K);
  * none.  The GEMM needs some only past 64 rows when it sums K in P > 1
  * parts (see nf4_gemm), which it runs on separate workgroups that meet
  * through the workspace: one 4-byte arrival counter per output tile of
- * 128 x 128 or 128 x 256, then every part's sums of every tile (about
- * 4 P M N bytes in all).  0 otherwise, and the workspace arguments may then
+ * 128 x 128, 128 x 224 or 128 x 256 (the largest need of the three tile
+ * widths), then every part's sums of every tile (about 4 P M N bytes in
+ * all).  0 otherwise, and the workspace arguments may then
  * be NULL with 0 bytes.  The workspace needs no initial contents: each call
  * that uses it first clears its counters with a small kernel on its stream.
  * Calls sharing one workspace must be ordered (one stream). */

@@ -99,8 +99,8 @@ def test_linear_validation():
 def split_bytes(M, N, K):
     """Workspace of the tiled GEMM with K in P > 1 parts: per output tile of
     128 rows x 16 RG columns one 4-byte counter (the counters padded to 256
-    bytes) and every part's fp32 sums; the larger of the two workgroup
-    widths RG = 16 and 8."""
+    bytes) and every part's fp32 sums; the largest of the three workgroup
+    widths RG = 16, 14 and 8."""
     P = k_parts(N, K)
     if P == 1:
         return 0
@@ -109,7 +109,7 @@ def split_bytes(M, N, K):
     def width(rg):
         tiles = -(-G // rg) * mt
         return -(-tiles * 4 // 256) * 256 + tiles * P * 128 * 16 * rg * 4
-    return max(width(16), width(8))
+    return max(width(16), width(14), width(8))
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 3584, 18944), (64, 3584, 18944), (65, 3584, 18944),

@@ -451,3 +451,27 @@ def test_gemm_skinny_three_per_cu_rows_identical(side, cb, N, K):
     picks = [5, 40, 163, 299]
     yr, b = oracle.linear(x[picks], packed, absmax, cb)
     assert_linear_ok(yt[picks][:, rows], yr, b, f"three per CU N={N} K={K}")
+
+
+def test_gemm_fourteen_row_group_tiles(side, cb):
+    """A tiled grid with K in parts that would leave CUs idle at 16 row
+    groups per workgroup (N = 3584, K = 8192 in two parts, 600 rows: 140
+    workgroups) runs 14 row groups per workgroup (160): rows equal the
+    skinny path's bit for bit (the ragged last row tile included), a reused
+    workspace full of stale bytes gives the same bits, and sampled outputs
+    match the oracle."""
+    N, K, M = 3584, 8192, 600
+    assert k_parts(N, K) == 2
+    packed, absmax, pw = case(side, cb, N, K, mid=43)
+    x = synth.activations(0, M, K, stream=14)
+    t = side.torch
+    ws = t.full((side.nf4.nf4_workspace_bytes(M, N, K),), 0xFF, dtype=t.uint8, device="cuda")
+    xd = side.x_dev(x)
+    y1 = side.linear("gemm", xd, M, pw, cb, ws=ws).cpu().numpy()
+    np.testing.assert_array_equal(side.linear("gemm", xd, M, pw, cb, ws=ws).cpu().numpy(), y1)
+    for m0 in (0, 536):
+        np.testing.assert_array_equal(side.run("gemm", x[m0:m0 + 64], pw, cb), y1[m0:m0 + 64],
+                                      err_msg=f"rows {m0}..")
+    picks = [0, 127, 128, 511, 599]
+    yr, b = oracle.linear(x[picks], packed, absmax, cb)
+    assert_linear_ok(y1[picks], yr, b, "14 row groups per workgroup")
