@@ -1613,7 +1613,7 @@ void launch_tile(const TilePlan &p, const uint16_t *x, int64_t M, const uint8_t 
   } else if (p.rg == 14 && !AFF) {
     // 128 x 224 tiles, 7 waves of two row groups, one workgroup per CU (the
     // plan takes them only with K in parts)
-    hipLaunchKernelGGL(gemm_wide_kernel<7, 14, true>, dim3(grid), dim3(448), 0, s, x, M, qw, am,
+    hipLaunchKernelGGL((gemm_wide_kernel<7, 14, true>), dim3(grid), dim3(448), 0, s, x, M, qw, am,
                        ct, N, K, KT, y, (int)p.nt, (int)p.mt, p.np, cnt, part);
   } else if (p.rg == 16)
     split ? go(gemm_tile_kernel<16, AFF, kTileMB, true>, 256 * 16 / kTileMB)
