@@ -855,14 +855,24 @@ def int4_leg(torch, nf4, args, s, mdl, launches, prof):
     }
 
 
+# warm-up replays before the dominant kernels are timed: in a fresh process
+# the gate|up GEMV's duration drifts over its first replays (a kernel trace
+# of 63 back-to-back replays of the 28 launches: 16.7 us per launch over
+# replays 0-3, 18-20 us over replays 4-21, 16.5-16.7 us from replay 22 on),
+# so the timed replays start after 30
+DOMINANT_WARM = 30
+
+
 def dominant(torch, s, mdl, amdl, reps, launches):
     """The dominant kernels timed alone, at a fixed point of a run (after the
-    weights are packed and one warm-up replay): 28 gate|up GEMV launches on
-    the 28 layers' distinct matrices replayed back to back in one graph, each
-    naming the next as its read-ahead hint as in a decode step, then the 28
-    gate|up GEMMs (M = 1024) the same way; `reps` timed replays each, events
-    on the launch stream around each replay, the median replay / 28 per
-    launch.  amdl: the same for the int4 group-128 format (or None)."""
+    weights are packed and DOMINANT_WARM warm-up replays): 28 gate|up GEMV
+    launches on the 28 layers' distinct matrices replayed back to back in one
+    graph, each naming the next as its read-ahead hint as in a decode step,
+    then the 28 gate|up GEMMs (M = 1024) the same way; `reps` timed replays
+    each, events on the launch stream around each replay, the median replay
+    / 28 per launch.  The warm-up launches carry labels of their own
+    ("warm:..."), so a kernel trace's mean covers the timed replays only.
+    amdl: the same for the int4 group-128 format (or None)."""
     name = DOMINANT[0]
     res = {}
     for fmt, m in (("nf4", mdl), ("int4", amdl)):
@@ -871,11 +881,13 @@ def dominant(torch, s, mdl, amdl, reps, launches):
         tag = "dom:" if fmt == "nf4" else "dom:int4:"
         res[fmt + "_gemv_us"] = graph_ms(
             torch, s, lambda: [m.gemv(name, l, (name, (l + 1) % LAYERS)) for l in range(LAYERS)],
-            reps) * 1e3 / LAYERS
-        launches += [("gemv", tag + name)] * (LAYERS * (reps + 1))
+            reps, warm=DOMINANT_WARM) * 1e3 / LAYERS
+        launches += [("gemv", "warm:" + tag + name)] * (LAYERS * DOMINANT_WARM) + \
+            [("gemv", tag + name)] * (LAYERS * reps)
         res[fmt + "_gemm_us"] = graph_ms(torch, s, lambda: [m.gemm(name, l) for l in range(LAYERS)],
-                                         reps) * 1e3 / LAYERS
-        launches += [("gemm", tag + name)] * (LAYERS * (reps + 1))
+                                         reps, warm=DOMINANT_WARM) * 1e3 / LAYERS
+        launches += [("gemm", "warm:" + tag + name)] * (LAYERS * DOMINANT_WARM) + \
+            [("gemm", tag + name)] * (LAYERS * reps)
     return res
 
 
