@@ -10,9 +10,13 @@
 // P = sum_k x*c in fp32 (exact products), then acc += s * P.
 //
 // Kernels:
-//   gemm_tile_kernel<RG, AFF, MB, SPLIT>  codebooks whose values are bf16 (the
-//     default one) and the asymmetric int4 format (AFF): 128 x 16 RG outputs
-//     per workgroup, waves of 16 MB x 32, copies straight from global memory
+//   gemm_wide_kernel<WAVES, RG, SPLIT>  codebooks whose values are bf16 (the
+//     default one) on grids of 16 (or 14) row groups per workgroup: 128 x
+//     16 RG outputs, each wave owning all 128 rows of its own row groups,
+//     a pipeline of one barrier per 64-k step;
+//   gemm_tile_kernel<RG, AFF, MB, SPLIT>  the asymmetric int4 format (AFF),
+//     and the codebook format on 8-row-group grids: 128 x 16 RG outputs per
+//     workgroup, waves of 16 MB x 32, copies straight from global memory
 //     into LDS rings, each wave expanding the code words of its own columns;
 //   gemm_skinny_kernel<MB, D, AFF, SPLIT, OCC>  few rows (below);
 //   gemm_narrow_kernel<AFF, SPLIT, LEAD>  up to 32 rows on a matrix of few row
