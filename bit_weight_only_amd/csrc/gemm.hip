@@ -1602,29 +1602,35 @@ void launch_tile(const TilePlan &p, const uint16_t *x, int64_t M, const uint8_t 
     hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, x, M, qw, am, ct, N, K, KT, y,
                        (int)p.nt, (int)p.mt, xsum, Mp, p.np, cnt, part);
   };
-  if (p.rg == 16 && !AFF) {
-    // two 4-wave workgroups per CU when the grid fills two rounds of CUs,
-    // else one workgroup of 8 waves
-    const bool two = (int64_t)grid >= 2 * (int64_t)device_cu_count();
-    auto gw = [&](auto kern, int threads) {
-      hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, x, M, qw, am, ct, N, K,
-                         KT, y, (int)p.nt, (int)p.mt, p.np, cnt, part);
-    };
-    if (two)
-      split ? gw(gemm_wide_kernel<4, 16, true>, 256) : gw(gemm_wide_kernel<4, 16, false>, 256);
-    else
-      split ? gw(gemm_wide_kernel<8, 16, true>, 512) : gw(gemm_wide_kernel<8, 16, false>, 512);
-  } else if (p.rg == 14 && !AFF) {
-    // 128 x 224 tiles, 7 waves of two row groups, one workgroup per CU (the
-    // plan takes them only with K in parts)
-    hipLaunchKernelGGL((gemm_wide_kernel<7, 14, true>), dim3(grid), dim3(448), 0, s, x, M, qw, am,
-                       ct, N, K, KT, y, (int)p.nt, (int)p.mt, p.np, cnt, part);
-  } else if (p.rg == 16)
+  if constexpr (!AFF) {
+    if (p.rg == 16) {
+      // two 4-wave workgroups per CU when the grid fills two rounds of CUs,
+      // else one workgroup of 8 waves
+      const bool two = (int64_t)grid >= 2 * (int64_t)device_cu_count();
+      auto gw = [&](auto kern, int threads) {
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, x, M, qw, am, ct, N, K,
+                           KT, y, (int)p.nt, (int)p.mt, p.np, cnt, part);
+      };
+      if (two)
+        split ? gw(gemm_wide_kernel<4, 16, true>, 256) : gw(gemm_wide_kernel<4, 16, false>, 256);
+      else
+        split ? gw(gemm_wide_kernel<8, 16, true>, 512) : gw(gemm_wide_kernel<8, 16, false>, 512);
+      return;
+    }
+    if (p.rg == 14) {
+      // 128 x 224 tiles, 7 waves of two row groups, one workgroup per CU (the
+      // plan takes them only with K in parts)
+      hipLaunchKernelGGL((gemm_wide_kernel<7, 14, true>), dim3(grid), dim3(448), 0, s, x, M, qw,
+                         am, ct, N, K, KT, y, (int)p.nt, (int)p.mt, p.np, cnt, part);
+      return;
+    }
+  } else if (p.rg == 16) {
     split ? go(gemm_tile_kernel<16, AFF, kTileMB, true>, 256 * 16 / kTileMB)
           : go(gemm_tile_kernel<16, AFF, kTileMB, false>, 256 * 16 / kTileMB);
-  else
-    split ? go(gemm_tile_kernel<8, AFF, kTileMB8, true>, 256 * 8 / kTileMB8)
-          : go(gemm_tile_kernel<8, AFF, kTileMB8, false>, 256 * 8 / kTileMB8);
+    return;
+  }
+  split ? go(gemm_tile_kernel<8, AFF, kTileMB8, true>, 256 * 8 / kTileMB8)
+        : go(gemm_tile_kernel<8, AFF, kTileMB8, false>, 256 * 8 / kTileMB8);
 }
 
 }  // namespace
