@@ -433,16 +433,19 @@ def test_gemm_k_parts_in_a_replayed_graph(side, cb):
                        eager[rep % 2].view(t.int32))
 
 
-@pytest.mark.parametrize("N,K", [(37888, 3584), (33024, 8192)])
+@pytest.mark.parametrize("N,K", [(37888, 3584), (33024, 8192), (33040, 1088)])
 def test_gemm_skinny_three_per_cu_rows_identical(side, cb, N, K):
     """Skinny grids of more than two rounds of two workgroups per CU (more
     than 2048 row groups up to 32 rows, 1024 from 33 to 64 rows: gate|up
     shapes) run three workgroups per CU with half the tiles in flight and a
     16-copy pair table.  Rows agree bit for bit with the tiled path, with K
-    in one part and in two, and sampled outputs match the oracle."""
+    in one part and in two, and with a row-group count that leaves the last
+    workgroup partly empty and a K that ends in a half tile (N = 33040,
+    K = 1088); sampled outputs match the oracle."""
     say(f"[gemm] skinny, three per CU: N={N} K={K}")
     rows = sample_rows(N, 7)
-    pw, packed, absmax = full_case(side, cb, 4, 70 + (K > 4096), N, K, rows)
+    pw, packed, absmax = full_case(side, cb, 4, 70 + (K > 4096) + 2 * (K % 128 != 0), N, K,
+                                   rows)
     x = synth.activations(4, 300, K, stream=9)
     yt = side.run("gemm", x, pw, cb)
     for M, m0 in ((1, 5), (16, 20), (29, 40), (64, 100)):
@@ -453,16 +456,18 @@ def test_gemm_skinny_three_per_cu_rows_identical(side, cb, N, K):
     assert_linear_ok(yt[picks][:, rows], yr, b, f"three per CU N={N} K={K}")
 
 
-def test_gemm_fourteen_row_group_tiles(side, cb):
+@pytest.mark.parametrize("N", [3584, 3328])
+def test_gemm_fourteen_row_group_tiles(side, cb, N):
     """A tiled grid with K in parts that would leave CUs idle at 16 row
-    groups per workgroup (N = 3584, K = 8192 in two parts, 600 rows: 140
-    workgroups) runs 14 row groups per workgroup (160): rows equal the
+    groups per workgroup (K = 8192 in two parts, 600 rows; N = 3584: 140
+    workgroups, N = 3328: 130) runs 14 row groups per workgroup (160 and
+    150; at N = 3328 the last tile holds 12 row groups): rows equal the
     skinny path's bit for bit (the ragged last row tile included), a reused
     workspace full of stale bytes gives the same bits, and sampled outputs
     match the oracle."""
-    N, K, M = 3584, 8192, 600
+    K, M = 8192, 600
     assert k_parts(N, K) == 2
-    packed, absmax, pw = case(side, cb, N, K, mid=43)
+    packed, absmax, pw = case(side, cb, N, K, mid=43 + (N != 3584))
     x = synth.activations(0, M, K, stream=14)
     t = side.torch
     ws = t.full((side.nf4.nf4_workspace_bytes(M, N, K),), 0xFF, dtype=t.uint8, device="cuda")
@@ -474,4 +479,4 @@ def test_gemm_fourteen_row_group_tiles(side, cb):
                                       err_msg=f"rows {m0}..")
     picks = [0, 127, 128, 511, 599]
     yr, b = oracle.linear(x[picks], packed, absmax, cb)
-    assert_linear_ok(y1[picks], yr, b, "14 row groups per workgroup")
+    assert_linear_ok(y1[picks], yr, b, f"14 row groups per workgroup, N={N}")
