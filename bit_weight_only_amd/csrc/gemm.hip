@@ -935,15 +935,17 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void gemm_wide_kern
 }
 
 // ---------------------------------------------------------------------------
-// Skinny path, M <= 64 (a decode batch, a short prefill chunk or the tail of
-// a long one).  There the weights dominate: the job is to stream them at the
-// memory rate, which a K loop synchronised at every step cannot do with few
-// tiles across N.  Instead each wave owns one row group and streams all of
-// its K on its own, like the decode GEMV, keeping kSkD weight tiles in
-// flight in registers; only x is shared, staged in LDS in 16 KB chunks
-// (double buffered, one barrier per chunk).  Per tile the lane's 16 code
-// bytes become the B fragments of four 32-k MFMA steps through the pair
-// table, and the MB m-blocks of x supply the A fragments.
+// Skinny path, M <= 64, and up to 256 rows on narrow N (a decode batch, a
+// short prefill chunk or the tail of a long one).  There the weights
+// dominate: the job is to stream them at the memory rate, which a K loop
+// synchronised at every step cannot do with few tiles across N.  Instead
+// each wave owns one row group and streams all of its K on its own, like the
+// decode GEMV, keeping D weight tiles in flight in registers; only x is
+// shared, staged in LDS in 16 KB chunks (double buffered, one barrier per
+// chunk).  Per tile the lane's 16 code bytes become the B fragments of four
+// 32-k MFMA steps through the pair table, and the MB m-blocks of x (one or
+// two 16-row blocks; more rows as further workgroups along the grid's y)
+// supply the A fragments.
 // Every output is computed with exactly the operations of gemm_tile_kernel:
 // per 64-block P = MFMA(kk=0, zero) then MFMA(kk=1, P), acc = fmaf(s, P, acc)
 // in K order, with the same operand values in the same lanes, so the two
