@@ -114,3 +114,19 @@ def test_write_profiles(tmp_path, prof):
     text = (out / "dominant_kernels_gate_up.md").read_text()
     assert "dom:gate_up" in text and "HBM traffic per launch" in text
     assert prof["dir"] not in text.split("\n", 1)[1]  # temporary paths read <tmp>
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py measures one GPU: --gpus above 1 (or a WORLD_SIZE above 1)
+    exits with status 2 and a message, before touching a GPU or rocprofv3."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for argv, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "4"})):
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), *argv],
+                           capture_output=True, text=True, timeout=120,
+                           env={**os.environ, **env})
+        assert r.returncode == 2, (argv, env, r.returncode, r.stderr[-500:])
+        assert "one GPU" in r.stderr
+        assert r.stdout == ""
