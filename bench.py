@@ -907,7 +907,7 @@ def pmc_pass(torch, nf4, cb, args, s):
     """Counter workload, each step synchronized: a plain device copy of 1 GiB
     (counter calibration), then three gate|up GEMVs on distinct weights, each
     naming the next as its hint, and one gate|up GEMM, in both formats; then
-    down at M = 29."""
+    down and gate|up at M = 29."""
     launches = []
     src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -935,10 +935,17 @@ def pmc_pass(torch, nf4, cb, args, s):
                      dmdl.yp["down"], dmdl.ws, dmdl.ws_bytes)
         s.synchronize()
     launches.append(("gemm", "pmc:c29:down"))
+    # and through gate|up (the skinny kernel, three workgroups per CU)
+    with torch.cuda.stream(s):
+        pw = mdl.weights[0]["gate_up"]
+        nf4.nf4_gemm(mdl.xp[pw.K], CHUNK_M, pw.qweight, pw.absmax, cb, pw.N, pw.K,
+                     mdl.yp["gate_up"], mdl.ws, mdl.ws_bytes)
+        s.synchronize()
+    launches.append(("gemm", "pmc:c29:gate_up"))
     with open(args.launch_log, "w") as f:
         json.dump(launches, f)
     log("[bench] pmc pass: copy 1 GiB, 3 x gate|up gemv, 1 x gate|up gemm, both formats; "
-        "down at M=29")
+        "down and gate|up at M=29")
 
 
 def _kernel_short(name):
