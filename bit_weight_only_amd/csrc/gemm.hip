@@ -1108,8 +1108,11 @@ __global__ __launch_bounds__(64 * skinny::kWaves, OCC) void gemm_skinny_kernel(
     for (int d = 0; d < D; ++d) {
       const int i = base + d;                // tile
       const int tl = d % TC, cbuf = (i / TC) & 1;
-      // Tiles past K run on clamped data and are not folded; neither is the
-      // empty second block of a half tile (selects, not branches).
+      // Tiles past K and the empty second block of a half tile run on
+      // clamped codes and scales and on x that is zero past K, so their
+      // products are exact zeros; they are folded with a zero scale, which
+      // leaves every accumulator as it is (an accumulator is never -0: it
+      // starts at +0 and a zero sum rounds to +0).
       const bool live0 = i < KT, live1 = live0 && !(half_tail && i == KT - 1);
       if (SPLIT && i == cut) {  // the next part of K starts from zero
 #pragma unroll
@@ -1141,22 +1144,28 @@ __global__ __launch_bounds__(64 * skinny::kWaves, OCC) void gemm_skinny_kernel(
           for (int j = 1; j < 4; ++j)
             P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[j], B[j], P, 0, 0, 0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float f = fmaf(sc, fmaf(nz, xz[e], P[e]), acc[mb][e]);
-            acc[mb][e] = live0 ? f : acc[mb][e];
-          }
+          for (int e = 0; e < 4; ++e)
+            acc[mb][e] = fmaf(live0 ? sc : 0.0f, fmaf(nz, xz[e], P[e]), acc[mb][e]);
           continue;
         }
         f32x4 p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0], B[0], zero, 0, 0, 0);
         p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1], B[1], p, 0, 0, 0);
         f32x4 q2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[2], B[2], zero, 0, 0, 0);
         q2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[3], B[3], q2, 0, 0, 0);
+        if constexpr (MB == 1 && OCC == 3) {
+          // selects on the accumulators: the zero-scale form spills here
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float f0 = fmaf(sb[d].x, p[e], acc[mb][e]);
-          const float a0 = live0 ? f0 : acc[mb][e];
-          const float f1 = fmaf(sb[d].y, q2[e], a0);
-          acc[mb][e] = live1 ? f1 : a0;
+          for (int e = 0; e < 4; ++e) {
+            const float f0 = fmaf(sb[d].x, p[e], acc[mb][e]);
+            const float a0 = live0 ? f0 : acc[mb][e];
+            const float f1 = fmaf(sb[d].y, q2[e], a0);
+            acc[mb][e] = live1 ? f1 : a0;
+          }
+        } else {
+          const float s0 = live0 ? sb[d].x : 0.0f, s1 = live1 ? sb[d].y : 0.0f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[mb][e] = fmaf(s1, q2[e], fmaf(s0, p[e], acc[mb][e]));
         }
       }
       // ---- refill this slot D tiles ahead (clamped: same loads every step)
