@@ -206,8 +206,9 @@ __device__ inline void wait_copies_and_barrier() {
 // the lookup address (code byte << 8) | (lane << 2) is one v_perm_b32 and the
 // 64 lanes hit 64 banks.  The 64-k step is split into two 32-k halves, each a
 // separate LDS block laid out [row][32 bf16], with the four 16-byte chunks of
-// a row stored at chunk ^ ((row >> 2) & 3) so that the 16 rows of a fragment
-// read fall in 16 different bank groups.  LDS (bytes): table 64 K at address
+// a row stored at chunk ^ ((row >> 1) & 3), which makes a fragment read free
+// of bank conflicts (the swizzle (row >> 2) & 3 measured 2-5 % slower on the
+// int4 GEMMs at 1024 rows).  LDS (bytes): table 64 K at address
 // 0, x 2 stages x 2 halves x 8 K, and per row group 2 device tiles of code
 // words (1 K each) and of scales (128 each).  Rings, filled by global->LDS
 // copies issued right after the barrier of step t: x of step t+1 (into the
@@ -309,7 +310,7 @@ __global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
   // Copy assignment (W waves).  x: copy i (16 per step, 1 KB each) fills
   // rows 16 (i % 8) .. + 15 of half i / 8; wave w issues i = w, w + W, ...
   // Lane l fills chunk slot l % 4 of row 16 (i % 8) + l / 4, i.e. logical
-  // chunk (l % 4) ^ ((l >> 4) & 3).  Code words and scales: wave w copies
+  // chunk (l % 4) ^ ((l >> 3) & 3).  Code words and scales: wave w copies
   // those of row groups w, w + W, ...  Rows past M and row groups past N
   // re-read the last valid one; their outputs are never stored.
   uint32_t aoff[L::kACopies], mA[L::kACopies];
@@ -318,7 +319,7 @@ __global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
     const int i = wave + v * L::kWaves, blk = i % 8, half = i / 8;
     const int64_t R = m0 + 16 * blk + (lane >> 2);
     const int64_t gm = R < M ? R : M - 1;
-    const int c = (lane & 3) ^ ((lane >> 4) & 3);
+    const int c = (lane & 3) ^ ((lane >> 3) & 3);
     aoff[v] = (uint32_t)((gm * K + half * 32 + c * 8) * 2);
     mA[v] = base + L::kOffA + half * tile::kAHalf + blk * 1024;
   }
@@ -382,7 +383,7 @@ __global__ __launch_bounds__(256 * RG / MB) void gemm_tile_kernel(
   const uint32_t lane4 = (uint32_t)lane << 2;
   // fragments: lane (r, h) holds row r of a 16-row block, bf16 8h .. 8h+7 of the half
   const uint32_t afr = (uint32_t)(wm * 16 * MB * pipe::kHalfRow + r * pipe::kHalfRow +
-                                  ((h ^ ((r >> 2) & 3)) * 16));
+                                  ((h ^ ((r >> 1) & 3)) * 16));
   // this wave's two row groups: code words (16 bytes per lane) and scales
   const char *cw = ldsC + (wn * 2) * 2 * kTileBytes + lane * 16;
   const char *sw = ldsS + (wn * 2) * 2 * kTileScales * 4 + r * (AFF ? 4 : 8);
@@ -1615,9 +1616,12 @@ void launch_tile(const TilePlan &p, const uint16_t *x, int64_t M, const uint8_t 
   };
   if constexpr (!AFF) {
     if (p.rg == 16) {
-      // two 4-wave workgroups per CU when the grid fills two rounds of CUs,
-      // else one workgroup of 8 waves
-      const bool two = (int64_t)grid >= 2 * (int64_t)device_cu_count();
+      // two 4-wave workgroups per CU when the grid holds more workgroups
+      // than CUs, else one workgroup of 8 waves (gate|up at 200 rows, 296
+      // workgroups: 119 us in two rounds of 8 waves, 111 us in one of two
+      // 4-wave workgroups per CU; at 113 rows, 148 workgroups, 8 waves per
+      // CU 64 us, 4 waves 76 us)
+      const bool two = (int64_t)grid > (int64_t)device_cu_count();
       auto gw = [&](auto kern, int threads) {
         hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, x, M, qw, am, ct, N, K,
                            KT, y, (int)p.nt, (int)p.mt, p.np, cnt, part);
