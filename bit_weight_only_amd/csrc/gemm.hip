@@ -1185,8 +1185,8 @@ __global__ __launch_bounds__(64 * skinny::kWaves, OCC) void gemm_skinny_kernel(
         load_x(cn + 1, xv);
         __syncthreads();
       }
-      // keep the next tiles' work from being hoisted across this one
-      __builtin_amdgcn_sched_barrier(0);
+      // (no scheduling barrier between tiles: letting the compiler overlap
+      // consecutive tiles measured 1-3 % faster on most shapes)
     }
   }
 
