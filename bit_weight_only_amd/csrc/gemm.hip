@@ -1489,6 +1489,238 @@ __global__ __launch_bounds__(64 * narrow::kWaves, LEAD == 2 ? 2 : 1) void gemm_n
 }
 
 // ---------------------------------------------------------------------------
+// Stream kernel (codebook format, up to 16 rows, few row groups).  As in the
+// narrow kernel, the four waves of a group share one row group and take its
+// tiles in turn (window j = tiles 4 j .. 4 j + 3 of the group's range, wave w
+// computing tile w), park the block products in LDS and fold them in K order
+// one window later.  What differs:
+//  - a wave reads only its own tile's 128 k of x, so its A fragments, code
+//    words and block scales come straight from global memory into registers,
+//    two windows ahead (a ring of three register slots; the window loop is
+//    unrolled by the ring), and no x is staged in LDS;
+//  - with K in two parts (PG = 2) the workgroup holds two such groups, waves
+//    0-3 folding part 0 and waves 4-7 part 1 side by side, and the group of
+//    part 0 adds the two sums in part order at the end: a long-K matrix of
+//    few row groups (down, N = 3584, K = 18944) runs twice the waves per
+//    row group with no workspace.  With one part (PG = 1) a workgroup is one
+//    group.
+// LDS holds the pair table (32 copies, lane % 32 reads its own) and, per
+// group, the block products and scales of two windows.  Every output gets
+// the other kernels' operations in their order (P = MFMA(kk=0, zero),
+// MFMA(kk=1, P), acc = fmaf(s, P, acc) in K order, parts added in part
+// order), so its rows are bit-identical to theirs.
+// ---------------------------------------------------------------------------
+namespace stream {
+constexpr int kW = 4;     // waves per group = tiles per window
+constexpr int kLead = 2;  // windows loaded ahead
+constexpr int kTable = 256 * 4 * 32;  // pair table, 32 copies
+constexpr int kPBuf = kW * 2 * 1024;  // block products of one window (two 64-blocks per tile)
+constexpr int kSBuf = kW * 16 * 8;    // their scales, a float2 per weight row
+template <int PG>
+struct Lay {
+  static constexpr int kOffP = kTable;                  // [group][window parity]
+  static constexpr int kOffSB = kOffP + PG * 2 * kPBuf;  // [group][window parity]
+  static constexpr int kBytes = kOffSB + PG * 2 * kSBuf;
+};
+}  // namespace stream
+
+template <bool SPLIT, int PG>
+__global__ __launch_bounds__(64 * stream::kW * PG, PG == 1 ? 2 : 1) void gemm_stream_kernel(
+    const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ qw,
+    const float *__restrict__ am, CodeTerms ct, int N, int K, int KT, float *__restrict__ y,
+    int np_arg) {
+  using L = stream::Lay<PG>;
+  constexpr int W = stream::kW, LEAD = stream::kLead;
+  constexpr int S = LEAD + 1;  // register ring slots
+  static_assert(PG == 1 || SPLIT, "two part groups need K in two parts");
+  const int np = SPLIT ? np_arg : 1;
+  // the only static LDS array: the pair table sits at LDS address 0
+  __shared__ __attribute__((aligned(16))) char lds[L::kBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pg = PG == 1 ? 0 : wave / W;      // part group
+  const int ww = PG == 1 ? wave : wave % W;   // wave within the group
+  const int r = lane & 15, h = lane >> 4;
+  const int g = blockIdx.x;                   // row group
+  const int m0 = blockIdx.y * 16;             // first x row
+  const bool half_tail = (K & (kTileK - 1)) != 0;  // last tile holds one 64-block
+  // this group's tiles [t0, t1); part 0 is the longer of two, so both groups
+  // run its number of windows (the other's last window may hold no tile of
+  // its own: it reloads its last tile and folds nothing)
+  const int t0 = PG == 1 ? 0 : part_begin(pg, KT, 2);
+  const int t1 = PG == 1 ? KT : part_begin(pg + 1, KT, 2);
+  const int NW = ((PG == 1 ? KT : part_begin(1, KT, 2)) + W - 1) / W;
+
+  // sources: the lane's x row (rows past M re-read row M - 1, k past K the
+  // row's last chunk: such values only reach products that are never folded
+  // or stored), the row group's code tiles and scales; byte offsets fit 32
+  // bits (checked on the host)
+  const uint32_t xro = (uint32_t)(m0 + r < M ? m0 + r : M - 1) * (uint32_t)K * 2u;
+  const char *xb = reinterpret_cast<const char *>(x);
+  const char *qb = reinterpret_cast<const char *>(qw) + (size_t)g * (size_t)KT * kTileBytes;
+  const char *sb = reinterpret_cast<const char *>(am) + (size_t)g * (size_t)KT * (kTileScales * 4);
+
+  uint4 cw[S];
+  float2 sv[S];
+  bf16x8 A[S][4];
+  // window j of this wave into ring slot SL: tile t0 + W j + ww (past the
+  // group's last tile: that tile again, never folded)
+  auto load = [&](int j, auto slc) {
+    constexpr int SL = decltype(slc)::value;
+    const int i = t0 + j * W + ww;
+    const uint32_t tl = (uint32_t)(i < t1 ? i : t1 - 1);
+    cw[SL] = *reinterpret_cast<const uint4 *>(qb + tl * (uint32_t)kTileBytes + (uint32_t)lane * 16u);
+    sv[SL] = *reinterpret_cast<const float2 *>(sb + tl * (uint32_t)(kTileScales * 4) + (uint32_t)r * 8u);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int k = (int)tl * kTileK + 32 * jj + 8 * h;
+      A[SL][jj] = *reinterpret_cast<const bf16x8 *>(xb + xro + (uint32_t)(k < K ? k : K - 8) * 2u);
+    }
+  };
+
+  // pair table (entry e, copy c at 4 (32 e + c)), from the codebook staged
+  // in the (not yet used) product buffers; built before the first loads are
+  // issued, since the codebook is a vector read of the argument block whose
+  // wait would wait for them too
+  {
+    uint16_t *codes16 = reinterpret_cast<uint16_t *>(lds + L::kOffP);
+    if (tid < 16) codes16[tid] = ct.t[0][tid];
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    for (int i = tid; i < stream::kTable / 16; i += 64 * W * PG) {
+      const int e = i >> 3;  // four copies per 16-byte store
+      const uint32_t v = (uint32_t)codes16[e & 15] | ((uint32_t)codes16[e >> 4] << 16);
+      reinterpret_cast<uint4 *>(lds)[i] = make_uint4(v, v, v, v);
+    }
+  }
+  const uint32_t tcopy = (uint32_t)(lane & 31) * 4u;
+  load(0, std::integral_constant<int, 0>{});
+  load(1, std::integral_constant<int, 1>{});
+
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  char *const pgrp = lds + L::kOffP + pg * 2 * stream::kPBuf;
+  char *const sgrp = lds + L::kOffSB + pg * 2 * stream::kSBuf;
+  // products of this wave's tile of window j (ring slot SL) into buffer j & 1
+  auto compute = [&](int j, auto slc) {
+    constexpr int SL = decltype(slc)::value;
+    const uint4 w = cw[SL];
+    bf16x8 B[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint32_t wd = jj == 0 ? w.x : jj == 1 ? w.y : jj == 2 ? w.z : w.w;
+      uint32_t bb[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        bb[q] = *reinterpret_cast<const uint32_t *>(lds + ((wd >> (8 * q)) & 0xFFu) * 128u + tcopy);
+      B[jj] = __builtin_bit_cast(bf16x8, make_uint4(bb[0], bb[1], bb[2], bb[3]));
+    }
+    char *pb = pgrp + (j & 1) * stream::kPBuf + ww * 2048 + lane * 16;
+    f32x4 p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[SL][0], B[0], zero, 0, 0, 0);
+    p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[SL][1], B[1], p, 0, 0, 0);
+    f32x4 q2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[SL][2], B[2], zero, 0, 0, 0);
+    q2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[SL][3], B[3], q2, 0, 0, 0);
+    *reinterpret_cast<f32x4 *>(pb) = p;
+    *reinterpret_cast<f32x4 *>(pb + 1024) = q2;
+    // the scales of weight row r, once per row
+    if (lane < 16)
+      *reinterpret_cast<float2 *>(sgrp + (j & 1) * stream::kSBuf + ww * 128 + lane * 8) = sv[SL];
+  };
+  // fold: this thread's output is element lane % 4 of output lane
+  // 16 ww + lane / 4 (x row m0 + 4 ww + lane % 4, weight row lane / 4)
+  float acc = 0.0f, tot = 0.0f;
+  int jn = 1, cut = (SPLIT && PG == 1) ? part_begin(1, KT, np) : -1;
+  auto fold_any = [&](int jf, auto wc) {
+    constexpr bool WHOLE = decltype(wc)::value;  // W whole tiles of the group: no selects
+    const char *pb = pgrp + (jf & 1) * stream::kPBuf + ww * 256 + lane * 4;
+    const char *sbp = sgrp + (jf & 1) * stream::kSBuf + (lane >> 2) * 8;
+#pragma unroll
+    for (int tw = 0; tw < W; ++tw) {
+      const int i = t0 + jf * W + tw;
+      if (SPLIT && PG == 1 && i == cut) {  // the next part of K starts from zero
+        tot = jn == 1 ? acc : tot + acc;
+        acc = 0.0f;
+        ++jn;
+        cut = jn < np ? part_begin(jn, KT, np) : -1;
+      }
+      const bool live0 = i < t1, live1 = live0 && !(half_tail && i == KT - 1);
+      const float2 s = *reinterpret_cast<const float2 *>(sbp + tw * 128);
+      const float p0 = *reinterpret_cast<const float *>(pb + tw * 2048);
+      const float p1 = *reinterpret_cast<const float *>(pb + tw * 2048 + 1024);
+      const float f0 = fmaf(s.x, p0, acc);
+      const float a0 = WHOLE || live0 ? f0 : acc;
+      const float f1 = fmaf(s.y, p1, a0);
+      acc = WHOLE || live1 ? f1 : a0;
+    }
+  };
+  // windows of this group whose fold is of W whole tiles
+  const int NWW = (t1 - (half_tail && t1 == KT ? 1 : 0) - t0) / W;
+  auto fold = [&](int jf) {
+    if (jf < NWW)
+      fold_any(jf, std::true_type{});
+    else
+      fold_any(jf, std::false_type{});
+  };
+
+  // window j (ring slot j % S): the products of window j - 1 are in LDS for
+  // every wave, and no wave still folds window j - 2, whose buffer window j
+  // fills.  The steady loop runs whole groups of S windows with nothing but
+  // whole folds and no branch between them, so the compiler's count of the
+  // loads in flight survives the loop's back edge and each window waits only
+  // for its own loads (a loop with branches between the windows waited for
+  // nearly every load in flight).  Every wave meets the same barriers.
+  auto window = [&](int j, auto slc, auto whole) {
+    constexpr int SL = decltype(slc)::value;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    load(j + LEAD, std::integral_constant<int, (SL + LEAD) % S>{});
+    compute(j, slc);
+    if constexpr (decltype(whole)::value)
+      fold_any(j - 1, std::true_type{});
+    else if (j > 0)
+      fold(j - 1);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  static_assert(S == 3, "the steady loop is unrolled by three ring slots");
+  window(0, I0{}, F{});
+  int j = 1;
+  // windows j, j + 1, j + 2 fold windows j - 1, j, j + 1
+  for (; j + S <= NW && j + 2 <= NWW; j += S) {
+    window(j, I1{}, T{});
+    window(j + 1, I2{}, T{});
+    window(j + 2, I0{}, T{});
+  }
+  // the rest, one window at a time, slot by j % S
+  for (; j < NW; ++j) {
+    const int sl = j % S;
+    if (sl == 0)
+      window(j, I0{}, F{});
+    else if (sl == 1)
+      window(j, I1{}, F{});
+    else
+      window(j, I2{}, F{});
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  fold(NW - 1);
+
+  float v = (SPLIT && PG == 1) ? tot + acc : acc;
+  if constexpr (PG == 2) {
+    // part 1's sums through LDS (the product buffers are free once every
+    // wave has folded), added to part 0's in part order
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    float *xch = reinterpret_cast<float *>(lds + L::kOffP);
+    const int gt = tid - pg * 64 * W;  // thread within the group
+    if (pg == 1) xch[gt] = v;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (pg == 1) return;
+    v = v + xch[gt];
+  }
+  const int m = m0 + 4 * ww + (lane & 3);
+  if (m < M) y[(int64_t)m * N + (int64_t)g * 16 + (lane >> 2)] = v;
+}
+
+// ---------------------------------------------------------------------------
 // Pre-pass of the affine GEMM: X[t][m] = sum of x[m][128 t .. 128 t + 127]
 // for m < Mp (zero past M), 16 lanes (a DPP row) per (t, m): each lane adds
 // its 8 values in k order, then row16_sum; the GEMV sums the same way.
@@ -1541,6 +1773,18 @@ bool prefer_narrow(int64_t M, int64_t N, int64_t K) {
 // Narrow launches: three windows ahead at one workgroup per CU when the grid
 // fits the CUs once, else two windows ahead at two per CU.
 inline bool narrow_long_lead(int64_t blocks) { return blocks <= device_cu_count(); }
+// The stream kernel rather than the narrow one (codebook format, same rows):
+// up to 16 rows on a grid that fits the CUs once, with K in one part or in
+// two (then two part groups per workgroup).  Measured per launch (rows
+// bit-identical): down (N = 3584, K = 18944) at 3-12 rows 28.2-28.5 ->
+// 17.8-21.2 us, at 16 rows 28.0 -> 24.6 us; Voxtral's w2 (3072 x 9216) at 4
+// rows 15.6 -> 10.6 us; o (3584 x 3584) at 4 rows 8.1 -> 7.1 us.  q|k|v
+// (288 row groups, more than the CUs) was slower (10.7 -> 12.3 us at 16
+// rows), as were 29- and 32-row batches in 32-row workgroups on the same
+// design (down at 32 rows 40.6 -> 41.3 us).
+inline bool prefer_stream(int64_t M, int64_t G, int np, int cus) {
+  return M <= 16 && np <= 2 && G <= cus;
+}
 
 // The skinny kernel rather than the tiled one (bit-identical rows, so the
 // choice is about speed only): up to 64 rows, and up to 256 rows when the
@@ -1760,6 +2004,15 @@ hipError_t launch_skinny(const uint16_t *x, int64_t M, const uint8_t *qw, const 
   const int64_t G = N / kTileRows;
   if (prefer_narrow(M, N, K)) {
     const int np = k_parts(N, K);
+    if (prefer_stream(M, G, np, device_cu_count())) {
+      const dim3 grid((unsigned)G, (unsigned)((M + 15) / 16)), block(np == 2 ? 512 : 256);
+      auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, block, 0, s, x, (int)M, qw, am, ct, (int)N, (int)K,
+                           (int)tiles_k(K), y, np);
+      };
+      np == 2 ? go(gemm_stream_kernel<true, 2>) : go(gemm_stream_kernel<false, 1>);
+      return hipGetLastError();
+    }
     const dim3 grid((unsigned)G, (unsigned)((M + 15) / 16)), block(64 * narrow::kWaves);
     auto go = [&](auto kern) {
       hipLaunchKernelGGL(kern, grid, block, 0, s, x, (int)M, qw, am, ct, (int)N, (int)K,

@@ -174,6 +174,31 @@ def test_gemm_skinny_and_tiled_rows_identical(side, cb, N, K):
     assert_linear_ok(yt[[0, 17, 299]], yr, b, f"tiled N={N} K={K}")
 
 
+@pytest.mark.parametrize("N,K", [(3584, 18944), (3584, 8256), (3072, 9216), (2048, 8256),
+                                 (3584, 3584), (2048, 704)])
+def test_gemm_stream_rows_identical(side, cb, N, K):
+    """Up to 16 rows on a matrix whose row groups fit the CUs once, with K
+    in one or two parts, run the stream path (x and code words loaded
+    straight into registers; with two parts, two groups of four waves fold
+    part 0 and part 1 side by side and add them in part order).  Its rows
+    equal the tiled path's bit for bit and sampled rows meet the bar against
+    the oracle.  Shapes: down (K in halves of 74 tiles), K = 8256 (halves of
+    33 and 32 tiles, the last one half: part 1's group runs one window with
+    no tile of its own), Voxtral's w2, o (one part, 28 tiles) and a 6-tile K
+    whose last tile is half (no steady loop)."""
+    assert k_parts(N, K) <= 2 and N // 16 <= 256
+    packed, absmax, pw = case(side, cb, N, K, mid=29)
+    x = synth.activations(0, 300, K, stream=4)
+    yt = side.run("gemm", x, pw, cb)            # 300 rows: tiled
+    for M, m0 in ((1, 0), (1, 299), (3, 7), (8, 100), (13, 31), (16, 284)):
+        say(f"[gemm] stream N={N} K={K} M={M} rows {m0}..")
+        np.testing.assert_array_equal(side.run("gemm", x[m0:m0 + M], pw, cb), yt[m0:m0 + M],
+                                      err_msg=f"N={N} K={K} M={M} rows {m0}..")
+    picks = [0, 31, 299]
+    yr, b = oracle.linear(x[picks], packed, absmax, cb)
+    assert_linear_ok(yt[picks], yr, b, f"stream shapes N={N} K={K}")
+
+
 def test_gemm_k_halves_repeat(side, cb):
     """K = 8320 (65 device tiles) at N = 1024 is summed in halves of 33 and 32
     tiles that meet through the workspace: calls with other inputs in
