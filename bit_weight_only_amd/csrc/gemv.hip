@@ -364,7 +364,7 @@ constexpr int kSchedAllButGlobalLoads = 0x1 | 0x2 | 0x4 | 0x8 | 0x80 | 0x100 | 0
 template <int M, bool ARGMAX, bool AFF>
 __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
     const uint4 *__restrict__ qw, const float2 *__restrict__ am, const uint16_t *__restrict__ x,
-    int KT, int G, int P, int K, int N, uint64_t cw0, uint64_t cw1, uint64_t cw2, uint64_t cw3,
+    int KT, int gbase_, int grem_, int K, int N, uint64_t cw0, uint64_t cw1, uint64_t cw2, uint64_t cw3,
     float *__restrict__ y, uint32_t *counter, uint64_t *cand, int32_t *index,
     const char *__restrict__ nq, const char *__restrict__ nsb, int nG, int nKT, int nP) {
   constexpr int D = kFastDepth;
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
   // such block waits again).  The empty asm statement needs them in
   // registers here; the read-ahead cursor, which needs later arguments, is
   // formed after the prefetch.
-  asm volatile("" ::"s"(x), "s"(qw), "s"(am), "s"(N), "s"(K), "s"(KT), "s"(G), "s"(P));
+  asm volatile("" ::"s"(x), "s"(qw), "s"(am), "s"(N), "s"(K), "s"(KT), "s"(gbase_), "s"(grem_));
   const int KP = KT * kTileK;                 // padded x row length
   const int XS = KP + kFastSkew;              // x row stride in LDS
   uint16_t *xs = reinterpret_cast<uint16_t *>(lds_dyn);
@@ -391,11 +391,14 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, h = lane >> 4;
-  // G row groups over P workgroups: the first G % P take one more.  32-bit
-  // arithmetic throughout (a 64-bit division is a long branching sequence,
-  // and the argument loads after each branch wait again).
+  // G row groups over P workgroups: the first G % P take one more.  The host
+  // passes G / P and G % P, so the first weight loads wait for no division
+  // (a per-launch integer division sequence and the x copies' division by
+  // their row length, both before those loads, cost 0.1-0.4 us per launch:
+  // o 4.88 -> 4.76 us, down 11.0 -> 10.4 us at M = 1); 32-bit arithmetic
+  // throughout.
   const uint32_t wg = blockIdx.x;
-  const uint32_t gbase = (uint32_t)G / (uint32_t)P, grem = (uint32_t)G % (uint32_t)P;
+  const uint32_t gbase = (uint32_t)gbase_, grem = (uint32_t)grem_;
   const int g0 = (int)(wg * gbase + (wg < grem ? wg : grem));
   const int Gw = (int)(gbase + (wg < grem ? 1u : 0u)), T0 = g0 * KT, Twg = Gw * KT;
   const int n = Twg > wave ? (Twg - wave + kFastWaves - 1) / kFastWaves : 0;
@@ -425,8 +428,9 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
   if constexpr (!AFF) {
     const int segs = (cpr + 63) / 64;
     const uint32_t xs_base = lds_addr(xs);
-    for (int q = wave; q < M * segs; q += kFastWaves) {
-      const int m = q / segs, seg = q - m * segs;
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+    for (int seg = wave; seg < segs; seg += kFastWaves) {
       const int c = seg * 64 + lane, k = c * 8;
       if (c < cpr && k < K)
         copy16_to_lds(xs_base + (uint32_t)(m * XS + seg * 512) * 2u, x,
@@ -699,7 +703,7 @@ __global__ __launch_bounds__(kFastWaves * 64) void gemv_fast_kernel(
   if constexpr (ARGMAX) {
     // the table is no longer read: its first bytes hold the reduction
     uint64_t *scratch = reinterpret_cast<uint64_t *>(table);
-    amax::finish<M>(bv, bn, blockIdx.x, P, counter, cand, index, scratch,
+    amax::finish<M>(bv, bn, blockIdx.x, (int)gridDim.x, counter, cand, index, scratch,
                     reinterpret_cast<int *>(table) + 2 * kFastWaves * M);
   }
 }
@@ -767,7 +771,8 @@ hipError_t launch_fast(const uint16_t *x, const uint4 *qw, const float2 *am, con
     for (int i = 0; i < 4; ++i) cw[j] |= (uint64_t)ct.t[0][4 * j + i] << (16 * i);
   }
   hipLaunchKernelGGL((gemv_fast_kernel<M, ARGMAX, AFF>), dim3(p.P), dim3(kFastWaves * 64), p.lds, s,
-                     qw, am, x, (int)tiles_k(K), (int)(N / kTileRows), p.P, (int)K, (int)N,
+                     qw, am, x, (int)tiles_k(K), (int)((N / kTileRows) / p.P),
+                     (int)((N / kTileRows) % p.P), (int)K, (int)N,
                      cw[0], cw[1], cw[2], cw[3], y,
                      counter, cand, index, nq, nsb, nG, nKT, nP);
   return hipGetLastError();
