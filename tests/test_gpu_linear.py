@@ -373,6 +373,23 @@ def test_qwen_decode_full_size(side, cb, name, M):
     assert np.all(np.isfinite(y))
 
 
+@pytest.mark.parametrize("M", [3, 8])
+def test_qwen_down_decode_batch(side, cb, M):
+    """A decode batch of 3 to 8 slots through down (K = 18944): x is too long
+    for the fast GEMV's LDS, so nf4_gemv takes the stream path (two groups
+    of four waves fold the two halves of K side by side).  Sampled columns
+    meet the bar against the oracle, and the rows equal nf4_gemm's."""
+    N, K = QWEN_FUSED["down"]
+    say(f"[gemv] qwen down batch M={M}")
+    rows = sample_rows(N, 2)
+    pw, packed, absmax = full_case(side, cb, 2, 61, N, K, rows)
+    x = synth.activations(2, M, K, stream=M)
+    y = side.run("gemv", x, pw, cb)
+    yr, b = oracle.linear(x, packed, absmax, cb)
+    assert_linear_ok(y[:, rows], yr, b, f"qwen down M={M}")
+    np.testing.assert_array_equal(side.run("gemm", x, pw, cb), y)
+
+
 @pytest.mark.parametrize("name", list(QWEN_FUSED))
 def test_qwen_prefill_full_size(side, cb, name):
     """M = 1024 prefill chunk; all N columns on token rows {0, 1023, 6 seeded}."""
