@@ -22,6 +22,8 @@ def test_label_work_decode_and_prefill():
     assert bench.label_work("gemm", "t113:down")[0] == 2 * 113 * 3584 * 18944
     assert bench.label_work("gemm", "c29:o")[0] == 2 * 29 * 3584 * 3584
     assert bench.label_work("gemm", "pmc:c29:down")[0] == 2 * 29 * 3584 * 18944
+    assert bench.label_work("gemm", "c4:gate_up")[0] == 2 * 1024 * 37888 * 3584
+    assert bench.label_work("gemm", "c4t:qkv")[0] == 2 * 113 * 4608 * 3584
     assert bench.label_work("gemv", "nonsense") is None
 
 
