@@ -21,6 +21,10 @@
 //   gemm_skinny_kernel<MB, D, AFF, SPLIT, OCC>  few rows (below);
 //   gemm_narrow_kernel<AFF, SPLIT, LEAD>  up to 32 rows on a matrix of few row
 //     groups, both formats: the waves of a workgroup share one row group;
+//   gemm_stream_kernel<SPLIT, PG>  up to 16 rows on a matrix whose row groups
+//     fit the CUs once (codebook format): as the narrow kernel, with x and the
+//     code words loaded straight into registers and K's two parts folded
+//     side by side;
 //   xsum_kernel           the int4 format's per-group sums of x (pre-pass);
 //   gemm_kernel<3>        any finite codebook (each value split into three
 //     bf16 terms), and shapes whose byte offsets exceed 32 bits.
